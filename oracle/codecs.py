@@ -1,0 +1,198 @@
+"""The four KV codecs, written step by step (encoders in fp32, decoders in fp64).
+
+A row is one (token, KV head) vector of D = 128 fp32 values.  Blocks are 32
+consecutive channels (4 per row).  The codec family and its sizes are the
+buun-llama-cpp page's "Codecs" table (f16 16 bpv, q8_0 8.5 bpv, q4_0 4.5 bpv,
+and the rotated scalar "turbo" codecs); the K=f16 / V=q8_0 pairing is the
+serving contract in the serverAppConfigs commit log (tests/frank_small_unit.bats
+page).  The pages print no encoder arithmetic, so each encoder below states
+its reading.  Shared rules (readings):
+
+* codes are computed from the fp32 scale through its fp32 reciprocal; only the
+  stored scale is rounded to fp16 (round-to-nearest-even);
+* integer rounding is round-half-away-from-zero;
+* a block whose largest magnitude is 0 stores scale +0.0 and the zero code.
+
+Logical outputs (what parity compares, bit for bit):
+  f16   codes uint16[N,128]              (fp16 bits)
+  q8_0  codes int8[N,128], scales uint16[N,4]
+  q4_0  codes uint8[N,128] in 0..15, scales uint16[N,4]
+  rot4  idx uint8[N,128] in 0..15, scales uint16[N,4], norms uint16[N]
+For q4_0 and rot4 the canonical byte packing of block b is
+byte j (0..15) = code[32b + j] | code[32b + j + 16] << 4   (``pack_nibbles``).
+"""
+
+import numpy as np
+
+from .fp import F32, f16_bits, f16_value, rhaz, safe_recip, tree_sum
+from .lloyd_max import codebook
+from .wht import sign_vector, wht
+
+D = 128
+QK = 32
+NB = D // QK
+
+CODECS = ("f16", "q8_0", "q4_0", "rot4")
+
+
+def _rows(x):
+    x = np.asarray(x, dtype=np.float32)
+    assert x.ndim == 2 and x.shape[1] == D, x.shape
+    assert np.all(np.isfinite(x)), "codec inputs must be finite"
+    return x
+
+
+# ----------------------------------------------------------------------- f16
+def quantize_f16(x):
+    """code_j = fp16(x_j), round-to-nearest-even."""
+    return {"codes": f16_bits(_rows(x))}
+
+
+def dequant_f16(q):
+    return f16_value(q["codes"]).astype(np.float64)
+
+
+# ---------------------------------------------------------------------- q8_0
+def quantize_q8_0(x):
+    """q8_0, per 32-value block (BASELINE scale rule amax/127, int8 codes).
+
+    amax = max_j |x_j|; d = amax / 127 (fp32 division); id = 1/d (0 if d = 0);
+    c_j = clamp(RHAZ(x_j * id), -127, 127); stored scale D = fp16(d).
+    """
+    x = _rows(x)
+    xb = x.reshape(-1, NB, QK)
+    amax = np.max(np.abs(xb), axis=-1)
+    d = (amax / F32(127.0)).astype(np.float32)
+    inv = safe_recip(d)
+    prod = (xb * inv[..., None]).astype(np.float32)
+    c = np.clip(rhaz(prod), -127, 127).astype(np.int8)
+    return {"codes": c.reshape(-1, D), "scales": f16_bits(d)}
+
+
+def dequant_q8_0(q):
+    s = f16_value(q["scales"]).astype(np.float64)
+    c = q["codes"].astype(np.float64).reshape(-1, NB, QK)
+    return (c * s[..., None]).reshape(-1, D)
+
+
+# ---------------------------------------------------------------------- q4_0
+def quantize_q4_0(x):
+    """q4_0, per 32-value block (signed-max / -8, offset +8, clamp 0..15).
+
+    j* = first j with |x_j| = amax; m = x_{j*};
+    d = +0.0 if amax == 0 else m / -8 (fp32); id = 1/d (0 if d == 0);
+    c_j = min(15, max(0, RHAZ(x_j * id) + 8)); stored scale D = fp16(d).
+    The clamp only acts on elements within |d|/2 of -m (they would round to +8).
+    """
+    x = _rows(x)
+    xb = x.reshape(-1, NB, QK)
+    a = np.abs(xb)
+    amax = a.max(axis=-1)
+    jstar = np.argmax(a, axis=-1)  # numpy returns the first maximal index
+    m = np.take_along_axis(xb, jstar[..., None], axis=-1)[..., 0]
+    d = np.where(amax == 0, F32(0.0), (m / F32(-8.0)).astype(np.float32)).astype(np.float32)
+    inv = safe_recip(d)
+    prod = (xb * inv[..., None]).astype(np.float32)
+    c = np.clip(rhaz(prod) + 8, 0, 15).astype(np.uint8)
+    return {"codes": c.reshape(-1, D), "scales": f16_bits(d)}
+
+
+def dequant_q4_0(q):
+    s = f16_value(q["scales"]).astype(np.float64)
+    c = q["codes"].astype(np.float64).reshape(-1, NB, QK) - 8.0
+    return (c * s[..., None]).reshape(-1, D)
+
+
+# ---------------------------------------------------------------------- rot4
+def quantize_rot4(x, signs16):
+    """Rotated 4-bit codec (random signs, WHT, fp16 norm, per-32 fp16 RMS scale,
+    16-level Lloyd-Max indices).
+
+    Steps, all fp32, in this order:
+      1. r_j = s_j x_j                      (s = +-1 from the 16-byte sign mask)
+      2. w = WHT(r)                         (unnormalised; stages h = 1..64)
+      3. n = sqrt(tree(x_j * x_j))          (norm of the model-domain row)
+      4. N = fp16(n)
+      5. g = 1/n (0 if n == 0);  u_j = w_j * g        (u has mean square ~1)
+      6. per block b: r_b = sqrt(tree32(u_j * u_j) * 0.03125);  S_b = fp16(r_b)
+      7. ib = 1/r_b (0 if r_b == 0);  t_j = u_j * ib
+      8. idx_j = #{k: t_j > th_k} + #{k: t_j == th_k and t_j >= 0}
+         (15 thresholds; a tie goes to the level farther from zero; 0 -> 8)
+    Reading for the two fp16 fields: the norm is ||x||_2 of the input row and
+    the block scale is the RMS of the norm-whitened rotated block, so N*S_b is
+    the per-block magnitude and the Lloyd-Max levels see unit-variance input.
+    """
+    x = _rows(x)
+    s = sign_vector(signs16)
+    r = np.where(s < 0, -x, x).astype(np.float32)
+    w = wht(r, np.float32)
+    n = np.sqrt(tree_sum((x * x).astype(np.float32))).astype(np.float32)
+    g = safe_recip(n)
+    u = (w * g[:, None]).astype(np.float32)
+    ub = u.reshape(-1, NB, QK)
+    ms = (tree_sum((ub * ub).astype(np.float32)) * F32(0.03125)).astype(np.float32)
+    rb = np.sqrt(ms).astype(np.float32)
+    ib = safe_recip(rb)
+    t = (ub * ib[..., None]).astype(np.float32)
+    _, thr, _ = codebook()
+    tt = t[..., None]
+    idx = (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+    return {
+        "codes": idx.astype(np.uint8).reshape(-1, D),
+        "scales": f16_bits(rb),
+        "norms": f16_bits(n),
+    }
+
+
+def dequant_rot4_rotated(q):
+    """Rotated-domain reconstruction y_j = N * S_b * level[idx_j] / sqrt(128)."""
+    lv, _, _ = codebook()
+    N = f16_value(q["norms"]).astype(np.float64)
+    S = f16_value(q["scales"]).astype(np.float64)
+    c = lv.astype(np.float64)[q["codes"].astype(np.int64)].reshape(-1, NB, QK)
+    y = c * S[..., None] * N[:, None, None] / np.sqrt(128.0)
+    return y.reshape(-1, D)
+
+
+def dequant_rot4(q, signs16):
+    """Model-domain reconstruction x = s * (H y) / sqrt(128), in fp64."""
+    y = dequant_rot4_rotated(q)
+    s = sign_vector(signs16).astype(np.float64)
+    return s * wht(y, np.float64) / np.sqrt(128.0)
+
+
+# ------------------------------------------------------------------ dispatch
+def quantize(codec, x, signs16=None):
+    if codec == "f16":
+        return quantize_f16(x)
+    if codec == "q8_0":
+        return quantize_q8_0(x)
+    if codec == "q4_0":
+        return quantize_q4_0(x)
+    if codec == "rot4":
+        return quantize_rot4(x, signs16)
+    raise ValueError(codec)
+
+
+def dequant(codec, q, signs16=None):
+    if codec == "f16":
+        return dequant_f16(q)
+    if codec == "q8_0":
+        return dequant_q8_0(q)
+    if codec == "q4_0":
+        return dequant_q4_0(q)
+    if codec == "rot4":
+        return dequant_rot4(q, signs16)
+    raise ValueError(codec)
+
+
+def pack_nibbles(codes):
+    """Canonical 4-bit packing of a [N,128] code array into [N,64] bytes:
+    byte 16b + j = code[32b + j] | code[32b + j + 16] << 4."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1, NB, QK)
+    return (c[..., :16] | (c[..., 16:] << 4)).reshape(-1, D // 2)
+
+
+def unpack_nibbles(packed):
+    p = np.asarray(packed, dtype=np.uint8).reshape(-1, NB, 16)
+    return np.concatenate([p & 15, p >> 4], axis=-1).reshape(-1, D)
