@@ -1,0 +1,206 @@
+/*
+ * vit.h -- quantized KV-cache append and flash-decode attention for MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no C++ or torch types.
+ *
+ * What the calls compute.  A decoder layer keeps, per (layer, side), one KV
+ * cache tensor whose codec is chosen per side and per layer: the per-side
+ * cache types (--cache-type-k / --cache-type-v) of the Randozart/VITRIOL page
+ * ("Configuration" flag table) and the per-(layer, side) degrade ladder of
+ * the buun-llama-cpp page ("VBR -- Variable Bit-Rate KV Cache").  Codecs:
+ * f16, q8_0 and q4_0 with 32-value blocks (buun-llama-cpp page, "Codecs"
+ * table) and rot4, a Walsh-Hadamard-rotated 4-bit scalar codec (same table's
+ * rotated "turbo4" row; step 1 of its "How it works" list).  Decode is
+ * flash attention only (buun-llama-cpp page, "Requirements" paragraph), for
+ * grouped-query heads, over a context whose per-sequence capacity is a
+ * multiple of 256 (serverAppConfigs commit log, tests/frank_small_unit.bats
+ * page: the 200,704-token slots "256-aligned for the FA path").
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked [host].  The library never
+ *    allocates or frees device memory; the caller owns every buffer.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.
+ *  - Arguments are validated on the host before anything is enqueued.  On a
+ *    failed validation the call returns a negative vit_status and enqueues
+ *    nothing.  After a launch, a HIP launch error maps to VIT_E_HIP.  Faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - The library keeps no state between calls and is re-entrant.  Two calls
+ *    that write the same cache rows must not run concurrently.
+ *  - head_dim must be 128.  Capacity must be a multiple of 256.  At most 64
+ *    sequences per call; query heads per KV head (G) at most 16.
+ *
+ * ------------------------------------------------------------------------
+ * Codecs (per 128-value row x of one (token, KV head); blocks of 32).
+ *  F16   code_j = fp16(x_j) (round to nearest even).
+ *  Q8_0  d = max|x| / 127 (fp32);  c_j = clamp(round_half_away(x_j / d), +-127)
+ *        computed as x_j * (1/d) in fp32;  scale = fp16(d).
+ *  Q4_0  m = the first x_j of largest magnitude; d = m / -8 (+0.0 if m == 0);
+ *        c_j = clamp(round_half_away(x_j * (1/d)) + 8, 0, 15);  scale = fp16(d).
+ *  ROT4  y = WHT(s .* x) (signs from the 16-byte mask, unnormalised Sylvester
+ *        transform, stages h = 1..64); n = ||x||_2 (stride-halving fp32 sum);
+ *        u = y / n; per block b: r_b = sqrt(mean(u_j^2)); t_j = u_j / r_b;
+ *        idx_j = number of the 15 thresholds below t_j (a value equal to a
+ *        threshold goes to the level farther from zero; 0 -> 8);
+ *        norm = fp16(n), scale_b = fp16(r_b).  Levels: the 16-level
+ *        Lloyd-Max quantizer for N(0,1), stored as fp16; thresholds are the
+ *        midpoints of adjacent levels.  Reconstruction in the rotated domain
+ *        is norm * scale_b * level[idx_j] / sqrt(128); the model-domain row is
+ *        s .* (WHT(that) / sqrt(128)).
+ *
+ * ------------------------------------------------------------------------
+ * Physical layout of one cache plane (one (layer, side) tensor).
+ * Rows of a (sequence, KV head) form a stream of `capacity` rows stored as
+ * tiles of 32 positions; plane index ph = seq * n_kv_heads + head.
+ *
+ *  codes   ph * capacity * RB bytes per stream, RB = 256 (F16), 128 (Q8_0),
+ *          64 (Q4_0, ROT4) bytes per row; a tile is 32 * RB bytes.
+ *  scales  fp16 [S][H][capacity/32][4][32]: scale of (tile t, block b, row p)
+ *          at ((ph * capacity/32 + t) * 4 + b) * 32 + p.  NULL for F16.
+ *  norms   fp16 [S][H][capacity] (ROT4 only; NULL otherwise).
+ *
+ *  A K-side tile ("row-major units") is two 16-row halves h = 0, 1; row r of
+ *  half h is position p = 8*(r>>2) + 4*h + (r&3).  Each half holds 16-byte
+ *  units U[c][b][r] (c < CB, b = block 0..3, r = row 0..15), unit byte offset
+ *  (((h*CB + c)*4 + b)*16 + r)*16, CB = RB/64.  A unit holds block b's
+ *  canonical bytes [16c, 16c+16) of that row:
+ *    F16: fp16 of channels 32b+8c .. 32b+8c+7;  Q8_0: int8 codes of channels
+ *    32b+16c .. +15;  Q4_0/ROT4: byte j = code[32b+j] | code[32b+j+16] << 4.
+ *  A V-side tile ("column units") stores, for each channel ch (N-tile
+ *  nt = ch>>4, n = ch&15) and each group of 8 positions g8 = p>>3, the 8
+ *  codes of positions 8*g8 .. 8*g8+7 of that channel:
+ *    F16 : 16 B at ((nt*4 + g8)*16 + n)*16, fp16 of position 8*g8+j at 2*j;
+ *    Q8_0: 8 B at ((nt>>1)*4 + g8)*16 + n)*16 + 8*(nt&1), position j at byte
+ *          P8[j], P8 = {0,2,1,3,4,6,5,7};
+ *    Q4_0: 4 B at ((nt>>2)*4 + g8)*16 + n)*16 + 4*(nt&3), position j in byte
+ *          Q4B[j] = {0,2,1,3,0,2,1,3}[j], low nibble for j < 4, high for j >= 4;
+ *    ROT4: 4 B as Q4_0, position j in byte j>>1, low nibble for even j.
+ *  K and V planes of the same codec differ only in this code layout (the
+ *  plane's side field); their sizes are equal.
+ *
+ * Input domain of the encoders: finite values; a nonzero 32-value block has
+ * largest magnitude >= 2^-100 (so the fp32 reciprocal of its scale is finite);
+ * stored fp16 scales and norms stay below 65504.  Outside it the codes are
+ * deterministic but unspecified.
+ *
+ * Sign mask (ROT4): 16 bytes, bit (j & 7) of byte (j >> 3) set => channel j
+ * is negated before the transform.  One mask per (layer, side).
+ */
+#ifndef VIT_H
+#define VIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vit_codec {
+  VIT_CODEC_F16 = 0,
+  VIT_CODEC_Q8_0 = 1,
+  VIT_CODEC_Q4_0 = 2,
+  VIT_CODEC_ROT4 = 3
+} vit_codec;
+
+typedef enum vit_side { VIT_SIDE_K = 0, VIT_SIDE_V = 1 } vit_side;
+
+typedef enum vit_status {
+  VIT_OK = 0,
+  VIT_E_ARG = -1,         /* bad value, NULL required pointer, k_new xor v_new */
+  VIT_E_UNSUPPORTED = -2, /* head_dim != 128, G > 16, > 64 sequences, unknown codec */
+  VIT_E_CAPACITY = -3,    /* rows outside 0..capacity-1, capacity % 256 != 0 */
+  VIT_E_ALIGN = -4,       /* plane pointer not 256-B aligned, other pointer not 16-B aligned */
+  VIT_E_HIP = -5          /* a HIP launch failed */
+} vit_status;
+
+#define VIT_HEAD_DIM 128
+#define VIT_CAPACITY_ALIGN 256
+#define VIT_MAX_SEQS 64
+#define VIT_MAX_GQA 16
+#define VIT_MAX_SPLITS 4096
+
+/* One (layer, side) cache tensor: caller-owned device memory in the layout
+ * above.  `signs` is a [host] pointer to 16 bytes (ROT4 only, else NULL),
+ * read during the call. */
+typedef struct vit_kv_plane {
+  int32_t codec;       /* vit_codec */
+  int32_t side;        /* vit_side: selects the K or V code layout */
+  int32_t n_seqs;
+  int32_t n_kv_heads;
+  int32_t head_dim;    /* must be 128 */
+  int32_t reserved;    /* must be 0 */
+  int64_t capacity;    /* rows per (sequence, KV head); multiple of 256 */
+  void *codes;
+  uint16_t *scales;    /* fp16 bits; NULL for F16 */
+  uint16_t *norms;     /* fp16 bits; ROT4 only, else NULL */
+  const uint8_t *signs;/* [host] 16 bytes; ROT4 only, else NULL */
+} vit_kv_plane;
+
+/* Byte sizes of the three arrays of a plane (host only, no device work).
+ * Returns VIT_OK or a negative status; any out pointer may be NULL. */
+int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_t head_dim,
+                       int64_t capacity, size_t *codes_bytes, size_t *scales_bytes,
+                       size_t *norms_bytes);
+
+/* Quantize new K or V rows and store them in a plane (the append of a
+ * ubatch of new tokens: buun-llama-cpp page, "Codecs" table for the codecs;
+ * serverAppConfigs commit log for ubatch <= batch and the 2048-row ubatch).
+ *  src     fp32 [n_seqs][n_tokens][n_kv_heads][128], 16-B aligned.
+ *  pos0    [host] int64 [n_seqs]: row of token 0 of each sequence; rows
+ *          pos0[s] .. pos0[s]+n_tokens-1 are written (VIT_E_CAPACITY if any
+ *          lies outside 0..capacity-1).  n_tokens == 0 is a no-op.
+ * Codes and fp16 scales are bit-exact with the codec definitions above.
+ * Rows not in the range are left untouched. */
+int vit_kv_append_quant(const vit_kv_plane *dst, const float *src, const int64_t *pos0,
+                        int32_t n_tokens, void *stream);
+
+/* Workspace bytes vit_attn_decode needs for n_splits > 1: fp32 partial
+ * outputs [S][Hq][n_splits][128] followed by (max, sum) pairs
+ * [S][Hq][n_splits][2].  Returns 0 for invalid sizes. */
+size_t vit_attn_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,
+                                int32_t n_splits);
+
+/* A split count that fills the GPU for this shape (host heuristic). */
+int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_heads,
+                                int64_t max_seq_len);
+
+/* Decode attention for one new query token per sequence over rows
+ * 0 .. seq_len[s]-1 of its KV head (grouped-query: kv_head = q_head / G,
+ * G = n_q_heads / n_kv_heads), dequantizing K and V on the fly.
+ *  k, v      planes with equal n_seqs, n_kv_heads, capacity; sides K and V.
+ *  q         fp32 [n_seqs][n_q_heads][128] in the model domain.
+ *  seq_len   [host] int64 [n_seqs], 1 .. capacity, counting the new row.
+ *  k_new, v_new  optional fp32 [n_seqs][n_kv_heads][128]: when given (both or
+ *            neither), the new token's K and V rows are quantized and stored
+ *            at row seq_len[s]-1 first, exactly as vit_kv_append_quant would.
+ *  scale     softmax scale (typically 1/sqrt(128)).
+ *  n_splits  1 .. VIT_MAX_SPLITS.  The context of each sequence is cut into
+ *            n_splits contiguous ranges of whole 32-row tiles (some may be
+ *            empty).  With n_splits == 1 the normalised output is written to
+ *            `out` and `workspace` may be NULL; otherwise partials go to
+ *            `workspace` and vit_attn_splitk_reduce produces `out`.
+ *  out       fp32 [n_seqs][n_q_heads][128], model domain.
+ * The result equals softmax(scale * q K^T) V over the dequantized rows to
+ * fp32 accumulation accuracy (not bitwise across split counts). */
+int vit_attn_decode(const vit_kv_plane *k, const vit_kv_plane *v, const float *q,
+                    int32_t n_q_heads, const int64_t *seq_len, const float *k_new,
+                    const float *v_new, float scale, int32_t n_splits, float *workspace,
+                    float *out, void *stream);
+
+/* Merge the split partials of vit_attn_decode: M = max m_s,
+ * L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L (max values are kept
+ * in base-2 units); for a ROT4 V plane the merged row is rotated back to the
+ * model domain with v's sign mask.  `v` is read only for its codec and signs.
+ *  out  fp32 [n_seqs][n_q_heads][128]. */
+int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_heads,
+                           int32_t head_dim, int32_t n_splits, const vit_kv_plane *v,
+                           float *out, void *stream);
+
+/* A static string for a status code. */
+const char *vit_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIT_H */

@@ -13,6 +13,11 @@ its reading.  Shared rules (readings):
 * integer rounding is round-half-away-from-zero;
 * a block whose largest magnitude is 0 stores scale +0.0 and the zero code.
 
+Domain: finite inputs; every nonzero 32-value block has largest magnitude at
+least 2^-100 (below that the fp32 reciprocal of the scale overflows and
+0 * inf leaves the codes undefined) and the stored fp16 fields do not overflow.
+The encoders assert the first two conditions.
+
 Logical outputs (what parity compares, bit for bit):
   f16   codes uint16[N,128]              (fp16 bits)
   q8_0  codes int8[N,128], scales uint16[N,4]
@@ -35,11 +40,19 @@ NB = D // QK
 CODECS = ("f16", "q8_0", "q4_0", "rot4")
 
 
+MIN_BLOCK_MAX = np.float32(2.0 ** -100)
+
+
 def _rows(x):
     x = np.asarray(x, dtype=np.float32)
     assert x.ndim == 2 and x.shape[1] == D, x.shape
     assert np.all(np.isfinite(x)), "codec inputs must be finite"
     return x
+
+
+def _check_block_domain(xb):
+    amax = np.max(np.abs(xb), axis=-1)
+    assert np.all((amax == 0) | (amax >= MIN_BLOCK_MAX)), "block maximum below 2^-100 is outside the domain"
 
 
 # ----------------------------------------------------------------------- f16
@@ -61,6 +74,7 @@ def quantize_q8_0(x):
     """
     x = _rows(x)
     xb = x.reshape(-1, NB, QK)
+    _check_block_domain(xb)
     amax = np.max(np.abs(xb), axis=-1)
     d = (amax / F32(127.0)).astype(np.float32)
     inv = safe_recip(d)
@@ -86,6 +100,7 @@ def quantize_q4_0(x):
     """
     x = _rows(x)
     xb = x.reshape(-1, NB, QK)
+    _check_block_domain(xb)
     a = np.abs(xb)
     amax = a.max(axis=-1)
     jstar = np.argmax(a, axis=-1)  # numpy returns the first maximal index

@@ -1,0 +1,183 @@
+"""Quantized KV-cache append and flash-decode attention for MI355X (gfx950).
+
+The compute lives in libvit.so (hand-written HIP kernels behind the C ABI of
+include/vit.h).  This module only marshals torch tensors into those calls:
+PyTorch provides device memory and the stream, nothing else.  The Python
+names mirror the C entry points:
+
+    vit_kv_plane_sizes, vit_kv_append_quant, vit_attn_workspace_bytes,
+    vit_attn_default_splits, vit_attn_decode, vit_attn_splitk_reduce
+
+``KVPlane`` allocates the three arrays of one (layer, side) cache tensor.
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _lib, layout
+from ._lib import CODEC_IDS, SIDE_IDS, VitError, VitKvPlane
+
+__all__ = [
+    "KVPlane", "VitError", "layout",
+    "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_attn_workspace_bytes",
+    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_splitk_reduce",
+]
+
+HEAD_DIM = 128
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _fptr(t, name, dtype_name="float32"):
+    import torch
+
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if str(t.dtype) != f"torch.{dtype_name}":
+        raise TypeError(f"{name} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def vit_kv_plane_sizes(codec, n_seqs, n_kv_heads, head_dim, capacity):
+    """(codes_bytes, scales_bytes, norms_bytes) of one plane."""
+    lib = _lib.load()
+    c, s, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = lib.vit_kv_plane_sizes(CODEC_IDS[codec] if isinstance(codec, str) else int(codec),
+                                n_seqs, n_kv_heads, head_dim, capacity,
+                                ctypes.byref(c), ctypes.byref(s), ctypes.byref(n))
+    _lib.check("vit_kv_plane_sizes", st)
+    return c.value, s.value, n.value
+
+
+class KVPlane:
+    """One (layer, side) KV cache tensor in device memory (torch-allocated).
+
+    ``side`` is "k" or "v"; ``signs`` (rot4 only) is the 16-byte sign mask,
+    kept on the host and passed by value at each call.
+    """
+
+    def __init__(self, codec, side, n_seqs, n_kv_heads, capacity, signs=None, device="cuda"):
+        import torch
+
+        self.codec, self.side = codec, side
+        self.n_seqs, self.n_kv_heads, self.capacity = n_seqs, n_kv_heads, capacity
+        cb, sb, nb = vit_kv_plane_sizes(codec, n_seqs, n_kv_heads, HEAD_DIM, capacity)
+        self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb // 2, dtype=torch.int16, device=device) if sb else None
+        self.norms = torch.empty(nb // 2, dtype=torch.int16, device=device) if nb else None
+        if codec == "rot4":
+            if signs is None:
+                raise ValueError("rot4 planes need a 16-byte sign mask")
+            self.signs = np.ascontiguousarray(signs, dtype=np.uint8).reshape(16).copy()
+        else:
+            self.signs = None
+
+    @classmethod
+    def like(cls, other, device="cuda"):
+        return cls(other.codec, other.side, other.n_seqs, other.n_kv_heads, other.capacity,
+                   other.signs, device)
+
+    def struct(self):
+        p = VitKvPlane()
+        p.codec = CODEC_IDS[self.codec]
+        p.side = SIDE_IDS[self.side]
+        p.n_seqs, p.n_kv_heads, p.head_dim, p.reserved = self.n_seqs, self.n_kv_heads, HEAD_DIM, 0
+        p.capacity = self.capacity
+        p.codes = self.codes.data_ptr()
+        p.scales = self.scales.data_ptr() if self.scales is not None else None
+        p.norms = self.norms.data_ptr() if self.norms is not None else None
+        p.signs = self.signs.ctypes.data if self.signs is not None else None
+        return p
+
+    def tensors(self):
+        return [t for t in (self.codes, self.scales, self.norms) if t is not None]
+
+    def copy_from(self, other):
+        for a, b in zip(self.tensors(), other.tensors()):
+            a.copy_(b, non_blocking=True)
+
+    def host_view(self):
+        """Logical contents on the host: dict(codes, scales, norms) shaped per row."""
+        S, H, cap = self.n_seqs, self.n_kv_heads, self.capacity
+        out = {"codes": layout.unpack_codes(self.codec, self.side, self.codes.cpu().numpy(), S, H, cap)}
+        if self.scales is not None:
+            out["scales"] = layout.unpack_scales(self.scales.cpu().numpy().view(np.uint16), S, H, cap)
+        if self.norms is not None:
+            out["norms"] = layout.unpack_norms(self.norms.cpu().numpy().view(np.uint16), S, H, cap)
+        return out
+
+
+def vit_kv_append_quant(plane, src, pos0, n_tokens=None, stream=None):
+    """Quantize src fp32 [S, T, Hkv, 128] into rows pos0[s] .. pos0[s]+T-1."""
+    lib = _lib.load()
+    if n_tokens is None:
+        n_tokens = src.shape[1]
+    p0 = (ctypes.c_int64 * len(pos0))(*[int(x) for x in pos0])
+    p = plane.struct()
+    st = lib.vit_kv_append_quant(ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
+    return _lib.check("vit_kv_append_quant", st)
+
+
+def vit_attn_workspace_bytes(n_seqs, n_q_heads, head_dim, n_splits):
+    return int(_lib.load().vit_attn_workspace_bytes(n_seqs, n_q_heads, head_dim, n_splits))
+
+
+def vit_attn_default_splits(n_seqs, n_kv_heads, n_q_heads, max_seq_len):
+    return int(_lib.load().vit_attn_default_splits(n_seqs, n_kv_heads, n_q_heads, int(max_seq_len)))
+
+
+def vit_attn_decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_splits=1,
+                    workspace=None, out=None, stream=None):
+    """Decode attention; returns ``out`` (fp32 [S, Hq, 128]), which holds the
+    result only when n_splits == 1 (otherwise call vit_attn_splitk_reduce)."""
+    import torch
+
+    lib = _lib.load()
+    if scale is None:
+        scale = 1.0 / np.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((k.n_seqs, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    st = lib.vit_attn_decode(ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), sl,
+                             _fptr(k_new, "k_new"), _fptr(v_new, "v_new"), float(scale), int(n_splits),
+                             _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
+                             _fptr(out, "out"), _stream_handle(stream))
+    _lib.check("vit_attn_decode", st)
+    return out
+
+
+def vit_attn_splitk_reduce(workspace, n_seqs, n_q_heads, head_dim, n_splits, v, out, stream=None):
+    lib = _lib.load()
+    vp = v.struct()
+    st = lib.vit_attn_splitk_reduce(_fptr(workspace, "workspace", "uint8"), int(n_seqs), int(n_q_heads),
+                                    int(head_dim), int(n_splits), ctypes.byref(vp), _fptr(out, "out"),
+                                    _stream_handle(stream))
+    return _lib.check("vit_attn_splitk_reduce", st)
+
+
+def decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_splits=None,
+           workspace=None, out=None, stream=None):
+    """vit_attn_decode followed (when n_splits > 1) by vit_attn_splitk_reduce."""
+    import torch
+
+    if n_splits is None:
+        n_splits = vit_attn_default_splits(k.n_seqs, k.n_kv_heads, n_q_heads, max(seq_len))
+    if n_splits > 1 and workspace is None:
+        workspace = torch.empty(vit_attn_workspace_bytes(k.n_seqs, n_q_heads, HEAD_DIM, n_splits),
+                                dtype=torch.uint8, device=q.device)
+    out = vit_attn_decode(k, v, q, n_q_heads, seq_len, k_new, v_new, scale, n_splits, workspace, out, stream)
+    if n_splits > 1:
+        vit_attn_splitk_reduce(workspace, k.n_seqs, n_q_heads, HEAD_DIM, n_splits, v, out, stream)
+    return out

@@ -1,0 +1,7 @@
+// Decode kernels with K codec 3 (see decode_impl.h); one file per K codec so
+// the 16 codec pairs x 3 row-group counts compile in parallel.
+#include "decode_impl.h"
+
+namespace vit {
+VIT_DECODE_FOR_K(3)
+}  // namespace vit

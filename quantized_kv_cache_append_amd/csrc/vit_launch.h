@@ -1,0 +1,63 @@
+// Kernel argument blocks and launch entry points (host <-> kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vit {
+
+constexpr int kMaxSeqs = 64;
+
+struct AppendArgs {
+  void* codes;
+  uint16_t* scales;
+  uint16_t* norms;
+  const float* src;
+  int64_t capacity;
+  int32_t n_kv_heads;
+  int32_t n_tokens;
+  uint32_t signs[4];
+  int64_t pos0[kMaxSeqs];
+};
+
+struct DecodeArgs {
+  const uint8_t* kcodes;
+  const uint16_t* kscales;
+  const uint16_t* knorms;
+  const uint8_t* vcodes;
+  const uint16_t* vscales;
+  const uint16_t* vnorms;
+  const float* q;
+  float* ws_o;     // [S][Hq][n_splits][128]
+  float* ws_ml;    // [S][Hq][n_splits][2]
+  float* out;      // [S][Hq][128]
+  int64_t capacity;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t gqa;
+  int32_t n_splits;
+  float qscale;    // softmax scale * log2(e)
+  uint32_t ksigns[4];
+  uint32_t vsigns[4];
+  int32_t seq_len[kMaxSeqs];
+};
+
+struct ReduceArgs {
+  const float* ws_o;
+  const float* ws_ml;
+  float* out;
+  int32_t n_q_heads;
+  int32_t n_splits;
+  int32_t rotate;  // 1: V codec is rot4, rotate the merged row back
+  uint32_t vsigns[4];
+};
+
+hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
+hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
+
+}  // namespace vit

@@ -1,0 +1,89 @@
+"""Shared helpers of the GPU parity tests (not a test module).
+
+Inputs come from ``synth`` (seeded) or from seeded numpy generators; expected
+values come only from ``oracle``.  The HIP path is reached only through the
+C ABI (``quantized_kv_cache_append_amd``)."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention, codecs
+
+TOL = 2e-3  # max |o - ref| <= TOL * RMS(ref)
+
+
+def torch_cuda():
+    import torch
+
+    if torch.cuda.device_count() == 0:
+        pytest.skip("no GPU visible")
+    return torch
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_plane(codec, side, S, H, cap, signs=None, poison=True):
+    from quantized_kv_cache_append_amd import KVPlane
+
+    p = KVPlane(codec, side, S, H, cap, signs)
+    if poison:
+        for t in p.tensors():
+            t.fill_(-1)  # all bits set: 0xFF codes, NaN fp16 scales / norms
+    return p
+
+
+def append_rows(plane, rows_host, pos0, stream=None):
+    """rows_host fp32 [S, T, H, 128] -> device -> vit_kv_append_quant."""
+    import torch
+
+    from quantized_kv_cache_append_amd import vit_kv_append_quant
+
+    src = torch.from_numpy(np.ascontiguousarray(rows_host, dtype=np.float32)).cuda()
+    vit_kv_append_quant(plane, src, pos0, stream=stream)
+    return src
+
+
+def oracle_quant(codec, rows, signs):
+    """Oracle codes of rows [N, 128] as (codes, scales, norms) arrays."""
+    q = codecs.quantize(codec, rows, signs)
+    return q["codes"], q.get("scales"), q.get("norms")
+
+
+def compare_plane_rows(plane, view, s, h, rows_idx, rows_fp32):
+    """Bit-exact comparison of rows of one (seq, head) against the oracle."""
+    c, sc, nm = oracle_quant(plane.codec, rows_fp32, plane.signs)
+    got = view["codes"][s, h, rows_idx]
+    if plane.codec == "q8_0":
+        got = got.astype(np.int8)
+    bad = np.argwhere(got != c)
+    assert bad.size == 0, f"{plane.codec}/{plane.side} code mismatch at rows {rows_idx[bad[:5, 0]]} ch {bad[:5, 1]}"
+    if sc is not None:
+        assert np.array_equal(view["scales"][s, h, rows_idx], sc), f"{plane.codec} scale mismatch"
+    if nm is not None:
+        assert np.array_equal(view["norms"][s, h, rows_idx], nm), f"{plane.codec} norm mismatch"
+
+
+def ref_unit(q_rows, k_rows, v_rows, kc, vc, scale, ks=None, vs=None):
+    return attention.decode_reference(q_rows, k_rows, v_rows, kc, vc, scale, ks, vs)
+
+
+def check_close(got, ref, what, tol=TOL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  {what}: max|err| / rms = {err / rms:.3e} (rms {rms:.3e})")
+    assert err <= tol * rms, f"{what}: max err {err:.3e} > {tol} x rms {rms:.3e}"
+    return err / rms
+
+
+__all__ = ["oracle", "torch_cuda", "say", "make_plane", "append_rows", "compare_plane_rows",
+           "ref_unit", "check_close", "TOL"]

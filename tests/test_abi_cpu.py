@@ -1,0 +1,185 @@
+"""C ABI checks that need no GPU: exports, sizes, and every validation path.
+
+Validation runs on the host before anything is enqueued, so these calls use
+fake (never dereferenced) device addresses and must return an error status.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_kv_cache_append_amd import _lib, layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vit.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(vit_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declarations_are_all_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 7, names
+    assert sorted(_lib.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_string(s)
+    assert _lib.status_string(7) == "unknown status"
+
+
+@pytest.mark.parametrize("codec,rb,sb,nb", [(0, 256, 0, 0), (1, 128, 8, 0), (2, 64, 8, 0), (3, 64, 8, 2)])
+def test_plane_sizes(lib, codec, rb, sb, nb):
+    c, s, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.vit_kv_plane_sizes(codec, 2, 8, 128, 200704, ctypes.byref(c), ctypes.byref(s), ctypes.byref(n)) == 0
+    rows = 2 * 8 * 200704
+    assert (c.value, s.value, n.value) == (rows * rb, rows * sb, rows * nb)
+    # bits per value of the plane = the codec's bits per value
+    assert 8 * (c.value + s.value + n.value) / (rows * 128) == {0: 16, 1: 8.5, 2: 4.5, 3: 4.625}[codec]
+
+
+def test_plane_size_errors(lib):
+    z = ctypes.c_size_t()
+    r = ctypes.byref(z)
+    assert lib.vit_kv_plane_sizes(4, 1, 1, 128, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
+    assert lib.vit_kv_plane_sizes(0, 1, 1, 64, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
+    assert lib.vit_kv_plane_sizes(0, 1, 1, 128, 300, r, r, r) == _lib.VIT_E_CAPACITY
+    assert lib.vit_kv_plane_sizes(0, 0, 1, 128, 256, r, r, r) == _lib.VIT_E_ARG
+    assert lib.vit_kv_plane_sizes(0, 65, 1, 128, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
+
+
+def test_workspace_and_splits(lib):
+    assert lib.vit_attn_workspace_bytes(8, 32, 128, 16) == 8 * 32 * 16 * 130 * 4
+    assert lib.vit_attn_workspace_bytes(8, 32, 64, 16) == 0
+    assert lib.vit_attn_workspace_bytes(8, 32, 128, 0) == 0
+    s = lib.vit_attn_default_splits(8, 8, 32, 8192)
+    assert 1 <= s <= 8192 // 32 // 8
+    assert lib.vit_attn_default_splits(1, 1, 4, 512) >= 1
+
+
+FAKE = 0x100000  # 256-aligned fake device address; never dereferenced
+
+
+def _plane(codec=1, side=0, S=2, H=2, cap=512, codes=FAKE, scales=FAKE, norms=FAKE, signs=None):
+    p = _lib.VitKvPlane()
+    p.codec, p.side, p.n_seqs, p.n_kv_heads, p.head_dim, p.reserved, p.capacity = codec, side, S, H, 128, 0, cap
+    p.codes, p.scales, p.norms = codes, scales, norms
+    p.signs = signs
+    return p
+
+
+_SIGNS = (ctypes.c_uint8 * 16)()
+
+
+def _append(lib, p, src=FAKE, pos0=(0, 0), n=1):
+    arr = (ctypes.c_int64 * len(pos0))(*pos0)
+    return lib.vit_kv_append_quant(ctypes.byref(p), src, arr, n, None)
+
+
+def test_append_validation(lib):
+    assert _append(lib, _plane(), pos0=(500, 0), n=13) == _lib.VIT_E_CAPACITY
+    assert _append(lib, _plane(), pos0=(-1, 0)) == _lib.VIT_E_CAPACITY
+    assert _append(lib, _plane(cap=300)) == _lib.VIT_E_CAPACITY
+    assert _append(lib, _plane(codec=9)) == _lib.VIT_E_UNSUPPORTED
+    assert _append(lib, _plane(side=2)) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(codes=FAKE + 16)) == _lib.VIT_E_ALIGN
+    assert _append(lib, _plane(scales=None)) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(codec=3, signs=None)) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(codec=3, norms=None, signs=ctypes.addressof(_SIGNS))) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(), src=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert _append(lib, _plane(), src=None) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(), n=-1) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(), n=0) == _lib.VIT_OK  # no-op, nothing enqueued
+    p = _plane()
+    p.head_dim = 64
+    assert _append(lib, p) == _lib.VIT_E_UNSUPPORTED
+    p = _plane()
+    p.reserved = 1
+    assert _append(lib, p) == _lib.VIT_E_ARG
+
+
+def _decode(lib, k, v, hq=4, seq_len=(10, 10), k_new=None, v_new=None, scale=0.088, ns=1, ws=None, q=FAKE, out=FAKE):
+    arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+    return lib.vit_attn_decode(ctypes.byref(k), ctypes.byref(v), q, hq, arr, k_new, v_new, scale, ns, ws, out, None)
+
+
+def test_decode_validation(lib):
+    K, V = _plane(side=0), _plane(side=1)
+    assert _decode(lib, K, V, seq_len=(513, 1)) == _lib.VIT_E_CAPACITY
+    assert _decode(lib, K, V, seq_len=(0, 1)) == _lib.VIT_E_ARG
+    assert _decode(lib, K, V, hq=3) == _lib.VIT_E_ARG            # Hq % Hkv != 0
+    assert _decode(lib, K, V, hq=34) == _lib.VIT_E_UNSUPPORTED   # G = 17
+    assert _decode(lib, K, V, k_new=FAKE) == _lib.VIT_E_ARG       # k_new xor v_new
+    assert _decode(lib, K, V, ns=0) == _lib.VIT_E_ARG
+    assert _decode(lib, K, V, ns=5000) == _lib.VIT_E_ARG
+    assert _decode(lib, K, V, ns=4, ws=None) == _lib.VIT_E_ARG
+    assert _decode(lib, K, V, q=None) == _lib.VIT_E_ARG
+    assert _decode(lib, K, V, out=FAKE + 8) == _lib.VIT_E_ALIGN
+    assert _decode(lib, K, V, scale=float("nan")) == _lib.VIT_E_ARG
+    assert _decode(lib, V, K) == _lib.VIT_E_ARG                  # sides swapped
+    assert _decode(lib, K, _plane(side=1, H=4)) == _lib.VIT_E_ARG
+    assert _decode(lib, K, _plane(side=1, cap=1024)) == _lib.VIT_E_ARG
+
+
+def test_reduce_validation(lib):
+    V = _plane(side=1)
+    r = lib.vit_attn_splitk_reduce
+    assert r(FAKE, 2, 4, 128, 1, ctypes.byref(V), FAKE, None) == _lib.VIT_E_ARG
+    assert r(FAKE, 2, 4, 64, 4, ctypes.byref(V), FAKE, None) == _lib.VIT_E_UNSUPPORTED
+    assert r(None, 2, 4, 128, 4, ctypes.byref(V), FAKE, None) == _lib.VIT_E_ARG
+    assert r(FAKE, 2, 4, 128, 4, ctypes.byref(_plane(side=1, codec=3)), FAKE, None) == _lib.VIT_E_ARG
+    assert r(FAKE + 4, 2, 4, 128, 4, ctypes.byref(V), FAKE, None) == _lib.VIT_E_ALIGN
+
+
+# ------------------------------------------------------------- host layout
+@pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("side", ["k", "v"])
+def test_layout_is_a_bijection(codec, side):
+    rng = np.random.default_rng(3)
+    S, H, cap = 2, 3, 256
+    if codec == "f16":
+        codes = rng.integers(0, 65536, (S, H, cap, 128)).astype(np.uint16)
+    elif codec == "q8_0":
+        codes = rng.integers(-127, 128, (S, H, cap, 128)).astype(np.int8)
+    else:
+        codes = rng.integers(0, 16, (S, H, cap, 128)).astype(np.uint8)
+    raw = np.zeros(S * H * cap * layout.ROW_BYTES[codec], np.uint8)
+    layout.pack_codes(codec, side, codes, raw)
+    back = layout.unpack_codes(codec, side, raw, S, H, cap)
+    assert np.array_equal(back, codes)
+
+
+def test_k_layout_16_byte_units_are_contiguous_per_lane():
+    """Each wave-wide 16-byte load of a K tile covers 1 KB of contiguous bytes:
+    unit (half, c) of lane l sits at ((half*CB + c)*64 + l)*16."""
+    for codec in ("f16", "q8_0", "q4_0"):
+        perm = layout._k_perm(codec)
+        cb = layout.ROW_BYTES[codec] // 64
+        offs = np.sort(perm.reshape(-1))
+        assert np.array_equal(offs, np.arange(32 * layout.ROW_BYTES[codec]))
+        for p in range(32):
+            h, r = (p >> 2) & 1, ((p >> 3) << 2) | (p & 3)
+            for b in range(4):
+                for c in range(cb):
+                    lane = b * 16 + r
+                    assert perm[p, b * 16 * cb + 16 * c] == ((h * cb + c) * 64 + lane) * 16
+
+
+def test_scales_layout_roundtrip():
+    rng = np.random.default_rng(4)
+    s = rng.integers(0, 65536, (2, 3, 256, 4)).astype(np.uint16)
+    assert np.array_equal(layout.unpack_scales(layout.pack_scales(s), 2, 3, 256), s)

@@ -1,0 +1,246 @@
+"""GPU parity of vit_attn_decode + vit_attn_splitk_reduce against the oracle.
+
+Bar: max |o_gpu - o_ref| <= 2e-3 x RMS(o_ref) per decode call, with o_ref the
+oracle's fp64 attention over its own quantization of the same fp32 rows.
+Covers all 16 (K codec, V codec) pairs, G in {1, 4, 5, 8, 16}, ragged lengths
+(1 row, partial tiles), empty splits, fused append, determinism, poisoned
+planes, and the five workloads at full size (sampled (seq, KV head) units).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import append_rows, check_close, make_plane, ref_unit, say, torch_cuda
+
+CODECS = ["f16", "q8_0", "q4_0", "rot4"]
+D = 128
+
+
+def _rand_rows(rng, shape, outliers=True):
+    x = rng.standard_normal(shape).astype(np.float32)
+    if outliers:
+        ch = rng.choice(D, 2, replace=False)
+        x[..., ch] *= 20.0
+    return x
+
+
+def _run_small(kc, vc, G, lens, n_splits, seed, S=2, H=2, cap=512):
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    rng = np.random.default_rng(seed)
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
+    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc == "rot4" else None
+    K = make_plane(kc, "k", S, H, cap, ks)
+    V = make_plane(vc, "v", S, H, cap, vs)
+    Lmax = max(lens)
+    kx = _rand_rows(rng, (S, Lmax, H, D))
+    vx = _rand_rows(rng, (S, Lmax, H, D))
+    append_rows(K, kx, [0] * S)
+    append_rows(V, vx, [0] * S)
+    Hq = H * G
+    q = _rand_rows(rng, (S, Hq, D))
+    qd = torch.from_numpy(q).cuda()
+    out = vit.decode(K, V, qd, Hq, lens, n_splits=n_splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = np.zeros_like(got, dtype=np.float64)
+    scale = 1.0 / math.sqrt(D)
+    for s in range(S):
+        for h in range(H):
+            L = lens[s]
+            ref[s, h * G:(h + 1) * G] = ref_unit(q[s, h * G:(h + 1) * G], kx[s, :L, h], vx[s, :L, h],
+                                                 kc, vc, scale, ks, vs)
+    return got, ref
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kc", CODECS)
+@pytest.mark.parametrize("vc", CODECS)
+def test_all_codec_pairs(kc, vc):
+    say(f"[decode-pairs] K={kc} V={vc}")
+    for G, lens, ns in ((4, [37, 300], 1), (8, [1, 257], 3)):
+        got, ref = _run_small(kc, vc, G, lens, ns, seed=100 * CODECS.index(kc) + 10 * CODECS.index(vc) + G)
+        check_close(got, ref, f"K={kc} V={vc} G={G} lens={lens} splits={ns}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("G", [1, 2, 5, 12, 16])
+def test_gqa_widths(G):
+    say(f"[decode-gqa] G={G}")
+    for kc, vc in (("q8_0", "q4_0"), ("rot4", "f16")):
+        got, ref = _run_small(kc, vc, G, [96, 33], 2, seed=500 + G)
+        check_close(got, ref, f"G={G} K={kc} V={vc}")
+
+
+@pytest.mark.gpu
+def test_split_counts_and_empty_splits():
+    say("[decode-splits]")
+    outs = []
+    for ns in (1, 2, 3, 7, 16, 64):
+        got, ref = _run_small("q4_0", "rot4", 4, [100, 33], ns, seed=77)
+        check_close(got, ref, f"splits={ns}")
+        outs.append(got)
+    # split counts change only fp32 rounding
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-4 * np.sqrt(np.mean(outs[0] ** 2))
+
+
+@pytest.mark.gpu
+def test_deterministic_bitwise():
+    say("[decode-determinism]")
+    a, _ = _run_small("q8_0", "q8_0", 4, [480, 512], 5, seed=9)
+    b, _ = _run_small("q8_0", "q8_0", 4, [480, 512], 5, seed=9)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kc,vc", [("q8_0", "q8_0"), ("rot4", "q4_0"), ("f16", "rot4")])
+def test_fused_append_matches_separate_append(kc, vc):
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    say(f"[decode-fused] K={kc} V={vc}")
+    rng = np.random.default_rng(31)
+    S, H, G, cap = 3, 2, 4, 512
+    ks = rng.integers(0, 256, 16, dtype=np.uint8)
+    lens = [200, 1, 512]
+    kx = _rand_rows(rng, (S, cap, H, D))
+    vx = _rand_rows(rng, (S, cap, H, D))
+    q = torch.from_numpy(_rand_rows(rng, (S, H * G, D))).cuda()
+    planes = []
+    for fused in (False, True):
+        K = make_plane(kc, "k", S, H, cap, ks if kc == "rot4" else None)
+        V = make_plane(vc, "v", S, H, cap, ks if vc == "rot4" else None)
+        # rows 0 .. max(len)-2 of every sequence; the new row then lands at len-1
+        T = max(lens) - 1
+        append_rows(K, kx[:, :T], [0] * S)
+        append_rows(V, vx[:, :T], [0] * S)
+        knew = np.stack([kx[s, lens[s] - 1] for s in range(S)])[:, None]
+        vnew = np.stack([vx[s, lens[s] - 1] for s in range(S)])[:, None]
+        if fused:
+            out = vit.decode(K, V, q, H * G, lens, k_new=torch.from_numpy(knew[:, 0]).cuda(),
+                             v_new=torch.from_numpy(vnew[:, 0]).cuda(), n_splits=4)
+        else:
+            append_rows(K, knew, [l - 1 for l in lens])
+            append_rows(V, vnew, [l - 1 for l in lens])
+            out = vit.decode(K, V, q, H * G, lens, n_splits=4)
+        torch.cuda.synchronize()
+        planes.append((K.host_view(), V.host_view(), out.cpu().numpy()))
+    (k0, v0, o0), (k1, v1, o1) = planes
+    for s in range(S):
+        L = lens[s]
+        for a, b in ((k0, k1), (v0, v1)):
+            for key in a:
+                assert np.array_equal(a[key][s, :, :L], b[key][s, :, :L]), key
+    assert np.array_equal(o0, o1)
+
+
+# ---------------------------------------------------------------- workloads
+def _synth_rows(cfg, side, layer, seq, head, start, count):
+    return synth.kv_rows(cfg, side, layer, seq, head, start, count)
+
+
+def _fill_plane(plane, cfg, layer, side, start, count, units, torch, gen):
+    """Rows start..start+count-1 of every (seq, head): synth rows for the
+    sampled units, seeded device normals elsewhere; then one append call."""
+    S, H = plane.n_seqs, plane.n_kv_heads
+    src = torch.randn((S, count, H, D), generator=gen, device="cuda", dtype=torch.float32)
+    for (s, h) in units:
+        src[s, :, h] = torch.from_numpy(_synth_rows(cfg, side, layer, s, h, start, count)).cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    vit.vit_kv_append_quant(plane, src, [start] * S)
+    return src
+
+
+def _run_workload(cfg, units, layers=(0,)):
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    c = synth.CONFIGS[cfg]
+    S, Hq, H, cap = c["seqs"], c["hq"], c["hkv"], c["capacity"]
+    G = Hq // H
+    cmap = synth.codec_map(cfg)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg)
+    scale = 1.0 / math.sqrt(D)
+    for layer in layers:
+        kc, vc = cmap[layer]
+        ks = synth.sign_mask(cfg, layer, "k") if kc == "rot4" else None
+        vs = synth.sign_mask(cfg, layer, "v") if vc == "rot4" else None
+        say(f"[workload {c['name']}] layer {layer} K={kc} V={vc} units={units}")
+        K = make_plane(kc, "k", S, H, cap, ks)
+        V = make_plane(vc, "v", S, H, cap, vs)
+        L = c["ctx"]
+        lens = [L] * S
+        q = np.stack([synth.q_rows(cfg, layer, s, Hq) for s in range(S)])
+        qd = torch.from_numpy(q).cuda()
+        ns = vit.vit_attn_default_splits(S, H, Hq, L)
+        if c["fused_append"]:
+            _fill_plane(K, cfg, layer, "k", 0, L - 1, units, torch, gen)
+            _fill_plane(V, cfg, layer, "v", 0, L - 1, units, torch, gen)
+            knew = torch.randn((S, H, D), generator=gen, device="cuda")
+            vnew = torch.randn((S, H, D), generator=gen, device="cuda")
+            for (s, h) in units:
+                knew[s, h] = torch.from_numpy(_synth_rows(cfg, "k", layer, s, h, L - 1, 1)[0]).cuda()
+                vnew[s, h] = torch.from_numpy(_synth_rows(cfg, "v", layer, s, h, L - 1, 1)[0]).cuda()
+            out = vit.decode(K, V, qd, Hq, lens, k_new=knew, v_new=vnew, n_splits=ns)
+        elif "prefill" in c:
+            pre, ub = c["prefill"], c["ubatch"]
+            _fill_plane(K, cfg, layer, "k", 0, pre, units, torch, gen)
+            _fill_plane(V, cfg, layer, "v", 0, pre, units, torch, gen)
+            _fill_plane(K, cfg, layer, "k", pre, ub, units, torch, gen)
+            _fill_plane(V, cfg, layer, "v", pre, ub, units, torch, gen)
+            out = vit.decode(K, V, qd, Hq, lens, n_splits=ns)
+        else:
+            _fill_plane(K, cfg, layer, "k", 0, L, units, torch, gen)
+            _fill_plane(V, cfg, layer, "v", 0, L, units, torch, gen)
+            out = vit.decode(K, V, qd, Hq, lens, n_splits=ns)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        gots, refs = [], []
+        for (s, h) in units:
+            kr = _synth_rows(cfg, "k", layer, s, h, 0, L)
+            vr = _synth_rows(cfg, "v", layer, s, h, 0, L)
+            r = ref_unit(q[s, h * G:(h + 1) * G], kr, vr, kc, vc, scale, ks, vs)
+            gots.append(got[s, h * G:(h + 1) * G])
+            refs.append(r)
+        check_close(np.stack(gots), np.stack(refs), f"{c['name']} layer {layer} ({kc},{vc}) splits={ns}")
+        del K, V
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+def test_workload_tiny():
+    _run_workload(1, [(0, 0)])
+
+
+@pytest.mark.gpu
+def test_workload_batched():
+    _run_workload(2, [(0, 0), (3, 5), (7, 7)])
+
+
+@pytest.mark.gpu
+def test_workload_lowbit():
+    _run_workload(3, [(0, 1), (3, 6)])
+
+
+@pytest.mark.gpu
+def test_workload_rotated():
+    _run_workload(4, [(0, 0), (0, 1)])
+
+
+@pytest.mark.gpu
+def test_workload_ladder_layers():
+    cmap = synth.codec_map(5)
+    # one layer per distinct (K, V) pair present, up to four layers
+    seen, layers = set(), []
+    for i, pair in enumerate(cmap):
+        if pair not in seen and len(layers) < 4:
+            seen.add(pair)
+            layers.append(i)
+    _run_workload(5, [(1, 6)], layers=layers)

@@ -317,3 +317,14 @@ def test_planted_q4_sign_mistake_is_caught(rng, monkeypatch):
     assert np.max(np.abs(good - x)) < 0.3
     assert np.max(np.abs(bad - x)) > 1.0
     del orig, monkeypatch
+
+
+def test_domain_guard_rejects_tiny_blocks():
+    x = np.zeros((1, D), np.float32)
+    x[0, 3] = np.float32(3.0e-39)
+    with pytest.raises(AssertionError):
+        codecs.quantize_q8_0(x)
+    with pytest.raises(AssertionError):
+        codecs.quantize_q4_0(x)
+    x[0, 3] = np.float32(2.0 ** -100)
+    assert codecs.quantize_q8_0(x)["codes"][0, 3] == 127
