@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of the quantized KV path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
+
+A step is one pass of the whole hot path over one batch: quantize-and-append
+the new token's K and V rows of every (sequence, KV head), flash-decode
+attention over the quantized cache, and the split-K merge.  The default
+workload is "batched": 8 sequences x 1 new token, 32 query heads on 8 KV
+heads, head_dim 128, 8192 cached rows per sequence, K and V both q8_0.
+Other workloads (tiny, lowbit, rotated, ladder) are available with
+--workload.
+
+Inputs are synthetic (seeded device normals shaped like the workload) and
+resident in HBM before timing starts.  Because the batched cache (143 MB)
+fits in the 256 MB last-level cache, each timed step reads a different one of
+R device replicas (R * footprint >= 1 GiB), round-robin.
+
+Prints ONE JSON line.  ``value`` is decode tokens/s (sequences / step time).
+``roofline`` describes the dominant kernel (decode): algorithmic KV bytes per
+launch / its mean duration from HIP events recorded on the launch stream
+around every timed decode launch, against the 8 TB/s HBM peak.  ``traffic``
+is the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
+a copy-kernel calibration), read from profiles/ only when it was measured on
+the current kernel sources.  ``cpu_baseline`` times the numpy oracle on the
+host for the same step (a baseline, not a target).
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {"tiny": 1, "batched": 2, "lowbit": 3, "rotated": 4, "ladder": 5}
+D = 128
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_kv_cache_append_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _row_bytes(codec):
+    return {"f16": 256, "q8_0": 136, "q4_0": 72, "rot4": 74}[codec]
+
+
+def _device_rows(torch, gen, shape, dist, scales=None):
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    if dist == "lognormal" and scales is not None:
+        x *= scales
+    elif dist == "outlier":
+        x[..., :2] *= 20.0
+    elif dist == "heavy":
+        # Student-t(3) = z / sqrt(chi2_3 / 3), drawn on the device
+        hit = torch.rand(shape, generator=gen, device="cuda") < 0.01
+        z = torch.randn((3,) + tuple(shape), generator=gen, device="cuda")
+        t = torch.randn(shape, generator=gen, device="cuda") / torch.sqrt((z * z).sum(0) / 3.0)
+        x = torch.where(hit, t, x)
+    return x
+
+
+class Layer:
+    """K and V planes of one layer plus cold-cache replicas."""
+
+    def __init__(self, vit, cfg, kc, vc, replicas, signs_k, signs_v):
+        S, H, cap = cfg["seqs"], cfg["hkv"], cfg["capacity"]
+        self.K = [vit.KVPlane(kc, "k", S, H, cap, signs_k)]
+        self.V = [vit.KVPlane(vc, "v", S, H, cap, signs_v)]
+        self.replicas = replicas
+        self.kc, self.vc = kc, vc
+
+    def make_replicas(self, vit):
+        for _ in range(self.replicas - 1):
+            k = vit.KVPlane.like(self.K[0])
+            v = vit.KVPlane.like(self.V[0])
+            k.copy_from(self.K[0])
+            v.copy_from(self.V[0])
+            self.K.append(k)
+            self.V.append(v)
+
+
+def run_gpu(args):
+    import numpy as np
+    import torch
+
+    import quantized_kv_cache_append_amd as vit
+    import synth
+
+    cfgno = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[cfgno]
+    S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
+    cmap = synth.codec_map(cfgno)
+    n_layers = cfg["layers"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED2026 + cfgno)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    kv_bytes = sum(S * H * L * (_row_bytes(kc) + _row_bytes(vc)) for kc, vc in cmap)
+    footprint = sum(S * H * cap * (_row_bytes(kc) + _row_bytes(vc)) for kc, vc in cmap)
+    replicas = args.replicas if args.replicas else max(1, math.ceil((1 << 30) / footprint))
+    if n_layers > 1:
+        replicas = 1  # the ladder's 13.8 GB footprint already dwarfs every cache
+
+    print(f"# workload {cfg['name']}: S={S} Hq={Hq} Hkv={H} L={L} layers={n_layers} "
+          f"codecs={cmap if n_layers == 1 else 'ladder'} replicas={replicas}", file=sys.stderr, flush=True)
+
+    layers = []
+    chan_scale = {}
+    for li, (kc, vc) in enumerate(cmap):
+        ks = synth.sign_mask(cfgno, li, "k") if kc == "rot4" else None
+        vs = synth.sign_mask(cfgno, li, "v") if vc == "rot4" else None
+        lay = Layer(vit, cfg, kc, vc, replicas, ks, vs)
+        for side, plane in (("k", lay.K[0]), ("v", lay.V[0])):
+            sc = None
+            if cfg["dist"] == "lognormal":
+                sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
+                chan_scale[(li, side)] = sc
+            pre = cfg.get("prefill", L - 1 if cfg["fused_append"] else L)
+            # fill the prefix in chunks to bound the fp32 staging buffer
+            chunk = 16384
+            for p0 in range(0, pre, chunk):
+                n = min(chunk, pre - p0)
+                src = _device_rows(torch, gen, (S, n, H, D), cfg["dist"], sc)
+                vit.vit_kv_append_quant(plane, src, [p0] * S)
+            del src
+        lay.make_replicas(vit)
+        layers.append(lay)
+    torch.cuda.synchronize()
+
+    # per-step inputs
+    q = [_device_rows(torch, gen, (S, Hq, D), cfg["dist"]) for _ in range(n_layers)]
+    if "ubatch" in cfg:
+        T, p_new = cfg["ubatch"], cfg["prefill"]
+    else:
+        T, p_new = 1, L - 1
+    new_rows = [[_device_rows(torch, gen, (S, T, H, D), cfg["dist"], chan_scale.get((li, s)))
+                 for s in ("k", "v")] for li in range(n_layers)]
+    n_splits = args.splits if args.splits else vit.vit_attn_default_splits(S, H, Hq, L)
+    ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq, D, n_splits), dtype=torch.uint8, device="cuda")
+    out = [torch.empty((S, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    lens = [L] * S
+    stream = torch.cuda.current_stream()
+
+    # every call of a step, marshalled once per replica (the host then only
+    # issues the C calls, so the GPU queue never runs dry)
+    calls = []
+    for r in range(replicas):
+        app, dec = [], []
+        for li, lay in enumerate(layers):
+            kn, vn = new_rows[li]
+            app.append(vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=stream))
+            app.append(vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=stream))
+            d = vit.prepare_decode(lay.K[r], lay.V[r], q[li], Hq, lens, out[li], n_splits=n_splits,
+                                   workspace=ws if n_splits > 1 else None, stream=stream)
+            red = vit.prepare_reduce(ws, S, Hq, n_splits, lay.V[r], out[li], stream=stream) if n_splits > 1 else None
+            dec.append((d, red))
+        calls.append((app, dec))
+
+    def step(i, ev=None):
+        app, dec = calls[i % replicas]
+        for c in app:
+            c()
+        for li, (d, red) in enumerate(dec):
+            if ev is not None:
+                ev[0][li].record(stream)
+            d()
+            if ev is not None:
+                ev[1][li].record(stream)
+            if red is not None:
+                red()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [([torch.cuda.Event(enable_timing=True) for _ in range(n_layers)],
+            [torch.cuda.Event(enable_timing=True) for _ in range(n_layers)]) for _ in range(args.steps)]
+    mode = "eager (pre-marshalled C calls)"
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [evs[i][0][li].elapsed_time(evs[i][1][li]) for i in range(args.steps) for li in range(n_layers)]
+    assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output"
+
+    ms_per_step = 1e3 * wall / args.steps
+    dec_mean_ms = float(np.mean(dec_ms))
+    per_launch_bytes = kv_bytes / n_layers
+    # algorithmic bytes of all timed decode launches / their summed duration
+    achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
+    return dict(cfg=cfg, cfgno=cfgno, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, mode=mode,
+                replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, dec_mean_ms=dec_mean_ms,
+                dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
+                achieved_gbs=achieved)
+
+
+def run_copy_calibration(steps):
+    """A plain device copy of known size, for scaling rocprofv3 counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": steps}))
+
+
+def cpu_baseline(r, budget_s=15.0):
+    """The numpy oracle on the host: for each (sequence, KV head) of the step,
+    quantize the new rows, dequantize the cache and attend in fp64."""
+    import numpy as np
+
+    from oracle import attention, codecs
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    cfgno, L, S, H, Hq = r["cfgno"], r["L"], r["S"], r["H"], r["Hq"]
+    G = Hq // H
+    kc, vc = r["cmap"][0]
+    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
+    vs = synth.sign_mask(cfgno, 0, "v") if vc == "rot4" else None
+    units = [(s, h) for s in range(S) for h in range(H)]
+    rows_unit = min(L, 8192)  # longer contexts are timed on an 8192-row slice and scaled
+    prep = []
+    for (s, h) in units[:4]:
+        kx = synth.kv_rows(cfgno, "k", 0, s, h, 0, rows_unit)
+        vx = synth.kv_rows(cfgno, "v", 0, s, h, 0, rows_unit)
+        qx = synth.q_rows(cfgno, 0, s, Hq)[h * G:(h + 1) * G]
+        prep.append((codecs.quantize(kc, kx[:-1], ks), codecs.quantize(vc, vx[:-1], vs),
+                     kx[-1:], vx[-1:], qx))
+    scale = 1.0 / math.sqrt(D)
+    n_done = 0
+    t0 = time.perf_counter()
+    while True:
+        for kq, vq, kn, vn, qx in prep:
+            kq2 = {k: np.concatenate([a, b]) for (k, a), b in
+                   zip(kq.items(), codecs.quantize(kc, kn, ks).values())}
+            vq2 = {k: np.concatenate([a, b]) for (k, a), b in
+                   zip(vq.items(), codecs.quantize(vc, vn, vs).values())}
+            attention.attend(qx, codecs.dequant(kc, kq2, ks), codecs.dequant(vc, vq2, vs), scale)
+            n_done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_unit = el / n_done * (L / rows_unit)
+    step_s = per_unit * len(units) * r["n_layers"]
+    return {"value": S / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{n_done} (sequence, KV head) units of the step ({kc}/{vc}, G={G}) over "
+                       f"{rows_unit} rows each, {el:.1f} s on 1 thread, scaled to {len(units)} units x "
+                       f"{L} rows x {r['n_layers']} layer(s) per step; step = quantize new row + "
+                       "dequantize cache + fp64 attention")}
+
+
+def load_traffic(workload, per_launch_bytes):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    only if they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", type=int, default=0, help="only run N plain 1 GiB copies")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by (sequence, KV head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        run_copy_calibration(args.calib_copy)
+        return
+    r = run_gpu(args)
+    cfg = r["cfg"]
+    tok_s = r["S"] / (r["ms_per_step"] * 1e-3)
+    traffic = load_traffic(args.workload, r["per_launch_bytes"])
+    line = {
+        "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q8_0/q4_0/rot4/f16 codes, fp16 MFMA operands (hi+lo split), fp32 accumulate",
+        "data": "synthetic (seeded device normals shaped like the workload; no model weights or dataset)",
+        "config": {
+            "workload": cfg["name"],
+            "n_seqs": r["S"], "n_q_heads": r["Hq"], "n_kv_heads": r["H"], "head_dim": D,
+            "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"],
+            "codecs": "ladder (seeded per layer/side)" if r["n_layers"] > 1 else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
+            "n_splits": r["n_splits"], "cold_cache_replicas": r["replicas"], "launch": r["mode"],
+        },
+        "effective_kv_read_gbs": round(r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+        "effective_kv_read_pct_of_hbm_peak": round(100 * r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel",
+            "achieved": round(r["achieved_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": r["per_launch_bytes"],
+            "mean_launch_ms": round(r["dec_mean_ms"], 5),
+            "min_launch_ms": round(r["dec_min_ms"], 5),
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,12 +54,14 @@
  *
  *  codes   ph * capacity * RB bytes per stream, RB = 256 (F16), 128 (Q8_0),
  *          64 (Q4_0, ROT4) bytes per row; a tile is 32 * RB bytes.
- *  scales  fp16 [S][H][capacity/32][4][32]: scale of (tile t, block b, row p)
- *          at ((ph * capacity/32 + t) * 4 + b) * 32 + p.  NULL for F16.
+ *  scales  fp16, 4 per row (one per 32-value block); NULL for F16.
+ *          K side: [S][H][capacity][4] (row-major);  V side:
+ *          [S][H][capacity/32][4][32], scale of (tile t, block b, row p) at
+ *          ((ph * capacity/32 + t) * 4 + b) * 32 + p.
  *  norms   fp16 [S][H][capacity] (ROT4 only; NULL otherwise).
  *
  *  A K-side tile ("row-major units") is two 16-row halves h = 0, 1; row r of
- *  half h is position p = 8*(r>>2) + 4*h + (r&3).  Each half holds 16-byte
+ *  half h is position p = 16*h + r.  Each half holds 16-byte
  *  units U[c][b][r] (c < CB, b = block 0..3, r = row 0..15), unit byte offset
  *  (((h*CB + c)*4 + b)*16 + r)*16, CB = RB/64.  A unit holds block b's
  *  canonical bytes [16c, 16c+16) of that row:
@@ -174,9 +176,10 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
  *            neither), the new token's K and V rows are quantized and stored
  *            at row seq_len[s]-1 first, exactly as vit_kv_append_quant would.
  *  scale     softmax scale (typically 1/sqrt(128)).
- *  n_splits  1 .. VIT_MAX_SPLITS.  The context of each sequence is cut into
- *            n_splits contiguous ranges of whole 32-row tiles (some may be
- *            empty).  With n_splits == 1 the normalised output is written to
+ *  n_splits  1 .. VIT_MAX_SPLITS.  The 32-row tiles of each sequence's
+ *            context are dealt to n_splits partial results, tile t to split
+ *            t % n_splits (a split may get none).  With n_splits == 1 the
+ *            normalised output is written to
  *            `out` and `workspace` may be NULL; otherwise partials go to
  *            `workspace` and vit_attn_splitk_reduce produces `out`.
  *  out       fp32 [n_seqs][n_q_heads][128], model domain.

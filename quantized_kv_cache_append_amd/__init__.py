@@ -89,6 +89,9 @@ class KVPlane:
                    other.signs, device)
 
     def struct(self):
+        """The C descriptor (built once: the arrays never move)."""
+        if getattr(self, "_struct", None) is not None:
+            return self._struct
         p = VitKvPlane()
         p.codec = CODEC_IDS[self.codec]
         p.side = SIDE_IDS[self.side]
@@ -98,6 +101,7 @@ class KVPlane:
         p.scales = self.scales.data_ptr() if self.scales is not None else None
         p.norms = self.norms.data_ptr() if self.norms is not None else None
         p.signs = self.signs.ctypes.data if self.signs is not None else None
+        self._struct = p
         return p
 
     def tensors(self):
@@ -112,7 +116,7 @@ class KVPlane:
         S, H, cap = self.n_seqs, self.n_kv_heads, self.capacity
         out = {"codes": layout.unpack_codes(self.codec, self.side, self.codes.cpu().numpy(), S, H, cap)}
         if self.scales is not None:
-            out["scales"] = layout.unpack_scales(self.scales.cpu().numpy().view(np.uint16), S, H, cap)
+            out["scales"] = layout.unpack_scales(self.side, self.scales.cpu().numpy().view(np.uint16), S, H, cap)
         if self.norms is not None:
             out["norms"] = layout.unpack_norms(self.norms.cpu().numpy().view(np.uint16), S, H, cap)
         return out
@@ -181,3 +185,46 @@ def decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_sp
     if n_splits > 1:
         vit_attn_splitk_reduce(workspace, k.n_seqs, n_q_heads, HEAD_DIM, n_splits, v, out, stream)
     return out
+
+
+class _Prepared:
+    """A C-ABI call with every argument already marshalled (for loops that
+    issue the same call many times, e.g. a decode step)."""
+
+    def __init__(self, name, fn, args, keep):
+        self.name, self.fn, self.args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            _lib.check(self.name, st)
+
+
+def prepare_append(plane, src, pos0, n_tokens=None, stream=None):
+    lib = _lib.load()
+    n_tokens = src.shape[1] if n_tokens is None else n_tokens
+    p0 = (ctypes.c_int64 * len(pos0))(*[int(x) for x in pos0])
+    p = plane.struct()
+    args = (ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
+    return _Prepared("vit_kv_append_quant", lib.vit_kv_append_quant, args, (p, p0, src, plane))
+
+
+def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, scale=None, n_splits=1,
+                   workspace=None, stream=None):
+    lib = _lib.load()
+    scale = 1.0 / np.sqrt(HEAD_DIM) if scale is None else scale
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), sl, _fptr(k_new, "k_new"),
+            _fptr(v_new, "v_new"), ctypes.c_float(scale), int(n_splits),
+            _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
+            _fptr(out, "out"), _stream_handle(stream))
+    return _Prepared("vit_attn_decode", lib.vit_attn_decode, args, (kp, vp, sl, q, k_new, v_new, workspace, out, k, v))
+
+
+def prepare_reduce(workspace, n_seqs, n_q_heads, n_splits, v, out, stream=None):
+    lib = _lib.load()
+    vp = v.struct()
+    args = (_fptr(workspace, "workspace", "uint8"), int(n_seqs), int(n_q_heads), HEAD_DIM, int(n_splits),
+            ctypes.byref(vp), _fptr(out, "out"), _stream_handle(stream))
+    return _Prepared("vit_attn_splitk_reduce", lib.vit_attn_splitk_reduce, args, (vp, workspace, out, v))

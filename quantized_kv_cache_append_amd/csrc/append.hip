@@ -57,8 +57,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     const int pt = static_cast<int>(p & 31);
     if (scales && (lane & 31) == 0) {
       const int b0 = lane >> 5;  // block of x0; x1 is in block 2 + b0
-      scales[scale_index(tile, b0, pt)] = rc.s0;
-      scales[scale_index(tile, 2 + b0, pt)] = rc.s1;
+      if constexpr (SIDE == 0) {
+        scales[k_scale_index(p, b0)] = rc.s0;
+        scales[k_scale_index(p, 2 + b0)] = rc.s1;
+      } else {
+        scales[v_scale_index(tile, b0, pt)] = rc.s0;
+        scales[v_scale_index(tile, 2 + b0, pt)] = rc.s1;
+      }
     }
     if (norms && lane == 0) norms[p] = rc.norm;
 

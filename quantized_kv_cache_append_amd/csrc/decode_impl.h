@@ -2,21 +2,22 @@
 //
 // One workgroup (4 waves) per (split, KV head, sequence).  The split's 32-row
 // tiles are dealt round-robin to the 4 waves; each wave keeps its own online
-// softmax state and the waves are merged through LDS at the end.
+// softmax state, prefetches its next tile into registers while it computes
+// the current one, and the waves are merged through LDS at the end.
 //
 // Both products run on MFMA 16x16x32 f16 with exact operands:
 //   * K and V codes are exact in fp16 (f16 values, int8 / 4-bit integers,
 //     fp16 rot4 levels), and every per-block scale is applied in fp32;
 //   * the query and the probabilities are split into fp16 hi + lo parts
-//     (two MFMAs), so operand rounding stays near 2^-22 relative.
-// Query rows are packed four per 16-column MFMA tile, one column per
-// (query row, 32-channel block) pair: lane group q (lanes 16q..16q+15) of the
-// A operand always holds block q of its K row, and the B operand is zero
-// except where column block == q.  One MFMA chain therefore yields per-block
-// partial dot products for four query rows at once, which are scaled by the
-// block scale in fp32 and summed across the four column lanes.  The same
-// (row, block) pairing builds the P.V operand, with the V block scale folded
-// into P per block, so no lane does dequantization work for padding rows.
+//     (two MFMAs), so operand rounding stays near 2^-21 relative.
+// S^T = Q K^T: the A operand has one row per (query row, 32-channel block)
+// pair, four query rows per 16-row tile; lane group q (lanes 16q..16q+15)
+// of the B operand holds block q of a K row, and A is zero except where the
+// row's block equals q.  Each output lane then holds, for one cached row and
+// one query row, the four per-block partial dot products, which it scales by
+// the fp32 block scales and sums in registers.  P is regrouped through a
+// small per-wave LDS buffer into the P.V operand, whose rows are again
+// (query row, block) pairs so the V block scale folds into P per block.
 #pragma once
 
 #include "vit_device.h"
@@ -30,6 +31,14 @@ __device__ inline float4v mfma16(half8 a, half8 b, float4v c) {
 
 // --- exact fp16 conversions of packed codes ---------------------------------
 __device__ inline half2v h2_bits(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+
+// (x & mask) | bits in one v_and_or_b32 (gfx9 VOP3 takes no literal, so the
+// mask comes in a VGPR and the constant bits in an SGPR).
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "s"(bits));
+  return r;
+}
 __device__ inline uint32_t bits_h2(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // four int8 codes -> fp16 pairs (b0,b2) and (b1,b3): (0x6400 | (c ^ 0x80)) is
@@ -38,8 +47,8 @@ __device__ inline u32x2 q8_pairs(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
   const half2v k = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
   u32x2 r;
-  r[0] = bits_h2(h2_bits((u & 0x00FF00FFu) | 0x64006400u) - k);
-  r[1] = bits_h2(h2_bits(((u >> 8) & 0x00FF00FFu) | 0x64006400u) - k);
+  r[0] = bits_h2(h2_bits(and_or(u, 0x00FF00FFu, 0x64006400u)) - k);
+  r[1] = bits_h2(h2_bits(and_or(u >> 8, 0x00FF00FFu, 0x64006400u)) - k);
   return r;
 }
 
@@ -56,10 +65,10 @@ __device__ inline half8 q4_unpack(uint32_t w) {
   const half2v s_hi = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
   const half2v k_hi = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
   const uint32_t w8 = w >> 8;
-  const half2v a = h2_bits((w & 0x000F000Fu) | 0x64006400u) - k_lo;
-  const half2v b = h2_bits((w8 & 0x000F000Fu) | 0x64006400u) - k_lo;
-  const half2v c = h2_bits((w & 0x00F000F0u) | 0x64006400u) * s_hi + k_hi;
-  const half2v d = h2_bits((w8 & 0x00F000F0u) | 0x64006400u) * s_hi + k_hi;
+  const half2v a = h2_bits(and_or(w, 0x000F000Fu, 0x64006400u)) - k_lo;
+  const half2v b = h2_bits(and_or(w8, 0x000F000Fu, 0x64006400u)) - k_lo;
+  const half2v c = h2_bits(and_or(w, 0x00F000F0u, 0x64006400u)) * s_hi + k_hi;
+  const half2v d = h2_bits(and_or(w8, 0x00F000F0u, 0x64006400u)) * s_hi + k_hi;
   half8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
@@ -127,30 +136,203 @@ constexpr int v_loads() {
   return C == F16 ? 8 : (C == Q8_0 ? 4 : 2);
 }
 
-__device__ inline float quad_xor1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+// DPP moves within 16-lane rows: quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, 8.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
-__device__ inline float quad_xor2(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  return fmaxf(v, dpp<0x128>(v));
+}
+__device__ inline float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  return v + dpp<0x128>(v);
 }
 
-// Per-row factors (fp32) of the 8 rows 8q..8q+7 for one block: fp16 scale,
-// times the fp16 norm for rot4.
-template <int C>
-__device__ inline void row_factors(u32x4 sc, u32x4 nm, float f[8]) {
+// hi + lo fp16 split of two fp32 values: hi = fp16(x) toward zero (so x - hi
+// is exact in fp32), lo = fp16(x - hi); |x - hi - lo| <= 2^-21 |x| + 2^-25.
+__device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  const float r0 = x0 - static_cast<float>(h[0]);
+  const float r1 = x1 - static_cast<float>(h[1]);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+}
+__device__ inline void split8(const float v[8], half8& hi, half8& lo) {
+  u32x4 h, l;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float v = f16_to_float(sc[j >> 1] >> ((j & 1) * 16));
-    if constexpr (C == ROT4) v *= f16_to_float(nm[j >> 1] >> ((j & 1) * 16));
-    f[j] = v;
+  for (int i = 0; i < 4; ++i) {
+    uint32_t hh, ll;
+    split_pair(v[2 * i], v[2 * i + 1], hh, ll);
+    h[i] = hh;
+    l[i] = ll;
+  }
+  hi = __builtin_bit_cast(half8, h);
+  lo = __builtin_bit_cast(half8, l);
+}
+
+// LDS traffic that stays inside one wave (written and read back by lanes of
+// the same wave) needs ordering, not a workgroup barrier.
+__device__ inline void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Registers of one 32-row tile for one lane.
+template <int KC, int VC>
+struct TileRegs {
+  u32x4 kd[2][units_per_block(KC)];  // K units of halves 0 and 1
+  u32x4 vd[v_loads<VC>()];           // V column units
+  u32x2 ks[2];                       // K scales of this lane's row in each half
+  uint32_t kn[2];                    // K norms (rot4)
+  u32x4 vs;                          // V scales: block (lane & 3), rows 8q .. 8q+7
+  u32x4 vn;                          // V norms (rot4), rows 8q .. 8q+7
+};
+
+template <int KC, int VC>
+__device__ inline void load_tile(TileRegs<KC, VC>& r, int t, int lane, const uint8_t* kbase,
+                                 const uint8_t* vbase, const uint16_t* ksb, const uint16_t* knb,
+                                 const uint16_t* vsb, const uint16_t* vnb) {
+  constexpr int KCB = units_per_block(KC);
+  const uint8_t* kt = kbase + static_cast<int64_t>(t) * tile_code_bytes(KC);
+  const uint8_t* vt = vbase + static_cast<int64_t>(t) * tile_code_bytes(VC);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < KCB; ++c)
+      r.kd[h][c] = *reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16);
+#pragma unroll
+  for (int i = 0; i < v_loads<VC>(); ++i) r.vd[i] = *reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16);
+  const int n16 = lane & 15, qg = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(t) * kTile;
+  if constexpr (has_scales(KC)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.ks[h] = *reinterpret_cast<const u32x2*>(ksb + (row0 + 16 * h + n16) * 4);
+  }
+  if constexpr (has_norms(KC)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.kn[h] = knb[row0 + 16 * h + n16];
+  }
+  if constexpr (has_scales(VC))
+    r.vs = *reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (lane & 3) * 32 + 8 * qg);
+  if constexpr (has_norms(VC)) r.vn = *reinterpret_cast<const u32x4*>(vnb + row0 + 8 * qg);
+}
+
+// Tiles kept in flight ahead of the one being used: two for the 4-bit pairs
+// (a tile is ~4.6 KB), one when a tile already carries >= 6 KB per wave.
+template <int KC, int VC>
+constexpr int prefetch_depth() {
+  return (tile_code_bytes(KC) + tile_code_bytes(VC)) <= 4096 ? 2 : 1;
+}
+
+// Per-wave online-softmax state for 4 query rows.
+struct WaveState {
+  float m_run;        // running max (base 2) of the lane's query row
+  float l_run;        // lane-partial running sum
+  float4v oacc[8];    // P.V accumulators: N-tile c, rows (query row, block)
+};
+
+// One 32-row tile for one wave: S^T = Q K^T, online softmax, O += P V.
+template <int KC, int VC>
+__device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t, int L, int lane,
+                                             const half8 (&aqh)[4], const half8 (&aql)[4], WaveState& st,
+                                             float (*s_p)[kTile], const uint32_t* lut) {
+  const int n16 = lane & 15, qg = lane >> 4;
+  const bool partial = (t + 1) * kTile > L;
+  // ---- S^T: per half h, lane (n16, qg) gets the 4 block partials of query
+  //      row qg at tile row 16h + n16 ----
+  float s[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    half8 bk[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bk[m] = unpack_k<KC>(cur.kd[h], m, lut);
+    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc = mfma16(aqh[m], bk[m], acc);
+      acc = mfma16(aql[m], bk[m], acc);
+    }
+    float v;
+    if constexpr (KC == F16) {
+      v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    } else {
+      float kf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
+      if constexpr (KC == ROT4) {
+        const float nrm = f16_to_float(cur.kn[h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] *= nrm;
+      }
+      v = (acc[0] * kf[0] + acc[1] * kf[1]) + (acc[2] * kf[2] + acc[3] * kf[3]);
+    }
+    if (partial && t * kTile + 16 * h + n16 >= L) v = -INFINITY;
+    s[h] = v;
+  }
+
+  // ---- online softmax (base 2); all lanes of a 16-lane row share the row state
+  const float tmax = row16_max(fmaxf(s[0], s[1]));
+  const float mnew = fmaxf(st.m_run, tmax);
+  if (__builtin_amdgcn_ballot_w64(mnew > st.m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - mnew);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.oacc[c] *= alpha;
+    st.m_run = mnew;
+  }
+  const float p0 = __builtin_amdgcn_exp2f(s[0] - st.m_run);
+  const float p1 = __builtin_amdgcn_exp2f(s[1] - st.m_run);
+  st.l_run += p0 + p1;
+  s_p[qg][n16] = p0;
+  s_p[qg][16 + n16] = p1;
+  wave_lds_fence();
+
+  // ---- O += P V: A row n16 = 4*(query row) + block b carries P times the
+  //      block-b factor of V over tile rows 8qg .. 8qg+7 ----
+  const float4v p_lo = *reinterpret_cast<const float4v*>(&s_p[n16 >> 2][8 * qg]);
+  const float4v p_hi = *reinterpret_cast<const float4v*>(&s_p[n16 >> 2][8 * qg + 4]);
+  wave_lds_fence();
+  float pv[8] = {p_lo[0], p_lo[1], p_lo[2], p_lo[3], p_hi[0], p_hi[1], p_hi[2], p_hi[3]};
+  if constexpr (VC != F16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = f16_to_float(cur.vs[j >> 1] >> ((j & 1) * 16));
+      if constexpr (VC == ROT4) f *= f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
+      pv[j] = (pv[j] != 0.0f) ? pv[j] * f : 0.0f;
+    }
+  }
+  half8 aph, apl;
+  split8(pv, aph, apl);
+  const int row8 = t * kTile + 8 * qg;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    half8 bv = unpack_v<VC>(cur.vd, c, lut);
+    if constexpr (VC == F16) {
+      if (partial) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
+      }
+    }
+    st.oacc[c] = mfma16(aph, bv, st.oacc[c]);
+    st.oacc[c] = mfma16(apl, bv, st.oacc[c]);
   }
 }
 
-template <int KC, int VC, int NT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int GP = 4 * NT;
-  constexpr int KCB = units_per_block(KC);
-  constexpr int NVL = v_loads<VC>();
+// Decode kernel.  Row groups: query rows 4k .. 4k+3 of the KV head are handled
+// by the waves w with w / (4 / n_groups) == k; those waves share out the
+// workgroup's tiles round-robin.
+template <int KC, int VC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+  constexpr int GMAX = 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -161,28 +343,66 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int seq = blockIdx.z;
   const int L = a.seq_len[seq];
   const int G = a.gqa;
+  const int n_groups = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
+  const int wpg = 4 / n_groups;          // waves per row group
+  const int group = wave / wpg;
+  const int GP = 4 * n_groups;           // padded query rows
   const int n_tiles = (L + kTile - 1) / kTile;
-  const int tps = (n_tiles + a.n_splits - 1) / a.n_splits;
-  const int t_begin = min(n_tiles, split * tps);
-  const int t_end = min(n_tiles, t_begin + tps);
 
-  __shared__ float sq[GP][kD];
+  __shared__ float sq[GMAX][kD];
   __shared__ uint32_t lut[256];
-  __shared__ float s_o[4][GP][kD];
-  __shared__ float s_m[4][GP];
-  __shared__ float s_l[4][GP];
+  __shared__ float s_p[4][4][kTile];
+  __shared__ float s_o[4][4][kD];
+  __shared__ float s_m[4][4];
+  __shared__ float s_l[4][4];
 
-  // ---- query rows (zero rows pad G up to GP); rot4 K: sign flip + WHT ----
+  const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
+  const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
+  const uint8_t* vbase = a.vcodes + ph * a.capacity * row_code_bytes(VC);
+  const uint16_t* ksb = has_scales(KC) ? a.kscales + ph * a.capacity * 4 : nullptr;
+  const uint16_t* vsb = has_scales(VC) ? a.vscales + ph * a.capacity * 4 : nullptr;
+  const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
+  const uint16_t* vnb = has_norms(VC) ? a.vnorms + ph * a.capacity : nullptr;
+
+  // Every global load below is unconditional: a load under a branch makes
+  // the compiler wait for all outstanding loads where the paths merge, which
+  // would serialise the prefetch.  Out-of-range indices are clamped instead.
+  // Query rows: thread tid stages floats 8*tid .. 8*tid+7 of the padded
+  // [16][128] block (rows >= G read row G-1 and are zeroed below).
   const float* qrow = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
-  for (int i = tid; i < GP * kD; i += 256) {
-    const int g = i >> 7, c = i & 127;
-    float v = g < G ? qrow[g * kD + c] : 0.0f;
-    if constexpr (KC == ROT4) v = ((a.ksigns[c >> 5] >> (c & 31)) & 1u) ? -v : v;
-    sq[g][c] = v;
+  const int qg_row = (8 * tid) >> 7;
+  const float* qsrc = qrow + min(qg_row, G - 1) * kD + ((8 * tid) & 127);
+  const float4v q0 = *reinterpret_cast<const float4v*>(qsrc);
+  const float4v q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
+
+  // Tiles are dealt out interleaved: split s owns tiles s, s + n_splits, ...
+  // and the wpg waves of a row group take every wpg-th of those, so at any
+  // moment the waves working on one stream read one contiguous window.
+  // This wave's tiles: t0, t0 + step, ... below n_tiles.  Loads of tiles
+  // past the last one are clamped to it; a wave without tiles re-reads tile
+  // 0 of the stream, which always exists.
+  const int step = a.n_splits * wpg;
+  const int t0 = split + a.n_splits * (wave - group * wpg);
+  const int t_end = n_tiles;
+  const int t_last = t0 < t_end ? t0 + ((t_end - 1 - t0) / step) * step : 0;
+  TileRegs<KC, VC> ta, tb;
+  [[maybe_unused]] TileRegs<KC, VC> tc;
+  load_tile<KC, VC>(ta, min(t0, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+  load_tile<KC, VC>(tb, min(t0 + step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+
+  // ---- query rows to LDS (zero rows pad G up to 16); rot4 K: sign flip + WHT
+  {
+    const int c0 = (8 * tid) & 127;
+    const bool live = qg_row < G;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
+      if constexpr (KC == ROT4) v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;
+      sq[qg_row][c0 + j] = v;
+    }
   }
   if constexpr (KC == ROT4 || VC == ROT4) {
-    const int i = tid;
-    lut[i] = static_cast<uint32_t>(kLevelBits[i & 15]) | (static_cast<uint32_t>(kLevelBits[i >> 4]) << 16);
+    lut[tid] = static_cast<uint32_t>(kLevelBits[tid & 15]) | (static_cast<uint32_t>(kLevelBits[tid >> 4]) << 16);
   }
   __syncthreads();
   if constexpr (KC == ROT4) {
@@ -200,194 +420,85 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // rot4 K rows reconstruct as N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
   const float qs = (KC == ROT4) ? a.qscale * (1.0f / 128.0f) : a.qscale;
 
-  // ---- B operands of S = K Q^T: column n16 = 4*(row) + block slot ----------
-  half8 bqh[NT][4], bql[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int g = 4 * nt + (n16 >> 2);
+  // ---- A operands of S^T = Q K^T for this wave's 4 query rows: row n16 =
+  //      4*(query row) + block slot; lane group qg carries block qg, and the
+  //      operand is zero unless slot == qg ----
+  half8 aqh[4], aql[4];
+  {
+    const int g = 4 * group + (n16 >> 2);
     const bool live = (n16 & 3) == qg;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = live ? sq[g][k_chan<KC>(qg, m, j)] * qs : 0.0f;
-        const _Float16 hi = static_cast<_Float16>(v);
-        bqh[nt][m][j] = hi;
-        bql[nt][m][j] = static_cast<_Float16>(v - static_cast<float>(hi));
+      for (int j = 0; j < 8; ++j) v[j] = live ? sq[g][k_chan<KC>(qg, m, j)] * qs : 0.0f;
+      split8(v, aqh[m], aql[m]);
+    }
+  }
+
+  WaveState st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.oacc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (t0 < t_end) {
+    if constexpr (prefetch_depth<KC, VC>() == 2) {
+      // three register buffers in rotation: two tiles in flight while one is used
+      for (int t = t0;;) {
+        load_tile<KC, VC>(tc, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+        process_tile<KC, VC>(ta, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        t += step;
+        if (t >= t_end) break;
+        load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+        process_tile<KC, VC>(tb, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        t += step;
+        if (t >= t_end) break;
+        load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+        process_tile<KC, VC>(tc, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        t += step;
+        if (t >= t_end) break;
+      }
+    } else {
+      // two buffers: the next tile is in flight while one is used
+      for (int t = t0;;) {
+        process_tile<KC, VC>(ta, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+        t += step;
+        if (t >= t_end) break;
+        process_tile<KC, VC>(tb, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+        t += step;
+        if (t >= t_end) break;
       }
     }
   }
 
-  const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
-  const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
-  const uint8_t* vbase = a.vcodes + ph * a.capacity * row_code_bytes(VC);
-  const uint16_t* ksb = has_scales(KC) ? a.kscales + ph * a.capacity * 4 : nullptr;
-  const uint16_t* vsb = has_scales(VC) ? a.vscales + ph * a.capacity * 4 : nullptr;
-  const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
-  const uint16_t* vnb = has_norms(VC) ? a.vnorms + ph * a.capacity : nullptr;
-
-  float m_run[NT], l_run[NT];
-  float4v oacc[NT][8];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) oacc[nt][c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  for (int t = t_begin + wave; t < t_end; t += 4) {
-    // ---- loads: every wave-wide 16-byte load covers 1 KB of contiguous bytes
-    const uint8_t* kt = kbase + static_cast<int64_t>(t) * tile_code_bytes(KC);
-    const uint8_t* vt = vbase + static_cast<int64_t>(t) * tile_code_bytes(VC);
-    u32x4 kd[2][KCB];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int c = 0; c < KCB; ++c)
-        kd[hf][c] = *reinterpret_cast<const u32x4*>(kt + ((hf * KCB + c) * 64 + lane) * 16);
-    u32x4 vd[NVL];
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) vd[i] = *reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16);
-    const int blk = lane & 3;
-    u32x4 kss{}, kns{}, vss{}, vns{};
-    if constexpr (has_scales(KC)) kss = *reinterpret_cast<const u32x4*>(ksb + static_cast<int64_t>(t) * 128 + blk * 32 + 8 * qg);
-    if constexpr (has_norms(KC)) kns = *reinterpret_cast<const u32x4*>(knb + static_cast<int64_t>(t) * 32 + 8 * qg);
-    if constexpr (has_scales(VC)) vss = *reinterpret_cast<const u32x4*>(vsb + static_cast<int64_t>(t) * 128 + blk * 32 + 8 * qg);
-    if constexpr (has_norms(VC)) vns = *reinterpret_cast<const u32x4*>(vnb + static_cast<int64_t>(t) * 32 + 8 * qg);
-
-    // ---- S = K Q^T per (row, block) column, two 16-row halves ----
-    float s[NT][8];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      half8 ak[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) ak[m] = unpack_k<KC>(kd[hf], m, lut);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          acc = mfma16(ak[m], bqh[nt][m], acc);
-          acc = mfma16(ak[m], bql[nt][m], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[nt][4 * hf + i] = acc[i];
-      }
-    }
-    if constexpr (KC != F16) {
-      float kf[8];
-      row_factors<KC>(kss, kns, kf);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s[nt][j] *= kf[j];
+  // ---- per-wave state to LDS (rows of this wave's group) ----
+  {
+    const float l = row16_sum(st.l_run);
+    if (n16 == 0) {
+      s_m[wave][qg] = st.m_run;
+      s_l[wave][qg] = l;
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = s[nt][j];
-        v += quad_xor1(v);
-        v += quad_xor2(v);
-        s[nt][j] = v;
-      }
-    const int row0 = t * kTile + 8 * qg;
-    const bool partial = (t + 1) * kTile > L;
-    if (partial) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (row0 + j >= L) s[nt][j] = -INFINITY;
-    }
-
-    // ---- online softmax (base 2) ----
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float tmax = s[nt][0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, s[nt][j]);
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[nt], tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mnew);
-      float psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(s[nt][j] - mnew);
-        s[nt][j] = p;
-        psum += p;
-      }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      m_run[nt] = mnew;
-      // the accumulator rows of lane group qg belong to query row 4*nt + qg
-      const float alpha_o = __shfl(alpha, 4 * qg, kWave);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) oacc[nt][c] *= alpha_o;
-    }
-
-    // ---- O += P V: A rows (query row, block) carry P times the V block factor
-    float vf[8];
-    if constexpr (VC != F16) row_factors<VC>(vss, vns, vf);
-    half8 aph[NT], apl[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = s[nt][j];
-        if constexpr (VC != F16) v = (v != 0.0f) ? v * vf[j] : 0.0f;
-        const _Float16 hi = static_cast<_Float16>(v);
-        aph[nt][j] = hi;
-        apl[nt][j] = static_cast<_Float16>(v - static_cast<float>(hi));
-      }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      half8 bv = unpack_v<VC>(vd, c, lut);
-      if constexpr (VC == F16) {
-        if (partial) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (row0 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        oacc[nt][c] = mfma16(aph[nt], bv, oacc[nt][c]);
-        oacc[nt][c] = mfma16(apl[nt], bv, oacc[nt][c]);
-      }
-    }
-  }
-
-  // ---- per-wave state to LDS ----
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = l_run[nt];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    if (qg == 0 && (n16 & 3) == 0) {
-      s_m[wave][4 * nt + (n16 >> 2)] = m_run[nt];
-      s_l[wave][4 * nt + (n16 >> 2)] = l;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) s_o[wave][4 * nt + qg][16 * c + n16] = oacc[nt][c][c >> 1];
+    for (int c = 0; c < 8; ++c) s_o[wave][qg][16 * c + n16] = st.oacc[c][c >> 1];
   }
   __syncthreads();
 
-  // ---- merge the 4 waves; write the partial or the final row ----
+  // ---- merge the waves of each row group; write the partial or final row ----
   const bool final_out = a.n_splits == 1;
   for (int i = tid; i < GP * kD; i += 256) {
     const int g = i >> 7, c = i & 127;
+    const int grp = g >> 2, r = g & 3;
     float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][g]);
+    for (int w = grp * wpg; w < (grp + 1) * wpg; ++w) M = fmaxf(M, s_m[w][r]);
     float O = 0.0f, Ls = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float lw = s_l[w][g];
+    for (int w = grp * wpg; w < (grp + 1) * wpg; ++w) {
+      const float lw = s_l[w][r];
       if (lw > 0.0f) {
-        const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-        O += s_o[w][g][c] * f;
+        const float f = __builtin_amdgcn_exp2f(s_m[w][r] - M);
+        O += s_o[w][r][c] * f;
         Ls += lw * f;
       }
     }
@@ -428,22 +539,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-#define VIT_DECODE_NT(KC, VC)                                                                 \
-  switch (nt) {                                                                               \
-    case 1: hipLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(256), 0, stream, args); break; \
-    case 2: hipLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(256), 0, stream, args); break; \
-    case 4: hipLaunchKernelGGL((decode_kernel<KC, VC, 4>), grid, dim3(256), 0, stream, args); break; \
-    default: return hipErrorInvalidValue;                                                     \
-  }
-
 #define VIT_DECODE_FOR_K(KC)                                                          \
-  hipError_t launch_decode_k##KC(int vc, int nt, dim3 grid, hipStream_t stream,       \
+  hipError_t launch_decode_k##KC(int vc, dim3 grid, hipStream_t stream,               \
                                  const DecodeArgs& args) {                            \
     switch (vc) {                                                                     \
-      case F16: VIT_DECODE_NT(KC, F16) break;                                         \
-      case Q8_0: VIT_DECODE_NT(KC, Q8_0) break;                                       \
-      case Q4_0: VIT_DECODE_NT(KC, Q4_0) break;                                       \
-      case ROT4: VIT_DECODE_NT(KC, ROT4) break;                                       \
+      case F16: hipLaunchKernelGGL((decode_kernel<KC, F16>), grid, dim3(256), 0, stream, args); break;   \
+      case Q8_0: hipLaunchKernelGGL((decode_kernel<KC, Q8_0>), grid, dim3(256), 0, stream, args); break; \
+      case Q4_0: hipLaunchKernelGGL((decode_kernel<KC, Q4_0>), grid, dim3(256), 0, stream, args); break; \
+      case ROT4: hipLaunchKernelGGL((decode_kernel<KC, ROT4>), grid, dim3(256), 0, stream, args); break; \
       default: return hipErrorInvalidValue;                                           \
     }                                                                                 \
     return hipGetLastError();                                                         \

@@ -43,9 +43,11 @@ __device__ constexpr float kThresholds[15] = {
 // Physical layout (see include/vit.h).  Offsets are within one 32-row tile.
 
 // K side: row p of the tile, block b, 16-byte unit c of that block's bytes.
+// Rows 16h .. 16h+15 form half h; lane 16b + r of a wave-wide 16-byte load of
+// (half h, unit c) reads row 16h + r, block b.
 __host__ __device__ inline int k_unit_offset(int codec, int p, int b, int c) {
-  const int h = (p >> 2) & 1;
-  const int r = ((p >> 3) << 2) | (p & 3);
+  const int h = p >> 4;
+  const int r = p & 15;
   const int cb = units_per_block(codec);
   return (((h * cb + c) * 4 + b) * 16 + r) * 16;
 }
@@ -69,8 +71,10 @@ __host__ __device__ inline int v_code_offset(int codec, int p, int ch, int* shif
   return base + (j >> 1);
 }
 
-// scales: fp16 [tile][block][32]
-__host__ __device__ inline int64_t scale_index(int64_t tile, int b, int p) { return tile * 128 + b * 32 + p; }
+// scales of one stream: K side in row order [row][block]; V side
+// block-major inside each tile [tile][block][32].
+__host__ __device__ inline int64_t k_scale_index(int64_t row, int b) { return row * 4 + b; }
+__host__ __device__ inline int64_t v_scale_index(int64_t tile, int b, int p) { return tile * 128 + b * 32 + p; }
 
 // ---------------------------------------------------------------------------
 // Scalar helpers (encode side: every operation is one IEEE binary32 rounding).

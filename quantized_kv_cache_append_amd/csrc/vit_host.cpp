@@ -187,10 +187,9 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   load_signs(k, a.ksigns);
   load_signs(v, a.vsigns);
   for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
-  const int nt = gqa <= 4 ? 1 : (gqa <= 8 ? 2 : 4);
   const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
                   static_cast<unsigned>(k->n_seqs));
-  return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  return vit::launch_decode(k->codec, v->codec, grid, hs, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 
 int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,

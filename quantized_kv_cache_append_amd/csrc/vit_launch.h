@@ -53,11 +53,11 @@ struct ReduceArgs {
 };
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
-hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode(int kc, int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k0(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k1(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k2(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k3(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
 
 }  // namespace vit

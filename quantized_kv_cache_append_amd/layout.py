@@ -24,8 +24,8 @@ def _k_perm(codec):
     b = byte // (16 * cb)
     c = (byte % (16 * cb)) // 16
     i = byte % 16
-    h = (p >> 2) & 1
-    r = ((p >> 3) << 2) | (p & 3)
+    h = p >> 4
+    r = p & 15
     return (((h * cb + c) * 4 + b) * 16 + r) * 16 + i
 
 
@@ -115,15 +115,21 @@ def pack_codes(codec, side, codes, raw):
     return raw
 
 
-def unpack_scales(raw, n_seqs, n_kv_heads, capacity):
-    """fp16 bits [S][H][cap/32][4][32] -> [S, H, capacity, 4]."""
-    s = np.asarray(raw, dtype=np.uint16).reshape(n_seqs, n_kv_heads, capacity // TILE, 4, TILE)
+def unpack_scales(side, raw, n_seqs, n_kv_heads, capacity):
+    """fp16 scale bits -> [S, H, capacity, 4].  K side: stored [S][H][cap][4];
+    V side: stored [S][H][cap/32][4][32]."""
+    s = np.asarray(raw, dtype=np.uint16)
+    if side == "k":
+        return s.reshape(n_seqs, n_kv_heads, capacity, 4)
+    s = s.reshape(n_seqs, n_kv_heads, capacity // TILE, 4, TILE)
     return np.ascontiguousarray(s.transpose(0, 1, 2, 4, 3)).reshape(n_seqs, n_kv_heads, capacity, 4)
 
 
-def pack_scales(scales):
+def pack_scales(side, scales):
     s = np.asarray(scales, dtype=np.uint16)
     S, H, cap, _ = s.shape
+    if side == "k":
+        return np.ascontiguousarray(s).reshape(-1)
     return np.ascontiguousarray(s.reshape(S, H, cap // TILE, TILE, 4).transpose(0, 1, 2, 4, 3)).reshape(-1)
 
 

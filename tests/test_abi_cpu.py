@@ -172,14 +172,15 @@ def test_k_layout_16_byte_units_are_contiguous_per_lane():
         offs = np.sort(perm.reshape(-1))
         assert np.array_equal(offs, np.arange(32 * layout.ROW_BYTES[codec]))
         for p in range(32):
-            h, r = (p >> 2) & 1, ((p >> 3) << 2) | (p & 3)
+            h, r = p >> 4, p & 15
             for b in range(4):
                 for c in range(cb):
                     lane = b * 16 + r
                     assert perm[p, b * 16 * cb + 16 * c] == ((h * cb + c) * 64 + lane) * 16
 
 
-def test_scales_layout_roundtrip():
+@pytest.mark.parametrize("side", ["k", "v"])
+def test_scales_layout_roundtrip(side):
     rng = np.random.default_rng(4)
     s = rng.integers(0, 65536, (2, 3, 256, 4)).astype(np.uint16)
-    assert np.array_equal(layout.unpack_scales(layout.pack_scales(s), 2, 3, 256), s)
+    assert np.array_equal(layout.unpack_scales(side, layout.pack_scales(side, s), 2, 3, 256), s)
