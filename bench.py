@@ -156,15 +156,21 @@ def run_gpu(args):
     stream = torch.cuda.current_stream()
 
     # every call of a step, marshalled once per replica (the host then only
-    # issues the C calls, so the GPU queue never runs dry)
+    # issues the C calls, so the GPU queue never runs dry).  One new token per
+    # sequence: its K/V rows go through the decode call's fused append.  A
+    # ubatch of new rows (the ladder) is appended by vit_kv_append_quant first.
+    fused = T == 1
     calls = []
     for r in range(replicas):
         app, dec = [], []
         for li, lay in enumerate(layers):
             kn, vn = new_rows[li]
-            app.append(vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=stream))
-            app.append(vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=stream))
+            if not fused:
+                app.append(vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=stream))
+                app.append(vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=stream))
             d = vit.prepare_decode(lay.K[r], lay.V[r], q[li], Hq, lens, out[li], n_splits=n_splits,
+                                   k_new=kn[:, 0].contiguous() if fused else None,
+                                   v_new=vn[:, 0].contiguous() if fused else None,
                                    workspace=ws if n_splits > 1 else None, stream=stream)
             red = vit.prepare_reduce(ws, S, Hq, n_splits, lay.V[r], out[li], stream=stream) if n_splits > 1 else None
             dec.append((d, red))

@@ -4,20 +4,21 @@
 // of the codec formats (codes and fp16 scales are bit-exact), so no multiply
 // may fuse with an add.
 //
-// Work split: one wave per (8-row group, KV head, sequence).  The wave walks
-// the group's rows that fall in [pos0, pos0 + n_tokens), encodes each row with
-// the row encoder (lane l holds channels l and l + 64), writes the K-side
-// units / scales / norms directly, and for the V side collects the group's
-// codes in LDS so that each V column unit (8 rows of one channel, several rows
-// sharing a byte for the 4-bit codecs) is read-modified-written by one lane.
-#include "vit_device.h"
-#include "vit_launch.h"
+// Work split: one 8-wave workgroup per (8-row group, KV head, sequence);
+// wave j encodes row 8g + j when it lies in [pos0, pos0 + n_tokens) (lane l
+// holds channels l and l + 64).  K rows go straight to their tile units.  For
+// the V side the group's codes are collected in LDS, and each V column word
+// (8 rows of one channel; rows share bytes in the 4-bit codecs) is then
+// read-modified-written by a single lane, keeping rows outside the range.
+#include "decode_impl.h"
 
 namespace vit {
 
 template <int CODEC, int SIDE>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(512) void append_kernel(AppendArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = tid >> 6;  // row of the group handled by this wave
   const int grp_local = blockIdx.x;
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
@@ -25,113 +26,83 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   const int64_t p_end = p_begin + a.n_tokens;
   const int64_t g = (p_begin >> 3) + grp_local;  // 8-row group index in the stream
   const int64_t g_first_row = g * 8;
-  if (g_first_row >= p_end) return;  // this sequence has fewer groups
+  if (g_first_row >= p_end) return;  // this sequence has fewer groups (uniform)
 
   constexpr int RB = row_code_bytes(CODEC);
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
   uint8_t* codes = static_cast<uint8_t*>(a.codes) + ph * a.capacity * RB;
-  uint16_t* scales = a.scales ? a.scales + ph * a.capacity * 4 : nullptr;
-  uint16_t* norms = a.norms ? a.norms + ph * a.capacity : nullptr;
+  uint16_t* scales = has_scales(CODEC) ? a.scales + ph * a.capacity * 4 : nullptr;
+  uint16_t* norms = has_norms(CODEC) ? a.norms + ph * a.capacity : nullptr;
   const uint32_t signs[4] = {a.signs[0], a.signs[1], a.signs[2], a.signs[3]};
 
-  __shared__ uint8_t row_bytes[256];        // canonical bytes of one K row
-  __shared__ uint32_t vcodes[8][128];       // V codes of the group's 8 rows
-  __shared__ uint32_t in_range[8];
+  __shared__ uint8_t rowbuf[8][256];
+  __shared__ uint32_t vcodes[8][128];
 
-  if (lane < 8) {
-    const int64_t p = g_first_row + lane;
-    in_range[lane] = (p >= p_begin && p < p_end) ? 1u : 0u;
-  }
-  __syncthreads();
+  const int64_t p = g_first_row + j;
+  const bool live = p >= p_begin && p < p_end;
+  const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + (p - p_begin)) * a.n_kv_heads + head) * kD;
 
-  for (int j = 0; j < 8; ++j) {
-    const int64_t p = g_first_row + j;
-    if (!in_range[j]) continue;
-    const int64_t t = p - p_begin;
-    const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + t) * a.n_kv_heads + head) * kD;
-    const float x0 = src[lane];
-    const float x1 = src[lane + 64];
-    const RowCodes rc = encode_row<CODEC>(x0, x1, lane, signs);
-
-    const int64_t tile = p >> 5;
-    const int pt = static_cast<int>(p & 31);
-    if (scales && (lane & 31) == 0) {
-      const int b0 = lane >> 5;  // block of x0; x1 is in block 2 + b0
-      if constexpr (SIDE == 0) {
-        scales[k_scale_index(p, b0)] = rc.s0;
-        scales[k_scale_index(p, 2 + b0)] = rc.s1;
-      } else {
-        scales[v_scale_index(tile, b0, pt)] = rc.s0;
-        scales[v_scale_index(tile, 2 + b0, pt)] = rc.s1;
-      }
-    }
-    if (norms && lane == 0) norms[p] = rc.norm;
-
-    if constexpr (SIDE == 0) {
-      // canonical row bytes in LDS, then 16-byte units to their tile slots
-      if constexpr (CODEC == F16) {
-        reinterpret_cast<uint16_t*>(row_bytes)[lane] = static_cast<uint16_t>(rc.c0);
-        reinterpret_cast<uint16_t*>(row_bytes)[lane + 64] = static_cast<uint16_t>(rc.c1);
-        __syncthreads();
-      } else if constexpr (CODEC == Q8_0) {
-        row_bytes[lane] = static_cast<uint8_t>(rc.c0);
-        row_bytes[lane + 64] = static_cast<uint8_t>(rc.c1);
-        __syncthreads();
-      } else {
-        // nibble codes: byte 16b + j = code[32b + j] | code[32b + j + 16] << 4
-        __shared__ uint8_t nib[128];
-        nib[lane] = static_cast<uint8_t>(rc.c0);
-        nib[lane + 64] = static_cast<uint8_t>(rc.c1);
-        __syncthreads();
-        const int b = lane >> 4, jj = lane & 15;
-        row_bytes[lane] = static_cast<uint8_t>(nib[32 * b + jj] | (nib[32 * b + jj + 16] << 4));
-        __syncthreads();
-      }
-      constexpr int CB = units_per_block(CODEC);
-      if (lane < 4 * CB) {
-        const int b = lane / CB, c = lane % CB;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row_bytes + b * 16 * CB + 16 * c);
-        *reinterpret_cast<u32x4*>(codes + tile * tile_code_bytes(CODEC) + k_unit_offset(CODEC, pt, b, c)) = v;
-      }
-      __syncthreads();
-    } else {
+  if constexpr (SIDE == 0) {
+    if (live) append_one_row<CODEC, 0>(codes, scales, norms, p, src, lane, signs, rowbuf[j]);
+  } else {
+    if (live) {
+      const RowCodes rc = encode_row<CODEC>(src[lane], src[lane + 64], lane, signs);
       vcodes[j][lane] = rc.c0;
       vcodes[j][lane + 64] = rc.c1;
-    }
-  }
-
-  if constexpr (SIDE == 1) {
-    __syncthreads();
-    // one lane per channel (two channels per lane): merge the group's rows
-    // into the channel's column unit, keeping rows outside the range.
-    const int64_t tile = g_first_row >> 5;
-    const int pbase = static_cast<int>(g_first_row & 31);  // 8-aligned
-    uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
-    for (int half = 0; half < 2; ++half) {
-      const int ch = lane + 64 * half;
-      int sh;
-      if constexpr (CODEC == F16) {
-        uint16_t* u = reinterpret_cast<uint16_t*>(tbase + v_code_offset(CODEC, pbase, ch, &sh));
-        for (int j = 0; j < 8; ++j)
-          if (in_range[j]) u[j] = static_cast<uint16_t>(vcodes[j][ch]);
-      } else if constexpr (CODEC == Q8_0) {
-        for (int j = 0; j < 8; ++j)
-          if (in_range[j]) tbase[v_code_offset(CODEC, pbase + j, ch, &sh)] = static_cast<uint8_t>(vcodes[j][ch]);
-      } else {
-        // 4-bit: the channel's 8 rows live in one aligned 32-bit word
-        const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
-        uint32_t* wp = reinterpret_cast<uint32_t*>(tbase + (off0 & ~3));
-        uint32_t w = 0;
-        bool all = true;
-        for (int j = 0; j < 8; ++j) all = all && in_range[j];
-        if (!all) w = *wp;
-        for (int j = 0; j < 8; ++j) {
-          if (!in_range[j]) continue;
-          const int off = v_code_offset(CODEC, pbase + j, ch, &sh);
-          const int bit = ((off & 3) << 3) + sh;
-          w = (w & ~(0xFu << bit)) | ((vcodes[j][ch] & 0xFu) << bit);
+      const int64_t tile = p >> 5;
+      const int pt = static_cast<int>(p & 31);
+      if constexpr (has_scales(CODEC)) {
+        if ((lane & 31) == 0) {
+          const int b0 = lane >> 5;
+          scales[v_scale_index(tile, b0, pt)] = rc.s0;
+          scales[v_scale_index(tile, 2 + b0, pt)] = rc.s1;
         }
-        *wp = w;
+      }
+      if constexpr (has_norms(CODEC)) {
+        if (lane == 0) norms[p] = rc.norm;
+      }
+    }
+    __syncthreads();
+    if (j == 0) {
+      // one lane per channel (two channels per lane): merge the group's rows
+      // into the channel's column unit, keeping rows outside the range.
+      bool in_range[8];
+      bool all = true;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        in_range[r] = g_first_row + r >= p_begin && g_first_row + r < p_end;
+        all = all && in_range[r];
+      }
+      const int64_t tile = g_first_row >> 5;
+      const int pbase = static_cast<int>(g_first_row & 31);  // 8-aligned
+      uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ch = lane + 64 * half;
+        int sh;
+        if constexpr (CODEC == F16) {
+          uint16_t* u = reinterpret_cast<uint16_t*>(tbase + v_code_offset(CODEC, pbase, ch, &sh));
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (in_range[r]) u[r] = static_cast<uint16_t>(vcodes[r][ch]);
+        } else if constexpr (CODEC == Q8_0) {
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (in_range[r]) tbase[v_code_offset(CODEC, pbase + r, ch, &sh)] = static_cast<uint8_t>(vcodes[r][ch]);
+        } else {
+          // 4-bit: the channel's 8 rows live in one aligned 32-bit word
+          const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
+          uint32_t* wp = reinterpret_cast<uint32_t*>(tbase + (off0 & ~3));
+          uint32_t w = all ? 0u : *wp;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            if (!in_range[r]) continue;
+            const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
+            const int bit = ((off & 3) << 3) + sh;
+            w = (w & ~(0xFu << bit)) | ((vcodes[r][ch] & 0xFu) << bit);
+          }
+          *wp = w;
+        }
       }
     }
   }
@@ -139,7 +110,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
 
 #define VIT_APPEND_CASE(C, S)                                                   \
   case (C)*2 + (S):                                                             \
-    hipLaunchKernelGGL((append_kernel<C, S>), grid, dim3(64), 0, stream, args); \
+    hipLaunchKernelGGL((append_kernel<C, S>), grid, dim3(512), 0, stream, args); \
     break;
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args) {

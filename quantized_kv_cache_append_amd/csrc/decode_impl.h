@@ -226,91 +226,213 @@ __device__ inline void load_tile(TileRegs<KC, VC>& r, int t, int lane, const uin
 }
 
 // Tiles kept in flight ahead of the one being used: two for the 4-bit pairs
-// (a tile is ~4.6 KB), one when a tile already carries >= 6 KB per wave.
-template <int KC, int VC>
+// with 4 query rows per wave (a tile is ~4.6 KB); one when a tile already
+// carries >= 6 KB per wave or when 8 query rows leave no registers for more.
+template <int KC, int VC, int NT>
 constexpr int prefetch_depth() {
-  return (tile_code_bytes(KC) + tile_code_bytes(VC)) <= 4096 ? 2 : 1;
+  return (NT == 1 && tile_code_bytes(KC) + tile_code_bytes(VC) <= 4096) ? 2 : 1;
 }
 
-// Per-wave online-softmax state for 4 query rows.
+// Quantize one new row of a (sequence, KV head) stream and store it, the way
+// the append kernel does, from a single wave (used for the fused append of
+// the decode call).  `rowbuf` is 256 bytes of LDS private to the calling wave.
+template <int C, int SIDE>
+__device__ inline void append_one_row(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t p,
+                                      const float* src, int lane, const uint32_t signs[4], uint8_t* rowbuf) {
+  const float x0 = src[lane];
+  const float x1 = src[lane + 64];
+  const RowCodes rc = encode_row<C>(x0, x1, lane, signs);
+  const int64_t tile = p >> 5;
+  const int pt = static_cast<int>(p & 31);
+  if constexpr (has_scales(C)) {
+    if ((lane & 31) == 0) {
+      const int b0 = lane >> 5;
+      if constexpr (SIDE == 0) {
+        scales[k_scale_index(p, b0)] = rc.s0;
+        scales[k_scale_index(p, 2 + b0)] = rc.s1;
+      } else {
+        scales[v_scale_index(tile, b0, pt)] = rc.s0;
+        scales[v_scale_index(tile, 2 + b0, pt)] = rc.s1;
+      }
+    }
+  }
+  if constexpr (has_norms(C)) {
+    if (lane == 0) norms[p] = rc.norm;
+  }
+  uint8_t* tbase = codes + tile * tile_code_bytes(C);
+  if constexpr (SIDE == 0) {
+    // canonical row bytes in LDS, then 16-byte units to their tile slots
+    if constexpr (C == F16) {
+      reinterpret_cast<uint16_t*>(rowbuf)[lane] = static_cast<uint16_t>(rc.c0);
+      reinterpret_cast<uint16_t*>(rowbuf)[lane + 64] = static_cast<uint16_t>(rc.c1);
+    } else if constexpr (C == Q8_0) {
+      rowbuf[lane] = static_cast<uint8_t>(rc.c0);
+      rowbuf[lane + 64] = static_cast<uint8_t>(rc.c1);
+    } else {
+      rowbuf[128 + lane] = static_cast<uint8_t>(rc.c0);
+      rowbuf[192 + lane] = static_cast<uint8_t>(rc.c1);
+      wave_lds_fence();
+      const int b = lane >> 4, j = lane & 15;
+      rowbuf[lane] = static_cast<uint8_t>(rowbuf[128 + 32 * b + j] | (rowbuf[128 + 32 * b + j + 16] << 4));
+    }
+    wave_lds_fence();
+    constexpr int CB = units_per_block(C);
+    if (lane < 4 * CB) {
+      const int b = lane / CB, c = lane % CB;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(rowbuf + b * 16 * CB + 16 * c);
+      *reinterpret_cast<u32x4*>(tbase + k_unit_offset(C, pt, b, c)) = v;
+    }
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ch = lane + 64 * half;
+      const uint32_t code = half ? rc.c1 : rc.c0;
+      int sh;
+      const int off = v_code_offset(C, pt, ch, &sh);
+      if constexpr (C == F16) {
+        *reinterpret_cast<uint16_t*>(tbase + off) = static_cast<uint16_t>(code);
+      } else if constexpr (C == Q8_0) {
+        tbase[off] = static_cast<uint8_t>(code);
+      } else {
+        // the channel's 8 rows share one aligned word; only this row changes
+        uint32_t* wp = reinterpret_cast<uint32_t*>(tbase + (off & ~3));
+        const int bit = ((off & 3) << 3) + sh;
+        *wp = (*wp & ~(0xFu << bit)) | ((code & 0xFu) << bit);
+      }
+    }
+  }
+}
+
+// Per-wave online-softmax state for 4*NT query rows.
+template <int NT>
 struct WaveState {
-  float m_run;        // running max (base 2) of the lane's query row
-  float l_run;        // lane-partial running sum
-  float4v oacc[8];    // P.V accumulators: N-tile c, rows (query row, block)
+  float m_run[NT];        // running max (base 2) of the lane's query row
+  float l_run[NT];        // lane-partial running sum
+  float4v oacc[NT][8];    // P.V accumulators: N-tile c, rows (query row, block)
+};
+
+// Q operands of S^T: in registers for 4 query rows per wave, in LDS (one
+// copy per row group, read once per tile and used for both halves) for 8.
+template <int NT>
+struct QOperands {
+  half8 h[NT][4], l[NT][4];
+};
+template <>
+struct QOperands<2> {
+  const half8* lds;  // [nt][m][hi/lo][64 lanes]
 };
 
 // One 32-row tile for one wave: S^T = Q K^T, online softmax, O += P V.
-template <int KC, int VC>
+template <int KC, int VC, int NT>
 __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t, int L, int lane,
-                                             const half8 (&aqh)[4], const half8 (&aql)[4], WaveState& st,
-                                             float (*s_p)[kTile], const uint32_t* lut) {
+                                             const QOperands<NT>& aq, WaveState<NT>& st,
+                                             float (*s_p)[4][kTile], const uint32_t* lut) {
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > L;
-  // ---- S^T: per half h, lane (n16, qg) gets the 4 block partials of query
-  //      row qg at tile row 16h + n16 ----
-  float s[2];
+  // ---- S^T: lane (n16, qg) gets the 4 block partials of query row 4*nt + qg
+  //      at tile row 16h + n16, for both halves h ----
+  half8 bk[2][4];
+  float kf[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    half8 bk[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) bk[m] = unpack_k<KC>(cur.kd[h], m, lut);
-    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 4; ++m) bk[h][m] = unpack_k<KC>(cur.kd[h], m, lut);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc = mfma16(aqh[m], bk[m], acc);
-      acc = mfma16(aql[m], bk[m], acc);
-    }
-    float v;
-    if constexpr (KC == F16) {
-      v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    } else {
-      float kf[4];
+    for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
+    if constexpr (KC != F16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
+      for (int i = 0; i < 4; ++i) kf[h][i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
       if constexpr (KC == ROT4) {
         const float nrm = f16_to_float(cur.kn[h]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kf[i] *= nrm;
+        for (int i = 0; i < 4; ++i) kf[h][i] *= nrm;
       }
-      v = (acc[0] * kf[0] + acc[1] * kf[1]) + (acc[2] * kf[2] + acc[3] * kf[3]);
     }
-    if (partial && t * kTile + 16 * h + n16 >= L) v = -INFINITY;
-    s[h] = v;
+  }
+  float s[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float4v acc_h[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    float4v acc_l[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      half8 qh, ql;
+      if constexpr (NT == 1) {
+        qh = aq.h[nt][m];
+        ql = aq.l[nt][m];
+      } else {
+        qh = aq.lds[((nt * 4 + m) * 2 + 0) * 64 + lane];
+        ql = aq.lds[((nt * 4 + m) * 2 + 1) * 64 + lane];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc_h[h] = mfma16(qh, bk[h][m], acc_h[h]);
+        acc_l[h] = mfma16(ql, bk[h][m], acc_l[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4v acc = acc_h[h] + acc_l[h];
+      float v;
+      if constexpr (KC == F16) v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      else v = (acc[0] * kf[h][0] + acc[1] * kf[h][1]) + (acc[2] * kf[h][2] + acc[3] * kf[h][3]);
+      const bool dead = partial && t * kTile + 16 * h + n16 >= L;
+      s[nt][h] = dead ? -INFINITY : v;
+    }
   }
 
   // ---- online softmax (base 2); all lanes of a 16-lane row share the row state
-  const float tmax = row16_max(fmaxf(s[0], s[1]));
-  const float mnew = fmaxf(st.m_run, tmax);
-  if (__builtin_amdgcn_ballot_w64(mnew > st.m_run)) {
-    const float alpha = __builtin_amdgcn_exp2f(st.m_run - mnew);
-    st.l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st.oacc[c] *= alpha;
-    st.m_run = mnew;
+  for (int nt = 0; nt < NT; ++nt) {
+    const float tmax = row16_max(fmaxf(s[nt][0], s[nt][1]));
+    const float mnew = fmaxf(st.m_run[nt], tmax);
+    if (__builtin_amdgcn_ballot_w64(mnew > st.m_run[nt])) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[nt] - mnew);
+      st.l_run[nt] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.oacc[nt][c] *= alpha;
+      st.m_run[nt] = mnew;
+    }
+    const float p0 = __builtin_amdgcn_exp2f(s[nt][0] - st.m_run[nt]);
+    const float p1 = __builtin_amdgcn_exp2f(s[nt][1] - st.m_run[nt]);
+    st.l_run[nt] += p0 + p1;
+    s_p[nt][qg][n16] = p0;
+    s_p[nt][qg][16 + n16] = p1;
   }
-  const float p0 = __builtin_amdgcn_exp2f(s[0] - st.m_run);
-  const float p1 = __builtin_amdgcn_exp2f(s[1] - st.m_run);
-  st.l_run += p0 + p1;
-  s_p[qg][n16] = p0;
-  s_p[qg][16 + n16] = p1;
+  wave_lds_fence();
+  float pv[NT][8];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float4v p_lo = *reinterpret_cast<const float4v*>(&s_p[nt][n16 >> 2][8 * qg]);
+    const float4v p_hi = *reinterpret_cast<const float4v*>(&s_p[nt][n16 >> 2][8 * qg + 4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[nt][j] = p_lo[j];
+      pv[nt][4 + j] = p_hi[j];
+    }
+  }
   wave_lds_fence();
 
   // ---- O += P V: A row n16 = 4*(query row) + block b carries P times the
   //      block-b factor of V over tile rows 8qg .. 8qg+7 ----
-  const float4v p_lo = *reinterpret_cast<const float4v*>(&s_p[n16 >> 2][8 * qg]);
-  const float4v p_hi = *reinterpret_cast<const float4v*>(&s_p[n16 >> 2][8 * qg + 4]);
-  wave_lds_fence();
-  float pv[8] = {p_lo[0], p_lo[1], p_lo[2], p_lo[3], p_hi[0], p_hi[1], p_hi[2], p_hi[3]};
+  float vf[8];
   if constexpr (VC != F16) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float f = f16_to_float(cur.vs[j >> 1] >> ((j & 1) * 16));
       if constexpr (VC == ROT4) f *= f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
-      pv[j] = (pv[j] != 0.0f) ? pv[j] * f : 0.0f;
+      vf[j] = f;
     }
   }
-  half8 aph, apl;
-  split8(pv, aph, apl);
+  half8 aph[NT], apl[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if constexpr (VC != F16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[nt][j] = (pv[nt][j] != 0.0f) ? pv[nt][j] * vf[j] : 0.0f;
+    }
+    split8(pv[nt], aph[nt], apl[nt]);
+  }
   const int row8 = t * kTile + 8 * qg;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -322,16 +444,21 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
           if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
       }
     }
-    st.oacc[c] = mfma16(aph, bv, st.oacc[c]);
-    st.oacc[c] = mfma16(apl, bv, st.oacc[c]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      st.oacc[nt][c] = mfma16(aph[nt], bv, st.oacc[nt][c]);
+      st.oacc[nt][c] = mfma16(apl[nt], bv, st.oacc[nt][c]);
+    }
   }
 }
 
-// Decode kernel.  Row groups: query rows 4k .. 4k+3 of the KV head are handled
-// by the waves w with w / (4 / n_groups) == k; those waves share out the
+// Decode kernel.  A wave handles RW = 4*NT query rows of its KV head; with
+// more than RW rows (G > RW) the rows form row groups, and row group k is
+// handled by the waves w with w / (4 / n_groups) == k, which share out the
 // workgroup's tiles round-robin.
-template <int KC, int VC>
+template <int KC, int VC, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+  constexpr int RW = 4 * NT;
   constexpr int GMAX = 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,18 +470,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int seq = blockIdx.z;
   const int L = a.seq_len[seq];
   const int G = a.gqa;
-  const int n_groups = G <= 4 ? 1 : (G <= 8 ? 2 : 4);
-  const int wpg = 4 / n_groups;          // waves per row group
+  const int n_groups = (G + RW - 1) / RW;   // 1, 2 or 4
+  const int wpg = 4 / n_groups;             // waves per row group
   const int group = wave / wpg;
-  const int GP = 4 * n_groups;           // padded query rows
+  const int GP = RW * n_groups;             // padded query rows
   const int n_tiles = (L + kTile - 1) / kTile;
 
   __shared__ float sq[GMAX][kD];
   __shared__ uint32_t lut[256];
-  __shared__ float s_p[4][4][kTile];
-  __shared__ float s_o[4][4][kD];
-  __shared__ float s_m[4][4];
-  __shared__ float s_l[4][4];
+  __shared__ float s_p[4][NT][4][kTile];
+  __shared__ float s_o[4][RW][kD];
+  __shared__ float s_m[4][RW];
+  __shared__ float s_l[4][RW];
+  __shared__ uint8_t s_row[2][256];
+  __shared__ half8 s_aq[NT == 2 ? 2 : 1][NT][4][2][64];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
   const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
@@ -364,23 +493,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
   const uint16_t* vnb = has_norms(VC) ? a.vnorms + ph * a.capacity : nullptr;
 
+  // ---- fused append: the workgroup owning the new row's tile stores the new
+  //      K and V rows before it reads any tile (no other workgroup reads it) ----
+  if (a.k_new != nullptr && ((L - 1) / kTile) % a.n_splits == split) {
+    const int64_t p = L - 1;
+    const int64_t src = (static_cast<int64_t>(seq) * a.n_kv_heads + head) * kD;
+    if (wave == 0) {
+      append_one_row<KC, 0>(const_cast<uint8_t*>(kbase), const_cast<uint16_t*>(ksb), const_cast<uint16_t*>(knb),
+                            p, a.k_new + src, lane, a.ksigns, s_row[0]);
+    } else if (wave == 1) {
+      append_one_row<VC, 1>(const_cast<uint8_t*>(vbase), const_cast<uint16_t*>(vsb), const_cast<uint16_t*>(vnb),
+                            p, a.v_new + src, lane, a.vsigns, s_row[1]);
+    }
+    // Only waves of this workgroup read the row back, and they share its L1:
+    // the barrier's workgroup-scope release/acquire is enough.  (A device-scope
+    // fence here writes back and invalidates the L2 and costs tens of us.)
+    __syncthreads();
+  }
+
   // Every global load below is unconditional: a load under a branch makes
   // the compiler wait for all outstanding loads where the paths merge, which
   // would serialise the prefetch.  Out-of-range indices are clamped instead.
-  // Query rows: thread tid stages floats 8*tid .. 8*tid+7 of the padded
-  // [16][128] block (rows >= G read row G-1 and are zeroed below).
   const float* qrow = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
-  const int qg_row = (8 * tid) >> 7;
-  const float* qsrc = qrow + min(qg_row, G - 1) * kD + ((8 * tid) & 127);
-  const float4v q0 = *reinterpret_cast<const float4v*>(qsrc);
-  const float4v q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
+  // query block qg of this lane's rows (non-rot4 K: operands come straight from here)
+  float4v qv[NT][8];
+  if constexpr (KC != ROT4) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int g = RW * group + 4 * nt + (n16 >> 2);
+      const float* qb = qrow + min(g, G - 1) * kD + 32 * qg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[nt][i] = *reinterpret_cast<const float4v*>(qb + 4 * i);
+    }
+  }
+  // rot4 K: thread tid stages floats 8*tid .. 8*tid+7 of the padded [16][128] rows
+  const int qs_row = (8 * tid) >> 7;
+  [[maybe_unused]] float4v q0, q1;
+  if constexpr (KC == ROT4) {
+    const float* qsrc = qrow + min(qs_row, G - 1) * kD + ((8 * tid) & 127);
+    q0 = *reinterpret_cast<const float4v*>(qsrc);
+    q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
+  }
 
   // Tiles are dealt out interleaved: split s owns tiles s, s + n_splits, ...
   // and the wpg waves of a row group take every wpg-th of those, so at any
   // moment the waves working on one stream read one contiguous window.
-  // This wave's tiles: t0, t0 + step, ... below n_tiles.  Loads of tiles
-  // past the last one are clamped to it; a wave without tiles re-reads tile
-  // 0 of the stream, which always exists.
+  // This wave's tiles: t0, t0 + step, ... below n_tiles.  Loads past the last
+  // one are clamped to it; a wave without tiles re-reads tile 0 (always there).
   const int step = a.n_splits * wpg;
   const int t0 = split + a.n_splits * (wave - group * wpg);
   const int t_end = n_tiles;
@@ -390,22 +549,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   load_tile<KC, VC>(ta, min(t0, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
   load_tile<KC, VC>(tb, min(t0 + step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
 
-  // ---- query rows to LDS (zero rows pad G up to 16); rot4 K: sign flip + WHT
-  {
-    const int c0 = (8 * tid) & 127;
-    const bool live = qg_row < G;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
-      if constexpr (KC == ROT4) v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;
-      sq[qg_row][c0 + j] = v;
-    }
-  }
   if constexpr (KC == ROT4 || VC == ROT4) {
     lut[tid] = static_cast<uint32_t>(kLevelBits[tid & 15]) | (static_cast<uint32_t>(kLevelBits[tid >> 4]) << 16);
   }
-  __syncthreads();
-  if constexpr (KC == ROT4) {
+  // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query
+  //      row) + block slot; lane group qg carries block qg, and the operand
+  //      is zero unless slot == qg ----
+  half8 aqh[NT][4], aql[NT][4];
+  bool aq_sync = false;
+  if constexpr (KC != ROT4) {
+    const float qs = a.qscale;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int g = RW * group + 4 * nt + (n16 >> 2);
+      const bool live = (n16 & 3) == qg && g < G;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = k_chan<KC>(0, m, j);  // channel within block qg
+          v[j] = live ? qv[nt][c >> 2][c & 3] * qs : 0.0f;
+        }
+        split8(v, aqh[nt][m], aql[nt][m]);
+      }
+    }
+    aq_sync = VC == ROT4;  // the LUT
+  } else {
+    // rot4 K: rotate the query rows like the keys (sign flip, WHT) in LDS
+    {
+      const int c0 = (8 * tid) & 127;
+      const bool live = qs_row < G;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
+        v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;
+        sq[qs_row][c0 + j] = v;
+      }
+    }
+    __syncthreads();
     for (int h = 1; h < kD; h <<= 1) {
       for (int i = tid; i < GP * 64; i += 256) {
         const int g = i >> 6, k = i & 63;
@@ -416,57 +598,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       __syncthreads();
     }
-  }
-  // rot4 K rows reconstruct as N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
-  const float qs = (KC == ROT4) ? a.qscale * (1.0f / 128.0f) : a.qscale;
-
-  // ---- A operands of S^T = Q K^T for this wave's 4 query rows: row n16 =
-  //      4*(query row) + block slot; lane group qg carries block qg, and the
-  //      operand is zero unless slot == qg ----
-  half8 aqh[4], aql[4];
-  {
-    const int g = 4 * group + (n16 >> 2);
-    const bool live = (n16 & 3) == qg;
+    // rot4 K rows reconstruct as N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
+    const float qs = a.qscale * (1.0f / 128.0f);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float v[8];
+    for (int nt = 0; nt < NT; ++nt) {
+      const int g = RW * group + 4 * nt + (n16 >> 2);
+      const bool live = (n16 & 3) == qg;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = live ? sq[g][k_chan<KC>(qg, m, j)] * qs : 0.0f;
-      split8(v, aqh[m], aql[m]);
+      for (int m = 0; m < 4; ++m) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = live ? sq[g][k_chan<KC>(qg, m, j)] * qs : 0.0f;
+        split8(v, aqh[nt][m], aql[nt][m]);
+      }
     }
   }
 
-  WaveState st;
-  st.m_run = -INFINITY;
-  st.l_run = 0.0f;
+  QOperands<NT> aq;
+  if constexpr (NT == 1) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) st.oacc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 4; ++m) {
+      aq.h[0][m] = aqh[0][m];
+      aq.l[0][m] = aql[0][m];
+    }
+    if (aq_sync) __syncthreads();
+  } else {
+    // one copy per row group, written by the group's first wave
+    if (wave == group * wpg) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s_aq[group][nt][m][0][lane] = aqh[nt][m];
+          s_aq[group][nt][m][1][lane] = aql[nt][m];
+        }
+    }
+    __syncthreads();
+    aq.lds = &s_aq[group][0][0][0][0];
+  }
+
+  WaveState<NT> st;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.m_run[nt] = -INFINITY;
+    st.l_run[nt] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.oacc[nt][c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   if (t0 < t_end) {
-    if constexpr (prefetch_depth<KC, VC>() == 2) {
+    if constexpr (prefetch_depth<KC, VC, NT>() == 2) {
       // three register buffers in rotation: two tiles in flight while one is used
       for (int t = t0;;) {
         load_tile<KC, VC>(tc, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC>(ta, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        process_tile<KC, VC, NT>(ta, t, L, lane, aq, st, s_p[wave], lut);
         t += step;
         if (t >= t_end) break;
         load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC>(tb, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        process_tile<KC, VC, NT>(tb, t, L, lane, aq, st, s_p[wave], lut);
         t += step;
         if (t >= t_end) break;
         load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC>(tc, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        process_tile<KC, VC, NT>(tc, t, L, lane, aq, st, s_p[wave], lut);
         t += step;
         if (t >= t_end) break;
       }
     } else {
       // two buffers: the next tile is in flight while one is used
       for (int t = t0;;) {
-        process_tile<KC, VC>(ta, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        process_tile<KC, VC, NT>(ta, t, L, lane, aq, st, s_p[wave], lut);
         load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
         t += step;
         if (t >= t_end) break;
-        process_tile<KC, VC>(tb, t, L, lane, aqh, aql, st, s_p[wave], lut);
+        process_tile<KC, VC, NT>(tb, t, L, lane, aq, st, s_p[wave], lut);
         load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
         t += step;
         if (t >= t_end) break;
@@ -474,15 +678,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ---- per-wave state to LDS (rows of this wave's group) ----
-  {
-    const float l = row16_sum(st.l_run);
+  // ---- per-wave state to LDS ----
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float l = row16_sum(st.l_run[nt]);
     if (n16 == 0) {
-      s_m[wave][qg] = st.m_run;
-      s_l[wave][qg] = l;
+      s_m[wave][4 * nt + qg] = st.m_run[nt];
+      s_l[wave][4 * nt + qg] = l;
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_o[wave][qg][16 * c + n16] = st.oacc[c][c >> 1];
+    for (int c = 0; c < 8; ++c) s_o[wave][4 * nt + qg][16 * c + n16] = st.oacc[nt][c][c >> 1];
   }
   __syncthreads();
 
@@ -490,7 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool final_out = a.n_splits == 1;
   for (int i = tid; i < GP * kD; i += 256) {
     const int g = i >> 7, c = i & 127;
-    const int grp = g >> 2, r = g & 3;
+    const int grp = g / RW, r = g % RW;
     float M = -INFINITY;
     for (int w = grp * wpg; w < (grp + 1) * wpg; ++w) M = fmaxf(M, s_m[w][r]);
     float O = 0.0f, Ls = 0.0f;
@@ -539,14 +744,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+#define VIT_DECODE_NT(KC, VC)                                                                 \
+  if (nt == 1) hipLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(256), 0, stream, args); \
+  else hipLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(256), 0, stream, args);
+
 #define VIT_DECODE_FOR_K(KC)                                                          \
-  hipError_t launch_decode_k##KC(int vc, dim3 grid, hipStream_t stream,               \
+  hipError_t launch_decode_k##KC(int vc, int nt, dim3 grid, hipStream_t stream,       \
                                  const DecodeArgs& args) {                            \
     switch (vc) {                                                                     \
-      case F16: hipLaunchKernelGGL((decode_kernel<KC, F16>), grid, dim3(256), 0, stream, args); break;   \
-      case Q8_0: hipLaunchKernelGGL((decode_kernel<KC, Q8_0>), grid, dim3(256), 0, stream, args); break; \
-      case Q4_0: hipLaunchKernelGGL((decode_kernel<KC, Q4_0>), grid, dim3(256), 0, stream, args); break; \
-      case ROT4: hipLaunchKernelGGL((decode_kernel<KC, ROT4>), grid, dim3(256), 0, stream, args); break; \
+      case F16: VIT_DECODE_NT(KC, F16) break;                                         \
+      case Q8_0: VIT_DECODE_NT(KC, Q8_0) break;                                       \
+      case Q4_0: VIT_DECODE_NT(KC, Q4_0) break;                                       \
+      case ROT4: VIT_DECODE_NT(KC, ROT4) break;                                       \
       default: return hipErrorInvalidValue;                                           \
     }                                                                                 \
     return hipGetLastError();                                                         \

@@ -1,66 +1,114 @@
 // Split-K merge of decode partials, plus the decode dispatch over K codecs.
 //
-// One 128-thread workgroup per (query head, sequence); thread c owns channel c.
-// Partial s of a row is (o_s[128] unnormalised, m_s in base-2 units, l_s):
-// M = max m_s, L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.  Empty
-// splits (l_s = 0, m_s = -inf) are skipped.  For a rot4 V plane the merged
-// row is in the rotated domain scaled by sqrt(128); it is mapped back with
-// x = s .* (H o) / 128.
+// One 256-thread workgroup per (query head, sequence).  Thread t owns channels
+// 4*(t & 31) .. +3 and the partials s = (t >> 5), (t >> 5) + 8, ... ; each
+// thread merges its partials online, then the 8 partial merges per channel are
+// combined through LDS.  Partial s of a row is (o_s[128] unnormalised, m_s in
+// base-2 units, l_s): M = max m_s, L = sum l_s 2^(m_s - M),
+// O = sum o_s 2^(m_s - M) / L.  Empty partials (l_s = 0, m_s = -inf) are
+// skipped.  For a rot4 V plane the merged row is in the rotated domain scaled
+// by sqrt(128); it is mapped back with x = s .* (H o) / 128.
 #include "vit_device.h"
 #include "vit_launch.h"
 
 namespace vit {
 
-__global__ __launch_bounds__(128) void reduce_kernel(ReduceArgs a) {
+__device__ inline void merge_into(float& M, float& L, float4v& O, float pm, float pl, float4v po) {
+  if (pl > 0.0f) {
+    if (pm > M) {
+      const float sc = __builtin_amdgcn_exp2f(M - pm);
+      O *= sc;
+      L *= sc;
+      M = pm;
+    }
+    const float f = __builtin_amdgcn_exp2f(pm - M);
+    O += po * f;
+    L += pl * f;
+  }
+}
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   const int hq = blockIdx.x;
   const int seq = blockIdx.y;
-  const int c = threadIdx.x;
+  const int t = threadIdx.x;
+  const int cg = t & 31, sl = t >> 5;
   const int64_t row = static_cast<int64_t>(seq) * a.n_q_heads + hq;
   const float* ml = a.ws_ml + row * a.n_splits * 2;
-  const float* o = a.ws_o + row * a.n_splits * kD;
+  const float* o = a.ws_o + row * a.n_splits * kD + 4 * cg;
 
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float O = 0.0f, L = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.0f) {
-      const float f = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-      O += o[static_cast<int64_t>(s) * kD + c] * f;
-      L += l * f;
+  __shared__ float s_m[8], s_l[8];
+  __shared__ float s_o[8][kD];
+  __shared__ float v[kD];
+
+  float M = -INFINITY, L = 0.0f;
+  float4v O = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 4 partials per round, all loads issued first (indices clamped, not branched)
+  for (int s0 = sl; s0 < a.n_splits; s0 += 32) {
+    float pm[4], pl[4];
+    float4v po[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(s0 + 8 * i, a.n_splits - 1);
+      pm[i] = ml[2 * s];
+      pl[i] = ml[2 * s + 1];
+      po[i] = *reinterpret_cast<const float4v*>(o + static_cast<int64_t>(s) * kD);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + 8 * i < a.n_splits) merge_into(M, L, O, pm[i], pl[i], po[i]);
   }
-  float r = L > 0.0f ? O / L : 0.0f;
+  if (cg == 0) {
+    s_m[sl] = M;
+    s_l[sl] = L;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_o[sl][4 * cg + i] = O[i];
+  __syncthreads();
+
+  if (t < kD) {
+    float Mf = -INFINITY, Lf = 0.0f, Of = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Mf = fmaxf(Mf, s_m[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s_l[i] > 0.0f) {
+        const float f = __builtin_amdgcn_exp2f(s_m[i] - Mf);
+        Of += s_o[i][t] * f;
+        Lf += s_l[i] * f;
+      }
+    }
+    v[t] = Lf > 0.0f ? Of / Lf : 0.0f;
+  }
   if (a.rotate) {
-    __shared__ float v[kD];
-    v[c] = r;
     __syncthreads();
     for (int h = 1; h < kD; h <<= 1) {
-      if (c < 64) {
-        const int lo = ((c & ~(h - 1)) << 1) | (c & (h - 1));
+      if (t < 64) {
+        const int lo = ((t & ~(h - 1)) << 1) | (t & (h - 1));
         const float x = v[lo], y = v[lo + h];
         v[lo] = x + y;
         v[lo + h] = x - y;
       }
       __syncthreads();
     }
-    r = v[c] * (1.0f / 128.0f);
-    r = ((a.vsigns[c >> 5] >> (c & 31)) & 1u) ? -r : r;
+    if (t < kD) {
+      float r = v[t] * (1.0f / 128.0f);
+      v[t] = ((a.vsigns[t >> 5] >> (t & 31)) & 1u) ? -r : r;
+    }
   }
-  a.out[row * kD + c] = r;
+  if (t < kD) a.out[row * kD + t] = v[t];
 }
 
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args) {
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(kD), 0, stream, args);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int kc, int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args) {
+hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args) {
   switch (kc) {
-    case F16: return launch_decode_k0(vc, grid, stream, args);
-    case Q8_0: return launch_decode_k1(vc, grid, stream, args);
-    case Q4_0: return launch_decode_k2(vc, grid, stream, args);
-    case ROT4: return launch_decode_k3(vc, grid, stream, args);
+    case F16: return launch_decode_k0(vc, nt, grid, stream, args);
+    case Q8_0: return launch_decode_k1(vc, nt, grid, stream, args);
+    case Q4_0: return launch_decode_k2(vc, nt, grid, stream, args);
+    case ROT4: return launch_decode_k3(vc, nt, grid, stream, args);
     default: return hipErrorInvalidValue;
   }
 }

@@ -115,6 +115,9 @@ __device__ inline T shfl_xor(T v, int m) {
 
 // ---------------------------------------------------------------------------
 // Wave-level row encoders.  Lane l holds channels l (x0) and l + 64 (x1).
+// Every encoder body disables fp contraction: the operation order of the
+// codec definitions is part of the format, whatever flags the including
+// translation unit uses.
 // Blocks: x0 is in block l>>5, x1 in block 2 + (l>>5); the 32 lanes of a
 // half-wave hold one block, so block reductions are xor-shuffles 16..1.
 
@@ -131,6 +134,7 @@ __device__ inline float block_max_abs(float v) {
 }
 
 __device__ inline RowCodes encode_f16(float x0, float x1) {
+#pragma clang fp contract(off)
   RowCodes r{};
   r.c0 = f16_bits(x0);
   r.c1 = f16_bits(x1);
@@ -138,12 +142,14 @@ __device__ inline RowCodes encode_f16(float x0, float x1) {
 }
 
 __device__ inline int8_t q8_code(float x, float inv) {
+#pragma clang fp contract(off)
   float c = roundf(x * inv);  // round half away from zero
   c = fminf(fmaxf(c, -127.0f), 127.0f);
   return static_cast<int8_t>(c);
 }
 
 __device__ inline RowCodes encode_q8_0(float x0, float x1) {
+#pragma clang fp contract(off)
   RowCodes r{};
   const float d0 = block_max_abs(x0) / 127.0f;
   const float d1 = block_max_abs(x1) / 127.0f;
@@ -157,6 +163,7 @@ __device__ inline RowCodes encode_q8_0(float x0, float x1) {
 
 // q4_0 block scale from the first element of largest magnitude.
 __device__ inline float q4_block_scale(float x, int lane) {
+#pragma clang fp contract(off)
   // key: |x| bits (monotone for non-negative floats) high, inverted index low,
   // so the max picks the largest magnitude and, among equals, the first index.
   const uint32_t j = static_cast<uint32_t>(lane & 31);
@@ -172,12 +179,14 @@ __device__ inline float q4_block_scale(float x, int lane) {
 }
 
 __device__ inline uint32_t q4_code(float x, float inv) {
+#pragma clang fp contract(off)
   float c = roundf(x * inv) + 8.0f;
   c = fminf(fmaxf(c, 0.0f), 15.0f);
   return static_cast<uint32_t>(c);
 }
 
 __device__ inline RowCodes encode_q4_0(float x0, float x1, int lane) {
+#pragma clang fp contract(off)
   RowCodes r{};
   const float d0 = q4_block_scale(x0, lane);
   const float d1 = q4_block_scale(x1, lane);
@@ -201,6 +210,7 @@ __device__ inline uint32_t rot4_index(float t) {
 
 // signs: the 128-bit mask as 4 words; bit j set => channel j negated.
 __device__ inline RowCodes encode_rot4(float x0, float x1, int lane, const uint32_t signs[4]) {
+#pragma clang fp contract(off)
   RowCodes r{};
   const int ch0 = lane, ch1 = lane + 64;
   float w0 = ((signs[ch0 >> 5] >> (ch0 & 31)) & 1u) ? -x0 : x0;

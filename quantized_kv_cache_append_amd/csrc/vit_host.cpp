@@ -156,14 +156,6 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
     return VIT_E_ALIGN;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (k_new) {
-    int64_t pos0[VIT_MAX_SEQS];
-    for (int s = 0; s < k->n_seqs; ++s) pos0[s] = seq_len[s] - 1;
-    st = enqueue_append(k, k_new, pos0, 1, hs);
-    if (st != VIT_OK) return st;
-    st = enqueue_append(v, v_new, pos0, 1, hs);
-    if (st != VIT_OK) return st;
-  }
 
   vit::DecodeArgs a{};
   a.kcodes = static_cast<const uint8_t*>(k->codes);
@@ -173,6 +165,8 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   a.vscales = v->scales;
   a.vnorms = v->norms;
   a.q = q;
+  a.k_new = k_new;  // quantized and stored in-kernel by the owning workgroup
+  a.v_new = v_new;
   a.ws_o = workspace;
   a.ws_ml = workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
                                                  ws_o_bytes(k->n_seqs, n_q_heads, n_splits))
@@ -189,7 +183,8 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
   const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
                   static_cast<unsigned>(k->n_seqs));
-  return vit::launch_decode(k->codec, v->codec, grid, hs, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  const int nt = gqa <= 4 ? 1 : 2;  // query rows per wave: 4 or 8
+  return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 
 int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,

@@ -28,6 +28,8 @@ struct DecodeArgs {
   const uint16_t* vscales;
   const uint16_t* vnorms;
   const float* q;
+  const float* k_new;  // fused append: new K rows [S][Hkv][128] or null
+  const float* v_new;
   float* ws_o;     // [S][Hq][n_splits][128]
   float* ws_ml;    // [S][Hq][n_splits][2]
   float* out;      // [S][Hq][128]
@@ -53,11 +55,11 @@ struct ReduceArgs {
 };
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
-hipError_t launch_decode(int kc, int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k0(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k1(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k2(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k3(int vc, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
 
 }  // namespace vit
