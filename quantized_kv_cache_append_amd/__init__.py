@@ -6,7 +6,8 @@ PyTorch provides device memory and the stream, nothing else.  The Python
 names mirror the C entry points:
 
     vit_kv_plane_sizes, vit_kv_append_quant, vit_attn_workspace_bytes,
-    vit_attn_default_splits, vit_attn_decode, vit_attn_splitk_reduce
+    vit_attn_default_splits, vit_attn_decode, vit_attn_splitk_reduce,
+    vit_arm_kernel_events (a measurement aid)
 
 ``KVPlane`` allocates the three arrays of one (layer, side) cache tensor.
 """
@@ -21,7 +22,7 @@ from ._lib import CODEC_IDS, SIDE_IDS, VitError, VitKvPlane
 __all__ = [
     "KVPlane", "VitError", "layout",
     "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_attn_workspace_bytes",
-    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_splitk_reduce",
+    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_splitk_reduce", "vit_arm_kernel_events",
 ]
 
 HEAD_DIM = 128
@@ -185,6 +186,22 @@ def decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_sp
     if n_splits > 1:
         vit_attn_splitk_reduce(workspace, k.n_seqs, n_q_heads, HEAD_DIM, n_splits, v, out, stream)
     return out
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    h = int(ev.cuda_event)
+    if h == 0:
+        raise ValueError("event has no HIP handle yet: record it once before arming")
+    return ctypes.c_void_p(h)
+
+
+def vit_arm_kernel_events(start, stop):
+    """Make the next decode kernel record torch.cuda.Event ``start``/``stop``
+    at its own dispatch start and end (both None disarms)."""
+    st = _lib.load().vit_arm_kernel_events(_event_handle(start), _event_handle(stop))
+    return _lib.check("vit_arm_kernel_events", st)
 
 
 class _Prepared:

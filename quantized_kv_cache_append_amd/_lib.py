@@ -28,6 +28,7 @@ EXPORTS = (
     "vit_attn_default_splits",
     "vit_attn_decode",
     "vit_attn_splitk_reduce",
+    "vit_arm_kernel_events",
     "vit_status_string",
 )
 
@@ -78,6 +79,8 @@ def load():
     lib.vit_attn_workspace_bytes.restype = sz
     lib.vit_attn_default_splits.argtypes = [i32, i32, i32, i64]
     lib.vit_attn_default_splits.restype = i32
+    lib.vit_arm_kernel_events.argtypes = [vp, vp]
+    lib.vit_arm_kernel_events.restype = ctypes.c_int
     lib.vit_attn_decode.argtypes = [plane_p, plane_p, vp, i32, P(i64), vp, vp, f32, i32, vp, vp, vp]
     lib.vit_attn_decode.restype = ctypes.c_int
     lib.vit_attn_splitk_reduce.argtypes = [vp, i32, i32, i32, i32, plane_p, vp, vp]

@@ -744,13 +744,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-#define VIT_DECODE_NT(KC, VC)                                                                 \
-  if (nt == 1) hipLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(256), 0, stream, args); \
-  else hipLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(256), 0, stream, args);
+#define VIT_DECODE_NT(KC, VC)                                                                   \
+  if (nt == 1)                                                                                  \
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, args); \
+  else                                                                                          \
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, args);
 
 #define VIT_DECODE_FOR_K(KC)                                                          \
   hipError_t launch_decode_k##KC(int vc, int nt, dim3 grid, hipStream_t stream,       \
-                                 const DecodeArgs& args) {                            \
+                                 const DecodeArgs& args, const KernelEvents& ev) {    \
     switch (vc) {                                                                     \
       case F16: VIT_DECODE_NT(KC, F16) break;                                         \
       case Q8_0: VIT_DECODE_NT(KC, Q8_0) break;                                       \

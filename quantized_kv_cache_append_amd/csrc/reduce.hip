@@ -103,12 +103,13 @@ hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args) 
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args) {
+hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args,
+                         const KernelEvents& ev) {
   switch (kc) {
-    case F16: return launch_decode_k0(vc, nt, grid, stream, args);
-    case Q8_0: return launch_decode_k1(vc, nt, grid, stream, args);
-    case Q4_0: return launch_decode_k2(vc, nt, grid, stream, args);
-    case ROT4: return launch_decode_k3(vc, nt, grid, stream, args);
+    case F16: return launch_decode_k0(vc, nt, grid, stream, args, ev);
+    case Q8_0: return launch_decode_k1(vc, nt, grid, stream, args, ev);
+    case Q4_0: return launch_decode_k2(vc, nt, grid, stream, args, ev);
+    case ROT4: return launch_decode_k3(vc, nt, grid, stream, args, ev);
     default: return hipErrorInvalidValue;
   }
 }

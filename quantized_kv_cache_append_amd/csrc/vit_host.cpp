@@ -12,6 +12,9 @@ namespace {
 
 constexpr int kRowBytes[4] = {256, 128, 64, 64};
 
+// events armed by vit_arm_kernel_events for this host thread's next decode
+thread_local vit::KernelEvents g_armed;
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int check_plane(const vit_kv_plane* p) {
@@ -133,6 +136,8 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
 int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads,
                     const int64_t* seq_len, const float* k_new, const float* v_new, float scale,
                     int32_t n_splits, float* workspace, float* out, void* stream) {
+  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
+  g_armed = vit::KernelEvents{};
   int st = check_plane(k);
   if (st != VIT_OK) return st;
   st = check_plane(v);
@@ -184,7 +189,14 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
                   static_cast<unsigned>(k->n_seqs));
   const int nt = gqa <= 4 ? 1 : 2;  // query rows per wave: 4 or 8
-  return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
+}
+
+int vit_arm_kernel_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return VIT_E_ARG;
+  g_armed.start = static_cast<hipEvent_t>(start_event);
+  g_armed.stop = static_cast<hipEvent_t>(stop_event);
+  return VIT_OK;
 }
 
 int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,

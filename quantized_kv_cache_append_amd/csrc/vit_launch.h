@@ -1,6 +1,7 @@
 // Kernel argument blocks and launch entry points (host <-> kernels).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,12 +55,20 @@ struct ReduceArgs {
   uint32_t vsigns[4];
 };
 
+// Optional events recorded by the decode dispatch itself (kernel start and
+// end, via hipExtLaunchKernel); null members record nothing.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
-hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args,
+                         const KernelEvents& ev);
+hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
+hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
+hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
+hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
 
 }  // namespace vit

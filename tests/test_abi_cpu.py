@@ -145,6 +145,17 @@ def test_reduce_validation(lib):
     assert r(FAKE + 4, 2, 4, 128, 4, ctypes.byref(V), FAKE, None) == _lib.VIT_E_ALIGN
 
 
+def test_arm_kernel_events_validation(lib):
+    assert lib.vit_arm_kernel_events(FAKE, None) == _lib.VIT_E_ARG
+    assert lib.vit_arm_kernel_events(None, FAKE) == _lib.VIT_E_ARG
+    assert lib.vit_arm_kernel_events(None, None) == _lib.VIT_OK
+    # armed fake events are consumed by the next decode call even when it fails
+    # validation, so they are never handed to the runtime
+    assert lib.vit_arm_kernel_events(FAKE, FAKE) == _lib.VIT_OK
+    assert _decode(lib, _plane(side=0), _plane(side=1), ns=0) == _lib.VIT_E_ARG
+    assert lib.vit_arm_kernel_events(None, None) == _lib.VIT_OK
+
+
 # ------------------------------------------------------------- host layout
 @pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4"])
 @pytest.mark.parametrize("side", ["k", "v"])

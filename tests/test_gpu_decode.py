@@ -98,6 +98,40 @@ def test_deterministic_bitwise():
 
 
 @pytest.mark.gpu
+def test_kernel_events_bracket_the_decode_kernel():
+    """vit_arm_kernel_events: the decode dispatch records both events, the
+    output is unchanged, and the arming is one-shot."""
+    say("[decode-events]")
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    rng = np.random.default_rng(12)
+    S, H, G, cap, L = 2, 2, 4, 512, 400
+    K = make_plane("q8_0", "k", S, H, cap)
+    V = make_plane("q4_0", "v", S, H, cap)
+    append_rows(K, _rand_rows(rng, (S, L, H, D)), [0] * S)
+    append_rows(V, _rand_rows(rng, (S, L, H, D)), [0] * S)
+    q = torch.from_numpy(_rand_rows(rng, (S, H * G, D))).cuda()
+    plain = vit.decode(K, V, q, H * G, [L] * S, n_splits=1).cpu().numpy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    vit.vit_arm_kernel_events(e0, e1)
+    timed = vit.decode(K, V, q, H * G, [L] * S, n_splits=1)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0, ms
+    assert np.array_equal(timed.cpu().numpy(), plain)
+    # consumed: a second decode does not touch the events again
+    e0.synchronize()
+    again = vit.decode(K, V, q, H * G, [L] * S, n_splits=1)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
+    assert np.array_equal(again.cpu().numpy(), plain)
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("kc,vc", [("q8_0", "q8_0"), ("rot4", "q4_0"), ("f16", "rot4")])
 def test_fused_append_matches_separate_append(kc, vc):
     torch = torch_cuda()
