@@ -41,20 +41,20 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
 }
 __device__ inline uint32_t bits_h2(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
-// four int8 codes -> fp16 pairs (b0,b2) and (b1,b3): (0x6400 | (c ^ 0x80)) is
-// the fp16 value 1024 + c + 128, so subtracting 1152 is exact.
-__device__ inline u32x2 q8_pairs(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  const half2v k = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
-  u32x2 r;
-  r[0] = bits_h2(h2_bits(and_or(u, 0x00FF00FFu, 0x64006400u)) - k);
-  r[1] = bits_h2(h2_bits(and_or(u >> 8, 0x00FF00FFu, 0x64006400u)) - k);
-  return r;
-}
-
+// eight int8 codes (two words) -> fp16, element order (b0, b2, b1, b3) of each
+// word.  v_perm_b32 builds the fp16 bit patterns 0x64 | (c ^ 0x80), i.e. the
+// values 1024 + c + 128, and one packed subtract of 1152 per pair is exact:
+// per four codes one xor, two perms, two subtracts.  (Keeping the 1152 in the
+// operand and removing it after the product is not exact enough: the MFMA's
+// f16 accumulation then loses the low bits of the code terms.)
 __device__ inline half8 q8_unpack(uint32_t w0, uint32_t w1) {
-  const u32x2 a = q8_pairs(w0), b = q8_pairs(w1);
-  const u32x4 r = {a[0], a[1], b[0], b[1]};
+  const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
+  const half2v k = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  u32x4 r;
+  r[0] = bits_h2(h2_bits(__builtin_amdgcn_perm(0x64646464u, a, 0x04020400u)) - k);  // bytes 0, 2
+  r[1] = bits_h2(h2_bits(__builtin_amdgcn_perm(0x64646464u, a, 0x04030401u)) - k);  // bytes 1, 3
+  r[2] = bits_h2(h2_bits(__builtin_amdgcn_perm(0x64646464u, b, 0x04020400u)) - k);
+  r[3] = bits_h2(h2_bits(__builtin_amdgcn_perm(0x64646464u, b, 0x04030401u)) - k);
   return __builtin_bit_cast(half8, r);
 }
 
@@ -428,8 +428,14 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if constexpr (VC != F16) {
+      // rows past L of a partial tile may hold any bits (their p is 0)
+      if (partial) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pv[nt][j] = (pv[nt][j] != 0.0f) ? pv[nt][j] * vf[j] : 0.0f;
+        for (int j = 0; j < 8; ++j) pv[nt][j] = (pv[nt][j] != 0.0f) ? pv[nt][j] * vf[j] : 0.0f;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[nt][j] *= vf[j];
+      }
     }
     split8(pv[nt], aph[nt], apl[nt]);
   }
