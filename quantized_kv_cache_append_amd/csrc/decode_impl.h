@@ -309,7 +309,25 @@ struct WaveState {
   float m_run[NT];        // running max (base 2) of the lane's query row
   float l_run[NT];        // lane-partial running sum
   float4v oacc[NT][8];    // P.V accumulators: N-tile c, rows (query row, block)
+  // The softmax reference is m_run + vexp: p = 2^(s - m_run - vexp), so the
+  // P.V operand p * f (f = V block factor) carries 2^-vexp and stays in the
+  // fp16 normal range whatever the magnitude of V.  vexp (an integer, wave
+  // wide) is re-chosen when a tile's largest |f| leaves
+  // [2^(vexp-12), 2^(vexp+4)]; l and O share the reference, so O / l and the
+  // split merge are unaffected.
+  float vexp;
+  float vlo, vhi;         // that window as thresholds on |f|
 };
+
+// Largest |f| of the wave (every lane gets it).
+__device__ inline float wave_max(float v) {
+  v = row16_max(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
 
 // Q operands of S^T: in registers for 4 query rows per wave, in LDS (one
 // copy per row group, read once per tile and used for both halves) for 8.
@@ -329,6 +347,37 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
                                              float (*s_p)[4][kTile], const uint32_t* lut) {
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > L;
+  // ---- V block factors of the lane's P.V operand rows (block n16 & 3, tile
+  //      rows 8qg .. 8qg+7) and the wave's V exponent check, first so that
+  //      they overlap the S^T products ----
+  float vf[8];
+  float vexp_new = st.vexp;
+  bool v_rescale = false;
+  if constexpr (VC != F16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = f16_to_float(cur.vs[j >> 1] >> ((j & 1) * 16));
+      if constexpr (VC == ROT4) f *= f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
+      vf[j] = f;
+    }
+    if (partial) {
+      // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vf[j] = t * kTile + 8 * qg + j < L ? vf[j] : 0.0f;
+    }
+    float vm = fabsf(vf[0]);  // largest |factor| among this lane's rows
+#pragma unroll
+    for (int j = 1; j < 8; ++j) vm = fmaxf(vm, fabsf(vf[j]));
+    if (__builtin_amdgcn_ballot_w64(vm > st.vhi) || !__builtin_amdgcn_ballot_w64(vm >= st.vlo)) {
+      int e;
+      (void)__builtin_frexpf(wave_max(vm), &e);  // wave max in [2^(e-1), 2^e)
+      vexp_new = static_cast<float>(e);
+      st.vlo = __builtin_ldexpf(1.0f, e - 12);
+      st.vhi = __builtin_ldexpf(1.0f, e + 4);
+      v_rescale = true;
+    }
+  }
+
   // ---- S^T: lane (n16, qg) gets the 4 block partials of query row 4*nt + qg
   //      at tile row 16h + n16, for both halves h ----
   half8 bk[2][4];
@@ -381,24 +430,27 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
     }
   }
 
-  // ---- online softmax (base 2); all lanes of a 16-lane row share the row state
+  // ---- online softmax (base 2); all lanes of a 16-lane row share the row
+  //      state; the reference is m_run + vexp ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float tmax = row16_max(fmaxf(s[nt][0], s[nt][1]));
     const float mnew = fmaxf(st.m_run[nt], tmax);
-    if (__builtin_amdgcn_ballot_w64(mnew > st.m_run[nt])) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run[nt] - mnew);
+    if (__builtin_amdgcn_ballot_w64(mnew > st.m_run[nt]) || v_rescale) {
+      const float alpha = __builtin_amdgcn_exp2f((st.m_run[nt] + st.vexp) - (mnew + vexp_new));
       st.l_run[nt] *= alpha;
 #pragma unroll
       for (int c = 0; c < 8; ++c) st.oacc[nt][c] *= alpha;
       st.m_run[nt] = mnew;
     }
-    const float p0 = __builtin_amdgcn_exp2f(s[nt][0] - st.m_run[nt]);
-    const float p1 = __builtin_amdgcn_exp2f(s[nt][1] - st.m_run[nt]);
+    const float mref = st.m_run[nt] + vexp_new;
+    const float p0 = __builtin_amdgcn_exp2f(s[nt][0] - mref);
+    const float p1 = __builtin_amdgcn_exp2f(s[nt][1] - mref);
     st.l_run[nt] += p0 + p1;
     s_p[nt][qg][n16] = p0;
     s_p[nt][qg][16 + n16] = p1;
   }
+  st.vexp = vexp_new;
   wave_lds_fence();
   float pv[NT][8];
 #pragma unroll
@@ -415,27 +467,13 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
 
   // ---- O += P V: A row n16 = 4*(query row) + block b carries P times the
   //      block-b factor of V over tile rows 8qg .. 8qg+7 ----
-  float vf[8];
-  if constexpr (VC != F16) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float f = f16_to_float(cur.vs[j >> 1] >> ((j & 1) * 16));
-      if constexpr (VC == ROT4) f *= f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
-      vf[j] = f;
-    }
-  }
+
   half8 aph[NT], apl[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if constexpr (VC != F16) {
-      // rows past L of a partial tile may hold any bits (their p is 0)
-      if (partial) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[nt][j] = (pv[nt][j] != 0.0f) ? pv[nt][j] * vf[j] : 0.0f;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[nt][j] *= vf[j];
-      }
+      for (int j = 0; j < 8; ++j) pv[nt][j] *= vf[j];
     }
     split8(pv[nt], aph[nt], apl[nt]);
   }
@@ -651,6 +689,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int c = 0; c < 8; ++c) st.oacc[nt][c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  st.vexp = 0.0f;
+  st.vlo = INFINITY;  // the first tile sets the exponent
+  st.vhi = INFINITY;
 
   if (t0 < t_end) {
     if constexpr (prefetch_depth<KC, VC, NT>() == 2) {
@@ -689,7 +730,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int nt = 0; nt < NT; ++nt) {
     const float l = row16_sum(st.l_run[nt]);
     if (n16 == 0) {
-      s_m[wave][4 * nt + qg] = st.m_run[nt];
+      s_m[wave][4 * nt + qg] = st.m_run[nt] + st.vexp;  // the reference of l and O
       s_l[wave][4 * nt + qg] = l;
     }
 #pragma unroll

@@ -27,7 +27,7 @@ def _rand_rows(rng, shape, outliers=True):
     return x
 
 
-def _run_small(kc, vc, G, lens, n_splits, seed, S=2, H=2, cap=512):
+def _run_small(kc, vc, G, lens, n_splits, seed, S=2, H=2, cap=512, vmul=1.0, kmul=1.0):
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
 
@@ -37,8 +37,8 @@ def _run_small(kc, vc, G, lens, n_splits, seed, S=2, H=2, cap=512):
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     Lmax = max(lens)
-    kx = _rand_rows(rng, (S, Lmax, H, D))
-    vx = _rand_rows(rng, (S, Lmax, H, D))
+    kx = _rand_rows(rng, (S, Lmax, H, D)) * np.float32(kmul)
+    vx = _rand_rows(rng, (S, Lmax, H, D)) * np.float32(vmul)
     append_rows(K, kx, [0] * S)
     append_rows(V, vx, [0] * S)
     Hq = H * G
@@ -74,6 +74,19 @@ def test_gqa_widths(G):
     for kc, vc in (("q8_0", "q4_0"), ("rot4", "f16")):
         got, ref = _run_small(kc, vc, G, [96, 33], 2, seed=500 + G)
         check_close(got, ref, f"G={G} K={kc} V={vc}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("vc", ["q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("vmul", [1e-5, 1e-3, 1e2])
+def test_v_magnitude_range(vc, vmul):
+    """V rows far from unit scale: the P.V operand (probability times V block
+    factor) must stay accurate whatever the magnitude of V (tiny block
+    scales would otherwise put it into fp16 subnormals)."""
+    say(f"[decode-vmag] V={vc} x{vmul:g}")
+    for G, kc, ns in ((4, "q8_0", 2), (8, "f16", 3)):
+        got, ref = _run_small(kc, vc, G, [300, 77], ns, seed=900 + G, vmul=vmul)
+        check_close(got, ref, f"V={vc} x{vmul:g} K={kc} G={G}")
 
 
 @pytest.mark.gpu
