@@ -4,29 +4,31 @@
 // of the codec formats (codes and fp16 scales are bit-exact), so no multiply
 // may fuse with an add.
 //
-// Work split: one 8-wave workgroup per (8-row group, KV head, sequence);
-// wave j encodes row 8g + j when it lies in [pos0, pos0 + n_tokens) (lane l
-// holds channels l and l + 64).  K rows go straight to their tile units.  For
-// the V side the group's codes are collected in LDS, and each V column word
-// (8 rows of one channel; rows share bytes in the 4-bit codecs) is then
-// read-modified-written by a single lane, keeping rows outside the range.
+// Work split: one wave per (8-row group, KV head, sequence), four groups per
+// workgroup.  The wave loads all of its rows first (so their loads are in
+// flight together), encodes them together (each encoder step is issued for
+// all rows before the next; lane l holds channels l and l + 64 of a row), and
+// stores them.  K rows go to their tile units one
+// by one.  On the V side a channel's 8 rows of the group form one column
+// unit, so a lane assembles the unit of its two channels in registers and
+// writes it whole; a group cut by the range edge keeps the rows outside the
+// range (per-row stores, read-modify-write of the shared 4-bit words).
 #include "decode_impl.h"
 
 namespace vit {
 
 template <int CODEC, int SIDE>
-__global__ __launch_bounds__(512) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int j = tid >> 6;  // row of the group handled by this wave
-  const int grp_local = blockIdx.x;
+  const int wave = tid >> 6;
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
   const int64_t p_begin = a.pos0[seq];
   const int64_t p_end = p_begin + a.n_tokens;
-  const int64_t g = (p_begin >> 3) + grp_local;  // 8-row group index in the stream
+  const int64_t g = (p_begin >> 3) + static_cast<int64_t>(blockIdx.x) * kAppendWaves + wave;  // 8-row group
   const int64_t g_first_row = g * 8;
-  if (g_first_row >= p_end) return;  // this sequence has fewer groups (uniform)
+  if (g_first_row >= p_end) return;  // past this sequence's range (uniform per wave)
 
   constexpr int RB = row_code_bytes(CODEC);
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
@@ -35,74 +37,88 @@ __global__ __launch_bounds__(512) void append_kernel(AppendArgs a) {
   uint16_t* norms = has_norms(CODEC) ? a.norms + ph * a.capacity : nullptr;
   const uint32_t signs[4] = {a.signs[0], a.signs[1], a.signs[2], a.signs[3]};
 
-  __shared__ uint8_t rowbuf[8][256];
-  __shared__ uint32_t vcodes[8][128];
+  __shared__ uint8_t rowbuf[kAppendWaves][8][256];
 
-  const int64_t p = g_first_row + j;
-  const bool live = p >= p_begin && p < p_end;
-  const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + (p - p_begin)) * a.n_kv_heads + head) * kD;
+  bool live[8];
+  bool all = true;
+  float x0[8], x1[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int64_t p = g_first_row + r;
+    live[r] = p >= p_begin && p < p_end;
+    all = all && live[r];
+    // rows outside the range read a row inside it (clamped) and are not stored
+    const int64_t pc = p < p_begin ? p_begin : (p >= p_end ? p_end - 1 : p);
+    const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + (pc - p_begin)) * a.n_kv_heads + head) * kD;
+    x0[r] = src[lane];
+    x1[r] = src[lane + 64];
+  }
+  RowCodes rc[8];
+  encode_rows<CODEC, 8>(x0, x1, lane, signs, rc);
 
   if constexpr (SIDE == 0) {
-    if (live) append_one_row<CODEC, 0>(codes, scales, norms, p, src, lane, signs, rowbuf[j]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (live[r]) store_row<CODEC, 0>(codes, scales, norms, g_first_row + r, rc[r], lane, rowbuf[wave][r]);
+    return;
   } else {
-    if (live) {
-      const RowCodes rc = encode_row<CODEC>(src[lane], src[lane + 64], lane, signs);
-      vcodes[j][lane] = rc.c0;
-      vcodes[j][lane + 64] = rc.c1;
-      const int64_t tile = p >> 5;
-      const int pt = static_cast<int>(p & 31);
-      if constexpr (has_scales(CODEC)) {
-        if ((lane & 31) == 0) {
-          const int b0 = lane >> 5;
-          scales[v_scale_index(tile, b0, pt)] = rc.s0;
-          scales[v_scale_index(tile, 2 + b0, pt)] = rc.s1;
+    if (!all) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (live[r]) store_row<CODEC, 1>(codes, scales, norms, g_first_row + r, rc[r], lane, rowbuf[wave][r]);
+      return;
+    }
+    // the whole group is in range: write column units, scales and norms whole
+    const int64_t tile = g_first_row >> 5;
+    const int pbase = static_cast<int>(g_first_row & 31);  // 0, 8, 16 or 24
+    uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ch = lane + 64 * half;
+      uint32_t c[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) c[r] = half ? rc[r].c1 : rc[r].c0;
+      int sh;
+      const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
+      if constexpr (CODEC == F16) {
+        const u32x4 u = {c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+        *reinterpret_cast<u32x4*>(tbase + off0) = u;
+      } else if constexpr (CODEC == Q8_0) {
+        // row r goes to byte P8[r] = {0,2,1,3,4,6,5,7}[r] of the 8-byte unit
+        const uint32_t lo = (c[0] & 0xFFu) | ((c[2] & 0xFFu) << 8) | ((c[1] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
+        const uint32_t hi = (c[4] & 0xFFu) | ((c[6] & 0xFFu) << 8) | ((c[5] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
+        *reinterpret_cast<u32x2*>(tbase + off0) = u32x2{lo, hi};
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
+          w |= (c[r] & 0xFu) << (((off & 3) << 3) + sh);
         }
-      }
-      if constexpr (has_norms(CODEC)) {
-        if (lane == 0) norms[p] = rc.norm;
+        *reinterpret_cast<uint32_t*>(tbase + (off0 & ~3)) = w;
       }
     }
-    __syncthreads();
-    if (j == 0) {
-      // one lane per channel (two channels per lane): merge the group's rows
-      // into the channel's column unit, keeping rows outside the range.
-      bool in_range[8];
-      bool all = true;
+    if constexpr (has_scales(CODEC)) {
+      // lane 0 holds blocks 0 and 2, lane 32 blocks 1 and 3 (uniform per half-wave)
+      if ((lane & 31) == 0) {
+        const int b0 = lane >> 5;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        in_range[r] = g_first_row + r >= p_begin && g_first_row + r < p_end;
-        all = all && in_range[r];
-      }
-      const int64_t tile = g_first_row >> 5;
-      const int pbase = static_cast<int>(g_first_row & 31);  // 8-aligned
-      uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+        for (int half = 0; half < 2; ++half) {
+          uint32_t sv[8];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ch = lane + 64 * half;
-        int sh;
-        if constexpr (CODEC == F16) {
-          uint16_t* u = reinterpret_cast<uint16_t*>(tbase + v_code_offset(CODEC, pbase, ch, &sh));
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            if (in_range[r]) u[r] = static_cast<uint16_t>(vcodes[r][ch]);
-        } else if constexpr (CODEC == Q8_0) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            if (in_range[r]) tbase[v_code_offset(CODEC, pbase + r, ch, &sh)] = static_cast<uint8_t>(vcodes[r][ch]);
-        } else {
-          // 4-bit: the channel's 8 rows live in one aligned 32-bit word
-          const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
-          uint32_t* wp = reinterpret_cast<uint32_t*>(tbase + (off0 & ~3));
-          uint32_t w = all ? 0u : *wp;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            if (!in_range[r]) continue;
-            const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
-            const int bit = ((off & 3) << 3) + sh;
-            w = (w & ~(0xFu << bit)) | ((vcodes[r][ch] & 0xFu) << bit);
-          }
-          *wp = w;
+          for (int r = 0; r < 8; ++r) sv[r] = half ? rc[r].s1 : rc[r].s0;
+          const u32x4 u = {sv[0] | (sv[1] << 16), sv[2] | (sv[3] << 16), sv[4] | (sv[5] << 16), sv[6] | (sv[7] << 16)};
+          *reinterpret_cast<u32x4*>(scales + v_scale_index(tile, b0 + 2 * half, pbase)) = u;
         }
+      }
+    }
+    if constexpr (has_norms(CODEC)) {
+      if (lane == 0) {
+        uint32_t nv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) nv[r] = rc[r].norm;
+        const u32x4 u = {nv[0] | (nv[1] << 16), nv[2] | (nv[3] << 16), nv[4] | (nv[5] << 16), nv[6] | (nv[7] << 16)};
+        *reinterpret_cast<u32x4*>(norms + g_first_row) = u;
       }
     }
   }
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(512) void append_kernel(AppendArgs a) {
 
 #define VIT_APPEND_CASE(C, S)                                                   \
   case (C)*2 + (S):                                                             \
-    hipLaunchKernelGGL((append_kernel<C, S>), grid, dim3(512), 0, stream, args); \
+    hipLaunchKernelGGL((append_kernel<C, S>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
     break;
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args) {

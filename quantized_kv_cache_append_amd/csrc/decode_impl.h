@@ -233,15 +233,13 @@ constexpr int prefetch_depth() {
   return (NT == 1 && tile_code_bytes(KC) + tile_code_bytes(VC) <= 4096) ? 2 : 1;
 }
 
-// Quantize one new row of a (sequence, KV head) stream and store it, the way
-// the append kernel does, from a single wave (used for the fused append of
-// the decode call).  `rowbuf` is 256 bytes of LDS private to the calling wave.
+// Store one encoded row p of a (sequence, KV head) stream from a single wave:
+// scales, norm and codes (K: canonical bytes staged in `rowbuf`, 256 bytes of
+// LDS private to the wave, then 16-byte units; V: the row's code in each
+// channel's column unit, a read-modify-write for the 4-bit codecs).
 template <int C, int SIDE>
-__device__ inline void append_one_row(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t p,
-                                      const float* src, int lane, const uint32_t signs[4], uint8_t* rowbuf) {
-  const float x0 = src[lane];
-  const float x1 = src[lane + 64];
-  const RowCodes rc = encode_row<C>(x0, x1, lane, signs);
+__device__ inline void store_row(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t p,
+                                 const RowCodes& rc, int lane, uint8_t* rowbuf) {
   const int64_t tile = p >> 5;
   const int pt = static_cast<int>(p & 31);
   if constexpr (has_scales(C)) {
@@ -301,6 +299,14 @@ __device__ inline void append_one_row(uint8_t* codes, uint16_t* scales, uint16_t
       }
     }
   }
+}
+
+// Quantize one new row and store it (the fused append of the decode call).
+template <int C, int SIDE>
+__device__ inline void append_one_row(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t p,
+                                      const float* src, int lane, const uint32_t signs[4], uint8_t* rowbuf) {
+  const RowCodes rc = encode_row<C>(src[lane], src[lane + 64], lane, signs);
+  store_row<C, SIDE>(codes, scales, norms, p, rc, lane, rowbuf);
 }
 
 // Per-wave online-softmax state for 4*NT query rows.

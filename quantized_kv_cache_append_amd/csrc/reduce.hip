@@ -1,11 +1,11 @@
 // Split-K merge of decode partials, plus the decode dispatch over K codecs.
 //
-// One 256-thread workgroup per (query head, sequence).  Thread t owns channels
-// 4*(t & 31) .. +3 and the partials s = (t >> 5), (t >> 5) + 8, ... ; each
-// thread merges its partials online, then the 8 partial merges per channel are
-// combined through LDS.  Partial s of a row is (o_s[128] unnormalised, m_s in
-// base-2 units, l_s): M = max m_s, L = sum l_s 2^(m_s - M),
-// O = sum o_s 2^(m_s - M) / L.  Empty partials (l_s = 0, m_s = -inf) are
+// One workgroup per (query head, sequence) of 32 x SL threads (SL = 8, or 32
+// above 64 splits).  Thread t owns channels 4*(t & 31) .. +3 and the partials
+// s = (t >> 5), (t >> 5) + SL, ... ; each thread merges its partials online,
+// then the SL partial merges per channel are combined through LDS.  Partial s
+// of a row is (o_s[128] unnormalised, m_s in base-2 units, l_s):
+// M = max m_s, L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.  Empty partials (l_s = 0, m_s = -inf) are
 // skipped.  For a rot4 V plane the merged row is in the rotated domain scaled
 // by sqrt(128); it is mapped back with x = s .* (H o) / 128.
 #include "vit_device.h"
@@ -27,7 +27,9 @@ __device__ inline void merge_into(float& M, float& L, float4v& O, float pm, floa
   }
 }
 
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+// SL split lanes x 32 channel groups; SL = 8 for few splits, 32 for many.
+template <int SL>
+__global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
   const int hq = blockIdx.x;
   const int seq = blockIdx.y;
   const int t = threadIdx.x;
@@ -36,26 +38,26 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   const float* ml = a.ws_ml + row * a.n_splits * 2;
   const float* o = a.ws_o + row * a.n_splits * kD + 4 * cg;
 
-  __shared__ float s_m[8], s_l[8];
-  __shared__ float s_o[8][kD];
+  __shared__ float s_m[SL], s_l[SL];
+  __shared__ float s_o[SL][kD];
   __shared__ float v[kD];
 
   float M = -INFINITY, L = 0.0f;
   float4v O = {0.0f, 0.0f, 0.0f, 0.0f};
   // 4 partials per round, all loads issued first (indices clamped, not branched)
-  for (int s0 = sl; s0 < a.n_splits; s0 += 32) {
+  for (int s0 = sl; s0 < a.n_splits; s0 += 4 * SL) {
     float pm[4], pl[4];
     float4v po[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int s = min(s0 + 8 * i, a.n_splits - 1);
+      const int s = min(s0 + SL * i, a.n_splits - 1);
       pm[i] = ml[2 * s];
       pl[i] = ml[2 * s + 1];
       po[i] = *reinterpret_cast<const float4v*>(o + static_cast<int64_t>(s) * kD);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (s0 + 8 * i < a.n_splits) merge_into(M, L, O, pm[i], pl[i], po[i]);
+      if (s0 + SL * i < a.n_splits) merge_into(M, L, O, pm[i], pl[i], po[i]);
   }
   if (cg == 0) {
     s_m[sl] = M;
@@ -68,9 +70,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   if (t < kD) {
     float Mf = -INFINITY, Lf = 0.0f, Of = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Mf = fmaxf(Mf, s_m[i]);
+    for (int i = 0; i < SL; ++i) Mf = fmaxf(Mf, s_m[i]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < SL; ++i) {
       if (s_l[i] > 0.0f) {
         const float f = __builtin_amdgcn_exp2f(s_m[i] - Mf);
         Of += s_o[i][t] * f;
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 }
 
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args) {
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, args);
+  if (args.n_splits > 64) hipLaunchKernelGGL(reduce_kernel<32>, grid, dim3(1024), 0, stream, args);
+  else hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -108,18 +108,32 @@ __device__ inline float sqrt_rn(float x) {
 
 __device__ inline float recip_or_zero(float d) { return d != 0.0f ? 1.0f / d : 0.0f; }
 
-template <typename T>
-__device__ inline T shfl_xor(T v, int m) {
-  return __shfl_xor(v, m, kWave);
+// Exchange with lane l ^ M.  Within 16-lane rows the moves are DPP (1, 2:
+// quad permutes; 8: a row rotation by 8, which is the xor-8 pairing);
+// 4 and 16 use ds_swizzle's xor mode (inside 32-lane groups); 32 uses
+// ds_bpermute.  Pure data movement: the encoders' arithmetic is unchanged.
+template <int M>
+__device__ inline uint32_t xshfl(uint32_t v) {
+  if constexpr (M == 1) return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (M == 2) return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (M == 8) return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, true);
+  else if constexpr (M == 4) return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));
+  else if constexpr (M == 16) return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F));
+  else return static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), M, kWave));
+}
+template <int M>
+__device__ inline float xshfl(float v) {
+  return __uint_as_float(xshfl<M>(__float_as_uint(v)));
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level row encoders.  Lane l holds channels l (x0) and l + 64 (x1).
-// Every encoder body disables fp contraction: the operation order of the
-// codec definitions is part of the format, whatever flags the including
-// translation unit uses.
+// Wave-level row encoders, R rows at a time (each step is issued for every
+// row before the next step, so the rows' lane exchanges overlap).  Lane l
+// holds channels l (x0) and l + 64 (x1) of each row.  Every encoder body
+// disables fp contraction: the operation order of the codec definitions is
+// part of the format, whatever flags the including translation unit uses.
 // Blocks: x0 is in block l>>5, x1 in block 2 + (l>>5); the 32 lanes of a
-// half-wave hold one block, so block reductions are xor-shuffles 16..1.
+// half-wave hold one block, so block reductions are xor exchanges 16..1.
 
 struct RowCodes {
   uint32_t c0, c1;     // codes of channels l and l+64 (fp16 bits, int8 as uint8, nibble)
@@ -127,18 +141,38 @@ struct RowCodes {
   uint16_t norm;       // rot4 row norm
 };
 
-__device__ inline float block_max_abs(float v) {
-  float a = fabsf(v);
-  for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, shfl_xor(a, m));
-  return a;
+template <int M, int N>
+__device__ inline void max_step(float (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = fmaxf(a[i], xshfl<M>(a[i]));
+}
+template <int M, int N>
+__device__ inline void sum_step(float (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = a[i] + xshfl<M>(a[i]);
 }
 
-__device__ inline RowCodes encode_f16(float x0, float x1) {
+// |x| maxima of the blocks: a[i] <- max over the lane's 32-lane half-wave
+template <int N>
+__device__ inline void block_max_abs(float (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = fabsf(a[i]);
+  max_step<16>(a);
+  max_step<8>(a);
+  max_step<4>(a);
+  max_step<2>(a);
+  max_step<1>(a);
+}
+
+template <int R>
+__device__ inline void encode_f16(const float (&x0)[R], const float (&x1)[R], RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
-  RowCodes r{};
-  r.c0 = f16_bits(x0);
-  r.c1 = f16_bits(x1);
-  return r;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    rc[r] = RowCodes{};
+    rc[r].c0 = f16_bits(x0[r]);
+    rc[r].c1 = f16_bits(x1[r]);
+  }
 }
 
 __device__ inline int8_t q8_code(float x, float inv) {
@@ -148,34 +182,70 @@ __device__ inline int8_t q8_code(float x, float inv) {
   return static_cast<int8_t>(c);
 }
 
-__device__ inline RowCodes encode_q8_0(float x0, float x1) {
+template <int R>
+__device__ inline void encode_q8_0(const float (&x0)[R], const float (&x1)[R], RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
-  RowCodes r{};
-  const float d0 = block_max_abs(x0) / 127.0f;
-  const float d1 = block_max_abs(x1) / 127.0f;
-  const float i0 = recip_or_zero(d0), i1 = recip_or_zero(d1);
-  r.c0 = static_cast<uint8_t>(q8_code(x0, i0));
-  r.c1 = static_cast<uint8_t>(q8_code(x1, i1));
-  r.s0 = f16_bits(d0);
-  r.s1 = f16_bits(d1);
-  return r;
+  float m[2 * R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[2 * r] = x0[r];
+    m[2 * r + 1] = x1[r];
+  }
+  block_max_abs(m);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float d0 = m[2 * r] / 127.0f;
+    const float d1 = m[2 * r + 1] / 127.0f;
+    const float i0 = recip_or_zero(d0), i1 = recip_or_zero(d1);
+    rc[r] = RowCodes{};
+    rc[r].c0 = static_cast<uint8_t>(q8_code(x0[r], i0));
+    rc[r].c1 = static_cast<uint8_t>(q8_code(x1[r], i1));
+    rc[r].s0 = f16_bits(d0);
+    rc[r].s1 = f16_bits(d1);
+  }
 }
 
-// q4_0 block scale from the first element of largest magnitude.
-__device__ inline float q4_block_scale(float x, int lane) {
-#pragma clang fp contract(off)
-  // key: |x| bits (monotone for non-negative floats) high, inverted index low,
-  // so the max picks the largest magnitude and, among equals, the first index.
-  const uint32_t j = static_cast<uint32_t>(lane & 31);
-  uint64_t key = (static_cast<uint64_t>(__float_as_uint(fabsf(x))) << 32) | (31u - j);
-  for (int m = 16; m >= 1; m >>= 1) {
-    const uint64_t o = shfl_xor(key, m);
-    key = o > key ? o : key;
+// q4_0 block scales d = m / -8 from the first element of largest magnitude.
+// key: |x| bits (monotone for non-negative floats) high, inverted index low,
+// so the max picks the largest magnitude and, among equals, the first index.
+template <int M, int N>
+__device__ inline void key_max_step(uint32_t (&hi)[N], uint32_t (&lo)[N]) {
+  uint32_t oh[N], ol[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    oh[i] = xshfl<M>(hi[i]);
+    ol[i] = xshfl<M>(lo[i]);
   }
-  const uint32_t amax_bits = static_cast<uint32_t>(key >> 32);
-  const int src = (lane & 32) | static_cast<int>(31u - static_cast<uint32_t>(key & 0xffffffffu));
-  const float m = __shfl(x, src, kWave);
-  return amax_bits == 0u ? 0.0f : m / -8.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool take = oh[i] > hi[i] || (oh[i] == hi[i] && ol[i] > lo[i]);
+    hi[i] = take ? oh[i] : hi[i];
+    lo[i] = take ? ol[i] : lo[i];
+  }
+}
+template <int N>
+__device__ inline void q4_block_scales(const float (&x)[N], int lane, float (&d)[N]) {
+#pragma clang fp contract(off)
+  uint32_t hi[N], lo[N];
+  const uint32_t j = static_cast<uint32_t>(lane & 31);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    hi[i] = __float_as_uint(fabsf(x[i]));
+    lo[i] = 31u - j;
+  }
+  key_max_step<16>(hi, lo);
+  key_max_step<8>(hi, lo);
+  key_max_step<4>(hi, lo);
+  key_max_step<2>(hi, lo);
+  key_max_step<1>(hi, lo);
+  float m[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int src = (lane & 32) | static_cast<int>(31u - lo[i]);
+    m[i] = __shfl(x[i], src, kWave);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) d[i] = hi[i] == 0u ? 0.0f : m[i] / -8.0f;
 }
 
 __device__ inline uint32_t q4_code(float x, float inv) {
@@ -185,16 +255,24 @@ __device__ inline uint32_t q4_code(float x, float inv) {
   return static_cast<uint32_t>(c);
 }
 
-__device__ inline RowCodes encode_q4_0(float x0, float x1, int lane) {
+template <int R>
+__device__ inline void encode_q4_0(const float (&x0)[R], const float (&x1)[R], int lane, RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
-  RowCodes r{};
-  const float d0 = q4_block_scale(x0, lane);
-  const float d1 = q4_block_scale(x1, lane);
-  r.c0 = q4_code(x0, recip_or_zero(d0));
-  r.c1 = q4_code(x1, recip_or_zero(d1));
-  r.s0 = f16_bits(d0);
-  r.s1 = f16_bits(d1);
-  return r;
+  float x[2 * R], d[2 * R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    x[2 * r] = x0[r];
+    x[2 * r + 1] = x1[r];
+  }
+  q4_block_scales(x, lane, d);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    rc[r] = RowCodes{};
+    rc[r].c0 = q4_code(x0[r], recip_or_zero(d[2 * r]));
+    rc[r].c1 = q4_code(x1[r], recip_or_zero(d[2 * r + 1]));
+    rc[r].s0 = f16_bits(d[2 * r]);
+    rc[r].s1 = f16_bits(d[2 * r + 1]);
+  }
 }
 
 __device__ inline uint32_t rot4_index(float t) {
@@ -208,66 +286,113 @@ __device__ inline uint32_t rot4_index(float t) {
   return idx;
 }
 
-// signs: the 128-bit mask as 4 words; bit j set => channel j negated.
-__device__ inline RowCodes encode_rot4(float x0, float x1, int lane, const uint32_t signs[4]) {
+// One Walsh-Hadamard stage across lanes for every row: lanes with bit h set
+// take (partner - own), the others (own + partner).
+template <int H, int R>
+__device__ inline void wht_stage(float (&w0)[R], float (&w1)[R], int lane) {
 #pragma clang fp contract(off)
-  RowCodes r{};
-  const int ch0 = lane, ch1 = lane + 64;
-  float w0 = ((signs[ch0 >> 5] >> (ch0 & 31)) & 1u) ? -x0 : x0;
-  float w1 = ((signs[ch1 >> 5] >> (ch1 & 31)) & 1u) ? -x1 : x1;
-  // Walsh-Hadamard stages h = 1..32 across lanes, then h = 64 inside the lane.
+  float p0[R], p1[R];
 #pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float p0 = shfl_xor(w0, h);
-    const float p1 = shfl_xor(w1, h);
-    if (lane & h) {
-      w0 = p0 - w0;
-      w1 = p1 - w1;
-    } else {
-      w0 = w0 + p0;
-      w1 = w1 + p1;
-    }
+  for (int r = 0; r < R; ++r) {
+    p0[r] = xshfl<H>(w0[r]);
+    p1[r] = xshfl<H>(w1[r]);
   }
-  {
-    const float a = w0 + w1, b = w0 - w1;
-    w0 = a;
-    w1 = b;
+  const bool upper = (lane & H) != 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    w0[r] = upper ? p0[r] - w0[r] : w0[r] + p0[r];
+    w1[r] = upper ? p1[r] - w1[r] : w1[r] + p1[r];
+  }
+}
+
+// signs: the 128-bit mask as 4 words; bit j set => channel j negated.
+template <int R>
+__device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
+                                   RowCodes (&rc)[R]) {
+#pragma clang fp contract(off)
+  const int ch0 = lane, ch1 = lane + 64;
+  const bool neg0 = ((signs[ch0 >> 5] >> (ch0 & 31)) & 1u) != 0;
+  const bool neg1 = ((signs[ch1 >> 5] >> (ch1 & 31)) & 1u) != 0;
+  float w0[R], w1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    w0[r] = neg0 ? -x0[r] : x0[r];
+    w1[r] = neg1 ? -x1[r] : x1[r];
+  }
+  // Walsh-Hadamard stages h = 1..32 across lanes, then h = 64 inside the lane.
+  wht_stage<1>(w0, w1, lane);
+  wht_stage<2>(w0, w1, lane);
+  wht_stage<4>(w0, w1, lane);
+  wht_stage<8>(w0, w1, lane);
+  wht_stage<16>(w0, w1, lane);
+  wht_stage<32>(w0, w1, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float a = w0[r] + w1[r], b = w0[r] - w1[r];
+    w0[r] = a;
+    w1[r] = b;
   }
   // row norm: stride-halving tree of the squares of the input row
-  const float sq0 = x0 * x0;
-  const float sq1 = x1 * x1;
-  float ss = sq0 + sq1;
-  for (int m = 32; m >= 1; m >>= 1) ss = ss + shfl_xor(ss, m);
-  const float n = sqrt_rn(ss);
-  r.norm = f16_bits(n);
-  const float g = n > 0.0f ? 1.0f / n : 0.0f;
-  const float u0 = w0 * g;
-  const float u1 = w1 * g;
-  // per-block RMS of the whitened values
-  const float uu0 = u0 * u0;
-  const float uu1 = u1 * u1;
-  float b0 = uu0, b1 = uu1;
-  for (int m = 16; m >= 1; m >>= 1) {
-    b0 = b0 + shfl_xor(b0, m);
-    b1 = b1 + shfl_xor(b1, m);
+  float ss[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float sq0 = x0[r] * x0[r];
+    const float sq1 = x1[r] * x1[r];
+    ss[r] = sq0 + sq1;
   }
-  const float r0 = sqrt_rn(b0 * 0.03125f);
-  const float r1 = sqrt_rn(b1 * 0.03125f);
-  r.s0 = f16_bits(r0);
-  r.s1 = f16_bits(r1);
-  const float ib0 = r0 > 0.0f ? 1.0f / r0 : 0.0f;
-  const float ib1 = r1 > 0.0f ? 1.0f / r1 : 0.0f;
-  r.c0 = rot4_index(u0 * ib0);
-  r.c1 = rot4_index(u1 * ib1);
-  return r;
+  sum_step<32>(ss);
+  sum_step<16>(ss);
+  sum_step<8>(ss);
+  sum_step<4>(ss);
+  sum_step<2>(ss);
+  sum_step<1>(ss);
+  float u[2 * R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float n = sqrt_rn(ss[r]);
+    rc[r] = RowCodes{};
+    rc[r].norm = f16_bits(n);
+    const float g = n > 0.0f ? 1.0f / n : 0.0f;
+    u[2 * r] = w0[r] * g;
+    u[2 * r + 1] = w1[r] * g;
+  }
+  // per-block RMS of the whitened values
+  float b[2 * R];
+#pragma unroll
+  for (int i = 0; i < 2 * R; ++i) b[i] = u[i] * u[i];
+  sum_step<16>(b);
+  sum_step<8>(b);
+  sum_step<4>(b);
+  sum_step<2>(b);
+  sum_step<1>(b);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float r0 = sqrt_rn(b[2 * r] * 0.03125f);
+    const float r1 = sqrt_rn(b[2 * r + 1] * 0.03125f);
+    rc[r].s0 = f16_bits(r0);
+    rc[r].s1 = f16_bits(r1);
+    const float ib0 = r0 > 0.0f ? 1.0f / r0 : 0.0f;
+    const float ib1 = r1 > 0.0f ? 1.0f / r1 : 0.0f;
+    rc[r].c0 = rot4_index(u[2 * r] * ib0);
+    rc[r].c1 = rot4_index(u[2 * r + 1] * ib1);
+  }
+}
+
+template <int CODEC, int R>
+__device__ inline void encode_rows(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
+                                   RowCodes (&rc)[R]) {
+  if constexpr (CODEC == F16) encode_f16(x0, x1, rc);
+  else if constexpr (CODEC == Q8_0) encode_q8_0(x0, x1, rc);
+  else if constexpr (CODEC == Q4_0) encode_q4_0(x0, x1, lane, rc);
+  else encode_rot4(x0, x1, lane, signs, rc);
 }
 
 template <int CODEC>
 __device__ inline RowCodes encode_row(float x0, float x1, int lane, const uint32_t signs[4]) {
-  if constexpr (CODEC == F16) return encode_f16(x0, x1);
-  else if constexpr (CODEC == Q8_0) return encode_q8_0(x0, x1);
-  else if constexpr (CODEC == Q4_0) return encode_q4_0(x0, x1, lane);
-  else return encode_rot4(x0, x1, lane, signs);
+  const float a[1] = {x0}, b[1] = {x1};
+  RowCodes rc[1];
+  encode_rows<CODEC, 1>(a, b, lane, signs, rc);
+  return rc[0];
 }
 
 }  // namespace vit

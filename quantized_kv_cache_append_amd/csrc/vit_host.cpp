@@ -65,7 +65,8 @@ int enqueue_append(const vit_kv_plane* dst, const float* src, const int64_t* pos
     const int64_t g = ((pos0[s] + n_tokens - 1) >> 3) - (pos0[s] >> 3) + 1;
     if (g > groups) groups = g;
   }
-  const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(dst->n_kv_heads),
+  const dim3 grid(static_cast<unsigned>((groups + vit::kAppendWaves - 1) / vit::kAppendWaves),
+                  static_cast<unsigned>(dst->n_kv_heads),
                   static_cast<unsigned>(dst->n_seqs));
   return vit::launch_append(dst->codec, dst->side, grid, stream, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }

@@ -8,6 +8,7 @@
 namespace vit {
 
 constexpr int kMaxSeqs = 64;
+constexpr int kAppendWaves = 4;  // append workgroup: one wave per 8-row group
 
 struct AppendArgs {
   void* codes;
