@@ -502,12 +502,16 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
   }
 }
 
-// Decode kernel.  A wave handles RW = 4*NT query rows of its KV head; with
-// more than RW rows (G > RW) the rows form row groups, and row group k is
-// handled by the waves w with w / (4 / n_groups) == k, which share out the
-// workgroup's tiles round-robin.
+// Decode kernel: one workgroup of kDecodeWaves waves per (split, KV head,
+// sequence), sized to be the only workgroup on its compute unit (two waves
+// per SIMD).  A wave handles RW = 4*NT query rows of its KV head; with more
+// than RW rows (G > RW) the rows form row groups, and row group k is handled
+// by the waves w with w / (kDecodeWaves / n_groups) == k.  The waves of a row
+// group take the split's tiles from a shared LDS counter as they go, so a
+// wave that issues more slowly (the SIMD arbiter favours older waves) simply
+// takes fewer tiles.
 template <int KC, int VC, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int RW = 4 * NT;
   constexpr int GMAX = 16;
   const int tid = threadIdx.x;
@@ -520,18 +524,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int seq = blockIdx.z;
   const int L = a.seq_len[seq];
   const int G = a.gqa;
+  constexpr int kThreads = 64 * kDecodeWaves;
   const int n_groups = (G + RW - 1) / RW;   // 1, 2 or 4
-  const int wpg = 4 / n_groups;             // waves per row group
+  const int wpg = kDecodeWaves / n_groups;  // waves per row group
   const int group = wave / wpg;
   const int GP = RW * n_groups;             // padded query rows
   const int n_tiles = (L + kTile - 1) / kTile;
 
   __shared__ float sq[GMAX][kD];
   __shared__ uint32_t lut[256];
-  __shared__ float s_p[4][NT][4][kTile];
-  __shared__ float s_o[4][RW][kD];
-  __shared__ float s_m[4][RW];
-  __shared__ float s_l[4][RW];
+  __shared__ float s_p[kDecodeWaves][NT][4][kTile];
+  __shared__ float s_o[kDecodeWaves][RW][kD];
+  __shared__ float s_m[kDecodeWaves][RW];
+  __shared__ float s_l[kDecodeWaves][RW];
+  __shared__ int s_next[4];  // per row group: next tile slot to hand out
   __shared__ uint8_t s_row[2][256];
   __shared__ half8 s_aq[NT == 2 ? 2 : 1][NT][4][2][64];
 
@@ -576,8 +582,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < 8; ++i) qv[nt][i] = *reinterpret_cast<const float4v*>(qb + 4 * i);
     }
   }
-  // rot4 K: thread tid stages floats 8*tid .. 8*tid+7 of the padded [16][128] rows
-  const int qs_row = (8 * tid) >> 7;
+  // rot4 K: thread tid < 256 stages floats 8*tid .. 8*tid+7 of the padded [16][128] rows
+  const int qs_row = min((8 * tid) >> 7, GMAX - 1);
   [[maybe_unused]] float4v q0, q1;
   if constexpr (KC == ROT4) {
     const float* qsrc = qrow + min(qs_row, G - 1) * kD + ((8 * tid) & 127);
@@ -585,22 +591,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
   }
 
-  // Tiles are dealt out interleaved: split s owns tiles s, s + n_splits, ...
-  // and the wpg waves of a row group take every wpg-th of those, so at any
-  // moment the waves working on one stream read one contiguous window.
-  // This wave's tiles: t0, t0 + step, ... below n_tiles.  Loads past the last
-  // one are clamped to it; a wave without tiles re-reads tile 0 (always there).
-  const int step = a.n_splits * wpg;
-  const int t0 = split + a.n_splits * (wave - group * wpg);
-  const int t_end = n_tiles;
-  const int t_last = t0 < t_end ? t0 + ((t_end - 1 - t0) / step) * step : 0;
+  // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
+  // k = 0, 1, ... (so at any moment the splits of one stream read one
+  // contiguous window).  Within a row group the slots k go to the waves in
+  // order: each wave starts with D = prefetch_depth + 1 slots (wig, wig + wpg,
+  // ...) and then takes the next free slot from s_next whenever it refills a
+  // buffer.  Loads of slots past the last tile are clamped to it; a split
+  // without tiles re-reads tile 0 (always there).
+  constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
+  const int wig = wave - group * wpg;  // wave index within its row group
+  const int n_mine = split < n_tiles ? (n_tiles - 1 - split) / a.n_splits + 1 : 0;  // this split's tiles
+  const int t_last = split < n_tiles ? split + a.n_splits * (n_mine - 1) : 0;
+  auto tile_of = [&](int k) { return split + a.n_splits * k; };
+  auto load_slot = [&](TileRegs<KC, VC>& r, int k) {
+    load_tile<KC, VC>(r, min(tile_of(k), t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+  };
+  if (tid < n_groups) s_next[tid] = D * wpg;
   TileRegs<KC, VC> ta, tb;
   [[maybe_unused]] TileRegs<KC, VC> tc;
-  load_tile<KC, VC>(ta, min(t0, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-  load_tile<KC, VC>(tb, min(t0 + step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
+  load_slot(ta, wig);
+  load_slot(tb, wig + wpg);
 
   if constexpr (KC == ROT4 || VC == ROT4) {
-    lut[tid] = static_cast<uint32_t>(kLevelBits[tid & 15]) | (static_cast<uint32_t>(kLevelBits[tid >> 4]) << 16);
+    if (tid < 256)
+      lut[tid] = static_cast<uint32_t>(kLevelBits[tid & 15]) | (static_cast<uint32_t>(kLevelBits[tid >> 4]) << 16);
   }
   // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query
   //      row) + block slot; lane group qg carries block qg, and the operand
@@ -627,7 +641,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     aq_sync = VC == ROT4;  // the LUT
   } else {
     // rot4 K: rotate the query rows like the keys (sign flip, WHT) in LDS
-    {
+    if (tid < 256) {
       const int c0 = (8 * tid) & 127;
       const bool live = qs_row < G;
 #pragma unroll
@@ -639,7 +653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
     for (int h = 1; h < kD; h <<= 1) {
-      for (int i = tid; i < GP * 64; i += 256) {
+      for (int i = tid; i < GP * 64; i += kThreads) {
         const int g = i >> 6, k = i & 63;
         const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
         const float x = sq[g][lo], y = sq[g][lo + h];
@@ -671,7 +685,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       aq.h[0][m] = aqh[0][m];
       aq.l[0][m] = aql[0][m];
     }
-    if (aq_sync) __syncthreads();
+    (void)aq_sync;
+    __syncthreads();  // s_next (and the LUT) before the tile loop
   } else {
     // one copy per row group, written by the group's first wave
     if (wave == group * wpg) {
@@ -699,35 +714,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   st.vlo = INFINITY;  // the first tile sets the exponent
   st.vhi = INFINITY;
 
-  if (t0 < t_end) {
-    if constexpr (prefetch_depth<KC, VC, NT>() == 2) {
-      // three register buffers in rotation: two tiles in flight while one is used
-      for (int t = t0;;) {
-        load_tile<KC, VC>(tc, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC, NT>(ta, t, L, lane, aq, st, s_p[wave], lut);
-        t += step;
-        if (t >= t_end) break;
-        load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC, NT>(tb, t, L, lane, aq, st, s_p[wave], lut);
-        t += step;
-        if (t >= t_end) break;
-        load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        process_tile<KC, VC, NT>(tc, t, L, lane, aq, st, s_p[wave], lut);
-        t += step;
-        if (t >= t_end) break;
-      }
-    } else {
-      // two buffers: the next tile is in flight while one is used
-      for (int t = t0;;) {
-        process_tile<KC, VC, NT>(ta, t, L, lane, aq, st, s_p[wave], lut);
-        load_tile<KC, VC>(ta, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        t += step;
-        if (t >= t_end) break;
-        process_tile<KC, VC, NT>(tb, t, L, lane, aq, st, s_p[wave], lut);
-        load_tile<KC, VC>(tb, min(t + 2 * step, t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
-        t += step;
-        if (t >= t_end) break;
-      }
+  // slot k is live while its tile exists; slots taken later are larger, so
+  // a wave stops at its first dead slot
+  auto live_slot = [&](int k) { return k < n_mine; };
+  auto take = [&]() {  // one LDS atomic per wave, broadcast from lane 0
+    int k = 0;
+    if (lane == 0) k = atomicAdd(&s_next[group], 1);
+    return __builtin_amdgcn_readfirstlane(k);
+  };
+  int ka = wig, kb = wig + wpg;
+  if constexpr (D == 3) {
+    // three register buffers in rotation: two tiles in flight while one is used
+    int kc = wig + 2 * wpg;
+    load_slot(tc, kc);
+    while (live_slot(ka)) {
+      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lut);
+      ka = take();
+      load_slot(ta, ka);
+      if (!live_slot(kb)) break;
+      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lut);
+      kb = take();
+      load_slot(tb, kb);
+      if (!live_slot(kc)) break;
+      process_tile<KC, VC, NT>(tc, tile_of(kc), L, lane, aq, st, s_p[wave], lut);
+      kc = take();
+      load_slot(tc, kc);
+    }
+  } else {
+    // two buffers: the next tile is in flight while one is used
+    while (live_slot(ka)) {
+      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lut);
+      ka = take();
+      load_slot(ta, ka);
+      if (!live_slot(kb)) break;
+      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lut);
+      kb = take();
+      load_slot(tb, kb);
     }
   }
 
@@ -746,7 +768,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- merge the waves of each row group; write the partial or final row ----
   const bool final_out = a.n_splits == 1;
-  for (int i = tid; i < GP * kD; i += 256) {
+  for (int i = tid; i < GP * kD; i += kThreads) {
     const int g = i >> 7, c = i & 127;
     const int grp = g / RW, r = g % RW;
     float M = -INFINITY;
@@ -775,7 +797,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     if constexpr (VC == ROT4) {
       for (int h = 1; h < kD; h <<= 1) {
-        for (int i = tid; i < GP * 64; i += 256) {
+        for (int i = tid; i < GP * 64; i += kThreads) {
           const int g = i >> 6, k = i & 63;
           const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
           const float x = sq[g][lo], y = sq[g][lo + h];
@@ -785,7 +807,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __syncthreads();
       }
     }
-    for (int i = tid; i < G * kD; i += 256) {
+    for (int i = tid; i < G * kD; i += kThreads) {
       const int g = i >> 7, c = i & 127;
       float v = sq[g][c];
       if constexpr (VC == ROT4) {
@@ -799,9 +821,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 #define VIT_DECODE_NT(KC, VC)                                                                   \
   if (nt == 1)                                                                                  \
-    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, args); \
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args); \
   else                                                                                          \
-    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, args);
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args);
 
 #define VIT_DECODE_FOR_K(KC)                                                          \
   hipError_t launch_decode_k##KC(int vc, int nt, dim3 grid, hipStream_t stream,       \

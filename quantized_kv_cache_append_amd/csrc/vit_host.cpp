@@ -126,8 +126,8 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
   if (n_seqs < 1 || n_kv_heads < 1 || max_seq_len < 1) return 1;
   const int64_t units = static_cast<int64_t>(n_seqs) * n_kv_heads;
   const int64_t tiles = (max_seq_len + 31) / 32;
-  int64_t s = (512 + units - 1) / units;        // ~2 workgroups per compute unit
-  const int64_t by_work = tiles / 8 > 0 ? tiles / 8 : 1;  // >= 8 tiles per split
+  int64_t s = (256 + units - 1) / units;        // ~one (8-wave) workgroup per compute unit
+  const int64_t by_work = tiles / 4 > 0 ? tiles / 4 : 1;  // >= 4 tiles per split
   if (s > by_work) s = by_work;
   if (s > VIT_MAX_SPLITS) s = VIT_MAX_SPLITS;
   if (s < 1) s = 1;

@@ -9,6 +9,7 @@ namespace vit {
 
 constexpr int kMaxSeqs = 64;
 constexpr int kAppendWaves = 4;  // append workgroup: one wave per 8-row group
+constexpr int kDecodeWaves = 8;  // decode workgroup: one per compute unit
 
 struct AppendArgs {
   void* codes;

@@ -67,7 +67,7 @@ def test_workspace_and_splits(lib):
     assert lib.vit_attn_workspace_bytes(8, 32, 64, 16) == 0
     assert lib.vit_attn_workspace_bytes(8, 32, 128, 0) == 0
     s = lib.vit_attn_default_splits(8, 8, 32, 8192)
-    assert 1 <= s <= 8192 // 32 // 8
+    assert 1 <= s <= 8192 // 32 // 4
     assert lib.vit_attn_default_splits(1, 1, 4, 512) >= 1
 
 
