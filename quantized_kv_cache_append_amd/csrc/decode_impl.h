@@ -185,7 +185,8 @@ __device__ inline void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Registers of one 32-row tile for one lane.
+// Registers of one 32-row tile for one lane.  The cache is streamed once per
+// call, so every tile load is a nontemporal (streaming) load.
 template <int KC, int VC>
 struct TileRegs {
   u32x4 kd[2][units_per_block(KC)];  // K units of halves 0 and 1
@@ -207,22 +208,24 @@ __device__ inline void load_tile(TileRegs<KC, VC>& r, int t, int lane, const uin
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int c = 0; c < KCB; ++c)
-      r.kd[h][c] = *reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16);
+      r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
 #pragma unroll
-  for (int i = 0; i < v_loads<VC>(); ++i) r.vd[i] = *reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16);
+  for (int i = 0; i < v_loads<VC>(); ++i)
+    r.vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16));
   const int n16 = lane & 15, qg = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(t) * kTile;
   if constexpr (has_scales(KC)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) r.ks[h] = *reinterpret_cast<const u32x2*>(ksb + (row0 + 16 * h + n16) * 4);
+    for (int h = 0; h < 2; ++h)
+      r.ks[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ksb + (row0 + 16 * h + n16) * 4));
   }
   if constexpr (has_norms(KC)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) r.kn[h] = knb[row0 + 16 * h + n16];
+    for (int h = 0; h < 2; ++h) r.kn[h] = __builtin_nontemporal_load(knb + row0 + 16 * h + n16);
   }
   if constexpr (has_scales(VC))
-    r.vs = *reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (lane & 3) * 32 + 8 * qg);
-  if constexpr (has_norms(VC)) r.vn = *reinterpret_cast<const u32x4*>(vnb + row0 + 8 * qg);
+    r.vs = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (lane & 3) * 32 + 8 * qg));
+  if constexpr (has_norms(VC)) r.vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vnb + row0 + 8 * qg));
 }
 
 // Tiles kept in flight ahead of the one being used: two for the 4-bit pairs
