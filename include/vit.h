@@ -109,7 +109,8 @@ typedef enum vit_side { VIT_SIDE_K = 0, VIT_SIDE_V = 1 } vit_side;
 typedef enum vit_status {
   VIT_OK = 0,
   VIT_E_ARG = -1,         /* bad value, NULL required pointer, k_new xor v_new */
-  VIT_E_UNSUPPORTED = -2, /* head_dim != 128, G > 16, > 64 sequences, unknown codec */
+  VIT_E_UNSUPPORTED = -2, /* head_dim != 128, G > 16, > 64 sequences, unknown codec,
+                             capacity > VIT_MAX_CAPACITY */
   VIT_E_CAPACITY = -3,    /* rows outside 0..capacity-1, capacity % 256 != 0 */
   VIT_E_ALIGN = -4,       /* plane pointer not 256-B aligned, other pointer not 16-B aligned */
   VIT_E_HIP = -5          /* a HIP launch failed */
@@ -120,6 +121,7 @@ typedef enum vit_status {
 #define VIT_MAX_SEQS 64
 #define VIT_MAX_GQA 16
 #define VIT_MAX_SPLITS 4096
+#define VIT_MAX_CAPACITY (1 << 30) /* rows per (sequence, KV head) */
 
 /* One (layer, side) cache tensor: caller-owned device memory in the layout
  * above.  `signs` is a [host] pointer to 16 bytes (ROT4 only, else NULL),
@@ -131,7 +133,7 @@ typedef struct vit_kv_plane {
   int32_t n_kv_heads;
   int32_t head_dim;    /* must be 128 */
   int32_t reserved;    /* must be 0 */
-  int64_t capacity;    /* rows per (sequence, KV head); multiple of 256 */
+  int64_t capacity;    /* rows per (sequence, KV head); multiple of 256, <= VIT_MAX_CAPACITY */
   void *codes;
   uint16_t *scales;    /* fp16 bits; NULL for F16 */
   uint16_t *norms;     /* fp16 bits; ROT4 only, else NULL */

@@ -1,9 +1,11 @@
 // Flash-decode attention over a quantized KV plane pair, for gfx950.
 //
-// One workgroup (4 waves) per (split, KV head, sequence).  The split's 32-row
-// tiles are dealt round-robin to the 4 waves; each wave keeps its own online
-// softmax state, prefetches its next tile into registers while it computes
-// the current one, and the waves are merged through LDS at the end.
+// One workgroup of 8 waves per (split, KV head, sequence), the only one on
+// its compute unit.  Split s owns the 32-row tiles s, s + n_splits, ...; the
+// waves of a row group take them one at a time from an LDS counter, each
+// keeping its own online softmax state and prefetching its next tiles into
+// registers while it computes the current one.  The waves are merged through
+// LDS at the end.
 //
 // Both products run on MFMA 16x16x32 f16 with exact operands:
 //   * K and V codes are exact in fp16 (f16 values, int8 / 4-bit integers,
@@ -75,14 +77,25 @@ __device__ inline half8 q4_unpack(uint32_t w) {
   return r;
 }
 
-// eight rot4 indices -> fp16 levels through the byte LUT (LUT[b] = level[b&15]
-// | level[b>>4] << 16), element order (lo b0, hi b0, lo b1, hi b1, ...).
-__device__ inline half8 rot4_unpack(uint32_t w, const uint32_t* lut) {
+// rot4 level table in LDS: byte b of packed indices -> the fp16 pair
+// (level[b & 15], level[b >> 4]).  It is replicated once per lane (entry b of
+// lane l at word 64 b + l), so the 64 lookups of one instruction always fall
+// in distinct banks however the code bytes are distributed.
+struct Lut {
+  const uint32_t* words;  // 256 * 64 words
+  uint32_t lane4;         // 4 * lane: the lane's byte offset within an entry
+};
+
+// eight rot4 indices -> fp16 levels, element order (lo b0, hi b0, lo b1,
+// hi b1, ...).  One v_perm_b32 per byte builds its table address
+// 256 * byte + 4 * lane.
+__device__ inline half8 rot4_unpack(uint32_t w, const Lut& lut) {
+  const char* base = reinterpret_cast<const char*>(lut.words);
   u32x4 r;
-  r[0] = lut[w & 0xFFu];
-  r[1] = lut[(w >> 8) & 0xFFu];
-  r[2] = lut[(w >> 16) & 0xFFu];
-  r[3] = lut[w >> 24];
+  r[0] = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lut.lane4, 0x0C0C0400u));
+  r[1] = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lut.lane4, 0x0C0C0500u));
+  r[2] = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lut.lane4, 0x0C0C0600u));
+  r[3] = *reinterpret_cast<const uint32_t*>(base + __builtin_amdgcn_perm(w, lut.lane4, 0x0C0C0700u));
   return __builtin_bit_cast(half8, r);
 }
 
@@ -103,7 +116,7 @@ __device__ inline int k_chan(int q, int m, int j) {
 }
 
 template <int KC>
-__device__ inline half8 unpack_k(const u32x4* units, int m, const uint32_t* lut) {
+__device__ inline half8 unpack_k(const u32x4* units, int m, const Lut& lut) {
   if constexpr (KC == F16) {
     return __builtin_bit_cast(half8, units[m]);
   } else if constexpr (KC == Q8_0) {
@@ -118,7 +131,7 @@ __device__ inline half8 unpack_k(const u32x4* units, int m, const uint32_t* lut)
 
 // V operand of N-tile nt (channels 16nt..16nt+15): element j = row 8q + j.
 template <int VC>
-__device__ inline half8 unpack_v(const u32x4* vd, int nt, const uint32_t* lut) {
+__device__ inline half8 unpack_v(const u32x4* vd, int nt, const Lut& lut) {
   if constexpr (VC == F16) {
     return __builtin_bit_cast(half8, vd[nt]);
   } else if constexpr (VC == Q8_0) {
@@ -353,7 +366,7 @@ struct QOperands<2> {
 template <int KC, int VC, int NT>
 __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t, int L, int lane,
                                              const QOperands<NT>& aq, WaveState<NT>& st,
-                                             float (*s_p)[4][kTile], const uint32_t* lut) {
+                                             float (*s_p)[4][kTile], const Lut& lut) {
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > L;
   // ---- V block factors of the lane's P.V operand rows (block n16 & 3, tile
@@ -389,12 +402,9 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
 
   // ---- S^T: lane (n16, qg) gets the 4 block partials of query row 4*nt + qg
   //      at tile row 16h + n16, for both halves h ----
-  half8 bk[2][4];
   float kf[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) bk[h][m] = unpack_k<KC>(cur.kd[h], m, lut);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
     if constexpr (KC != F16) {
@@ -408,6 +418,11 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
     }
   }
   float s[NT][2];
+  half8 bk[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bk[h][m] = unpack_k<KC>(cur.kd[h], m, lut);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float4v acc_h[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -535,7 +550,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const int n_tiles = (L + kTile - 1) / kTile;
 
   __shared__ float sq[GMAX][kD];
-  __shared__ uint32_t lut[256];
+  constexpr bool kRot4 = KC == ROT4 || VC == ROT4;
+  __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
   __shared__ float s_p[kDecodeWaves][NT][4][kTile];
   __shared__ float s_o[kDecodeWaves][RW][kD];
   __shared__ float s_m[kDecodeWaves][RW];
@@ -588,11 +604,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // rot4 K: thread tid < 256 stages floats 8*tid .. 8*tid+7 of the padded [16][128] rows
   const int qs_row = min((8 * tid) >> 7, GMAX - 1);
   [[maybe_unused]] float4v q0, q1;
+  [[maybe_unused]] uint32_t ksw = 0;
   if constexpr (KC == ROT4) {
     const float* qsrc = qrow + min(qs_row, G - 1) * kD + ((8 * tid) & 127);
     q0 = *reinterpret_cast<const float4v*>(qsrc);
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
+    ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
   }
+  // rot4 levels: lane l (< 16) fetches level l; issued before the tile loads
+  // so that building the table below does not wait for them
+  [[maybe_unused]] uint32_t lv = 0;
+  if constexpr (kRot4) lv = kLevelBits[lane & 15];
 
   // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
   // k = 0, 1, ... (so at any moment the splits of one stream read one
@@ -615,15 +637,25 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   load_slot(ta, wig);
   load_slot(tb, wig + wpg);
 
-  if constexpr (KC == ROT4 || VC == ROT4) {
-    if (tid < 256)
-      lut[tid] = static_cast<uint32_t>(kLevelBits[tid & 15]) | (static_cast<uint32_t>(kLevelBits[tid >> 4]) << 16);
+  if constexpr (kRot4) {
+    // word 4 (tid + 512 i) + j (j < 4) is entry e = tid / 16 + 32 i of lane
+    // 4 (tid % 16) + j: low level (e & 15) = (tid / 16) % 16, high level
+    // (e >> 4) = tid / 256 + 2 i, the same for the whole wave
+    const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(lv), (tid >> 4) & 15));
+    const int hb = __builtin_amdgcn_readfirstlane(tid >> 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lv), hb + 2 * i));
+      const uint32_t e = lo | (hi << 16);
+      *reinterpret_cast<u32x4*>(&lut[4 * (tid + 512 * i)]) = u32x4{e, e, e, e};
+    }
   }
+  const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
+  QOperands<NT> aq;
   // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query
   //      row) + block slot; lane group qg carries block qg, and the operand
   //      is zero unless slot == qg ----
   half8 aqh[NT][4], aql[NT][4];
-  bool aq_sync = false;
   if constexpr (KC != ROT4) {
     const float qs = a.qscale;
 #pragma unroll
@@ -641,7 +673,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
         split8(v, aqh[nt][m], aql[nt][m]);
       }
     }
-    aq_sync = VC == ROT4;  // the LUT
   } else {
     // rot4 K: rotate the query rows like the keys (sign flip, WHT) in LDS
     if (tid < 256) {
@@ -650,7 +681,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
-        v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;
+        v = ((ksw >> ((c0 + j) & 31)) & 1u) ? -v : v;
         sq[qs_row][c0 + j] = v;
       }
     }
@@ -681,14 +712,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
   }
 
-  QOperands<NT> aq;
   if constexpr (NT == 1) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       aq.h[0][m] = aqh[0][m];
       aq.l[0][m] = aql[0][m];
     }
-    (void)aq_sync;
     __syncthreads();  // s_next (and the LUT) before the tile loop
   } else {
     // one copy per row group, written by the group's first wave
@@ -731,26 +760,26 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     int kc = wig + 2 * wpg;
     load_slot(tc, kc);
     while (live_slot(ka)) {
-      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lut);
+      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lutr);
       ka = take();
       load_slot(ta, ka);
       if (!live_slot(kb)) break;
-      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lut);
+      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lutr);
       kb = take();
       load_slot(tb, kb);
       if (!live_slot(kc)) break;
-      process_tile<KC, VC, NT>(tc, tile_of(kc), L, lane, aq, st, s_p[wave], lut);
+      process_tile<KC, VC, NT>(tc, tile_of(kc), L, lane, aq, st, s_p[wave], lutr);
       kc = take();
       load_slot(tc, kc);
     }
   } else {
     // two buffers: the next tile is in flight while one is used
     while (live_slot(ka)) {
-      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lut);
+      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lutr);
       ka = take();
       load_slot(ta, ka);
       if (!live_slot(kb)) break;
-      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lut);
+      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lutr);
       kb = take();
       load_slot(tb, kb);
     }

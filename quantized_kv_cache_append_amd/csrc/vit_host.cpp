@@ -25,7 +25,7 @@ int check_plane(const vit_kv_plane* p) {
   if (p->reserved != 0) return VIT_E_ARG;
   if (p->n_seqs < 1 || p->n_kv_heads < 1 || p->capacity <= 0) return VIT_E_ARG;
   if (p->n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
-  if (p->capacity > (int64_t{1} << 30)) return VIT_E_UNSUPPORTED;
+  if (p->capacity > VIT_MAX_CAPACITY) return VIT_E_UNSUPPORTED;
   if (p->capacity % VIT_CAPACITY_ALIGN != 0) return VIT_E_CAPACITY;
   if (!p->codes) return VIT_E_ARG;
   if (p->codec != VIT_CODEC_F16 && !p->scales) return VIT_E_ARG;
@@ -94,6 +94,7 @@ int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_
   if (head_dim != VIT_HEAD_DIM) return VIT_E_UNSUPPORTED;
   if (n_seqs < 1 || n_kv_heads < 1 || capacity <= 0) return VIT_E_ARG;
   if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
+  if (capacity > VIT_MAX_CAPACITY) return VIT_E_UNSUPPORTED;
   if (capacity % VIT_CAPACITY_ALIGN != 0) return VIT_E_CAPACITY;
   const size_t rows = static_cast<size_t>(n_seqs) * n_kv_heads * capacity;
   if (codes_bytes) *codes_bytes = rows * kRowBytes[codec];

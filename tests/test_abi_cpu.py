@@ -60,6 +60,8 @@ def test_plane_size_errors(lib):
     assert lib.vit_kv_plane_sizes(0, 1, 1, 128, 300, r, r, r) == _lib.VIT_E_CAPACITY
     assert lib.vit_kv_plane_sizes(0, 0, 1, 128, 256, r, r, r) == _lib.VIT_E_ARG
     assert lib.vit_kv_plane_sizes(0, 65, 1, 128, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
+    assert lib.vit_kv_plane_sizes(0, 1, 1, 128, 1 << 30, r, r, r) == _lib.VIT_OK
+    assert lib.vit_kv_plane_sizes(0, 1, 1, 128, (1 << 30) + 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
 
 
 def test_workspace_and_splits(lib):
@@ -110,6 +112,7 @@ def test_append_validation(lib):
     p = _plane()
     p.reserved = 1
     assert _append(lib, p) == _lib.VIT_E_ARG
+    assert _append(lib, _plane(cap=(1 << 30) + 256)) == _lib.VIT_E_UNSUPPORTED
 
 
 def _decode(lib, k, v, hq=4, seq_len=(10, 10), k_new=None, v_new=None, scale=0.088, ns=1, ws=None, q=FAKE, out=FAKE):
