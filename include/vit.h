@@ -61,12 +61,15 @@
  *  norms   fp16 [S][H][capacity] (ROT4 only; NULL otherwise).
  *
  *  A K-side tile ("row-major units") is two 16-row halves h = 0, 1; row r of
- *  half h is position p = 16*h + r.  Each half holds 16-byte
- *  units U[c][b][r] (c < CB, b = block 0..3, r = row 0..15), unit byte offset
- *  (((h*CB + c)*4 + b)*16 + r)*16, CB = RB/64.  A unit holds block b's
- *  canonical bytes [16c, 16c+16) of that row:
- *    F16: fp16 of channels 32b+8c .. 32b+8c+7;  Q8_0: int8 codes of channels
- *    32b+16c .. +15;  Q4_0/ROT4: byte j = code[32b+j] | code[32b+j+16] << 4.
+ *  half h is position p = 16*h + r.  The canonical bytes of block b of a row
+ *  (RB/4 of them) are:  F16: fp16 of channels 32b .. 32b+31;  Q8_0: int8
+ *  codes of channels 32b .. 32b+31;  Q4_0/ROT4: byte j (< 16) =
+ *  code[32b+j] | code[32b+j+16] << 4.  Chunk g (0..3) of a block is its
+ *  canonical bytes [g*CHB, (g+1)*CHB), CHB = RB/16.  Each half holds 16-byte
+ *  units U[c][g][r] (c < CB = RB/64, r = row 0..15), unit byte offset
+ *  (((h*CB + c)*4 + g)*16 + r)*16; unit U[c][g][r] holds chunk g of blocks
+ *  c*BPU .. c*BPU+BPU-1 of row r in block order, BPU = 4/CB (F16: 1 block,
+ *  16 B; Q8_0: 2 blocks, 8 B each; Q4_0/ROT4: 4 blocks, 4 B each).
  *  A V-side tile ("column units") stores, for each channel ch (N-tile
  *  nt = ch>>4, n = ch&15) and each group of 8 positions g8 = p>>3, the 8
  *  codes of positions 8*g8 .. 8*g8+7 of that channel:

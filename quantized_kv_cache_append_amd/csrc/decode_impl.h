@@ -12,12 +12,13 @@
 //     fp16 rot4 levels), and every per-block scale is applied in fp32;
 //   * the query and the probabilities are split into fp16 hi + lo parts
 //     (two MFMAs), so operand rounding stays near 2^-21 relative.
-// S^T = Q K^T: the A operand has one row per (query row, 32-channel block)
-// pair, four query rows per 16-row tile; lane group q (lanes 16q..16q+15)
-// of the B operand holds block q of a K row, and A is zero except where the
-// row's block equals q.  Each output lane then holds, for one cached row and
-// one query row, the four per-block partial dot products, which it scales by
-// the fp32 block scales and sums in registers.  P is regrouped through a
+// S^T = Q K^T: MFMA m's B operand is block m of 16 K rows (lane group q,
+// lanes 16q..16q+15, holds its 8-channel chunk q).  The A operand has one
+// row per (query row, block) pair, four query rows per 16-row tile, and is
+// zero except in MFMA m for the rows of block m.  Each output lane then
+// holds, for one cached row and one query row, the four per-block partial
+// dot products, which it scales by the fp32 block scales and sums in
+// registers.  P is regrouped through a
 // small per-wave LDS buffer into the P.V operand, whose rows are again
 // (query row, block) pairs so the V block scale folds into P per block.
 #pragma once
@@ -99,19 +100,20 @@ __device__ inline half8 rot4_unpack(uint32_t w, const Lut& lut) {
   return __builtin_bit_cast(half8, r);
 }
 
-// Channel (within the row) of element j of lane group q's K operand in MFMA m.
+// Channel (within the row) of element j of the K operand of MFMA m in lane
+// group g: MFMA m covers block m, lane group g its chunk g (8 channels).
 template <int KC>
-__device__ inline int k_chan(int q, int m, int j) {
+__device__ inline int k_chan(int g, int m, int j) {
   if constexpr (KC == F16) {
-    return 32 * q + 8 * m + j;
+    return 32 * m + 8 * g + j;
   } else if constexpr (KC == Q8_0) {
     const int p8 = (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1);
-    return 32 * q + 16 * (m >> 1) + 8 * (m & 1) + p8;
+    return 32 * m + 8 * g + p8;
   } else if constexpr (KC == Q4_0) {
-    const int byte = 4 * m + (((j & 1) << 1) | ((j >> 1) & 1));
-    return 32 * q + byte + ((j >> 2) << 4);
+    const int byte = ((j & 1) << 1) | ((j >> 1) & 1);
+    return 32 * m + 4 * g + byte + ((j >> 2) << 4);
   } else {
-    return 32 * q + 4 * m + (j >> 1) + ((j & 1) << 4);
+    return 32 * m + 4 * g + (j >> 1) + ((j & 1) << 4);
   }
 }
 
@@ -290,11 +292,19 @@ __device__ inline void store_row(uint8_t* codes, uint16_t* scales, uint16_t* nor
       rowbuf[lane] = static_cast<uint8_t>(rowbuf[128 + 32 * b + j] | (rowbuf[128 + 32 * b + j + 16] << 4));
     }
     wave_lds_fence();
+    // unit (c, g): chunk g (CHB bytes) of each of the BPU blocks of unit c
     constexpr int CB = units_per_block(C);
+    constexpr int BPU = 4 / CB, CHB = 4 * CB;
     if (lane < 4 * CB) {
-      const int b = lane / CB, c = lane % CB;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(rowbuf + b * 16 * CB + 16 * c);
-      *reinterpret_cast<u32x4*>(tbase + k_unit_offset(C, pt, b, c)) = v;
+      const int g = lane / CB, c = lane % CB;
+      uint32_t w[4];
+#pragma unroll
+      for (int bb = 0; bb < BPU; ++bb)
+#pragma unroll
+        for (int k = 0; k < CHB / 4; ++k)
+          w[bb * (CHB / 4) + k] =
+              *reinterpret_cast<const uint32_t*>(rowbuf + (c * BPU + bb) * 16 * CB + g * CHB + 4 * k);
+      *reinterpret_cast<u32x4*>(tbase + k_unit_offset(C, pt, g, c)) = u32x4{w[0], w[1], w[2], w[3]};
     }
   } else {
 #pragma unroll
@@ -590,26 +600,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // the compiler wait for all outstanding loads where the paths merge, which
   // would serialise the prefetch.  Out-of-range indices are clamped instead.
   const float* qrow = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
-  // query block qg of this lane's rows (non-rot4 K: operands come straight from here)
-  float4v qv[NT][8];
-  if constexpr (KC != ROT4) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int g = RW * group + 4 * nt + (n16 >> 2);
-      const float* qb = qrow + min(g, G - 1) * kD + 32 * qg;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qv[nt][i] = *reinterpret_cast<const float4v*>(qb + 4 * i);
-    }
-  }
-  // rot4 K: thread tid < 256 stages floats 8*tid .. 8*tid+7 of the padded [16][128] rows
+  // The query rows are staged through LDS: thread tid < 256 holds floats
+  // 8*tid .. 8*tid+7 of the padded [16][128] rows (two registers per thread,
+  // so nothing needs the query before the tile prefetch is issued).
   const int qs_row = min((8 * tid) >> 7, GMAX - 1);
-  [[maybe_unused]] float4v q0, q1;
+  float4v q0, q1;
   [[maybe_unused]] uint32_t ksw = 0;
-  if constexpr (KC == ROT4) {
+  {
     const float* qsrc = qrow + min(qs_row, G - 1) * kD + ((8 * tid) & 127);
     q0 = *reinterpret_cast<const float4v*>(qsrc);
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
-    ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
+    if constexpr (KC == ROT4) ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
   }
   // rot4 levels: lane l (< 16) fetches level l; issued before the tile loads
   // so that building the table below does not wait for them
@@ -653,39 +654,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
   QOperands<NT> aq;
   // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query
-  //      row) + block slot; lane group qg carries block qg, and the operand
-  //      is zero unless slot == qg ----
-  half8 aqh[NT][4], aql[NT][4];
-  if constexpr (KC != ROT4) {
-    const float qs = a.qscale;
+  //      row) + block slot; MFMA m covers block m (lane group qg its chunk
+  //      qg), so a row's operand is zero except in MFMA m = its slot ----
+  if (tid < 256) {
+    const int c0 = (8 * tid) & 127;
+    const bool live = qs_row < G;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int g = RW * group + 4 * nt + (n16 >> 2);
-      const bool live = (n16 & 3) == qg && g < G;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = k_chan<KC>(0, m, j);  // channel within block qg
-          v[j] = live ? qv[nt][c >> 2][c & 3] * qs : 0.0f;
-        }
-        split8(v, aqh[nt][m], aql[nt][m]);
-      }
+    for (int j = 0; j < 8; ++j) {
+      float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
+      if constexpr (KC == ROT4) v = ((ksw >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
+      sq[qs_row][c0 + j] = v;
     }
-  } else {
-    // rot4 K: rotate the query rows like the keys (sign flip, WHT) in LDS
-    if (tid < 256) {
-      const int c0 = (8 * tid) & 127;
-      const bool live = qs_row < G;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
-        v = ((ksw >> ((c0 + j) & 31)) & 1u) ? -v : v;
-        sq[qs_row][c0 + j] = v;
-      }
-    }
-    __syncthreads();
+  }
+  __syncthreads();
+  float qs = a.qscale;
+  if constexpr (KC == ROT4) {
+    // rotate the query rows like the keys (WHT); the keys reconstruct as
+    // N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
     for (int h = 1; h < kD; h <<= 1) {
       for (int i = tid; i < GP * 64; i += kThreads) {
         const int g = i >> 6, k = i & 63;
@@ -696,19 +681,25 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       }
       __syncthreads();
     }
-    // rot4 K rows reconstruct as N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
-    const float qs = a.qscale * (1.0f / 128.0f);
+    qs *= 1.0f / 128.0f;
+  }
+  // the lane's row is block slot = n16 & 3 of its query row (rows past G
+  // are zero in sq); its operand is that block's chunk qg in MFMA m = slot
+  half8 aqh[NT][4], aql[NT][4];
+  const int slot = n16 & 3;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int g = RW * group + 4 * nt + (n16 >> 2);
-      const bool live = (n16 & 3) == qg;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int g = RW * group + 4 * nt + (n16 >> 2);
+    float v[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float v[8];
+    for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, slot, j)] * qs;
+    half8 h, l;
+    split8(v, h, l);
+    const half8 z = {};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = live ? sq[g][k_chan<KC>(qg, m, j)] * qs : 0.0f;
-        split8(v, aqh[nt][m], aql[nt][m]);
-      }
+    for (int m = 0; m < 4; ++m) {
+      aqh[nt][m] = m == slot ? h : z;
+      aql[nt][m] = m == slot ? l : z;
     }
   }
 
@@ -718,7 +709,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       aq.h[0][m] = aqh[0][m];
       aq.l[0][m] = aql[0][m];
     }
-    __syncthreads();  // s_next (and the LUT) before the tile loop
+    // (s_next and the LUT were written before the staging barrier)
   } else {
     // one copy per row group, written by the group's first wave
     if (wave == group * wpg) {

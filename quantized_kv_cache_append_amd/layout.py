@@ -16,17 +16,23 @@ D = 128
 
 
 def _k_perm(codec):
-    """Physical byte offset (within a tile) of each logical row byte [32, RB]."""
+    """Physical byte offset (within a tile) of each canonical row byte [32, RB].
+
+    Unit (h, c, g, r) holds chunk g (bytes [g*CHB, (g+1)*CHB) of the block's
+    canonical bytes) of each of the 4/CB blocks of unit c, in block order."""
     rb = ROW_BYTES[codec]
     cb = rb // 64
+    bpu, chb = 4 // cb, 4 * cb
     p = np.arange(TILE)[:, None]
     byte = np.arange(rb)[None, :]
-    b = byte // (16 * cb)
-    c = (byte % (16 * cb)) // 16
-    i = byte % 16
+    b = byte // (rb // 4)
+    wb = byte % (rb // 4)
+    g = wb // chb
+    c = b // bpu
+    i = (b % bpu) * chb + wb % chb
     h = p >> 4
     r = p & 15
-    return (((h * cb + c) * 4 + b) * 16 + r) * 16 + i
+    return (((h * cb + c) * 4 + g) * 16 + r) * 16 + i
 
 
 def _v_map(codec):

@@ -179,18 +179,25 @@ def test_layout_is_a_bijection(codec, side):
 
 def test_k_layout_16_byte_units_are_contiguous_per_lane():
     """Each wave-wide 16-byte load of a K tile covers 1 KB of contiguous bytes:
-    unit (half, c) of lane l sits at ((half*CB + c)*64 + l)*16."""
-    for codec in ("f16", "q8_0", "q4_0"):
+    unit (half, c) of lane l = 16 g + r sits at ((half*CB + c)*64 + l)*16 and
+    holds chunk g (CHB = RB/16 canonical bytes) of each of the 4/CB blocks of
+    unit c, in block order (include/vit.h, K-side tile)."""
+    for codec in ("f16", "q8_0", "q4_0", "rot4"):
+        rb = layout.ROW_BYTES[codec]
         perm = layout._k_perm(codec)
-        cb = layout.ROW_BYTES[codec] // 64
+        cb = rb // 64
+        bpu, chb = 4 // cb, rb // 16
         offs = np.sort(perm.reshape(-1))
-        assert np.array_equal(offs, np.arange(32 * layout.ROW_BYTES[codec]))
+        assert np.array_equal(offs, np.arange(32 * rb))
         for p in range(32):
             h, r = p >> 4, p & 15
-            for b in range(4):
+            for g in range(4):
                 for c in range(cb):
-                    lane = b * 16 + r
-                    assert perm[p, b * 16 * cb + 16 * c] == ((h * cb + c) * 64 + lane) * 16
+                    unit = ((h * cb + c) * 64 + 16 * g + r) * 16
+                    for bb in range(bpu):
+                        for k in range(chb):
+                            byte = (c * bpu + bb) * (rb // 4) + g * chb + k
+                            assert perm[p, byte] == unit + bb * chb + k
 
 
 @pytest.mark.parametrize("side", ["k", "v"])
