@@ -202,18 +202,19 @@ __device__ inline void wave_lds_fence() {
 
 // Registers of one 32-row tile for one lane.  The cache is streamed once per
 // call, so every tile load is a nontemporal (streaming) load.
-template <int KC, int VC>
+template <int KC, int VC, int NT>
 struct TileRegs {
   u32x4 kd[2][units_per_block(KC)];  // K units of halves 0 and 1
   u32x4 vd[v_loads<VC>()];           // V column units
   u32x2 ks[2];                       // K scales of this lane's row in each half
   uint32_t kn[2];                    // K norms (rot4)
-  u32x4 vs;                          // V scales: block (lane & 3), rows 8q .. 8q+7
+  u32x4 vs[NT == 2 ? 4 : 1];         // V scales, rows 8q .. 8q+7: block (lane & 3)
+                                     // for 4 query rows per wave, blocks 0..3 for 8
   u32x4 vn;                          // V norms (rot4), rows 8q .. 8q+7
 };
 
-template <int KC, int VC>
-__device__ inline void load_tile(TileRegs<KC, VC>& r, int t, int lane, const uint8_t* kbase,
+template <int KC, int VC, int NT>
+__device__ inline void load_tile(TileRegs<KC, VC, NT>& r, int t, int lane, const uint8_t* kbase,
                                  const uint8_t* vbase, const uint16_t* ksb, const uint16_t* knb,
                                  const uint16_t* vsb, const uint16_t* vnb) {
   constexpr int KCB = units_per_block(KC);
@@ -238,8 +239,12 @@ __device__ inline void load_tile(TileRegs<KC, VC>& r, int t, int lane, const uin
 #pragma unroll
     for (int h = 0; h < 2; ++h) r.kn[h] = __builtin_nontemporal_load(knb + row0 + 16 * h + n16);
   }
-  if constexpr (has_scales(VC))
-    r.vs = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (lane & 3) * 32 + 8 * qg));
+  if constexpr (has_scales(VC)) {
+#pragma unroll
+    for (int b = 0; b < (NT == 2 ? 4 : 1); ++b)
+      r.vs[b] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (NT == 2 ? b : (lane & 3)) * 32 + 8 * qg));
+  }
   if constexpr (has_norms(VC)) r.vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vnb + row0 + 8 * qg));
 }
 
@@ -340,7 +345,8 @@ template <int NT>
 struct WaveState {
   float m_run[NT];        // running max (base 2) of the lane's query row
   float l_run[NT];        // lane-partial running sum
-  float4v oacc[NT][8];    // P.V accumulators: N-tile c, rows (query row, block)
+  float4v oacc[8];        // P.V accumulators of N-tile c: rows (query row, block)
+                          // for 4 query rows, (query row, hi/lo part) for 8
   // The softmax reference is m_run + vexp: p = 2^(s - m_run - vexp), so the
   // P.V operand p * f (f = V block factor) carries 2^-vexp and stays in the
   // fp16 normal range whatever the magnitude of V.  vexp (an integer, wave
@@ -369,14 +375,16 @@ struct QOperands {
 };
 template <>
 struct QOperands<2> {
-  const half8* lds;  // [nt][m][hi/lo][64 lanes]
+  half8 w[4];  // MFMA b: row n16 = 2 q + part of query q, chunk qg of block b
 };
 
-// One 32-row tile for one wave: S^T = Q K^T, online softmax, O += P V.
+// One 32-row tile for one wave with 4 query rows: S^T = Q K^T, online
+// softmax, O += P V.
 template <int KC, int VC, int NT>
-__device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t, int L, int lane,
+__device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, int t, int L, int lane,
                                              const QOperands<NT>& aq, WaveState<NT>& st,
                                              float (*s_p)[4][kTile], const Lut& lut) {
+  static_assert(NT == 1, "4 query rows per wave");
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > L;
   // ---- V block factors of the lane's P.V operand rows (block n16 & 3, tile
@@ -388,7 +396,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
   if constexpr (VC != F16) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float f = f16_to_float(cur.vs[j >> 1] >> ((j & 1) * 16));
+      float f = f16_to_float(cur.vs[0][j >> 1] >> ((j & 1) * 16));
       if constexpr (VC == ROT4) f *= f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
       vf[j] = f;
     }
@@ -439,14 +447,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
     float4v acc_l[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      half8 qh, ql;
-      if constexpr (NT == 1) {
-        qh = aq.h[nt][m];
-        ql = aq.l[nt][m];
-      } else {
-        qh = aq.lds[((nt * 4 + m) * 2 + 0) * 64 + lane];
-        ql = aq.lds[((nt * 4 + m) * 2 + 1) * 64 + lane];
-      }
+      const half8 qh = aq.h[nt][m], ql = aq.l[nt][m];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         acc_h[h] = mfma16(qh, bk[h][m], acc_h[h]);
@@ -474,7 +475,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
       const float alpha = __builtin_amdgcn_exp2f((st.m_run[nt] + st.vexp) - (mnew + vexp_new));
       st.l_run[nt] *= alpha;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) st.oacc[nt][c] *= alpha;
+      for (int c = 0; c < 8; ++c) st.oacc[c] *= alpha;
       st.m_run[nt] = mnew;
     }
     const float mref = st.m_run[nt] + vexp_new;
@@ -524,9 +525,179 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC>& cur, int t,
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      st.oacc[nt][c] = mfma16(aph[nt], bv, st.oacc[nt][c]);
-      st.oacc[nt][c] = mfma16(apl[nt], bv, st.oacc[nt][c]);
+      st.oacc[c] = mfma16(aph[nt], bv, st.oacc[c]);
+      st.oacc[c] = mfma16(apl[nt], bv, st.oacc[c]);
     }
+  }
+}
+
+// One 32-row tile for one wave with 8 query rows.  Both products use rows
+// r = 2 q + p: query q of the wave's 8, part p of its fp16 hi/lo split
+// (0 = hi, 1 = lo), so no operand row is zero when 8 rows are live.
+//   S^T: MFMA b covers block b; output lane (n16, qg) holds, for cached row
+//        16h + n16, block b's partial dots of queries 2qg and 2qg+1 (hi and
+//        lo rows), which are summed, scaled by the K block scale and summed
+//        over the blocks.
+//   P.V: for block b the A rows carry part p of P(q, row) times the V factor
+//        of (row, block b) over the tile rows 8qg .. 8qg+7, and N-tile c uses
+//        the operand of its block c / 2; the output rows are (query, part)
+//        again, and the two parts are added at the end.
+template <int KC, int VC>
+__device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur, int t, int L, int lane,
+                                                  const QOperands<2>& aq, WaveState<2>& st, float* s_p,
+                                                  const Lut& lut) {
+  const int n16 = lane & 15, qg = lane >> 4;
+  const bool partial = (t + 1) * kTile > L;
+  // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
+  //      check, first so that they overlap the S^T products ----
+  float vf[4][8];
+  float vexp_new = st.vexp;
+  bool v_rescale = false;
+  if constexpr (VC != F16) {
+    float nrm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) nrm[j] = VC == ROT4 ? f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16)) : 1.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vf[b][j] = f16_to_float(cur.vs[b][j >> 1] >> ((j & 1) * 16)) * nrm[j];
+    if (partial) {
+      // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool dead = t * kTile + 8 * qg + j >= L;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) vf[b][j] = dead ? 0.0f : vf[b][j];
+      }
+    }
+    float vm = 0.0f;  // largest |factor| among this lane's rows
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vm = fmaxf(vm, fabsf(vf[b][j]));
+    if (__builtin_amdgcn_ballot_w64(vm > st.vhi) || !__builtin_amdgcn_ballot_w64(vm >= st.vlo)) {
+      int e;
+      (void)__builtin_frexpf(wave_max(vm), &e);  // wave max in [2^(e-1), 2^e)
+      vexp_new = static_cast<float>(e);
+      st.vlo = __builtin_ldexpf(1.0f, e - 12);
+      st.vhi = __builtin_ldexpf(1.0f, e + 4);
+      v_rescale = true;
+    }
+  }
+
+  // ---- S^T: lane (n16, qg) gets queries 2qg + jj at tile row 16h + n16 ----
+  float kf[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
+    if constexpr (KC != F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[h][i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
+      if constexpr (KC == ROT4) {
+        const float nrm = f16_to_float(cur.kn[h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[h][i] *= nrm;
+      }
+    }
+  }
+  float s[2][2];  // [query 2qg + jj][half]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float4v acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      acc[b] = mfma16(aq.w[b], unpack_k<KC>(cur.kd[h], b, lut), float4v{0.0f, 0.0f, 0.0f, 0.0f});
+    const bool dead = partial && t * kTile + 16 * h + n16 >= L;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float d[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) d[b] = acc[b][2 * jj] + acc[b][2 * jj + 1];
+      float v;
+      if constexpr (KC == F16) v = (d[0] + d[1]) + (d[2] + d[3]);
+      else v = (d[0] * kf[h][0] + d[1] * kf[h][1]) + (d[2] * kf[h][2] + d[3] * kf[h][3]);
+      s[jj][h] = dead ? -INFINITY : v;
+    }
+  }
+
+  // ---- online softmax (base 2); the 16 lanes of a lane group share the
+  //      state of its two queries; the reference is m_run + vexp ----
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const float tmax = row16_max(fmaxf(s[jj][0], s[jj][1]));
+    const float mnew = fmaxf(st.m_run[jj], tmax);
+    if (__builtin_amdgcn_ballot_w64(mnew > st.m_run[jj]) || v_rescale) {
+      const float alpha = __builtin_amdgcn_exp2f((st.m_run[jj] + st.vexp) - (mnew + vexp_new));
+      st.l_run[jj] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        st.oacc[c][2 * jj] *= alpha;
+        st.oacc[c][2 * jj + 1] *= alpha;
+      }
+      st.m_run[jj] = mnew;
+    }
+    const float mref = st.m_run[jj] + vexp_new;
+    const float p0 = __builtin_amdgcn_exp2f(s[jj][0] - mref);
+    const float p1 = __builtin_amdgcn_exp2f(s[jj][1] - mref);
+    st.l_run[jj] += p0 + p1;
+    s_p[(2 * qg + jj) * kTile + n16] = p0;
+    s_p[(2 * qg + jj) * kTile + 16 + n16] = p1;
+  }
+  st.vexp = vexp_new;
+  wave_lds_fence();
+  // P of this lane's A row: query n16 >> 1 over tile rows 8qg .. 8qg+7
+  float pv[8];
+  {
+    const float4v p_lo = *reinterpret_cast<const float4v*>(&s_p[(n16 >> 1) * kTile + 8 * qg]);
+    const float4v p_hi = *reinterpret_cast<const float4v*>(&s_p[(n16 >> 1) * kTile + 8 * qg + 4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[j] = p_lo[j];
+      pv[4 + j] = p_hi[j];
+    }
+  }
+  wave_lds_fence();
+
+  // ---- O += P V ----
+  // Part p of x: hi rows take fp16(x) toward zero, lo rows fp16(x - hi), the
+  // same split as split8, chosen per lane by the row's parity.
+  const float lom = (n16 & 1) ? 1.0f : 0.0f;
+  auto part = [&](const float x[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
+      const float r0 = x[2 * i] - static_cast<float>(hh[0]) * lom;
+      const float r1 = x[2 * i + 1] - static_cast<float>(hh[1]) * lom;
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+    return __builtin_bit_cast(half8, r);
+  };
+  half8 ap[4];
+  if constexpr (VC == F16) {
+    ap[0] = part(pv);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+      ap[b] = part(x);
+    }
+  }
+  const int row8 = t * kTile + 8 * qg;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    half8 bv = unpack_v<VC>(cur.vd, c, lut);
+    if constexpr (VC == F16) {
+      if (partial) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
+      }
+    }
+    st.oacc[c] = mfma16(VC == F16 ? ap[0] : ap[c >> 1], bv, st.oacc[c]);
   }
 }
 
@@ -568,7 +739,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   __shared__ float s_l[kDecodeWaves][RW];
   __shared__ int s_next[4];  // per row group: next tile slot to hand out
   __shared__ uint8_t s_row[2][256];
-  __shared__ half8 s_aq[NT == 2 ? 2 : 1][NT][4][2][64];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
   const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
@@ -629,12 +799,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const int n_mine = split < n_tiles ? (n_tiles - 1 - split) / a.n_splits + 1 : 0;  // this split's tiles
   const int t_last = split < n_tiles ? split + a.n_splits * (n_mine - 1) : 0;
   auto tile_of = [&](int k) { return split + a.n_splits * k; };
-  auto load_slot = [&](TileRegs<KC, VC>& r, int k) {
+  auto load_slot = [&](TileRegs<KC, VC, NT>& r, int k) {
     load_tile<KC, VC>(r, min(tile_of(k), t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
   };
   if (tid < n_groups) s_next[tid] = D * wpg;
-  TileRegs<KC, VC> ta, tb;
-  [[maybe_unused]] TileRegs<KC, VC> tc;
+  TileRegs<KC, VC, NT> ta, tb;
+  [[maybe_unused]] TileRegs<KC, VC, NT> tc;
   load_slot(ta, wig);
   load_slot(tb, wig + wpg);
 
@@ -685,11 +855,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   }
   // the lane's row is block slot = n16 & 3 of its query row (rows past G
   // are zero in sq); its operand is that block's chunk qg in MFMA m = slot
-  half8 aqh[NT][4], aql[NT][4];
-  const int slot = n16 & 3;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int g = RW * group + 4 * nt + (n16 >> 2);
+  if constexpr (NT == 1) {
+    // row n16 = 4 * (query row) + block slot: the operand of the lane's row
+    // is its slot's chunk qg, in MFMA m = slot, zero in the others
+    const int slot = n16 & 3;
+    const int g = RW * group + (n16 >> 2);
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, slot, j)] * qs;
@@ -698,41 +868,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     const half8 z = {};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      aqh[nt][m] = m == slot ? h : z;
-      aql[nt][m] = m == slot ? l : z;
+      aq.h[0][m] = m == slot ? h : z;
+      aq.l[0][m] = m == slot ? l : z;
     }
-  }
-
-  if constexpr (NT == 1) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      aq.h[0][m] = aqh[0][m];
-      aq.l[0][m] = aql[0][m];
-    }
-    // (s_next and the LUT were written before the staging barrier)
   } else {
-    // one copy per row group, written by the group's first wave
-    if (wave == group * wpg) {
+    // row n16 = 2 * (query row) + part: in MFMA b the lane holds part
+    // n16 & 1 of chunk qg of block b of its query row
+    const int g = RW * group + (n16 >> 1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int b = 0; b < 4; ++b) {
+      float v[8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          s_aq[group][nt][m][0][lane] = aqh[nt][m];
-          s_aq[group][nt][m][1][lane] = aql[nt][m];
-        }
+      for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, b, j)] * qs;
+      half8 h, l;
+      split8(v, h, l);
+      aq.w[b] = (n16 & 1) ? l : h;
     }
-    __syncthreads();
-    aq.lds = &s_aq[group][0][0][0][0];
   }
+  // (s_next and the LUT were written before the staging barrier)
 
   WaveState<NT> st;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     st.m_run[nt] = -INFINITY;
     st.l_run[nt] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) st.oacc[nt][c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.oacc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   st.vexp = 0.0f;
   st.vlo = INFINITY;  // the first tile sets the exponent
   st.vhi = INFINITY;
@@ -745,47 +907,56 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     if (lane == 0) k = atomicAdd(&s_next[group], 1);
     return __builtin_amdgcn_readfirstlane(k);
   };
+  auto proc = [&](const TileRegs<KC, VC, NT>& r, int t) {
+    if constexpr (NT == 1) process_tile<KC, VC, NT>(r, t, L, lane, aq, st, s_p[wave], lutr);
+    else process_tile_wide<KC, VC>(r, t, L, lane, aq, st, &s_p[wave][0][0][0], lutr);
+  };
   int ka = wig, kb = wig + wpg;
   if constexpr (D == 3) {
     // three register buffers in rotation: two tiles in flight while one is used
     int kc = wig + 2 * wpg;
     load_slot(tc, kc);
     while (live_slot(ka)) {
-      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lutr);
+      proc(ta, tile_of(ka));
       ka = take();
       load_slot(ta, ka);
       if (!live_slot(kb)) break;
-      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lutr);
+      proc(tb, tile_of(kb));
       kb = take();
       load_slot(tb, kb);
       if (!live_slot(kc)) break;
-      process_tile<KC, VC, NT>(tc, tile_of(kc), L, lane, aq, st, s_p[wave], lutr);
+      proc(tc, tile_of(kc));
       kc = take();
       load_slot(tc, kc);
     }
   } else {
     // two buffers: the next tile is in flight while one is used
     while (live_slot(ka)) {
-      process_tile<KC, VC, NT>(ta, tile_of(ka), L, lane, aq, st, s_p[wave], lutr);
+      proc(ta, tile_of(ka));
       ka = take();
       load_slot(ta, ka);
       if (!live_slot(kb)) break;
-      process_tile<KC, VC, NT>(tb, tile_of(kb), L, lane, aq, st, s_p[wave], lutr);
+      proc(tb, tile_of(kb));
       kb = take();
       load_slot(tb, kb);
     }
   }
 
-  // ---- per-wave state to LDS ----
+  // ---- per-wave state to LDS: row r of the wave's RW query rows ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    const int r = NT == 1 ? qg : 2 * qg + nt;  // the lane's query row of state nt
     const float l = row16_sum(st.l_run[nt]);
     if (n16 == 0) {
-      s_m[wave][4 * nt + qg] = st.m_run[nt] + st.vexp;  // the reference of l and O
-      s_l[wave][4 * nt + qg] = l;
+      s_m[wave][r] = st.m_run[nt] + st.vexp;  // the reference of l and O
+      s_l[wave][r] = l;
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s_o[wave][4 * nt + qg][16 * c + n16] = st.oacc[nt][c][c >> 1];
+    for (int c = 0; c < 8; ++c) {
+      // 4 rows: the output row of (query, block of N-tile c); 8 rows: hi + lo
+      const float o = NT == 1 ? st.oacc[c][c >> 1] : st.oacc[c][2 * nt] + st.oacc[c][2 * nt + 1];
+      s_o[wave][r][16 * c + n16] = o;
+    }
   }
   __syncthreads();
 
