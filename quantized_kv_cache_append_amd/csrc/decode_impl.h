@@ -33,6 +33,7 @@ __device__ inline float4v mfma16(half8 a, half8 b, float4v c) {
 }
 
 // --- exact fp16 conversions of packed codes ---------------------------------
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 __device__ inline half2v h2_bits(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 // (x & mask) | bits in one v_and_or_b32 (gfx9 VOP3 takes no literal, so the
@@ -43,6 +44,16 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
   return r;
 }
 __device__ inline uint32_t bits_h2(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// a times the fp16 in half HI of w, in fp32: one v_fma_mix_f32 (exact
+// product, one rounding, the same value as converting the fp16 first).
+template <int HI>
+__device__ inline float mul_f16(float a, uint32_t w) {
+  float r;
+  if constexpr (HI) __asm__("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(w));
+  else __asm__("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(w));
+  return r;
+}
 
 // eight int8 codes (two words) -> fp16, element order (b0, b2, b1, b3) of each
 // word.  v_perm_b32 builds the fp16 bit patterns 0x64 | (c ^ 0x80), i.e. the
@@ -549,32 +560,62 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > L;
   // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
-  //      check, first so that they overlap the S^T products ----
-  float vf[4][8];
+  //      check, first so that they overlap the S^T products.  For q8_0 and
+  //      q4_0 the factor is the fp16 scale itself: it stays in fp16 (the
+  //      largest magnitude is an integer max over the bit patterns, and the
+  //      products take the fp16 operand directly); rot4 multiplies in the
+  //      row norm in fp32 ----
+  [[maybe_unused]] float vf[4][8];
+  [[maybe_unused]] uint32_t fw[4][4];  // fp16 factor pairs: block b, rows 8qg + 2i, 2i + 1
   float vexp_new = st.vexp;
   bool v_rescale = false;
   if constexpr (VC != F16) {
-    float nrm[8];
+    float vm;  // largest |factor| among this lane's rows
+    if constexpr (VC == ROT4) {
+      float nrm[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) nrm[j] = VC == ROT4 ? f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16)) : 1.0f;
+      for (int j = 0; j < 8; ++j) nrm[j] = f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vf[b][j] = f16_to_float(cur.vs[b][j >> 1] >> ((j & 1) * 16)) * nrm[j];
-    if (partial) {
-      // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+        for (int j = 0; j < 8; ++j) vf[b][j] = f16_to_float(cur.vs[b][j >> 1] >> ((j & 1) * 16)) * nrm[j];
+      if (partial) {
+        // rows past L may hold any bits: their factor is 0 (their p is 0 too)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool dead = t * kTile + 8 * qg + j >= L;
+        for (int j = 0; j < 8; ++j) {
+          const bool dead = t * kTile + 8 * qg + j >= L;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) vf[b][j] = dead ? 0.0f : vf[b][j];
+          for (int b = 0; b < 4; ++b) vf[b][j] = dead ? 0.0f : vf[b][j];
+        }
       }
+      vm = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vm = fmaxf(vm, fabsf(vf[b][j]));
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fw[b][i] = cur.vs[b][i];
+      if (partial) {
+        // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r0 = t * kTile + 8 * qg + 2 * i;
+          const uint32_t keep = (r0 < L ? 0x0000FFFFu : 0u) | (r0 + 1 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) fw[b][i] = fw[b][i] & keep;
+        }
+      }
+      // fp16 magnitudes order like their bit patterns
+      u16x2 mx = {0, 0};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, fw[b][i] & 0x7FFF7FFFu));
+      vm = f16_to_float(mx[0] > mx[1] ? mx[0] : mx[1]);
     }
-    float vm = 0.0f;  // largest |factor| among this lane's rows
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vm = fmaxf(vm, fabsf(vf[b][j]));
     if (__builtin_amdgcn_ballot_w64(vm > st.vhi) || !__builtin_amdgcn_ballot_w64(vm >= st.vlo)) {
       int e;
       (void)__builtin_frexpf(wave_max(vm), &e);  // wave max in [2^(e-1), 2^e)
@@ -622,21 +663,27 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
   }
 
   // ---- online softmax (base 2); the 16 lanes of a lane group share the
-  //      state of its two queries; the reference is m_run + vexp ----
+  //      state of its two queries; the reference is m_run + vexp.  One
+  //      decision rescales both queries, so the accumulators are scaled as
+  //      whole vectors {a0, a0, a1, a1} ----
+  float mnew[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) mnew[jj] = fmaxf(st.m_run[jj], row16_max(fmaxf(s[jj][0], s[jj][1])));
+  if (__builtin_amdgcn_ballot_w64(mnew[0] > st.m_run[0]) || __builtin_amdgcn_ballot_w64(mnew[1] > st.m_run[1]) ||
+      v_rescale) {
+    float alpha[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      alpha[jj] = __builtin_amdgcn_exp2f((st.m_run[jj] + st.vexp) - (mnew[jj] + vexp_new));
+      st.l_run[jj] *= alpha[jj];
+      st.m_run[jj] = mnew[jj];
+    }
+    const float4v av = {alpha[0], alpha[0], alpha[1], alpha[1]};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.oacc[c] *= av;
+  }
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
-    const float tmax = row16_max(fmaxf(s[jj][0], s[jj][1]));
-    const float mnew = fmaxf(st.m_run[jj], tmax);
-    if (__builtin_amdgcn_ballot_w64(mnew > st.m_run[jj]) || v_rescale) {
-      const float alpha = __builtin_amdgcn_exp2f((st.m_run[jj] + st.vexp) - (mnew + vexp_new));
-      st.l_run[jj] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        st.oacc[c][2 * jj] *= alpha;
-        st.oacc[c][2 * jj + 1] *= alpha;
-      }
-      st.m_run[jj] = mnew;
-    }
     const float mref = st.m_run[jj] + vexp_new;
     const float p0 = __builtin_amdgcn_exp2f(s[jj][0] - mref);
     const float p1 = __builtin_amdgcn_exp2f(s[jj][1] - mref);
@@ -681,8 +728,16 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       float x[8];
+      if constexpr (VC == ROT4) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+        for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = mul_f16<0>(pv[2 * i], fw[b][i]);
+          x[2 * i + 1] = mul_f16<1>(pv[2 * i + 1], fw[b][i]);
+        }
+      }
       ap[b] = part(x);
     }
   }
