@@ -16,12 +16,16 @@ resident in HBM before timing starts.  Because the batched cache (143 MB)
 fits in the 256 MB last-level cache, each timed step reads a different one of
 R device replicas (R * footprint >= 1 GiB), round-robin.
 
+The timed steps are eager C calls with pre-marshalled arguments, and every
+decode dispatch records a pair of HIP events at its own start and end
+(vit_arm_kernel_events -> hipExtLaunchKernel), so the duration covers the
+kernel alone, as rocprofv3's kernel trace does.  ``--graph`` adds a second
+pass that captures each replica's step once into a HIP graph and replays one
+graph per step (reported as ``graph_ms_per_step``).
+
 Prints ONE JSON line.  ``value`` is decode tokens/s (sequences / step time).
 ``roofline`` describes the dominant kernel (decode): algorithmic KV bytes per
-launch / its mean duration, against the 8 TB/s HBM peak.  The duration comes
-from a pair of HIP events per timed decode launch, recorded by that kernel's
-own dispatch (vit_arm_kernel_events -> hipExtLaunchKernel), so it covers the
-kernel alone, as rocprofv3's kernel trace does.  ``traffic``
+launch / its mean duration, against the 8 TB/s HBM peak.  ``traffic``
 is the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
 a copy-kernel calibration), read from profiles/ only when it was measured on
 the current kernel sources.  ``cpu_baseline`` times the numpy oracle on the
@@ -159,7 +163,8 @@ def run_gpu(args):
     ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq, D, n_splits), dtype=torch.uint8, device="cuda")
     out = [torch.empty((S, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
     lens = [L] * S
-    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
 
     # every call of a step, marshalled once per replica (the host then only
     # issues the C calls, so the GPU queue never runs dry).  One new token per
@@ -194,8 +199,9 @@ def run_gpu(args):
             if red is not None:
                 red()
 
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
 
     evs = [([torch.cuda.Event(enable_timing=True) for _ in range(n_layers)],
@@ -204,23 +210,53 @@ def run_gpu(args):
         for e in pair[0] + pair[1]:
             e.record(stream)
     arm = vit.vit_arm_kernel_events
-    mode = "eager (pre-marshalled C calls)"
+    # Pass 1, eager: every decode dispatch records its own start/stop events
+    # (the kernel's duration for the roofline).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
     dec_ms = [evs[i][0][li].elapsed_time(evs[i][1][li]) for i in range(args.steps) for li in range(n_layers)]
     assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output"
+    eager_ms_per_step = 1e3 * eager_wall / args.steps
 
-    ms_per_step = 1e3 * wall / args.steps
+    # Optional pass 2: each replica's step (the same C calls) captured once
+    # into a HIP graph and replayed, one graph launch per step.  (On this
+    # stack a graph launch costs about as much host and dispatch time as the
+    # eager calls, so the eager pass stays the default.)
+    graph_ms_per_step = None
+    mode, ms_per_step = "eager (pre-marshalled C calls)", eager_ms_per_step
+    if args.graph:
+        graphs = []
+        with torch.cuda.stream(stream):
+            for r in range(replicas):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(r)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                graphs[i % replicas].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                graphs[(args.warmup + i) % replicas].replay()
+        torch.cuda.synchronize()
+        graph_ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+        assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output (graph replay)"
+        del graphs
     dec_mean_ms = float(np.mean(dec_ms))
     per_launch_bytes = kv_bytes / n_layers
     # algorithmic bytes of all timed decode launches / their summed duration
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
     return dict(cfg=cfg, cfgno=cfgno, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, mode=mode,
-                replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, dec_mean_ms=dec_mean_ms,
+                replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
+                dec_mean_ms=dec_mean_ms,
                 dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
                 achieved_gbs=achieved)
 
@@ -399,6 +435,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps as HIP graph replays (one captured graph per replica)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", type=int, default=0, help="only run N plain 1 GiB copies")
     ap.add_argument("--summarize", metavar="PROF_DIR", default=None,
@@ -450,6 +488,7 @@ def main():
             "codecs": "ladder (seeded per layer/side)" if r["n_layers"] > 1 else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
             "n_splits": r["n_splits"], "cold_cache_replicas": r["replicas"], "launch": r["mode"],
         },
+        "graph_ms_per_step": None if r["graph_ms_per_step"] is None else round(r["graph_ms_per_step"], 5),
         "effective_kv_read_gbs": round(r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
         "effective_kv_read_pct_of_hbm_peak": round(100 * r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": {

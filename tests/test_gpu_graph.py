@@ -1,0 +1,90 @@
+"""A decode step (fused append + vit_attn_decode + vit_attn_splitk_reduce)
+captured into a HIP graph and replayed, as a serving loop (or bench.py --graph)
+would do.
+
+Each replay runs after unrelated eager work and a synchronization, and its
+output is checked against the eager call (same kernels and inputs; the waves'
+dynamic tile hand-out may change the fp32 summation order, so the bar is
+1e-5 x RMS) and against the oracle (the usual 2e-3 x RMS).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from gpu_helpers import append_rows, check_close, make_plane, ref_unit, say, torch_cuda
+
+D = 128
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kc,vc,G", [("q8_0", "q8_0", 4), ("q4_0", "rot4", 8), ("rot4", "f16", 5)])
+def test_captured_step_replays_match_eager(kc, vc, G):
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    say(f"[graph] K={kc} V={vc} G={G}")
+    rng = np.random.default_rng(2024 + G)
+    S, H, cap, n_splits = 2, 2, 512, 3
+    lens = [300, 97]
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
+    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc == "rot4" else None
+    K = make_plane(kc, "k", S, H, cap, ks)
+    V = make_plane(vc, "v", S, H, cap, vs)
+    kx = rng.standard_normal((S, max(lens), H, D)).astype(np.float32)
+    vx = rng.standard_normal((S, max(lens), H, D)).astype(np.float32)
+    # rows 0 .. 298 appended here; row L-1 of each sequence comes again with
+    # the decode call (fused append, same values)
+    append_rows(K, kx[:, :max(lens) - 1], [0] * S)
+    append_rows(V, vx[:, :max(lens) - 1], [0] * S)
+    q = rng.standard_normal((S, H * G, D)).astype(np.float32)
+    k_new = np.stack([kx[s, lens[s] - 1] for s in range(S)])  # [S][H][D]
+    v_new = np.stack([vx[s, lens[s] - 1] for s in range(S)])
+    qd = torch.from_numpy(q).cuda()
+    knd = torch.from_numpy(np.ascontiguousarray(k_new)).cuda()
+    vnd = torch.from_numpy(np.ascontiguousarray(v_new)).cuda()
+    ws = torch.empty(vit.vit_attn_workspace_bytes(S, H * G, D, n_splits), dtype=torch.uint8, device="cuda")
+
+    eager = vit.decode(K, V, qd, H * G, lens, k_new=knd, v_new=vnd, n_splits=n_splits, workspace=ws)
+    torch.cuda.synchronize()
+    ref_e = eager.cpu().numpy()
+
+    ref = np.zeros_like(ref_e, dtype=np.float64)
+    for s in range(S):
+        L = lens[s]
+        for h in range(H):
+            ref[s, h * G:(h + 1) * G] = ref_unit(q[s, h * G:(h + 1) * G], kx[s, :L, h], vx[s, :L, h], kc, vc,
+                                                 1.0 / math.sqrt(D), ks, vs)
+    check_close(ref_e, ref, f"eager K={kc} V={vc} G={G}")
+
+    stream = torch.cuda.Stream()
+    out = torch.empty_like(eager)
+    with torch.cuda.stream(stream):
+        d = vit.prepare_decode(K, V, qd, H * G, lens, out, k_new=knd, v_new=vnd, n_splits=n_splits,
+                               workspace=ws, stream=stream)
+        red = vit.prepare_reduce(ws, S, H * G, n_splits, V, out, stream=stream)
+        d()
+        red()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        d()
+        red()
+    torch.cuda.synchronize()
+
+    rms = float(np.sqrt(np.mean(ref_e.astype(np.float64) ** 2)))
+    other = torch.empty_like(eager)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        # unrelated eager work between replays
+        vit.decode(K, V, qd, H * G, [l - 1 for l in lens], n_splits=2, out=other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        err = float(np.max(np.abs(got.astype(np.float64) - ref_e)))
+        say(f"  replay {rep}: max|graph - eager| / rms = {err / rms:.2e}")
+        assert np.all(np.isfinite(got)), f"replay {rep}: non-finite output"
+        assert err <= 1e-5 * rms, f"replay {rep}: graph output differs from eager by {err:.3e}"
+        check_close(got, ref, f"replay {rep} K={kc} V={vc} G={G}")
