@@ -9,7 +9,10 @@ attention over the quantized cache, and the split-K merge.  The default
 workload is "batched": 8 sequences x 1 new token, 32 query heads on 8 KV
 heads, head_dim 128, 8192 cached rows per sequence, K and V both q8_0.
 Other workloads (tiny, lowbit, rotated, ladder) are available with
---workload.
+--workload.  ``--q-len N`` (2 .. 4, single-layer workloads) makes each step
+verify N new tokens per sequence at once, causal among themselves
+(vit_attn_decode_mq, all N rows appended by the decode call); ``value`` then
+counts the N tokens of every sequence.
 
 Inputs are synthetic (seeded device normals shaped like the workload) and
 resident in HBM before timing starts.  Because the batched cache (143 MB)
@@ -110,6 +113,9 @@ def run_gpu(args):
     cfgno = WORKLOADS[args.workload]
     cfg = synth.CONFIGS[cfgno]
     S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
+    QL = args.q_len
+    if QL > 1 and ("ubatch" in cfg or (Hq // H) * QL > 16 or QL > 4):
+        raise SystemExit(f"--q-len {QL} needs a single-layer workload with (n_q_heads / n_kv_heads) x q_len <= 16")
     cmap = synth.codec_map(cfgno)
     n_layers = cfg["layers"]
     gen = torch.Generator(device="cuda")
@@ -138,7 +144,7 @@ def run_gpu(args):
             if cfg["dist"] == "lognormal":
                 sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
                 chan_scale[(li, side)] = sc
-            pre = cfg.get("prefill", L - 1 if cfg["fused_append"] else L)
+            pre = cfg.get("prefill", L - QL if cfg["fused_append"] else L)
             # fill the prefix in chunks to bound the fp32 staging buffer
             chunk = 16384
             for p0 in range(0, pre, chunk):
@@ -154,25 +160,27 @@ def run_gpu(args):
     torch.cuda.synchronize()
 
     # per-step inputs
-    q = [_device_rows(torch, gen, (S, Hq, D), cfg["dist"]) for _ in range(n_layers)]
+    qshape = (S, Hq, D) if QL == 1 else (S, QL, Hq, D)
+    q = [_device_rows(torch, gen, qshape, cfg["dist"]) for _ in range(n_layers)]
     if "ubatch" in cfg:
         T, p_new = cfg["ubatch"], cfg["prefill"]
     else:
-        T, p_new = 1, L - 1
+        T, p_new = QL, L - QL
     new_rows = [[_device_rows(torch, gen, (S, T, H, D), cfg["dist"], chan_scale.get((li, s)))
                  for s in ("k", "v")] for li in range(n_layers)]
     n_splits = args.splits if args.splits else vit.vit_attn_default_splits(S, H, Hq, L)
-    ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq, D, n_splits), dtype=torch.uint8, device="cuda")
-    out = [torch.empty((S, Hq, D), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq * QL, D, n_splits), dtype=torch.uint8, device="cuda")
+    out = [torch.empty(qshape, dtype=torch.float32, device="cuda") for _ in range(n_layers)]
     lens = [L] * S
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
 
     # every call of a step, marshalled once per replica (the host then only
-    # issues the C calls, so the GPU queue never runs dry).  One new token per
-    # sequence: its K/V rows go through the decode call's fused append.  A
-    # ubatch of new rows (the ladder) is appended by vit_kv_append_quant first.
-    fused = T == 1
+    # issues the C calls, so the GPU queue never runs dry).  One (or q_len)
+    # new token(s) per sequence: their K/V rows go through the decode call's
+    # fused append.  A ubatch of new rows (the ladder) is appended by
+    # vit_kv_append_quant first.
+    fused = "ubatch" not in cfg
     calls = []
     for r in range(replicas):
         app, dec = [], []
@@ -181,11 +189,14 @@ def run_gpu(args):
             if not fused:
                 app.append(vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=stream))
                 app.append(vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=stream))
+            # [S][H][128] rows for one token, [S][q_len][H][128] for several
+            k_in = (kn[:, 0].contiguous() if QL == 1 else kn) if fused else None
+            v_in = (vn[:, 0].contiguous() if QL == 1 else vn) if fused else None
             d = vit.prepare_decode(lay.K[r], lay.V[r], q[li], Hq, lens, out[li], n_splits=n_splits,
-                                   k_new=kn[:, 0].contiguous() if fused else None,
-                                   v_new=vn[:, 0].contiguous() if fused else None,
-                                   workspace=ws if n_splits > 1 else None, stream=stream)
-            red = vit.prepare_reduce(ws, S, Hq, n_splits, lay.V[r], out[li], stream=stream) if n_splits > 1 else None
+                                   k_new=k_in, v_new=v_in, workspace=ws if n_splits > 1 else None,
+                                   stream=stream, q_len=QL if QL > 1 else None)
+            red = (vit.prepare_reduce(ws, S, Hq * QL, n_splits, lay.V[r], out[li], stream=stream)
+                   if n_splits > 1 else None)
             dec.append((d, red))
         calls.append((app, dec))
 
@@ -262,7 +273,7 @@ def run_gpu(args):
     per_launch_bytes = kv_bytes / n_layers
     # algorithmic bytes of all timed decode launches / their summed duration
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
-    return dict(cfg=cfg, cfgno=cfgno, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, mode=mode,
+    return dict(cfg=cfg, cfgno=cfgno, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
                 dec_mean_ms=dec_mean_ms,
                 dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
@@ -286,7 +297,8 @@ def run_copy_calibration(steps):
 
 def cpu_baseline(r, budget_s=15.0):
     """The numpy oracle on the host: for each (sequence, KV head) of the step,
-    quantize the new rows, dequantize the cache and attend in fp64."""
+    quantize the new rows, dequantize the cache and attend in fp64 (each of
+    q_len new tokens over the rows up to its own)."""
     import numpy as np
 
     from oracle import attention, codecs
@@ -297,7 +309,7 @@ def cpu_baseline(r, budget_s=15.0):
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    cfgno, L, S, H, Hq = r["cfgno"], r["L"], r["S"], r["H"], r["Hq"]
+    cfgno, L, S, H, Hq, QL = r["cfgno"], r["L"], r["S"], r["H"], r["Hq"], r["QL"]
     G = Hq // H
     kc, vc = r["cmap"][0]
     ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
@@ -309,8 +321,8 @@ def cpu_baseline(r, budget_s=15.0):
         kx = synth.kv_rows(cfgno, "k", 0, s, h, 0, rows_unit)
         vx = synth.kv_rows(cfgno, "v", 0, s, h, 0, rows_unit)
         qx = synth.q_rows(cfgno, 0, s, Hq)[h * G:(h + 1) * G]
-        prep.append((codecs.quantize(kc, kx[:-1], ks), codecs.quantize(vc, vx[:-1], vs),
-                     kx[-1:], vx[-1:], qx))
+        prep.append((codecs.quantize(kc, kx[:-QL], ks), codecs.quantize(vc, vx[:-QL], vs),
+                     kx[-QL:], vx[-QL:], qx))
     scale = 1.0 / math.sqrt(D)
     n_done = 0
     t0 = time.perf_counter()
@@ -320,7 +332,10 @@ def cpu_baseline(r, budget_s=15.0):
                    zip(kq.items(), codecs.quantize(kc, kn, ks).values())}
             vq2 = {k: np.concatenate([a, b]) for (k, a), b in
                    zip(vq.items(), codecs.quantize(vc, vn, vs).values())}
-            attention.attend(qx, codecs.dequant(kc, kq2, ks), codecs.dequant(vc, vq2, vs), scale)
+            kd, vd = codecs.dequant(kc, kq2, ks), codecs.dequant(vc, vq2, vs)
+            n = kd.shape[0]
+            for t in range(QL):  # token t sees rows 0 .. n - QL + t (the timing does not depend on q's values)
+                attention.attend(qx, kd[:n - QL + 1 + t], vd[:n - QL + 1 + t], scale)
             n_done += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -329,11 +344,16 @@ def cpu_baseline(r, budget_s=15.0):
         limiter.unregister() if hasattr(limiter, "unregister") else None
     per_unit = el / n_done * (L / rows_unit)
     step_s = per_unit * len(units) * r["n_layers"]
-    return {"value": S / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{n_done} (sequence, KV head) units of the step ({kc}/{vc}, G={G}) over "
+    return {"value": S * QL / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{n_done} (sequence, KV head) units of the step ({kc}/{vc}, G={G}, {QL} new token(s)) over "
                        f"{rows_unit} rows each, {el:.1f} s on 1 thread, scaled to {len(units)} units x "
-                       f"{L} rows x {r['n_layers']} layer(s) per step; step = quantize new row + "
+                       f"{L} rows x {r['n_layers']} layer(s) per step; step = quantize new row(s) + "
                        "dequantize cache + fp64 attention")}
+
+
+def profile_tag(workload, q_len):
+    """Name of a workload's profiles: the workload, plus the verify width."""
+    return workload if q_len == 1 else f"{workload}_verify{q_len}"
 
 
 def load_traffic(workload, per_launch_bytes):
@@ -442,6 +462,8 @@ def main():
     ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS))
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new tokens per sequence verified per step (vit_attn_decode_mq when > 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps as HIP graph replays (one captured graph per replica)")
@@ -451,17 +473,18 @@ def main():
                     help="write profiles/ summaries for --workload from rocprofv3 output under PROF_DIR (no GPU)")
     args = ap.parse_args()
     if args.summarize:
-        w = args.workload
-        cmds = [f"python3 bench.py --workload {w} --no-cpu-baseline > PROF/{w}/bench.json",
+        w = profile_tag(args.workload, args.q_len)
+        b = f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
+        cmds = [f"{b} --no-cpu-baseline > PROF/{w}/bench.json",
                 f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{w}/trace -o run -- "
-                f"python3 bench.py --workload {w} --no-cpu-baseline > PROF/{w}/bench_traced.json",
+                f"{b} --no-cpu-baseline > PROF/{w}/bench_traced.json",
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/{w}/fetch -o run -- "
-                f"python3 bench.py --workload {w} --steps 20 --warmup 3 --no-cpu-baseline",
+                f"{b} --steps 20 --warmup 3 --no-cpu-baseline",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/{w}/write -o run -- "
-                f"python3 bench.py --workload {w} --steps 20 --warmup 3 --no-cpu-baseline",
+                f"{b} --steps 20 --warmup 3 --no-cpu-baseline",
                 "rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/copy_fetch -o run -- python3 bench.py --calib-copy 4",
                 "rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/copy_write -o run -- python3 bench.py --calib-copy 4",
-                f"python3 bench.py --workload {w} --summarize PROF"]
+                f"{b} --summarize PROF"]
         summarize_profiles(w, args.summarize, cmds)
         return
     if args.gpus != 1:
@@ -474,8 +497,8 @@ def main():
         return
     r = run_gpu(args)
     cfg = r["cfg"]
-    tok_s = r["S"] / (r["ms_per_step"] * 1e-3)
-    traffic = load_traffic(args.workload, r["per_launch_bytes"])
+    tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
+    traffic = load_traffic(profile_tag(args.workload, r["QL"]), r["per_launch_bytes"])
     line = {
         "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(tok_s, 1),
@@ -490,9 +513,9 @@ def main():
         "dtype": "q8_0/q4_0/rot4/f16 codes, fp16 MFMA operands (hi+lo split), fp32 accumulate",
         "data": "synthetic (seeded device normals shaped like the workload; no model weights or dataset)",
         "config": {
-            "workload": cfg["name"],
+            "workload": profile_tag(cfg["name"], r["QL"]),
             "n_seqs": r["S"], "n_q_heads": r["Hq"], "n_kv_heads": r["H"], "head_dim": D,
-            "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"],
+            "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"], "query_tokens_per_seq": r["QL"],
             "codecs": "ladder (seeded per layer/side)" if r["n_layers"] > 1 else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
             "n_splits": r["n_splits"], "cold_cache_replicas": r["replicas"], "launch": r["mode"],
         },

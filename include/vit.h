@@ -122,7 +122,8 @@ typedef enum vit_status {
 #define VIT_HEAD_DIM 128
 #define VIT_CAPACITY_ALIGN 256
 #define VIT_MAX_SEQS 64
-#define VIT_MAX_GQA 16
+#define VIT_MAX_GQA 16 /* query rows per KV head: G, or G * q_len for vit_attn_decode_mq */
+#define VIT_MAX_QLEN 4 /* new tokens per sequence in one vit_attn_decode_mq call */
 #define VIT_MAX_SPLITS 4096
 #define VIT_MAX_CAPACITY (1 << 30) /* rows per (sequence, KV head) */
 
@@ -194,6 +195,31 @@ int vit_attn_decode(const vit_kv_plane *k, const vit_kv_plane *v, const float *q
                     int32_t n_q_heads, const int64_t *seq_len, const float *k_new,
                     const float *v_new, float scale, int32_t n_splits, float *workspace,
                     float *out, void *stream);
+
+/* Decode attention for q_len new query tokens per sequence at once, causal
+ * among themselves, as when a run of drafted tokens is verified in one pass
+ * (Randozart/VITRIOL page: "How It Works -- Resident mode" drafts ahead with
+ * parallel verification; "Configuration" runs up to 3 drafted tokens).
+ * Token t (0 .. q_len-1) of sequence s attends rows
+ * 0 .. seq_len[s] - q_len + t, i.e. the cached rows and the new rows up to
+ * and including its own.  vit_attn_decode is the q_len == 1 case.
+ *  q         fp32 [n_seqs][q_len][n_q_heads][128], model domain.
+ *  q_len     1 .. VIT_MAX_QLEN, with G * q_len <= VIT_MAX_GQA.
+ *  seq_len   [host] int64 [n_seqs], q_len .. capacity: rows attended by the
+ *            last new token (the q_len new rows are its last rows).
+ *  k_new, v_new  optional fp32 [n_seqs][q_len][n_kv_heads][128], stored at
+ *            rows seq_len[s] - q_len + t first (both or neither).
+ *  workspace vit_attn_workspace_bytes(n_seqs, n_q_heads * q_len, 128,
+ *            n_splits) bytes; merge with vit_attn_splitk_reduce(workspace,
+ *            n_seqs, n_q_heads * q_len, 128, n_splits, v, out).
+ *  out       fp32 [n_seqs][q_len][n_q_heads][128].
+ * Other arguments, errors and accuracy as vit_attn_decode; seq_len[s] <
+ * q_len is VIT_E_ARG, q_len > VIT_MAX_QLEN or G * q_len > VIT_MAX_GQA is
+ * VIT_E_UNSUPPORTED. */
+int vit_attn_decode_mq(const vit_kv_plane *k, const vit_kv_plane *v, const float *q,
+                       int32_t n_q_heads, int32_t q_len, const int64_t *seq_len,
+                       const float *k_new, const float *v_new, float scale, int32_t n_splits,
+                       float *workspace, float *out, void *stream);
 
 /* Merge the split partials of vit_attn_decode: M = max m_s,
  * L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L (max values are kept

@@ -83,3 +83,26 @@ def decode_reference(q_rows, k_rows, v_rows, k_codec, v_codec, scale,
     kd = codecs.dequant(k_codec, kq, k_signs)
     vd = codecs.dequant(v_codec, vq, v_signs)
     return attend(q_rows, kd, vd, scale)
+
+
+def decode_multi_reference(q_rows, k_rows, v_rows, k_codec, v_codec, scale,
+                           k_signs=None, v_signs=None):
+    """T new query tokens of one (sequence, KV head) at once, causal among
+    themselves, as when a drafted run of tokens is verified in one pass
+    (Randozart/VITRIOL page: "How It Works -- Resident mode" has the MTP head
+    draft ahead with parallel verification; "Configuration" runs up to 3
+    drafted tokens).  Reading: token t (0-based among the T) attends the
+    cached rows and the new rows up to and including its own, i.e. rows
+    0 .. L - T + t of k_rows / v_rows, which end with the T new rows.
+
+    q_rows [T,G,128] fp32; k_rows, v_rows [L,128] fp32 (L >= T).  Returns
+    fp64 [T,G,128].
+    """
+    T, L = len(q_rows), len(k_rows)
+    if not 1 <= T <= L:
+        raise ValueError("need 1 <= T <= L")
+    kq = codecs.quantize(k_codec, k_rows, k_signs)
+    vq = codecs.quantize(v_codec, v_rows, v_signs)
+    kd = codecs.dequant(k_codec, kq, k_signs)
+    vd = codecs.dequant(v_codec, vq, v_signs)
+    return np.stack([attend(q_rows[t], kd[:L - T + 1 + t], vd[:L - T + 1 + t], scale) for t in range(T)])

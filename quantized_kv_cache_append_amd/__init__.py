@@ -22,7 +22,8 @@ from ._lib import CODEC_IDS, SIDE_IDS, VitError, VitKvPlane
 __all__ = [
     "KVPlane", "VitError", "layout",
     "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_attn_workspace_bytes",
-    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_splitk_reduce", "vit_arm_kernel_events",
+    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_splitk_reduce",
+    "vit_arm_kernel_events",
 ]
 
 HEAD_DIM = 128
@@ -163,6 +164,29 @@ def vit_attn_decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=N
     return out
 
 
+def vit_attn_decode_mq(k, v, q, n_q_heads, q_len, seq_len, k_new=None, v_new=None, scale=None, n_splits=1,
+                       workspace=None, out=None, stream=None):
+    """Decode attention for ``q_len`` new tokens per sequence, causal among
+    themselves; q fp32 [S, q_len, Hq, 128]; returns ``out`` (fp32
+    [S, q_len, Hq, 128]), which holds the result only when n_splits == 1
+    (otherwise vit_attn_splitk_reduce with n_q_heads * q_len rows)."""
+    import torch
+
+    lib = _lib.load()
+    if scale is None:
+        scale = 1.0 / np.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((k.n_seqs, q_len, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    st = lib.vit_attn_decode_mq(ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len), sl,
+                                _fptr(k_new, "k_new"), _fptr(v_new, "v_new"), float(scale), int(n_splits),
+                                _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
+                                _fptr(out, "out"), _stream_handle(stream))
+    _lib.check("vit_attn_decode_mq", st)
+    return out
+
+
 def vit_attn_splitk_reduce(workspace, n_seqs, n_q_heads, head_dim, n_splits, v, out, stream=None):
     lib = _lib.load()
     vp = v.struct()
@@ -173,18 +197,24 @@ def vit_attn_splitk_reduce(workspace, n_seqs, n_q_heads, head_dim, n_splits, v, 
 
 
 def decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_splits=None,
-           workspace=None, out=None, stream=None):
-    """vit_attn_decode followed (when n_splits > 1) by vit_attn_splitk_reduce."""
+           workspace=None, out=None, stream=None, q_len=None):
+    """vit_attn_decode (or, with ``q_len``, vit_attn_decode_mq: q
+    [S, q_len, Hq, 128]) followed when n_splits > 1 by vit_attn_splitk_reduce."""
     import torch
 
+    rows = n_q_heads * (q_len or 1)
     if n_splits is None:
         n_splits = vit_attn_default_splits(k.n_seqs, k.n_kv_heads, n_q_heads, max(seq_len))
     if n_splits > 1 and workspace is None:
-        workspace = torch.empty(vit_attn_workspace_bytes(k.n_seqs, n_q_heads, HEAD_DIM, n_splits),
+        workspace = torch.empty(vit_attn_workspace_bytes(k.n_seqs, rows, HEAD_DIM, n_splits),
                                 dtype=torch.uint8, device=q.device)
-    out = vit_attn_decode(k, v, q, n_q_heads, seq_len, k_new, v_new, scale, n_splits, workspace, out, stream)
+    if q_len is None:
+        out = vit_attn_decode(k, v, q, n_q_heads, seq_len, k_new, v_new, scale, n_splits, workspace, out, stream)
+    else:
+        out = vit_attn_decode_mq(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, workspace,
+                                 out, stream)
     if n_splits > 1:
-        vit_attn_splitk_reduce(workspace, k.n_seqs, n_q_heads, HEAD_DIM, n_splits, v, out, stream)
+        vit_attn_splitk_reduce(workspace, k.n_seqs, rows, HEAD_DIM, n_splits, v, out, stream)
     return out
 
 
@@ -227,16 +257,20 @@ def prepare_append(plane, src, pos0, n_tokens=None, stream=None):
 
 
 def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, scale=None, n_splits=1,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, q_len=None):
     lib = _lib.load()
     scale = 1.0 / np.sqrt(HEAD_DIM) if scale is None else scale
     sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
     kp, vp = k.struct(), v.struct()
-    args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), sl, _fptr(k_new, "k_new"),
-            _fptr(v_new, "v_new"), ctypes.c_float(scale), int(n_splits),
+    tail = (_fptr(k_new, "k_new"), _fptr(v_new, "v_new"), ctypes.c_float(scale), int(n_splits),
             _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
             _fptr(out, "out"), _stream_handle(stream))
-    return _Prepared("vit_attn_decode", lib.vit_attn_decode, args, (kp, vp, sl, q, k_new, v_new, workspace, out, k, v))
+    keep = (kp, vp, sl, q, k_new, v_new, workspace, out, k, v)
+    if q_len is None:
+        args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), sl) + tail
+        return _Prepared("vit_attn_decode", lib.vit_attn_decode, args, keep)
+    args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len), sl) + tail
+    return _Prepared("vit_attn_decode_mq", lib.vit_attn_decode_mq, args, keep)
 
 
 def prepare_reduce(workspace, n_seqs, n_q_heads, n_splits, v, out, stream=None):

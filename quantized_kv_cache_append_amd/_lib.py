@@ -27,6 +27,7 @@ EXPORTS = (
     "vit_attn_workspace_bytes",
     "vit_attn_default_splits",
     "vit_attn_decode",
+    "vit_attn_decode_mq",
     "vit_attn_splitk_reduce",
     "vit_arm_kernel_events",
     "vit_status_string",
@@ -83,6 +84,8 @@ def load():
     lib.vit_arm_kernel_events.restype = ctypes.c_int
     lib.vit_attn_decode.argtypes = [plane_p, plane_p, vp, i32, P(i64), vp, vp, f32, i32, vp, vp, vp]
     lib.vit_attn_decode.restype = ctypes.c_int
+    lib.vit_attn_decode_mq.argtypes = [plane_p, plane_p, vp, i32, i32, P(i64), vp, vp, f32, i32, vp, vp, vp]
+    lib.vit_attn_decode_mq.restype = ctypes.c_int
     lib.vit_attn_splitk_reduce.argtypes = [vp, i32, i32, i32, i32, plane_p, vp, vp]
     lib.vit_attn_splitk_reduce.restype = ctypes.c_int
     lib.vit_status_string.argtypes = [ctypes.c_int]

@@ -391,13 +391,15 @@ struct QOperands<2> {
 
 // One 32-row tile for one wave with 4 query rows: S^T = Q K^T, online
 // softmax, O += P V.
+//   L:    rows of the stream that hold data (the last query row's length);
+//   lmin: the shortest query row's length; lim: this lane's query row length.
 template <int KC, int VC, int NT>
-__device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, int t, int L, int lane,
-                                             const QOperands<NT>& aq, WaveState<NT>& st,
-                                             float (*s_p)[4][kTile], const Lut& lut) {
+__device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, int t, int L, int lmin,
+                                             const int (&lim)[NT], int lane, const QOperands<NT>& aq,
+                                             WaveState<NT>& st, float (*s_p)[4][kTile], const Lut& lut) {
   static_assert(NT == 1, "4 query rows per wave");
   const int n16 = lane & 15, qg = lane >> 4;
-  const bool partial = (t + 1) * kTile > L;
+  const bool partial = (t + 1) * kTile > lmin;
   // ---- V block factors of the lane's P.V operand rows (block n16 & 3, tile
   //      rows 8qg .. 8qg+7) and the wave's V exponent check, first so that
   //      they overlap the S^T products ----
@@ -471,7 +473,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
       float v;
       if constexpr (KC == F16) v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       else v = (acc[0] * kf[h][0] + acc[1] * kf[h][1]) + (acc[2] * kf[h][2] + acc[3] * kf[h][3]);
-      const bool dead = partial && t * kTile + 16 * h + n16 >= L;
+      const bool dead = partial && t * kTile + 16 * h + n16 >= lim[nt];
       s[nt][h] = dead ? -INFINITY : v;
     }
   }
@@ -554,11 +556,11 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
 //        the operand of its block c / 2; the output rows are (query, part)
 //        again, and the two parts are added at the end.
 template <int KC, int VC>
-__device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur, int t, int L, int lane,
-                                                  const QOperands<2>& aq, WaveState<2>& st, float* s_p,
-                                                  const Lut& lut) {
+__device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur, int t, int L, int lmin,
+                                                  const int (&lim)[2], int lane, const QOperands<2>& aq,
+                                                  WaveState<2>& st, float* s_p, const Lut& lut) {
   const int n16 = lane & 15, qg = lane >> 4;
-  const bool partial = (t + 1) * kTile > L;
+  const bool partial = (t + 1) * kTile > lmin;
   // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
   //      check, first so that they overlap the S^T products.  For q8_0 and
   //      q4_0 the factor is the fp16 scale itself: it stays in fp16 (the
@@ -649,9 +651,9 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       acc[b] = mfma16(aq.w[b], unpack_k<KC>(cur.kd[h], b, lut), float4v{0.0f, 0.0f, 0.0f, 0.0f});
-    const bool dead = partial && t * kTile + 16 * h + n16 >= L;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
+      const bool dead = partial && t * kTile + 16 * h + n16 >= lim[jj];
       float d[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) d[b] = acc[b][2 * jj] + acc[b][2 * jj + 1];
@@ -776,8 +778,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const int split = blockIdx.x;
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
-  const int L = a.seq_len[seq];
-  const int G = a.gqa;
+  // Query rows of this KV head: r = t * gqa + g for new token t < q_len and
+  // q-head g < gqa; row r attends rows 0 .. lmin - 1 + t of the stream.
+  const int L = a.seq_len[seq];  // rows attended by the last new token
+  const int QL = a.q_len;
+  const int lmin = L - QL + 1;    // rows attended by the first new token
+  const int G = a.gqa * QL;       // query rows
   constexpr int kThreads = 64 * kDecodeWaves;
   const int n_groups = (G + RW - 1) / RW;   // 1, 2 or 4
   const int wpg = kDecodeWaves / n_groups;  // waves per row group
@@ -793,7 +799,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   __shared__ float s_m[kDecodeWaves][RW];
   __shared__ float s_l[kDecodeWaves][RW];
   __shared__ int s_next[4];  // per row group: next tile slot to hand out
-  __shared__ uint8_t s_row[2][256];
+  __shared__ uint8_t s_row[5][256];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
   const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
@@ -803,28 +809,44 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
   const uint16_t* vnb = has_norms(VC) ? a.vnorms + ph * a.capacity : nullptr;
 
-  // ---- fused append: the workgroup owning the new row's tile stores the new
-  //      K and V rows before it reads any tile (no other workgroup reads it) ----
-  if (a.k_new != nullptr && ((L - 1) / kTile) % a.n_splits == split) {
-    const int64_t p = L - 1;
-    const int64_t src = (static_cast<int64_t>(seq) * a.n_kv_heads + head) * kD;
-    if (wave == 0) {
-      append_one_row<KC, 0>(const_cast<uint8_t*>(kbase), const_cast<uint16_t*>(ksb), const_cast<uint16_t*>(knb),
-                            p, a.k_new + src, lane, a.ksigns, s_row[0]);
-    } else if (wave == 1) {
-      append_one_row<VC, 1>(const_cast<uint8_t*>(vbase), const_cast<uint16_t*>(vsb), const_cast<uint16_t*>(vnb),
-                            p, a.v_new + src, lane, a.vsigns, s_row[1]);
+  // ---- fused append: the new rows p = lmin - 1 + i (i < q_len) are stored
+  //      by the workgroup owning their tile, before it reads any tile (no
+  //      other workgroup reads that tile).  K row i goes on wave 2i; the V
+  //      rows go in order on wave 1, because 4-bit V rows of one 8-row group
+  //      share 32-bit words that each store rewrites ----
+  if (a.k_new != nullptr) {
+    auto owned = [&](int i) { return ((lmin - 1 + i) / kTile) % a.n_splits == split; };
+    bool mine = false;
+    for (int i = 0; i < QL; ++i) mine = mine || owned(i);
+    if (mine) {
+      auto src = [&](int i) { return ((static_cast<int64_t>(seq) * QL + i) * a.n_kv_heads + head) * kD; };
+      for (int i = 0; i < QL; ++i) {
+        if (owned(i) && wave == 2 * i)
+          append_one_row<KC, 0>(const_cast<uint8_t*>(kbase), const_cast<uint16_t*>(ksb), const_cast<uint16_t*>(knb),
+                                lmin - 1 + i, a.k_new + src(i), lane, a.ksigns, s_row[i]);
+      }
+      if (wave == 1) {
+        for (int i = 0; i < QL; ++i)
+          if (owned(i))
+            append_one_row<VC, 1>(const_cast<uint8_t*>(vbase), const_cast<uint16_t*>(vsb),
+                                  const_cast<uint16_t*>(vnb), lmin - 1 + i, a.v_new + src(i), lane, a.vsigns,
+                                  s_row[4]);
+      }
+      // Only waves of this workgroup read the rows back, and they share its
+      // L1: the barrier's workgroup-scope release/acquire is enough.  (A
+      // device-scope fence here writes back and invalidates the L2 and costs
+      // tens of us.)
+      __syncthreads();
     }
-    // Only waves of this workgroup read the row back, and they share its L1:
-    // the barrier's workgroup-scope release/acquire is enough.  (A device-scope
-    // fence here writes back and invalidates the L2 and costs tens of us.)
-    __syncthreads();
   }
 
   // Every global load below is unconditional: a load under a branch makes
   // the compiler wait for all outstanding loads where the paths merge, which
   // would serialise the prefetch.  Out-of-range indices are clamped instead.
-  const float* qrow = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
+  // index (into [S][q_len][Hq]) of query row r; also the output row
+  auto qrow_index = [&](int r) {
+    return (static_cast<int64_t>(seq) * QL + r / a.gqa) * a.n_q_heads + static_cast<int64_t>(head) * a.gqa + r % a.gqa;
+  };
   // The query rows are staged through LDS: thread tid < 256 holds floats
   // 8*tid .. 8*tid+7 of the padded [16][128] rows (two registers per thread,
   // so nothing needs the query before the tile prefetch is issued).
@@ -832,7 +854,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   float4v q0, q1;
   [[maybe_unused]] uint32_t ksw = 0;
   {
-    const float* qsrc = qrow + min(qs_row, G - 1) * kD + ((8 * tid) & 127);
+    const float* qsrc = a.q + qrow_index(min(qs_row, G - 1)) * kD + ((8 * tid) & 127);
     q0 = *reinterpret_cast<const float4v*>(qsrc);
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
     if constexpr (KC == ROT4) ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
@@ -945,7 +967,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   WaveState<NT> st;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    st.m_run[nt] = -INFINITY;
+    // finite, so that a row whose tiles so far were all masked (an early new
+    // token on a tile past its last row) gets p = 2^(-inf) = 0 and alpha
+    // stays finite; no real score lies below it
+    st.m_run[nt] = -__FLT_MAX__;
     st.l_run[nt] = 0.0f;
   }
 #pragma unroll
@@ -953,6 +978,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   st.vexp = 0.0f;
   st.vlo = INFINITY;  // the first tile sets the exponent
   st.vhi = INFINITY;
+
+  // length of the lane's query row of state nt (4 rows: qg; 8 rows: 2qg + nt);
+  // padding rows past G stop at L like the last live row
+  int lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + (RW * group + (NT == 1 ? qg : 2 * qg + nt)) / a.gqa, L);
 
   // slot k is live while its tile exists; slots taken later are larger, so
   // a wave stops at its first dead slot
@@ -963,8 +994,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     return __builtin_amdgcn_readfirstlane(k);
   };
   auto proc = [&](const TileRegs<KC, VC, NT>& r, int t) {
-    if constexpr (NT == 1) process_tile<KC, VC, NT>(r, t, L, lane, aq, st, s_p[wave], lutr);
-    else process_tile_wide<KC, VC>(r, t, L, lane, aq, st, &s_p[wave][0][0][0], lutr);
+    if constexpr (NT == 1) process_tile<KC, VC, NT>(r, t, L, lmin, lim, lane, aq, st, s_p[wave], lutr);
+    else process_tile_wide<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
   };
   int ka = wig, kb = wig + wpg;
   if constexpr (D == 3) {
@@ -1034,7 +1065,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     if (final_out) {
       sq[g][c] = Ls > 0.0f ? O / Ls : 0.0f;
     } else if (g < G) {
-      const int64_t row = (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G + g) * a.n_splits + split;
+      const int64_t row = qrow_index(g) * a.n_splits + split;
       a.ws_o[row * kD + c] = O;
       if (c == 0) {
         a.ws_ml[row * 2] = M;
@@ -1063,7 +1094,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
         v *= (1.0f / 128.0f);
         v = ((a.vsigns[c >> 5] >> (c & 31)) & 1u) ? -v : v;
       }
-      a.out[(static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G + g) * kD + c] = v;
+      a.out[qrow_index(g) * kD + c] = v;
     }
   }
 }

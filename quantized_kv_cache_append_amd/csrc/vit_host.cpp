@@ -138,6 +138,12 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
 int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads,
                     const int64_t* seq_len, const float* k_new, const float* v_new, float scale,
                     int32_t n_splits, float* workspace, float* out, void* stream) {
+  return vit_attn_decode_mq(k, v, q, n_q_heads, 1, seq_len, k_new, v_new, scale, n_splits, workspace, out, stream);
+}
+
+int vit_attn_decode_mq(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads,
+                       int32_t q_len, const int64_t* seq_len, const float* k_new, const float* v_new, float scale,
+                       int32_t n_splits, float* workspace, float* out, void* stream) {
   const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
   g_armed = vit::KernelEvents{};
   int st = check_plane(k);
@@ -148,14 +154,15 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   if (k->n_seqs != v->n_seqs || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity) return VIT_E_ARG;
   if (!q || !out || !seq_len) return VIT_E_ARG;
   if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return VIT_E_ARG;
+  if (q_len < 1) return VIT_E_ARG;
   const int32_t gqa = n_q_heads / k->n_kv_heads;
-  if (gqa > VIT_MAX_GQA) return VIT_E_UNSUPPORTED;
+  if (q_len > VIT_MAX_QLEN || gqa * q_len > VIT_MAX_GQA) return VIT_E_UNSUPPORTED;
   if ((k_new == nullptr) != (v_new == nullptr)) return VIT_E_ARG;
   if (n_splits < 1 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
   if (n_splits > 1 && !workspace) return VIT_E_ARG;
   if (!isfinite(scale)) return VIT_E_ARG;
   for (int s = 0; s < k->n_seqs; ++s) {
-    if (seq_len[s] < 1) return VIT_E_ARG;
+    if (seq_len[s] < q_len) return VIT_E_ARG;
     if (seq_len[s] > k->capacity) return VIT_E_CAPACITY;
   }
   if (!aligned(q, 16) || !aligned(out, 16) || (workspace && !aligned(workspace, 16)) ||
@@ -176,13 +183,14 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   a.v_new = v_new;
   a.ws_o = workspace;
   a.ws_ml = workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                                 ws_o_bytes(k->n_seqs, n_q_heads, n_splits))
+                                                 ws_o_bytes(k->n_seqs, n_q_heads * q_len, n_splits))
                       : nullptr;
   a.out = out;
   a.capacity = k->capacity;
   a.n_kv_heads = k->n_kv_heads;
   a.n_q_heads = n_q_heads;
   a.gqa = gqa;
+  a.q_len = q_len;
   a.n_splits = n_splits;
   a.qscale = scale * 1.4426950408889634f;
   load_signs(k, a.ksigns);
@@ -190,7 +198,7 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
   for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
   const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
                   static_cast<unsigned>(k->n_seqs));
-  const int nt = gqa <= 4 ? 1 : 2;  // query rows per wave: 4 or 8
+  const int nt = gqa * q_len <= 4 ? 1 : 2;  // query rows per wave: 4 or 8
   return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 

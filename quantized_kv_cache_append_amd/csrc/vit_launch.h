@@ -31,15 +31,16 @@ struct DecodeArgs {
   const uint16_t* vscales;
   const uint16_t* vnorms;
   const float* q;
-  const float* k_new;  // fused append: new K rows [S][Hkv][128] or null
+  const float* k_new;  // fused append: new K rows [S][q_len][Hkv][128] or null
   const float* v_new;
-  float* ws_o;     // [S][Hq][n_splits][128]
-  float* ws_ml;    // [S][Hq][n_splits][2]
-  float* out;      // [S][Hq][128]
+  float* ws_o;     // [S][q_len][Hq][n_splits][128]
+  float* ws_ml;    // [S][q_len][Hq][n_splits][2]
+  float* out;      // [S][q_len][Hq][128]
   int64_t capacity;
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int32_t gqa;
+  int32_t q_len;   // new query tokens per sequence (causal among themselves)
   int32_t n_splits;
   float qscale;    // softmax scale * log2(e)
   uint32_t ksigns[4];

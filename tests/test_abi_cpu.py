@@ -138,6 +138,24 @@ def test_decode_validation(lib):
     assert _decode(lib, K, _plane(side=1, cap=1024)) == _lib.VIT_E_ARG
 
 
+def _decode_mq(lib, k, v, hq=4, q_len=2, seq_len=(10, 10), ns=1, ws=None):
+    arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+    return lib.vit_attn_decode_mq(ctypes.byref(k), ctypes.byref(v), FAKE, hq, q_len, arr, None, None, 0.088, ns, ws,
+                                  FAKE, None)
+
+
+def test_decode_mq_validation(lib):
+    """Several new tokens per call: q_len 1..4, G * q_len <= 16 and every
+    sequence at least q_len rows long (no compute: every case fails)."""
+    K, V = _plane(side=0), _plane(side=1)
+    assert _decode_mq(lib, K, V, q_len=0) == _lib.VIT_E_ARG
+    assert _decode_mq(lib, K, V, q_len=5) == _lib.VIT_E_UNSUPPORTED
+    assert _decode_mq(lib, K, V, hq=18, q_len=2) == _lib.VIT_E_UNSUPPORTED   # G 9 x 2 rows
+    assert _decode_mq(lib, K, V, q_len=3, seq_len=(10, 2)) == _lib.VIT_E_ARG  # shorter than q_len
+    assert _decode_mq(lib, K, V, q_len=2, seq_len=(513, 10)) == _lib.VIT_E_CAPACITY
+    assert _decode_mq(lib, K, V, q_len=2, ns=3, ws=None) == _lib.VIT_E_ARG
+
+
 def test_reduce_validation(lib):
     V = _plane(side=1)
     r = lib.vit_attn_splitk_reduce

@@ -260,3 +260,46 @@ def test_decode_read_bytes_of_workloads():
     assert bytes_model.decode_kv_read_bytes("q8_0", "q8_0", 8, 8, 8192) == 142606336
     assert bytes_model.decode_kv_read_bytes("q4_0", "q4_0", 4, 8, 32768) == 150994944
     assert bytes_model.decode_kv_read_bytes("rot4", "rot4", 1, 2, 131072) == 38797312
+
+
+# --- several new tokens per sequence (drafted tokens verified together) ---
+
+def test_multi_token_single_token_is_decode(rng):
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    k = rng.standard_normal((40, 128)).astype(np.float32)
+    v = rng.standard_normal((40, 128)).astype(np.float32)
+    got = attention.decode_multi_reference(q[None], k, v, "q8_0", "q4_0", 1 / np.sqrt(128))
+    assert np.array_equal(got[0], attention.decode_reference(q, k, v, "q8_0", "q4_0", 1 / np.sqrt(128)))
+
+
+def test_multi_token_causality_and_last_token(rng):
+    """Token t must not see rows past its own position: changing those rows
+    leaves it unchanged, and the last token sees every row."""
+    T, L = 3, 50
+    q = rng.standard_normal((T, 2, 128)).astype(np.float32)
+    k = rng.standard_normal((L, 128)).astype(np.float32)
+    v = rng.standard_normal((L, 128)).astype(np.float32)
+    a = attention.decode_multi_reference(q, k, v, "f16", "f16", 0.1)
+    k2, v2 = k.copy(), v.copy()
+    k2[L - 1] += 5.0  # the last new row: only token T-1 sees it
+    v2[L - 1] -= 7.0
+    b = attention.decode_multi_reference(q, k2, v2, "f16", "f16", 0.1)
+    assert np.array_equal(a[:T - 1], b[:T - 1])
+    assert not np.allclose(a[T - 1], b[T - 1])
+    assert np.array_equal(a[T - 1], attention.decode_reference(q[T - 1], k, v, "f16", "f16", 0.1))
+
+
+def test_multi_token_bruteforce(rng):
+    """Tiny case against explicit loops over the causal row sets (f16 codec:
+    the oracle's dequantized rows are the fp16-rounded inputs)."""
+    T, L, G = 2, 5, 2
+    q = rng.standard_normal((T, G, 128)).astype(np.float32)
+    k = rng.standard_normal((L, 128)).astype(np.float32)
+    v = rng.standard_normal((L, 128)).astype(np.float32)
+    got = attention.decode_multi_reference(q, k, v, "f16", "f16", 0.2)
+    kr = k.astype(np.float16).astype(np.float64)
+    vr = v.astype(np.float16).astype(np.float64)
+    for t in range(T):
+        n = L - T + 1 + t
+        want = attention.attend_bruteforce(q[t].tolist(), kr[:n].tolist(), vr[:n].tolist(), 0.2)
+        assert np.allclose(got[t], want, rtol=1e-12, atol=1e-12)
