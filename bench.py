@@ -55,9 +55,15 @@ WORKLOADS = {"tiny": 1, "batched": 2, "lowbit": 3, "rotated": 4, "ladder": 5}
 D = 128
 
 
+# the decode kernel's own sources (the kernel, its device helpers, its argument block)
+DECODE_SOURCES = ("decode_impl.h", "decode_k*.hip", "vit_device.h", "vit_launch.h")
+
+
 def kernel_source_hash():
+    """sha256 prefix over the decode kernel's sources."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_kv_cache_append_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "quantized_kv_cache_append_amd", "csrc")
+    for p in sorted(q for pat in DECODE_SOURCES for q in glob.glob(os.path.join(csrc, pat))):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -356,15 +362,15 @@ def profile_tag(workload, q_len):
     return workload if q_len == 1 else f"{workload}_verify{q_len}"
 
 
-def load_traffic(workload, per_launch_bytes):
+def load_traffic(workload, n_splits):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    only if they were taken on the current kernel sources."""
+    only if they were taken on the current decode sources at this split count."""
     p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("n_splits") != n_splits:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -421,13 +427,14 @@ def summarize_profiles(workload, prof, commands):
         "algorithmic_bytes_per_launch": alg,
         "hbm_over_algorithmic": round(hbm / alg, 4),
         "kernel_source_hash": line["kernel_source_hash"],
+        "n_splits": line["config"]["n_splits"],
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
     md = [f"# decode_kernel, workload {workload}: rocprofv3 kernel statistics", "",
-          f"Kernel sources: {line['kernel_source_hash']} (sha256 prefix over the csrc/ files, as bench.py computes it).", "",
+          f"Kernel sources: {line['kernel_source_hash']} (sha256 prefix over the decode kernel's csrc/ files, as bench.py computes it).", "",
           "Commands (from the repository root, with TMPDIR=/tmp):", "", "```"] + commands + ["```", "",
           "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
@@ -498,7 +505,7 @@ def main():
     r = run_gpu(args)
     cfg = r["cfg"]
     tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
-    traffic = load_traffic(profile_tag(args.workload, r["QL"]), r["per_launch_bytes"])
+    traffic = load_traffic(profile_tag(args.workload, r["QL"]), r["n_splits"])
     line = {
         "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(tok_s, 1),

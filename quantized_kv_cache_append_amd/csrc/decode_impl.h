@@ -219,8 +219,8 @@ struct TileRegs {
   u32x4 vd[v_loads<VC>()];           // V column units
   u32x2 ks[2];                       // K scales of this lane's row in each half
   uint32_t kn[2];                    // K norms (rot4)
-  u32x4 vs[NT == 2 ? 4 : 1];         // V scales, rows 8q .. 8q+7: block (lane & 3)
-                                     // for 4 query rows per wave, blocks 0..3 for 8
+  u32x4 vs[NT >= 2 ? 4 : 1];         // V scales, rows 8q .. 8q+7: block (lane & 3)
+                                     // for 4 query rows per wave, blocks 0..3 for 8 or 16
   u32x4 vn;                          // V norms (rot4), rows 8q .. 8q+7
 };
 
@@ -252,9 +252,9 @@ __device__ inline void load_tile(TileRegs<KC, VC, NT>& r, int t, int lane, const
   }
   if constexpr (has_scales(VC)) {
 #pragma unroll
-    for (int b = 0; b < (NT == 2 ? 4 : 1); ++b)
+    for (int b = 0; b < (NT >= 2 ? 4 : 1); ++b)
       r.vs[b] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (NT == 2 ? b : (lane & 3)) * 32 + 8 * qg));
+          reinterpret_cast<const u32x4*>(vsb + row0 * 4 + (NT >= 2 ? b : (lane & 3)) * 32 + 8 * qg));
   }
   if constexpr (has_norms(VC)) r.vn = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vnb + row0 + 8 * qg));
 }
@@ -378,8 +378,9 @@ __device__ inline float wave_max(float v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// Q operands of S^T: in registers for 4 query rows per wave, in LDS (one
-// copy per row group, read once per tile and used for both halves) for 8.
+// Q operands of S^T, in registers: rows (query row, block) with separate hi
+// and lo operands for 4 query rows per wave; rows (query, hi/lo part) for 8;
+// query rows with separate hi and lo operands for 16.
 template <int NT>
 struct QOperands {
   half8 h[NT][4], l[NT][4];
@@ -388,6 +389,30 @@ template <>
 struct QOperands<2> {
   half8 w[4];  // MFMA b: row n16 = 2 q + part of query q, chunk qg of block b
 };
+template <>
+struct QOperands<4> {
+  half8 h[4], l[4];  // MFMA b: row n16 = query n16, chunk qg of block b, fp16 hi and lo parts
+};
+
+// K factors of the lane's tile row 16h + n16 for blocks 0..3: the fp16 block
+// scale (rot4: times the row norm); 1 for f16 planes.
+template <int KC, int VC, int NT>
+__device__ __forceinline__ void k_block_factors(const TileRegs<KC, VC, NT>& cur, float (&kf)[2][4]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
+    if constexpr (KC != F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[h][i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
+      if constexpr (KC == ROT4) {
+        const float nrm = f16_to_float(cur.kn[h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[h][i] *= nrm;
+      }
+    }
+  }
+}
 
 // One 32-row tile for one wave with 4 query rows: S^T = Q K^T, online
 // softmax, O += P V.
@@ -434,20 +459,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
   // ---- S^T: lane (n16, qg) gets the 4 block partials of query row 4*nt + qg
   //      at tile row 16h + n16, for both halves h ----
   float kf[2][4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
-    if constexpr (KC != F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kf[h][i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
-      if constexpr (KC == ROT4) {
-        const float nrm = f16_to_float(cur.kn[h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kf[h][i] *= nrm;
-      }
-    }
-  }
+  k_block_factors(cur, kf);
   float s[NT][2];
   half8 bk[2][4];
 #pragma unroll
@@ -544,33 +556,18 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
   }
 }
 
-// One 32-row tile for one wave with 8 query rows.  Both products use rows
-// r = 2 q + p: query q of the wave's 8, part p of its fp16 hi/lo split
-// (0 = hi, 1 = lo), so no operand row is zero when 8 rows are live.
-//   S^T: MFMA b covers block b; output lane (n16, qg) holds, for cached row
-//        16h + n16, block b's partial dots of queries 2qg and 2qg+1 (hi and
-//        lo rows), which are summed, scaled by the K block scale and summed
-//        over the blocks.
-//   P.V: for block b the A rows carry part p of P(q, row) times the V factor
-//        of (row, block b) over the tile rows 8qg .. 8qg+7, and N-tile c uses
-//        the operand of its block c / 2; the output rows are (query, part)
-//        again, and the two parts are added at the end.
-template <int KC, int VC>
-__device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur, int t, int L, int lmin,
-                                                  const int (&lim)[2], int lane, const QOperands<2>& aq,
-                                                  WaveState<2>& st, float* s_p, const Lut& lut) {
-  const int n16 = lane & 15, qg = lane >> 4;
-  const bool partial = (t + 1) * kTile > lmin;
-  // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
-  //      check, first so that they overlap the S^T products.  For q8_0 and
-  //      q4_0 the factor is the fp16 scale itself: it stays in fp16 (the
-  //      largest magnitude is an integer max over the bit patterns, and the
-  //      products take the fp16 operand directly); rot4 multiplies in the
-  //      row norm in fp32 ----
-  [[maybe_unused]] float vf[4][8];
-  [[maybe_unused]] uint32_t fw[4][4];  // fp16 factor pairs: block b, rows 8qg + 2i, 2i + 1
-  float vexp_new = st.vexp;
-  bool v_rescale = false;
+// V factors of (tile row 8qg + j, block b) for all four blocks, as the 8-
+// and 16-row layouts use them, with the rows past L zeroed, and the wave's V
+// exponent check.  For q8_0 and q4_0 the factor is the fp16 scale itself: it
+// stays in fp16 (fw[b][i]: rows 8qg + 2i and 2i + 1; the largest magnitude is
+// an integer max over the bit patterns, and the products take the fp16
+// operand directly); rot4 multiplies in the row norm in fp32 (vf[b][j]).
+template <int KC, int VC, int NT>
+__device__ __forceinline__ void v_block_factors(const TileRegs<KC, VC, NT>& cur, int t, int L, int qg, bool partial,
+                                                WaveState<NT>& st, float (&vf)[4][8], uint32_t (&fw)[4][4],
+                                                float& vexp_new, bool& v_rescale) {
+  vexp_new = st.vexp;
+  v_rescale = false;
   if constexpr (VC != F16) {
     float vm;  // largest |factor| among this lane's rows
     if constexpr (VC == ROT4) {
@@ -628,22 +625,36 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
     }
   }
 
+}
+
+// One 32-row tile for one wave with 8 query rows.  Both products use rows
+// r = 2 q + p: query q of the wave's 8, part p of its fp16 hi/lo split
+// (0 = hi, 1 = lo), so no operand row is zero when 8 rows are live.
+//   S^T: MFMA b covers block b; output lane (n16, qg) holds, for cached row
+//        16h + n16, block b's partial dots of queries 2qg and 2qg+1 (hi and
+//        lo rows), which are summed, scaled by the K block scale and summed
+//        over the blocks.
+//   P.V: for block b the A rows carry part p of P(q, row) times the V factor
+//        of (row, block b) over the tile rows 8qg .. 8qg+7, and N-tile c uses
+//        the operand of its block c / 2; the output rows are (query, part)
+//        again, and the two parts are added at the end.
+template <int KC, int VC>
+__device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur, int t, int L, int lmin,
+                                                  const int (&lim)[2], int lane, const QOperands<2>& aq,
+                                                  WaveState<2>& st, float* s_p, const Lut& lut) {
+  const int n16 = lane & 15, qg = lane >> 4;
+  const bool partial = (t + 1) * kTile > lmin;
+  // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
+  //      check, first so that they overlap the S^T products ----
+  [[maybe_unused]] float vf[4][8];
+  [[maybe_unused]] uint32_t fw[4][4];
+  float vexp_new;
+  bool v_rescale;
+  v_block_factors(cur, t, L, qg, partial, st, vf, fw, vexp_new, v_rescale);
+
   // ---- S^T: lane (n16, qg) gets queries 2qg + jj at tile row 16h + n16 ----
   float kf[2][4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kf[h][i] = 1.0f;
-    if constexpr (KC != F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kf[h][i] = f16_to_float(cur.ks[h][i >> 1] >> ((i & 1) * 16));
-      if constexpr (KC == ROT4) {
-        const float nrm = f16_to_float(cur.kn[h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kf[h][i] *= nrm;
-      }
-    }
-  }
+  k_block_factors(cur, kf);
   float s[2][2];  // [query 2qg + jj][half]
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -755,6 +766,135 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
       }
     }
     st.oacc[c] = mfma16(VC == F16 ? ap[0] : ap[c >> 1], bv, st.oacc[c]);
+  }
+}
+
+// One 32-row tile for one wave with 16 query rows (9 .. 16 per KV head: the
+// tile is read and unpacked once for all of them).  The MFMA rows are the
+// 16 queries in both products; the fp16 hi and lo parts of Q and of P go
+// to two chained MFMAs.
+//   S^T: for half h and block b, lane (n16, qg) gets block b's partial dots
+//        of queries 4qg .. 4qg+3 at tile row 16h + n16, which are scaled by
+//        the K block scale and summed over the blocks.
+//   P.V: the A operand of block b is P(query n16, tile rows 8qg .. 8qg+7)
+//        times the V factor of (row, block b); N-tile c uses the operands
+//        of its block c / 2, and output lane (n16, qg) holds channel
+//        16c + n16 of queries 4qg .. 4qg+3.
+template <int KC, int VC>
+__device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, int t, int L, int lmin,
+                                                const int (&lim)[4], int lane, const QOperands<4>& aq,
+                                                WaveState<4>& st, float* s_p, const Lut& lut) {
+  const int n16 = lane & 15, qg = lane >> 4;
+  const bool partial = (t + 1) * kTile > lmin;
+  [[maybe_unused]] float vf[4][8];
+  [[maybe_unused]] uint32_t fw[4][4];
+  float vexp_new;
+  bool v_rescale;
+  v_block_factors(cur, t, L, qg, partial, st, vf, fw, vexp_new, v_rescale);
+
+  // ---- S^T ----
+  float kf[2][4];
+  k_block_factors(cur, kf);
+  float s[4][2];  // [query 4qg + i][half]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float4v acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const half8 kb = unpack_k<KC>(cur.kd[h], b, lut);
+      acc[b] = mfma16(aq.h[b], kb, float4v{0.0f, 0.0f, 0.0f, 0.0f});
+      acc[b] = mfma16(aq.l[b], kb, acc[b]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool dead = partial && t * kTile + 16 * h + n16 >= lim[i];
+      float v;
+      if constexpr (KC == F16) v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      else v = (acc[0][i] * kf[h][0] + acc[1][i] * kf[h][1]) + (acc[2][i] * kf[h][2] + acc[3][i] * kf[h][3]);
+      s[i][h] = dead ? -INFINITY : v;
+    }
+  }
+
+  // ---- online softmax (base 2); the 16 lanes of a lane group share the
+  //      state of its four queries.  One decision rescales all four ----
+  float mnew[4];
+  bool grow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mnew[i] = fmaxf(st.m_run[i], row16_max(fmaxf(s[i][0], s[i][1])));
+    grow = grow || mnew[i] > st.m_run[i];
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) || v_rescale) {
+    float alpha[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      alpha[i] = __builtin_amdgcn_exp2f((st.m_run[i] + st.vexp) - (mnew[i] + vexp_new));
+      st.l_run[i] *= alpha[i];
+      st.m_run[i] = mnew[i];
+    }
+    const float4v av = {alpha[0], alpha[1], alpha[2], alpha[3]};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.oacc[c] *= av;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mref = st.m_run[i] + vexp_new;
+    const float p0 = __builtin_amdgcn_exp2f(s[i][0] - mref);
+    const float p1 = __builtin_amdgcn_exp2f(s[i][1] - mref);
+    st.l_run[i] += p0 + p1;
+    s_p[(4 * qg + i) * kTile + n16] = p0;
+    s_p[(4 * qg + i) * kTile + 16 + n16] = p1;
+  }
+  st.vexp = vexp_new;
+  wave_lds_fence();
+  // P of this lane's A row: query n16 over tile rows 8qg .. 8qg+7
+  float pv[8];
+  {
+    const float4v p_lo = *reinterpret_cast<const float4v*>(&s_p[n16 * kTile + 8 * qg]);
+    const float4v p_hi = *reinterpret_cast<const float4v*>(&s_p[n16 * kTile + 8 * qg + 4]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[j] = p_lo[j];
+      pv[4 + j] = p_hi[j];
+    }
+  }
+  wave_lds_fence();
+
+  // ---- O += P V ----
+  half8 ah[4], al[4];
+  if constexpr (VC == F16) {
+    split8(pv, ah[0], al[0]);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float x[8];
+      if constexpr (VC == ROT4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = mul_f16<0>(pv[2 * i], fw[b][i]);
+          x[2 * i + 1] = mul_f16<1>(pv[2 * i + 1], fw[b][i]);
+        }
+      }
+      split8(x, ah[b], al[b]);
+    }
+  }
+  const int row8 = t * kTile + 8 * qg;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    half8 bv = unpack_v<VC>(cur.vd, c, lut);
+    if constexpr (VC == F16) {
+      if (partial) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
+      }
+    }
+    const int b = VC == F16 ? 0 : c >> 1;
+    st.oacc[c] = mfma16(ah[b], bv, st.oacc[c]);
+    st.oacc[c] = mfma16(al[b], bv, st.oacc[c]);
   }
 }
 
@@ -948,6 +1088,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       aq.h[0][m] = m == slot ? h : z;
       aq.l[0][m] = m == slot ? l : z;
     }
+  } else if constexpr (NT == 4) {
+    // row n16 = query row: in MFMA b the lane holds chunk qg of block b,
+    // hi and lo parts in separate operands
+    const int g = RW * group + n16;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, b, j)] * qs;
+      split8(v, aq.h[b], aq.l[b]);
+    }
   } else {
     // row n16 = 2 * (query row) + part: in MFMA b the lane holds part
     // n16 & 1 of chunk qg of block b of its query row
@@ -979,11 +1130,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   st.vlo = INFINITY;  // the first tile sets the exponent
   st.vhi = INFINITY;
 
-  // length of the lane's query row of state nt (4 rows: qg; 8 rows: 2qg + nt);
-  // padding rows past G stop at L like the last live row
+  // the lane's query row of state nt within the wave's RW rows
+  auto state_row = [&](int nt) { return NT == 1 ? qg : NT * qg + nt; };
+  // length of that row; padding rows past G stop at L like the last live row
   int lim[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + (RW * group + (NT == 1 ? qg : 2 * qg + nt)) / a.gqa, L);
+  for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + (RW * group + state_row(nt)) / a.gqa, L);
 
   // slot k is live while its tile exists; slots taken later are larger, so
   // a wave stops at its first dead slot
@@ -995,7 +1147,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   };
   auto proc = [&](const TileRegs<KC, VC, NT>& r, int t) {
     if constexpr (NT == 1) process_tile<KC, VC, NT>(r, t, L, lmin, lim, lane, aq, st, s_p[wave], lutr);
-    else process_tile_wide<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
+    else if constexpr (NT == 2) process_tile_wide<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
+    else process_tile_16<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
   };
   int ka = wig, kb = wig + wpg;
   if constexpr (D == 3) {
@@ -1031,7 +1184,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // ---- per-wave state to LDS: row r of the wave's RW query rows ----
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int r = NT == 1 ? qg : 2 * qg + nt;  // the lane's query row of state nt
+    const int r = state_row(nt);
     const float l = row16_sum(st.l_run[nt]);
     if (n16 == 0) {
       s_m[wave][r] = st.m_run[nt] + st.vexp;  // the reference of l and O
@@ -1039,8 +1192,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      // 4 rows: the output row of (query, block of N-tile c); 8 rows: hi + lo
-      const float o = NT == 1 ? st.oacc[c][c >> 1] : st.oacc[c][2 * nt] + st.oacc[c][2 * nt + 1];
+      // 4 rows: the output row of (query, block of N-tile c); 8 rows: hi + lo;
+      // 16 rows: the query's own row
+      const float o = NT == 1   ? st.oacc[c][c >> 1]
+                      : NT == 2 ? st.oacc[c][2 * nt] + st.oacc[c][2 * nt + 1]
+                                : st.oacc[c][nt];
       s_o[wave][r][16 * c + n16] = o;
     }
   }
@@ -1102,8 +1258,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #define VIT_DECODE_NT(KC, VC)                                                                   \
   if (nt == 1)                                                                                  \
     hipExtLaunchKernelGGL((decode_kernel<KC, VC, 1>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args); \
+  else if (nt == 2)                                                                             \
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args); \
   else                                                                                          \
-    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 2>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args);
+    hipExtLaunchKernelGGL((decode_kernel<KC, VC, 4>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start, ev.stop, 0, args);
 
 #define VIT_DECODE_FOR_K(KC)                                                          \
   hipError_t launch_decode_k##KC(int vc, int nt, dim3 grid, hipStream_t stream,       \

@@ -198,7 +198,8 @@ int vit_attn_decode_mq(const vit_kv_plane* k, const vit_kv_plane* v, const float
   for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
   const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
                   static_cast<unsigned>(k->n_seqs));
-  const int nt = gqa * q_len <= 4 ? 1 : 2;  // query rows per wave: 4 or 8
+  const int rows = gqa * q_len;  // query rows per KV head, all in every wave
+  const int nt = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;  // query rows per wave: 4, 8 or 16
   return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 
