@@ -2,25 +2,27 @@
 //
 // One workgroup of 8 waves per (split, KV head, sequence), the only one on
 // its compute unit.  Split s owns the 32-row tiles s, s + n_splits, ...; the
-// waves of a row group take them one at a time from an LDS counter, each
-// keeping its own online softmax state and prefetching its next tiles into
-// registers while it computes the current one.  The waves are merged through
-// LDS at the end.
+// waves take them one at a time from an LDS counter, each handling all query
+// rows of the KV head, keeping its own online softmax state and prefetching
+// its next tiles into registers while it computes the current one.  The
+// waves are merged through LDS at the end.
 //
 // Both products run on MFMA 16x16x32 f16 with exact operands:
 //   * K and V codes are exact in fp16 (f16 values, int8 / 4-bit integers,
 //     fp16 rot4 levels), and every per-block scale is applied in fp32;
-//   * the query and the probabilities are split into fp16 hi + lo parts
-//     (two MFMAs), so operand rounding stays near 2^-21 relative.
-// S^T = Q K^T: MFMA m's B operand is block m of 16 K rows (lane group q,
-// lanes 16q..16q+15, holds its 8-channel chunk q).  The A operand has one
-// row per (query row, block) pair, four query rows per 16-row tile, and is
-// zero except in MFMA m for the rows of block m.  Each output lane then
-// holds, for one cached row and one query row, the four per-block partial
-// dot products, which it scales by the fp32 block scales and sums in
-// registers.  P is regrouped through a
-// small per-wave LDS buffer into the P.V operand, whose rows are again
-// (query row, block) pairs so the V block scale folds into P per block.
+//   * the query and the probabilities are split into fp16 hi + lo parts,
+//     so operand rounding stays near 2^-21 relative.
+// MFMA m's B operand in S^T = Q K^T is block m of 16 K rows (lane group q,
+// lanes 16q..16q+15, holds its 8-channel chunk q); each output lane gets,
+// for one cached row, per-block partial dot products, which it scales by
+// the fp32 block scales and sums in registers.  P is regrouped through a
+// small per-wave LDS buffer into the P.V operand, where the V block scale
+// folds into P per block.  Three row layouts share this scheme, by the
+// number of query rows per KV head (G, or G * q_len for several new tokens):
+//   <= 4 rows: (query row, block) rows, zero outside their block's MFMA,
+//              hi and lo in separate MFMAs;
+//   <= 8 rows: (query, hi/lo part) rows, one MFMA per block;
+//   <= 16 rows: query rows, hi and lo in two chained MFMAs.
 #pragma once
 
 #include "vit_device.h"
@@ -900,12 +902,10 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
 
 // Decode kernel: one workgroup of kDecodeWaves waves per (split, KV head,
 // sequence), sized to be the only workgroup on its compute unit (two waves
-// per SIMD).  A wave handles RW = 4*NT query rows of its KV head; with more
-// than RW rows (G > RW) the rows form row groups, and row group k is handled
-// by the waves w with w / (kDecodeWaves / n_groups) == k.  The waves of a row
-// group take the split's tiles from a shared LDS counter as they go, so a
-// wave that issues more slowly (the SIMD arbiter favours older waves) simply
-// takes fewer tiles.
+// per SIMD).  Every wave handles all query rows of its KV head (RW = 4*NT
+// >= G rows, padded with zero rows).  The waves take the split's tiles from
+// a shared LDS counter as they go, so a wave that issues more slowly (the
+// SIMD arbiter favours older waves) simply takes fewer tiles.
 template <int KC, int VC, int NT>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int RW = 4 * NT;
@@ -925,10 +925,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const int lmin = L - QL + 1;    // rows attended by the first new token
   const int G = a.gqa * QL;       // query rows
   constexpr int kThreads = 64 * kDecodeWaves;
-  const int n_groups = (G + RW - 1) / RW;   // 1, 2 or 4
-  const int wpg = kDecodeWaves / n_groups;  // waves per row group
-  const int group = wave / wpg;
-  const int GP = RW * n_groups;             // padded query rows
+  static_assert(RW <= GMAX, "query rows per wave");
   const int n_tiles = (L + kTile - 1) / kTile;
 
   __shared__ float sq[GMAX][kD];
@@ -938,7 +935,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   __shared__ float s_o[kDecodeWaves][RW][kD];
   __shared__ float s_m[kDecodeWaves][RW];
   __shared__ float s_l[kDecodeWaves][RW];
-  __shared__ int s_next[4];  // per row group: next tile slot to hand out
+  __shared__ int s_next;  // next tile slot to hand out
   __shared__ uint8_t s_row[5][256];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
@@ -1006,24 +1003,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
   // k = 0, 1, ... (so at any moment the splits of one stream read one
-  // contiguous window).  Within a row group the slots k go to the waves in
-  // order: each wave starts with D = prefetch_depth + 1 slots (wig, wig + wpg,
-  // ...) and then takes the next free slot from s_next whenever it refills a
-  // buffer.  Loads of slots past the last tile are clamped to it; a split
+  // contiguous window).  The slots k go to the waves in order: wave w starts
+  // with D = prefetch_depth + 1 slots (w, w + kDecodeWaves, ...) and then
+  // takes the next free slot from s_next whenever it refills a buffer.  Loads of slots past the last tile are clamped to it; a split
   // without tiles re-reads tile 0 (always there).
   constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
-  const int wig = wave - group * wpg;  // wave index within its row group
   const int n_mine = split < n_tiles ? (n_tiles - 1 - split) / a.n_splits + 1 : 0;  // this split's tiles
   const int t_last = split < n_tiles ? split + a.n_splits * (n_mine - 1) : 0;
   auto tile_of = [&](int k) { return split + a.n_splits * k; };
   auto load_slot = [&](TileRegs<KC, VC, NT>& r, int k) {
     load_tile<KC, VC>(r, min(tile_of(k), t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
   };
-  if (tid < n_groups) s_next[tid] = D * wpg;
+  if (tid == 0) s_next = D * kDecodeWaves;
   TileRegs<KC, VC, NT> ta, tb;
   [[maybe_unused]] TileRegs<KC, VC, NT> tc;
-  load_slot(ta, wig);
-  load_slot(tb, wig + wpg);
+  load_slot(ta, wave);
+  load_slot(tb, wave + kDecodeWaves);
 
   if constexpr (kRot4) {
     // word 4 (tid + 512 i) + j (j < 4) is entry e = tid / 16 + 32 i of lane
@@ -1059,7 +1054,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // rotate the query rows like the keys (WHT); the keys reconstruct as
     // N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
     for (int h = 1; h < kD; h <<= 1) {
-      for (int i = tid; i < GP * 64; i += kThreads) {
+      for (int i = tid; i < RW * 64; i += kThreads) {
         const int g = i >> 6, k = i & 63;
         const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
         const float x = sq[g][lo], y = sq[g][lo + h];
@@ -1076,7 +1071,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     // row n16 = 4 * (query row) + block slot: the operand of the lane's row
     // is its slot's chunk qg, in MFMA m = slot, zero in the others
     const int slot = n16 & 3;
-    const int g = RW * group + (n16 >> 2);
+    const int g = n16 >> 2;
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, slot, j)] * qs;
@@ -1091,7 +1086,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   } else if constexpr (NT == 4) {
     // row n16 = query row: in MFMA b the lane holds chunk qg of block b,
     // hi and lo parts in separate operands
-    const int g = RW * group + n16;
+    const int g = n16;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       float v[8];
@@ -1102,7 +1097,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   } else {
     // row n16 = 2 * (query row) + part: in MFMA b the lane holds part
     // n16 & 1 of chunk qg of block b of its query row
-    const int g = RW * group + (n16 >> 1);
+    const int g = n16 >> 1;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       float v[8];
@@ -1135,14 +1130,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // length of that row; padding rows past G stop at L like the last live row
   int lim[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + (RW * group + state_row(nt)) / a.gqa, L);
+  for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + state_row(nt) / a.gqa, L);
 
   // slot k is live while its tile exists; slots taken later are larger, so
   // a wave stops at its first dead slot
   auto live_slot = [&](int k) { return k < n_mine; };
   auto take = [&]() {  // one LDS atomic per wave, broadcast from lane 0
     int k = 0;
-    if (lane == 0) k = atomicAdd(&s_next[group], 1);
+    if (lane == 0) k = atomicAdd(&s_next, 1);
     return __builtin_amdgcn_readfirstlane(k);
   };
   auto proc = [&](const TileRegs<KC, VC, NT>& r, int t) {
@@ -1150,10 +1145,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     else if constexpr (NT == 2) process_tile_wide<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
     else process_tile_16<KC, VC>(r, t, L, lmin, lim, lane, aq, st, &s_p[wave][0][0][0], lutr);
   };
-  int ka = wig, kb = wig + wpg;
+  int ka = wave, kb = wave + kDecodeWaves;
   if constexpr (D == 3) {
     // three register buffers in rotation: two tiles in flight while one is used
-    int kc = wig + 2 * wpg;
+    int kc = wave + 2 * kDecodeWaves;
     load_slot(tc, kc);
     while (live_slot(ka)) {
       proc(ta, tile_of(ka));
@@ -1202,19 +1197,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   }
   __syncthreads();
 
-  // ---- merge the waves of each row group; write the partial or final row ----
+  // ---- merge the waves; write the partial or final row ----
   const bool final_out = a.n_splits == 1;
-  for (int i = tid; i < GP * kD; i += kThreads) {
+  for (int i = tid; i < RW * kD; i += kThreads) {
     const int g = i >> 7, c = i & 127;
-    const int grp = g / RW, r = g % RW;
     float M = -INFINITY;
-    for (int w = grp * wpg; w < (grp + 1) * wpg; ++w) M = fmaxf(M, s_m[w][r]);
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][g]);
     float O = 0.0f, Ls = 0.0f;
-    for (int w = grp * wpg; w < (grp + 1) * wpg; ++w) {
-      const float lw = s_l[w][r];
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float lw = s_l[w][g];
       if (lw > 0.0f) {
-        const float f = __builtin_amdgcn_exp2f(s_m[w][r] - M);
-        O += s_o[w][r][c] * f;
+        const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
+        O += s_o[w][g][c] * f;
         Ls += lw * f;
       }
     }
@@ -1233,7 +1227,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     __syncthreads();
     if constexpr (VC == ROT4) {
       for (int h = 1; h < kD; h <<= 1) {
-        for (int i = tid; i < GP * 64; i += kThreads) {
+        for (int i = tid; i < RW * 64; i += kThreads) {
           const int g = i >> 6, k = i & 63;
           const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
           const float x = sq[g][lo], y = sq[g][lo + h];
