@@ -50,6 +50,21 @@ def append_rows(plane, rows_host, pos0, stream=None):
     return src
 
 
+def fill_plane_synth(plane, cfg, layer, side, start, count, units, torch, gen):
+    """Rows start..start+count-1 of every (seq, head) of a workload plane:
+    the seeded synth rows for the sampled units, seeded device normals
+    elsewhere; then one vit_kv_append_quant call."""
+    import synth
+    from quantized_kv_cache_append_amd import vit_kv_append_quant
+
+    S, H = plane.n_seqs, plane.n_kv_heads
+    src = torch.randn((S, count, H, 128), generator=gen, device="cuda", dtype=torch.float32)
+    for (s, h) in units:
+        src[s, :, h] = torch.from_numpy(synth.kv_rows(cfg, side, layer, s, h, start, count)).cuda()
+    vit_kv_append_quant(plane, src, [start] * S)
+    return src
+
+
 def oracle_quant(codec, rows, signs):
     """Oracle codes of rows [N, 128] as (codes, scales, norms) arrays."""
     q = codecs.quantize(codec, rows, signs)
@@ -85,5 +100,5 @@ def check_close(got, ref, what, tol=TOL):
     return err / rms
 
 
-__all__ = ["oracle", "torch_cuda", "say", "make_plane", "append_rows", "compare_plane_rows",
+__all__ = ["oracle", "torch_cuda", "say", "make_plane", "append_rows", "fill_plane_synth", "compare_plane_rows",
            "ref_unit", "check_close", "TOL"]

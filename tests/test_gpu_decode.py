@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import append_rows, check_close, make_plane, ref_unit, say, torch_cuda
+from gpu_helpers import append_rows, check_close, fill_plane_synth, make_plane, ref_unit, say, torch_cuda
 
 CODECS = ["f16", "q8_0", "q4_0", "rot4"]
 D = 128
@@ -187,21 +187,6 @@ def test_fused_append_matches_separate_append(kc, vc):
 
 
 # ---------------------------------------------------------------- workloads
-def _synth_rows(cfg, side, layer, seq, head, start, count):
-    return synth.kv_rows(cfg, side, layer, seq, head, start, count)
-
-
-def _fill_plane(plane, cfg, layer, side, start, count, units, torch, gen):
-    """Rows start..start+count-1 of every (seq, head): synth rows for the
-    sampled units, seeded device normals elsewhere; then one append call."""
-    S, H = plane.n_seqs, plane.n_kv_heads
-    src = torch.randn((S, count, H, D), generator=gen, device="cuda", dtype=torch.float32)
-    for (s, h) in units:
-        src[s, :, h] = torch.from_numpy(_synth_rows(cfg, side, layer, s, h, start, count)).cuda()
-    import quantized_kv_cache_append_amd as vit
-
-    vit.vit_kv_append_quant(plane, src, [start] * S)
-    return src
 
 
 def _run_workload(cfg, units, layers=(0,)):
@@ -228,31 +213,31 @@ def _run_workload(cfg, units, layers=(0,)):
         qd = torch.from_numpy(q).cuda()
         ns = vit.vit_attn_default_splits(S, H, Hq, L)
         if c["fused_append"]:
-            _fill_plane(K, cfg, layer, "k", 0, L - 1, units, torch, gen)
-            _fill_plane(V, cfg, layer, "v", 0, L - 1, units, torch, gen)
+            fill_plane_synth(K, cfg, layer, "k", 0, L - 1, units, torch, gen)
+            fill_plane_synth(V, cfg, layer, "v", 0, L - 1, units, torch, gen)
             knew = torch.randn((S, H, D), generator=gen, device="cuda")
             vnew = torch.randn((S, H, D), generator=gen, device="cuda")
             for (s, h) in units:
-                knew[s, h] = torch.from_numpy(_synth_rows(cfg, "k", layer, s, h, L - 1, 1)[0]).cuda()
-                vnew[s, h] = torch.from_numpy(_synth_rows(cfg, "v", layer, s, h, L - 1, 1)[0]).cuda()
+                knew[s, h] = torch.from_numpy(synth.kv_rows(cfg, "k", layer, s, h, L - 1, 1)[0]).cuda()
+                vnew[s, h] = torch.from_numpy(synth.kv_rows(cfg, "v", layer, s, h, L - 1, 1)[0]).cuda()
             out = vit.decode(K, V, qd, Hq, lens, k_new=knew, v_new=vnew, n_splits=ns)
         elif "prefill" in c:
             pre, ub = c["prefill"], c["ubatch"]
-            _fill_plane(K, cfg, layer, "k", 0, pre, units, torch, gen)
-            _fill_plane(V, cfg, layer, "v", 0, pre, units, torch, gen)
-            _fill_plane(K, cfg, layer, "k", pre, ub, units, torch, gen)
-            _fill_plane(V, cfg, layer, "v", pre, ub, units, torch, gen)
+            fill_plane_synth(K, cfg, layer, "k", 0, pre, units, torch, gen)
+            fill_plane_synth(V, cfg, layer, "v", 0, pre, units, torch, gen)
+            fill_plane_synth(K, cfg, layer, "k", pre, ub, units, torch, gen)
+            fill_plane_synth(V, cfg, layer, "v", pre, ub, units, torch, gen)
             out = vit.decode(K, V, qd, Hq, lens, n_splits=ns)
         else:
-            _fill_plane(K, cfg, layer, "k", 0, L, units, torch, gen)
-            _fill_plane(V, cfg, layer, "v", 0, L, units, torch, gen)
+            fill_plane_synth(K, cfg, layer, "k", 0, L, units, torch, gen)
+            fill_plane_synth(V, cfg, layer, "v", 0, L, units, torch, gen)
             out = vit.decode(K, V, qd, Hq, lens, n_splits=ns)
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         gots, refs = [], []
         for (s, h) in units:
-            kr = _synth_rows(cfg, "k", layer, s, h, 0, L)
-            vr = _synth_rows(cfg, "v", layer, s, h, 0, L)
+            kr = synth.kv_rows(cfg, "k", layer, s, h, 0, L)
+            vr = synth.kv_rows(cfg, "v", layer, s, h, 0, L)
             r = ref_unit(q[s, h * G:(h + 1) * G], kr, vr, kc, vc, scale, ks, vs)
             gots.append(got[s, h * G:(h + 1) * G])
             refs.append(r)

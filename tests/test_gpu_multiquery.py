@@ -5,7 +5,9 @@ decode_multi_reference.
 Bar: max |o_gpu - o_ref| <= 2e-3 x RMS(o_ref) per call.  Covers both wave
 layouts (4 and 8 query rows), two row groups (G * q_len = 16), fused appends
 whose new rows straddle tiles owned by different splits (codes checked
-bit-exact), and q_len = 1 against vit_attn_decode.
+bit-exact), q_len = 1 against vit_attn_decode, and the verify steps bench.py
+times at full size (sampled (sequence, KV head) units, the library's default
+split count).
 """
 
 import math
@@ -13,7 +15,8 @@ import math
 import numpy as np
 import pytest
 
-from gpu_helpers import append_rows, check_close, compare_plane_rows, make_plane, say, torch_cuda
+import synth
+from gpu_helpers import append_rows, check_close, compare_plane_rows, fill_plane_synth, make_plane, say, torch_cuda
 from oracle import attention
 
 D = 128
@@ -122,3 +125,61 @@ def test_single_token_mq_equals_decode():
     a, b = a.cpu().numpy(), b.cpu().numpy()[:, 0]
     rms = float(np.sqrt(np.mean(a.astype(np.float64) ** 2)))
     assert np.max(np.abs(a - b)) <= 1e-5 * rms
+
+
+def _run_workload_verify(cfg, q_len, units):
+    """A workload's cache at full size, q_len new tokens per sequence appended
+    by the decode call, as bench.py --q-len runs it; the sampled units are
+    checked against the oracle over the same synth rows."""
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    c = synth.CONFIGS[cfg]
+    S, Hq, H, cap, L = c["seqs"], c["hq"], c["hkv"], c["capacity"], c["ctx"]
+    G = Hq // H
+    kc, vc = synth.codec_map(cfg)[0]
+    ks = synth.sign_mask(cfg, 0, "k") if kc == "rot4" else None
+    vs = synth.sign_mask(cfg, 0, "v") if vc == "rot4" else None
+    say(f"[verify {c['name']}] K={kc} V={vc} q_len={q_len} units={units}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + cfg)
+    K = make_plane(kc, "k", S, H, cap, ks)
+    V = make_plane(vc, "v", S, H, cap, vs)
+    fill_plane_synth(K, cfg, 0, "k", 0, L - q_len, units, torch, gen)
+    fill_plane_synth(V, cfg, 0, "v", 0, L - q_len, units, torch, gen)
+    k_new = torch.randn((S, q_len, H, D), generator=gen, device="cuda")
+    v_new = torch.randn((S, q_len, H, D), generator=gen, device="cuda")
+    for (s, h) in units:
+        k_new[s, :, h] = torch.from_numpy(synth.kv_rows(cfg, "k", 0, s, h, L - q_len, q_len)).cuda()
+        v_new[s, :, h] = torch.from_numpy(synth.kv_rows(cfg, "v", 0, s, h, L - q_len, q_len)).cuda()
+    q = np.random.default_rng(4242 + cfg).standard_normal((S, q_len, Hq, D)).astype(np.float32)
+    ns = vit.vit_attn_default_splits(S, H, Hq, L)
+    out = vit.decode(K, V, torch.from_numpy(q).cuda(), Hq, [L] * S, k_new=k_new, v_new=v_new, n_splits=ns,
+                     q_len=q_len)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gots, refs = [], []
+    for (s, h) in units:
+        kr = synth.kv_rows(cfg, "k", 0, s, h, 0, L)
+        vr = synth.kv_rows(cfg, "v", 0, s, h, 0, L)
+        refs.append(attention.decode_multi_reference(q[s, :, h * G:(h + 1) * G], kr, vr, kc, vc,
+                                                     1.0 / math.sqrt(D), ks, vs))
+        gots.append(got[s, :, h * G:(h + 1) * G])
+    check_close(np.stack(gots), np.stack(refs), f"{c['name']} verify q_len={q_len} splits={ns}")
+    del K, V
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+def test_workload_batched_verify4():
+    _run_workload_verify(2, 4, [(0, 0), (5, 3)])
+
+
+@pytest.mark.gpu
+def test_workload_lowbit_verify3():
+    _run_workload_verify(3, 3, [(2, 6)])
+
+
+@pytest.mark.gpu
+def test_workload_rotated_verify2():
+    _run_workload_verify(4, 2, [(0, 1)])
