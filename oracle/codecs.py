@@ -67,7 +67,7 @@ def dequant_f16(q):
 
 # ---------------------------------------------------------------------- q8_0
 def quantize_q8_0(x):
-    """q8_0, per 32-value block (BASELINE scale rule amax/127, int8 codes).
+    """q8_0, per 32-value block (scale amax/127, int8 codes).
 
     amax = max_j |x_j|; d = amax / 127 (fp32 division); id = 1/d (0 if d = 0);
     c_j = clamp(RHAZ(x_j * id), -127, 127); stored scale D = fp16(d).
