@@ -162,6 +162,47 @@ int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_
 int vit_kv_append_quant(const vit_kv_plane *dst, const float *src, const int64_t *pos0,
                         int32_t n_tokens, void *stream);
 
+/* One degrade step of a variable bit-rate cache: re-encode the rows one
+ * (layer, side) tensor holds into a plane of a codec with fewer bits per
+ * value (buun-llama-cpp page, "VBR -- Variable Bit-Rate KV Cache": the cache
+ * starts at f16 and moves one (layer, side) tensor at a time down a ladder;
+ * the classic ladder is f16 -> q8_0 -> q4_0).  Each stored row of `src` is
+ * decoded to its values, which are exact in fp32 for these sources (an fp16
+ * value, or an int8 / 4-bit code times its fp16 scale), and encoded into the
+ * same row of `dst` exactly as vit_kv_append_quant would encode those values
+ * (so codes, scales and norms are bit-exact with the codec definitions).
+ *  src, dst  planes with equal side, n_seqs, n_kv_heads and capacity, whose
+ *            arrays do not overlap (VIT_E_ARG).  The codec pair is one of
+ *            f16 -> q8_0, q4_0 or rot4 and q8_0 -> q4_0 or rot4 (rot4 being
+ *            the rotated 4-bit rung); any other pair is VIT_E_UNSUPPORTED.
+ *  n_rows    [host] int64 [n_seqs]: rows 0 .. n_rows[s]-1 of every KV head of
+ *            sequence s are re-encoded, 0 <= n_rows[s] <= capacity
+ *            (VIT_E_CAPACITY otherwise).  Rows of dst past them are left
+ *            untouched; src is only read.
+ * The caller then uses dst in place of src and may free src: the peak extra
+ * memory of a step is one destination plane. */
+int vit_kv_transcode(const vit_kv_plane *src, const vit_kv_plane *dst, const int64_t *n_rows,
+                     void *stream);
+
+/* Host only: the next step of the classic ladder f16 -> q8_0 -> q4_0 (same
+ * page and section: the order is strictly banded, i.e. every movable tensor
+ * reaches q8_0 before any goes on to q4_0; a side pinned to a fixed type is
+ * never degraded; degrades stop at the last step whose aggregate bits/value
+ * is still at or above the floor).
+ *  codecs       [host] int32 [n_tensors]: each tensor's codec, f16, q8_0 or
+ *               q4_0 (VIT_E_ARG otherwise); tensors are equally sized.
+ *  price_order  [host] int32 [n_tensors]: tensor indices, cheapest to degrade
+ *               first (a permutation of 0 .. n_tensors-1, else VIT_E_ARG).
+ *  movable      [host] uint8 [n_tensors] or NULL (all movable): 0 = pinned.
+ *  floor_bpv    minimum aggregate bits/value after the step (mean of 16, 8.5
+ *               and 4.5 over the tensors); <= 0 means no floor.
+ * On VIT_OK, *tensor / *new_codec name the step: among the movable tensors on
+ * the least degraded rung that can still move, the first in price order moves
+ * one rung down; *tensor = -1 when no step is left. */
+int vit_vbr_classic_next_step(int32_t n_tensors, const int32_t *codecs, const int32_t *price_order,
+                              const uint8_t *movable, double floor_bpv, int32_t *tensor,
+                              int32_t *new_codec);
+
 /* Workspace bytes vit_attn_decode needs for n_splits > 1: fp32 partial
  * outputs [S][Hq][n_splits][128] followed by (max, sum) pairs
  * [S][Hq][n_splits][2].  Returns 0 for invalid sizes. */

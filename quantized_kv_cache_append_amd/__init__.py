@@ -5,9 +5,10 @@ include/vit.h).  This module only marshals torch tensors into those calls:
 PyTorch provides device memory and the stream, nothing else.  The Python
 names mirror the C entry points:
 
-    vit_kv_plane_sizes, vit_kv_append_quant, vit_attn_workspace_bytes,
-    vit_attn_default_splits, vit_attn_decode, vit_attn_splitk_reduce,
-    vit_arm_kernel_events (a measurement aid)
+    vit_kv_plane_sizes, vit_kv_append_quant, vit_kv_transcode,
+    vit_vbr_classic_next_step, vit_attn_workspace_bytes,
+    vit_attn_default_splits, vit_attn_decode, vit_attn_decode_mq,
+    vit_attn_splitk_reduce, vit_arm_kernel_events (a measurement aid)
 
 ``KVPlane`` allocates the three arrays of one (layer, side) cache tensor.
 """
@@ -21,7 +22,8 @@ from ._lib import CODEC_IDS, SIDE_IDS, VitError, VitKvPlane
 
 __all__ = [
     "KVPlane", "VitError", "layout",
-    "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_attn_workspace_bytes",
+    "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_kv_transcode", "vit_vbr_classic_next_step",
+    "vit_attn_workspace_bytes",
     "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_splitk_reduce",
     "vit_arm_kernel_events",
 ]
@@ -133,6 +135,33 @@ def vit_kv_append_quant(plane, src, pos0, n_tokens=None, stream=None):
     p = plane.struct()
     st = lib.vit_kv_append_quant(ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
     return _lib.check("vit_kv_append_quant", st)
+
+
+def vit_kv_transcode(src, dst, n_rows, stream=None):
+    """Re-encode rows 0 .. n_rows[s]-1 of every KV head of plane ``src`` into
+    plane ``dst`` (a VBR degrade step: f16 -> q8_0 / q4_0 / rot4,
+    q8_0 -> q4_0 / rot4)."""
+    lib = _lib.load()
+    nr = (ctypes.c_int64 * len(n_rows))(*[int(x) for x in n_rows])
+    sp, dp = src.struct(), dst.struct()
+    st = lib.vit_kv_transcode(ctypes.byref(sp), ctypes.byref(dp), nr, _stream_handle(stream))
+    return _lib.check("vit_kv_transcode", st)
+
+
+def vit_vbr_classic_next_step(codecs, price_order, movable=None, floor_bpv=None):
+    """The classic ladder's next degrade step for tensors with these codec
+    names, as (tensor index, new codec name), or None when no step is left."""
+    lib = _lib.load()
+    n = len(codecs)
+    ids = {v: k for k, v in _lib.CODEC_IDS.items()}
+    c = (ctypes.c_int32 * n)(*[_lib.CODEC_IDS[x] for x in codecs])
+    o = (ctypes.c_int32 * n)(*[int(x) for x in price_order])
+    m = None if movable is None else (ctypes.c_uint8 * n)(*[1 if x else 0 for x in movable])
+    t, nc = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.vit_vbr_classic_next_step(n, c, o, m, 0.0 if floor_bpv is None else float(floor_bpv),
+                                       ctypes.byref(t), ctypes.byref(nc))
+    _lib.check("vit_vbr_classic_next_step", st)
+    return None if t.value < 0 else (t.value, ids[nc.value])
 
 
 def vit_attn_workspace_bytes(n_seqs, n_q_heads, head_dim, n_splits):

@@ -24,6 +24,8 @@ SIDE_IDS = {"k": 0, "v": 1}
 EXPORTS = (
     "vit_kv_plane_sizes",
     "vit_kv_append_quant",
+    "vit_kv_transcode",
+    "vit_vbr_classic_next_step",
     "vit_attn_workspace_bytes",
     "vit_attn_default_splits",
     "vit_attn_decode",
@@ -76,6 +78,11 @@ def load():
     lib.vit_kv_plane_sizes.restype = ctypes.c_int
     lib.vit_kv_append_quant.argtypes = [plane_p, vp, P(i64), i32, vp]
     lib.vit_kv_append_quant.restype = ctypes.c_int
+    lib.vit_kv_transcode.argtypes = [plane_p, plane_p, P(i64), vp]
+    lib.vit_kv_transcode.restype = ctypes.c_int
+    lib.vit_vbr_classic_next_step.argtypes = [i32, P(i32), P(i32), P(ctypes.c_uint8), ctypes.c_double,
+                                              P(i32), P(i32)]
+    lib.vit_vbr_classic_next_step.restype = ctypes.c_int
     lib.vit_attn_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.vit_attn_workspace_bytes.restype = sz
     lib.vit_attn_default_splits.argtypes = [i32, i32, i32, i64]

@@ -1,21 +1,92 @@
-// Append: quantize new K or V rows and store them in a cache plane.
+// Append: quantize new K or V rows and store them in a cache plane; and the
+// VBR degrade step, which re-encodes the rows a plane holds into a plane of
+// a codec with fewer bits per value.
 //
 // Compiled with -ffp-contract=off: the encoders' fp32 operation order is part
 // of the codec formats (codes and fp16 scales are bit-exact), so no multiply
 // may fuse with an add.
 //
-// Work split: one wave per (8-row group, KV head, sequence), four groups per
-// workgroup.  The wave loads all of its rows first (so their loads are in
-// flight together), encodes them together (each encoder step is issued for
-// all rows before the next; lane l holds channels l and l + 64 of a row), and
-// stores them.  K rows go to their tile units one
-// by one.  On the V side a channel's 8 rows of the group form one column
-// unit, so a lane assembles the unit of its two channels in registers and
-// writes it whole; a group cut by the range edge keeps the rows outside the
-// range (per-row stores, read-modify-write of the shared 4-bit words).
+// Append's work split: one wave per (8-row group, KV head, sequence), four
+// groups per workgroup.  The wave loads all of its rows first (so their
+// loads are in flight together), encodes them together (each encoder step is
+// issued for all rows before the next; lane l holds channels l and l + 64 of
+// a row), and stores them (store_group).
 #include "decode_impl.h"
 
 namespace vit {
+
+// Store the encoded rows g0 .. g0+7 (one 8-row group, g0 % 8 == 0) of one
+// (sequence, KV head) stream; only rows with live[r] are written.  K rows go
+// to their tile units one by one.  On the V side a channel's 8 rows form one
+// column unit: a whole group is assembled in registers and written whole; a
+// group cut by the range edge keeps the rows outside it (per-row stores,
+// read-modify-write of the shared 4-bit words).
+template <int CODEC, int SIDE>
+__device__ inline void store_group(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t g0,
+                                   const RowCodes (&rc)[8], const bool (&live)[8], int lane, uint8_t (*rowbuf)[256]) {
+  bool all = true;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) all = all && live[r];
+  if (SIDE == 0 || !all) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (live[r]) store_row<CODEC, SIDE>(codes, scales, norms, g0 + r, rc[r], lane, rowbuf[r]);
+    return;
+  }
+  // the whole group is in range: write column units, scales and norms whole
+  const int64_t tile = g0 >> 5;
+  const int pbase = static_cast<int>(g0 & 31);  // 0, 8, 16 or 24
+  uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int ch = lane + 64 * half;
+    uint32_t c[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) c[r] = half ? rc[r].c1 : rc[r].c0;
+    int sh;
+    const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
+    if constexpr (CODEC == F16) {
+      const u32x4 u = {c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+      *reinterpret_cast<u32x4*>(tbase + off0) = u;
+    } else if constexpr (CODEC == Q8_0) {
+      // row r goes to byte P8[r] = {0,2,1,3,4,6,5,7}[r] of the 8-byte unit
+      const uint32_t lo = (c[0] & 0xFFu) | ((c[2] & 0xFFu) << 8) | ((c[1] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
+      const uint32_t hi = (c[4] & 0xFFu) | ((c[6] & 0xFFu) << 8) | ((c[5] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
+      *reinterpret_cast<u32x2*>(tbase + off0) = u32x2{lo, hi};
+    } else {
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
+        w |= (c[r] & 0xFu) << (((off & 3) << 3) + sh);
+      }
+      *reinterpret_cast<uint32_t*>(tbase + (off0 & ~3)) = w;
+    }
+  }
+  if constexpr (has_scales(CODEC)) {
+    // lane 0 holds blocks 0 and 2, lane 32 blocks 1 and 3 (uniform per half-wave)
+    if ((lane & 31) == 0) {
+      const int b0 = lane >> 5;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t sv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sv[r] = half ? rc[r].s1 : rc[r].s0;
+        const u32x4 u = {sv[0] | (sv[1] << 16), sv[2] | (sv[3] << 16), sv[4] | (sv[5] << 16), sv[6] | (sv[7] << 16)};
+        *reinterpret_cast<u32x4*>(scales + v_scale_index(tile, b0 + 2 * half, pbase)) = u;
+      }
+    }
+  }
+  if constexpr (has_norms(CODEC)) {
+    if (lane == 0) {
+      uint32_t nv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) nv[r] = rc[r].norm;
+      const u32x4 u = {nv[0] | (nv[1] << 16), nv[2] | (nv[3] << 16), nv[4] | (nv[5] << 16), nv[6] | (nv[7] << 16)};
+      *reinterpret_cast<u32x4*>(norms + g0) = u;
+    }
+  }
+}
 
 template <int CODEC, int SIDE>
 __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a) {
@@ -40,13 +111,11 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a)
   __shared__ uint8_t rowbuf[kAppendWaves][8][256];
 
   bool live[8];
-  bool all = true;
   float x0[8], x1[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int64_t p = g_first_row + r;
     live[r] = p >= p_begin && p < p_end;
-    all = all && live[r];
     // rows outside the range read a row inside it (clamped) and are not stored
     const int64_t pc = p < p_begin ? p_begin : (p >= p_end ? p_end - 1 : p);
     const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + (pc - p_begin)) * a.n_kv_heads + head) * kD;
@@ -55,73 +124,89 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a)
   }
   RowCodes rc[8];
   encode_rows<CODEC, 8>(x0, x1, lane, signs, rc);
+  store_group<CODEC, SIDE>(codes, scales, norms, g_first_row, rc, live, lane, rowbuf[wave]);
+}
 
-  if constexpr (SIDE == 0) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (live[r]) store_row<CODEC, 0>(codes, scales, norms, g_first_row + r, rc[r], lane, rowbuf[wave][r]);
-    return;
-  } else {
-    if (!all) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (live[r]) store_row<CODEC, 1>(codes, scales, norms, g_first_row + r, rc[r], lane, rowbuf[wave][r]);
-      return;
+// Re-encode (a VBR degrade step): one workgroup per 32-row tile of one
+// (sequence, KV head) stream.  The source tile (codes and scales) is staged
+// in LDS with 16-byte loads; wave w then decodes rows 8w .. 8w+7 (lane l:
+// channels l and l + 64) to their values, which are exact in fp32 (an fp16
+// value, or an integer code times an fp16 scale), encodes them as append
+// does, and stores the group.  Rows at or past n_rows are neither decoded
+// nor written.
+template <int SRC, int DST, int SIDE>
+__global__ __launch_bounds__(64 * kAppendWaves) void transcode_kernel(TranscodeArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int64_t n = a.n_rows[seq];
+  const int64_t row0 = tile * kTile;
+  if (row0 >= n) return;  // uniform per workgroup
+
+  const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
+  __shared__ u32x4 stile[tile_code_bytes(SRC) / 16];
+  __shared__ uint16_t sscale[128];
+  __shared__ uint8_t rowbuf[kAppendWaves][8][256];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.src_codes + ph * a.capacity * row_code_bytes(SRC) +
+                                                      tile * tile_code_bytes(SRC));
+    for (int i = tid; i < tile_code_bytes(SRC) / 16; i += 64 * kAppendWaves) stile[i] = __builtin_nontemporal_load(src + i);
+    if constexpr (has_scales(SRC)) {
+      // the tile's 128 scales are contiguous on both sides: K [row][block],
+      // V [block][row]
+      const u32x4* ssrc = reinterpret_cast<const u32x4*>(a.src_scales + ph * a.capacity * 4 + tile * 128);
+      if (tid < 16) reinterpret_cast<u32x4*>(sscale)[tid] = __builtin_nontemporal_load(ssrc + tid);
     }
-    // the whole group is in range: write column units, scales and norms whole
-    const int64_t tile = g_first_row >> 5;
-    const int pbase = static_cast<int>(g_first_row & 31);  // 0, 8, 16 or 24
-    uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+  }
+  __syncthreads();
+  const int64_t g0 = row0 + 8 * wave;
+  if (g0 >= n) return;  // no live row in this wave's group (uniform per wave)
+
+  const uint8_t* t8 = reinterpret_cast<const uint8_t*>(stile);
+  bool live[8];
+  float x0[8], x1[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int p = 8 * wave + r;  // row within the tile
+    live[r] = row0 + p < n;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int ch = lane + 64 * half;
-      uint32_t c[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) c[r] = half ? rc[r].c1 : rc[r].c0;
-      int sh;
-      const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
-      if constexpr (CODEC == F16) {
-        const u32x4 u = {c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
-        *reinterpret_cast<u32x4*>(tbase + off0) = u;
-      } else if constexpr (CODEC == Q8_0) {
-        // row r goes to byte P8[r] = {0,2,1,3,4,6,5,7}[r] of the 8-byte unit
-        const uint32_t lo = (c[0] & 0xFFu) | ((c[2] & 0xFFu) << 8) | ((c[1] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
-        const uint32_t hi = (c[4] & 0xFFu) | ((c[6] & 0xFFu) << 8) | ((c[5] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
-        *reinterpret_cast<u32x2*>(tbase + off0) = u32x2{lo, hi};
+      float v;
+      if constexpr (SRC == F16) {
+        int sh;
+        const int off = SIDE == 0 ? k_canon_offset(F16, p, 2 * ch) : v_code_offset(F16, p, ch, &sh);
+        v = f16_to_float(*reinterpret_cast<const uint16_t*>(t8 + off));
       } else {
-        uint32_t w = 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
-          w |= (c[r] & 0xFu) << (((off & 3) << 3) + sh);
+        const int b = ch >> 5;
+        const float d = f16_to_float(sscale[SIDE == 0 ? p * 4 + b : b * 32 + p]);
+        int code;
+        if constexpr (SRC == Q8_0) {
+          int sh;
+          const int off = SIDE == 0 ? k_canon_offset(Q8_0, p, ch) : v_code_offset(Q8_0, p, ch, &sh);
+          code = static_cast<int8_t>(t8[off]);
+        } else {  // Q4_0: canonical byte 16b + (j & 15), high nibble for j >= 16
+          int sh = ((ch & 31) >> 4) * 4;
+          const int off = SIDE == 0 ? k_canon_offset(Q4_0, p, 16 * b + (ch & 15)) : v_code_offset(Q4_0, p, ch, &sh);
+          code = static_cast<int>((t8[off] >> sh) & 0xFu) - 8;
         }
-        *reinterpret_cast<uint32_t*>(tbase + (off0 & ~3)) = w;
+        v = static_cast<float>(code) * d;  // exact: <= 19 significant bits
       }
-    }
-    if constexpr (has_scales(CODEC)) {
-      // lane 0 holds blocks 0 and 2, lane 32 blocks 1 and 3 (uniform per half-wave)
-      if ((lane & 31) == 0) {
-        const int b0 = lane >> 5;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t sv[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) sv[r] = half ? rc[r].s1 : rc[r].s0;
-          const u32x4 u = {sv[0] | (sv[1] << 16), sv[2] | (sv[3] << 16), sv[4] | (sv[5] << 16), sv[6] | (sv[7] << 16)};
-          *reinterpret_cast<u32x4*>(scales + v_scale_index(tile, b0 + 2 * half, pbase)) = u;
-        }
-      }
-    }
-    if constexpr (has_norms(CODEC)) {
-      if (lane == 0) {
-        uint32_t nv[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) nv[r] = rc[r].norm;
-        const u32x4 u = {nv[0] | (nv[1] << 16), nv[2] | (nv[3] << 16), nv[4] | (nv[5] << 16), nv[6] | (nv[7] << 16)};
-        *reinterpret_cast<u32x4*>(norms + g_first_row) = u;
-      }
+      v = live[r] ? v : 0.0f;  // rows past n_rows (any bits) are encoded as zeros and not stored
+      if (half) x1[r] = v;
+      else x0[r] = v;
     }
   }
+  RowCodes rc[8];
+  encode_rows<DST, 8>(x0, x1, lane, a.signs, rc);
+  constexpr int RB = row_code_bytes(DST);
+  uint8_t* codes = static_cast<uint8_t*>(a.codes) + ph * a.capacity * RB;
+  uint16_t* scales = has_scales(DST) ? a.scales + ph * a.capacity * 4 : nullptr;
+  uint16_t* norms = has_norms(DST) ? a.norms + ph * a.capacity : nullptr;
+  store_group<DST, SIDE>(codes, scales, norms, g0, rc, live, lane, rowbuf[wave]);
 }
 
 #define VIT_APPEND_CASE(C, S)                                                   \
@@ -139,6 +224,29 @@ hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, con
     VIT_APPEND_CASE(Q4_0, 1)
     VIT_APPEND_CASE(ROT4, 0)
     VIT_APPEND_CASE(ROT4, 1)
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The degrade steps: f16 -> q8_0 / q4_0 / rot4, q8_0 -> q4_0 / rot4.
+#define VIT_TRANSCODE_CASE(S, D)                                                                         \
+  case (S)*4 + (D):                                                                                      \
+    if (side == 0)                                                                                       \
+      hipLaunchKernelGGL((transcode_kernel<S, D, 0>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
+    else                                                                                                 \
+      hipLaunchKernelGGL((transcode_kernel<S, D, 1>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
+    break;
+
+hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
+                            const TranscodeArgs& args) {
+  switch (src_codec * 4 + dst_codec) {
+    VIT_TRANSCODE_CASE(F16, Q8_0)
+    VIT_TRANSCODE_CASE(F16, Q4_0)
+    VIT_TRANSCODE_CASE(F16, ROT4)
+    VIT_TRANSCODE_CASE(Q8_0, Q4_0)
+    VIT_TRANSCODE_CASE(Q8_0, ROT4)
     default:
       return hipErrorInvalidValue;
   }

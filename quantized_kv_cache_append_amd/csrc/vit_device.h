@@ -42,14 +42,25 @@ __device__ constexpr float kThresholds[15] = {
 // ---------------------------------------------------------------------------
 // Physical layout (see include/vit.h).  Offsets are within one 32-row tile.
 
-// K side: row p of the tile, block b, 16-byte unit c of that block's bytes.
-// Rows 16h .. 16h+15 form half h; lane 16b + r of a wave-wide 16-byte load of
-// (half h, unit c) reads row 16h + r, block b.
-__host__ __device__ inline int k_unit_offset(int codec, int p, int b, int c) {
+// K side: row p of the tile, chunk g (0..3) of unit c.  A row's canonical
+// bytes (codes in channel order; 4-bit codes packed as in q4_0) are cut into
+// blocks of 16 * CB bytes (CB = units_per_block) and each block into four
+// chunks of 4 * CB bytes; unit c of the row holds chunk g of its blocks
+// c * BPU .. c * BPU + BPU - 1 (BPU = 4 / CB), 16 bytes.  Rows 16h .. 16h+15
+// form half h; lane 16g + r of a wave-wide 16-byte load of (half h, unit c)
+// reads row 16h + r, chunk g.
+__host__ __device__ inline int k_unit_offset(int codec, int p, int g, int c) {
   const int h = p >> 4;
   const int r = p & 15;
   const int cb = units_per_block(codec);
-  return (((h * cb + c) * 4 + b) * 16 + r) * 16;
+  return (((h * cb + c) * 4 + g) * 16 + r) * 16;
+}
+
+// K side: tile offset of canonical byte k of row p.
+__host__ __device__ inline int k_canon_offset(int codec, int p, int k) {
+  const int cb = units_per_block(codec), bpu = 4 / cb, chb = 4 * cb;
+  const int blk = k / (16 * cb), off = k % (16 * cb);
+  return k_unit_offset(codec, p, off / chb, blk / bpu) + (blk % bpu) * chb + off % chb;
 }
 
 // V side: byte offset of the code of (row p, channel ch) and, for 4-bit

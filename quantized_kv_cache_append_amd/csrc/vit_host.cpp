@@ -116,6 +116,95 @@ int vit_kv_append_quant(const vit_kv_plane* dst, const float* src, const int64_t
   return enqueue_append(dst, src, pos0, n_tokens, static_cast<hipStream_t>(stream));
 }
 
+int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int64_t* n_rows, void* stream) {
+  int st = check_plane(src);
+  if (st != VIT_OK) return st;
+  st = check_plane(dst);
+  if (st != VIT_OK) return st;
+  if (!n_rows) return VIT_E_ARG;
+  if (src->side != dst->side || src->n_seqs != dst->n_seqs || src->n_kv_heads != dst->n_kv_heads ||
+      src->capacity != dst->capacity)
+    return VIT_E_ARG;
+  // the degrade steps: f16 -> q8_0 / q4_0 / rot4, q8_0 -> q4_0 / rot4
+  const bool step = (src->codec == VIT_CODEC_F16 && dst->codec != VIT_CODEC_F16) ||
+                    (src->codec == VIT_CODEC_Q8_0 && (dst->codec == VIT_CODEC_Q4_0 || dst->codec == VIT_CODEC_ROT4));
+  if (!step) return VIT_E_UNSUPPORTED;
+  // the two planes' arrays must be disjoint
+  const void* sp[3] = {src->codes, src->scales, src->norms};
+  const void* dp[3] = {dst->codes, dst->scales, dst->norms};
+  size_t sb[3], db[3];
+  vit_kv_plane_sizes(src->codec, src->n_seqs, src->n_kv_heads, VIT_HEAD_DIM, src->capacity, &sb[0], &sb[1], &sb[2]);
+  vit_kv_plane_sizes(dst->codec, dst->n_seqs, dst->n_kv_heads, VIT_HEAD_DIM, dst->capacity, &db[0], &db[1], &db[2]);
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) {
+      if (!sp[i] || !dp[j] || sb[i] == 0 || db[j] == 0) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(sp[i]), b0 = reinterpret_cast<uintptr_t>(dp[j]);
+      if (a0 < b0 + db[j] && b0 < a0 + sb[i]) return VIT_E_ARG;
+    }
+  int64_t max_rows = 0;
+  for (int s = 0; s < src->n_seqs; ++s) {
+    if (n_rows[s] < 0 || n_rows[s] > src->capacity) return VIT_E_CAPACITY;
+    if (n_rows[s] > max_rows) max_rows = n_rows[s];
+  }
+  if (max_rows == 0) return VIT_OK;
+
+  vit::TranscodeArgs a{};
+  a.src_codes = static_cast<const uint8_t*>(src->codes);
+  a.src_scales = src->scales;
+  a.codes = dst->codes;
+  a.scales = dst->scales;
+  a.norms = dst->norms;
+  a.capacity = dst->capacity;
+  a.n_kv_heads = dst->n_kv_heads;
+  load_signs(dst, a.signs);
+  for (int s = 0; s < src->n_seqs; ++s) a.n_rows[s] = n_rows[s];
+  const dim3 grid(static_cast<unsigned>((max_rows + 31) / 32), static_cast<unsigned>(dst->n_kv_heads),
+                  static_cast<unsigned>(dst->n_seqs));
+  return vit::launch_transcode(src->codec, dst->codec, dst->side, grid, static_cast<hipStream_t>(stream), a) ==
+                 hipSuccess
+             ? VIT_OK
+             : VIT_E_HIP;
+}
+
+int vit_vbr_classic_next_step(int32_t n_tensors, const int32_t* codecs, const int32_t* price_order,
+                              const uint8_t* movable, double floor_bpv, int32_t* tensor, int32_t* new_codec) {
+  if (n_tensors < 1 || !codecs || !price_order || !tensor || !new_codec) return VIT_E_ARG;
+  // rung of each tensor on the ladder f16 (0) -> q8_0 (1) -> q4_0 (2)
+  auto rung_of = [](int32_t c) { return c == VIT_CODEC_F16 ? 0 : c == VIT_CODEC_Q8_0 ? 1 : c == VIT_CODEC_Q4_0 ? 2 : -1; };
+  static const int32_t kLadder[3] = {VIT_CODEC_F16, VIT_CODEC_Q8_0, VIT_CODEC_Q4_0};
+  static const double kBpv[3] = {16.0, 8.5, 4.5};
+  // every tensor on the ladder, and the price order a permutation of 0 .. n-1
+  int top = 3;  // least degraded rung held by a movable tensor that can still move
+  for (int32_t i = 0; i < n_tensors; ++i) {
+    const int r = rung_of(codecs[i]);
+    if (r < 0) return VIT_E_ARG;
+    if ((!movable || movable[i]) && r < 2 && r < top) top = r;
+  }
+  for (int32_t k = 0; k < n_tensors; ++k) {  // each index in range and named once
+    const int32_t i = price_order[k];
+    if (i < 0 || i >= n_tensors) return VIT_E_ARG;
+    for (int32_t m = 0; m < k; ++m)
+      if (price_order[m] == i) return VIT_E_ARG;
+  }
+  *tensor = -1;
+  *new_codec = -1;
+  if (top == 3) return VIT_OK;  // every movable tensor is at q4_0
+  for (int32_t k = 0; k < n_tensors; ++k) {
+    const int32_t i = price_order[k];
+    if ((movable && !movable[i]) || rung_of(codecs[i]) != top) continue;
+    if (floor_bpv > 0.0) {
+      // aggregate bits/value after the step, summed in tensor order
+      double total = 0.0;
+      for (int32_t j = 0; j < n_tensors; ++j) total += j == i ? kBpv[top + 1] : kBpv[rung_of(codecs[j])];
+      if (total / n_tensors < floor_bpv) return VIT_OK;
+    }
+    *tensor = i;
+    *new_codec = kLadder[top + 1];
+    return VIT_OK;
+  }
+  return VIT_OK;
+}
+
 size_t vit_attn_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t head_dim, int32_t n_splits) {
   if (head_dim != VIT_HEAD_DIM || n_seqs < 1 || n_q_heads < 1 || n_splits < 1 || n_splits > VIT_MAX_SPLITS)
     return 0;

@@ -23,6 +23,20 @@ struct AppendArgs {
   int64_t pos0[kMaxSeqs];
 };
 
+// Re-encoding the rows a plane holds into a plane of another codec (same
+// geometry and side).
+struct TranscodeArgs {
+  const uint8_t* src_codes;
+  const uint16_t* src_scales;  // null for an f16 source
+  void* codes;                 // destination plane
+  uint16_t* scales;
+  uint16_t* norms;
+  int64_t capacity;
+  int32_t n_kv_heads;
+  uint32_t signs[4];           // destination signs (rot4)
+  int64_t n_rows[kMaxSeqs];    // rows 0 .. n_rows[s]-1 of sequence s
+};
+
 struct DecodeArgs {
   const uint8_t* kcodes;
   const uint16_t* kscales;
@@ -66,6 +80,8 @@ struct KernelEvents {
 };
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
+hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
+                            const TranscodeArgs& args);
 hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args,
                          const KernelEvents& ev);
 hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);

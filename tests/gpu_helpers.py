@@ -65,6 +65,24 @@ def fill_plane_synth(plane, cfg, layer, side, start, count, units, torch, gen):
     return src
 
 
+def unit_view(plane, s, h):
+    """Logical contents of one (sequence, KV head) stream of a plane (the
+    slice of each array that holds it), as host_view shapes them with S = H = 1."""
+    from quantized_kv_cache_append_amd import layout
+
+    cap = plane.capacity
+    u = s * plane.n_kv_heads + h
+    rb = plane.codes.numel() // (plane.n_seqs * plane.n_kv_heads * cap)
+    out = {"codes": layout.unpack_codes(plane.codec, plane.side,
+                                        plane.codes[u * cap * rb:(u + 1) * cap * rb].cpu().numpy(), 1, 1, cap)[0, 0]}
+    if plane.scales is not None:
+        raw = plane.scales[u * cap * 4:(u + 1) * cap * 4].cpu().numpy().view(np.uint16)
+        out["scales"] = layout.unpack_scales(plane.side, raw, 1, 1, cap)[0, 0]
+    if plane.norms is not None:
+        out["norms"] = layout.unpack_norms(plane.norms[u * cap:(u + 1) * cap].cpu().numpy().view(np.uint16), 1, 1, cap)[0, 0]
+    return out
+
+
 def oracle_quant(codec, rows, signs):
     """Oracle codes of rows [N, 128] as (codes, scales, norms) arrays."""
     q = codecs.quantize(codec, rows, signs)
@@ -100,5 +118,5 @@ def check_close(got, ref, what, tol=TOL):
     return err / rms
 
 
-__all__ = ["oracle", "torch_cuda", "say", "make_plane", "append_rows", "fill_plane_synth", "compare_plane_rows",
+__all__ = ["oracle", "torch_cuda", "say", "make_plane", "append_rows", "fill_plane_synth", "unit_view", "compare_plane_rows",
            "ref_unit", "check_close", "TOL"]

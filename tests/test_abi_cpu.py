@@ -156,6 +156,84 @@ def test_decode_mq_validation(lib):
     assert _decode_mq(lib, K, V, q_len=2, ns=3, ws=None) == _lib.VIT_E_ARG
 
 
+def _transcode(lib, src, dst, n_rows=(10, 10)):
+    arr = None if n_rows is None else (ctypes.c_int64 * len(n_rows))(*n_rows)
+    return lib.vit_kv_transcode(ctypes.byref(src), ctypes.byref(dst), arr, None)
+
+
+def test_transcode_validation(lib):
+    """Codec pairs, matching geometry, disjoint arrays and row counts are all
+    checked on the host (no compute: every call fails or has no rows)."""
+    S16 = 0x1000000  # f16 plane: codes 2 x 2 x 512 x 256 B = 512 KiB
+    src = _plane(codec=0, codes=S16, scales=None, norms=None)
+    dst = _plane(codec=1, codes=0x2000000, scales=0x3000000, norms=None)
+    assert _transcode(lib, src, dst, n_rows=(0, 0)) == _lib.VIT_OK       # nothing to do
+    assert _transcode(lib, src, dst, n_rows=(513, 0)) == _lib.VIT_E_CAPACITY
+    assert _transcode(lib, src, dst, n_rows=(-1, 0)) == _lib.VIT_E_CAPACITY
+    assert _transcode(lib, src, dst, n_rows=None) == _lib.VIT_E_ARG
+    # overlapping arrays: the destination codes inside the source codes
+    assert _transcode(lib, src, _plane(codec=1, codes=S16 + 0x40000, scales=0x3000000, norms=None)) == _lib.VIT_E_ARG
+    # destination scales inside the source codes
+    assert _transcode(lib, src, _plane(codec=1, codes=0x2000000, scales=S16 + 0x100, norms=None)) == _lib.VIT_E_ARG
+    # geometry and side must match
+    assert _transcode(lib, src, _plane(codec=1, side=1, codes=0x2000000, scales=0x3000000, norms=None)) == _lib.VIT_E_ARG
+    assert _transcode(lib, src, _plane(codec=1, H=4, codes=0x2000000, scales=0x3000000, norms=None)) == _lib.VIT_E_ARG
+    assert _transcode(lib, src, _plane(codec=1, cap=1024, codes=0x2000000, scales=0x3000000, norms=None)) == _lib.VIT_E_ARG
+    # only degrade steps from an exactly decodable source
+    q8 = _plane(codec=1, codes=0x4000000, scales=0x5000000, norms=None)
+    q4 = _plane(codec=2, codes=0x6000000, scales=0x7000000, norms=None)
+    r4 = _plane(codec=3, codes=0x8000000, scales=0x9000000, norms=0xA000000, signs=ctypes.addressof(_SIGNS))
+    f16b = _plane(codec=0, codes=0xB000000, scales=None, norms=None)
+    for a, b in ((q4, q8), (q8, f16b), (r4, q4), (q4, r4), (src, f16b), (q8, _plane(codec=1, codes=0xC000000,
+                                                                                        scales=0xD000000, norms=None))):
+        assert _transcode(lib, a, b) == _lib.VIT_E_UNSUPPORTED
+    for a, b in ((src, q8), (src, q4), (src, r4), (q8, q4), (q8, r4)):
+        assert _transcode(lib, a, b, n_rows=(0, 0)) == _lib.VIT_OK
+
+
+def test_classic_next_step_matches_the_oracle():
+    """The C controller step against oracle.vbr.classic_next_step on random
+    ladder states, price orders, pinned sides and floors (host logic only)."""
+    from oracle import vbr
+
+    import quantized_kv_cache_append_amd as vit
+
+    rng = np.random.default_rng(11)
+    ladder = ["f16", "q8_0", "q4_0"]
+    for trial in range(300):
+        n = int(rng.integers(1, 48))
+        state = [ladder[i] for i in rng.integers(0, 3, n)]
+        order = [int(i) for i in rng.permutation(n)]
+        movable = None if trial % 3 == 0 else [bool(x) for x in rng.random(n) < 0.8]
+        floor = None if trial % 2 else float(rng.choice([4.5, 6.0, 8.5, 10.25, 12.0, 15.5]))
+        assert vit.vit_vbr_classic_next_step(state, order, movable, floor) == \
+            vbr.classic_next_step(state, order, movable, floor), (state, order, movable, floor)
+    # a whole schedule, stepped through the C function
+    state, order = ["f16"] * 32, [int(i) for i in rng.permutation(32)]
+    steps = []
+    while (st := vit.vit_vbr_classic_next_step(state, order, floor_bpv=6.0)) is not None:
+        state[st[0]] = st[1]
+        steps.append(st)
+    assert steps == vbr.classic_schedule(["f16"] * 32, order, floor_bpv=6.0)
+
+
+def test_classic_next_step_validation(lib):
+    t, c = ctypes.c_int32(), ctypes.c_int32()
+
+    def call(codecs, order, n=None):
+        n = len(codecs) if n is None else n
+        ca = (ctypes.c_int32 * max(1, len(codecs)))(*codecs)
+        oa = (ctypes.c_int32 * max(1, len(order)))(*order)
+        return lib.vit_vbr_classic_next_step(n, ca, oa, None, 0.0, ctypes.byref(t), ctypes.byref(c))
+
+    assert call([0, 1], [1, 0]) == _lib.VIT_OK and (t.value, c.value) == (0, 1)
+    assert call([0, 3], [0, 1]) == _lib.VIT_E_ARG   # rot4 is not on the classic ladder
+    assert call([0, 0], [0, 0]) == _lib.VIT_E_ARG   # not a permutation
+    assert call([0, 0], [0, 2]) == _lib.VIT_E_ARG
+    assert call([], [], n=0) == _lib.VIT_E_ARG
+    assert call([2, 2], [0, 1]) == _lib.VIT_OK and t.value == -1  # nothing left to degrade
+
+
 def test_reduce_validation(lib):
     V = _plane(side=1)
     r = lib.vit_attn_splitk_reduce
