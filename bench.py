@@ -55,15 +55,19 @@ WORKLOADS = {"tiny": 1, "batched": 2, "lowbit": 3, "rotated": 4, "ladder": 5}
 D = 128
 
 
-# the decode kernel's own sources (the kernel, its device helpers, its argument block)
-DECODE_SOURCES = ("decode_impl.h", "decode_k*.hip", "vit_device.h", "vit_launch.h")
+# each measured kernel's own sources (the kernel, its device helpers, its argument block)
+KERNEL_SOURCES = {
+    "decode": ("decode_impl.h", "decode_k*.hip", "vit_device.h", "vit_launch.h"),
+    "transcode": ("append.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
+}
+TRANSCODE_PAIRS = ("f16:q8_0", "f16:q4_0", "f16:rot4", "q8_0:q4_0", "q8_0:rot4")
 
 
-def kernel_source_hash():
-    """sha256 prefix over the decode kernel's sources."""
+def kernel_source_hash(kind="decode"):
+    """sha256 prefix over one measured kernel's sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_append_amd", "csrc")
-    for p in sorted(q for pat in DECODE_SOURCES for q in glob.glob(os.path.join(csrc, pat))):
+    for p in sorted(q for pat in KERNEL_SOURCES[kind] for q in glob.glob(os.path.join(csrc, pat))):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -286,6 +290,134 @@ def run_gpu(args):
                 achieved_gbs=achieved)
 
 
+def run_transcode(args):
+    """One VBR degrade step of one (layer, side) tensor of the ladder
+    workload's slots: every row of 2 sequences x 8 KV heads x 200,704 rows
+    re-encoded from the source codec into a destination plane.  The source
+    is filled once (seeded device rows, log-normal channel scales); each timed
+    step re-encodes it into the same destination."""
+    import numpy as np
+    import torch
+
+    import quantized_kv_cache_append_amd as vit
+    import synth
+
+    src_c, dst_c = args.transcode.split(":")
+    cfg = synth.CONFIGS[5]
+    S, H, cap = cfg["seqs"], cfg["hkv"], cfg["capacity"]
+    side = args.side
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED2026 + 77)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    signs = synth.sign_mask(5, 0, side) if dst_c == "rot4" else None
+    src = vit.KVPlane(src_c, side, S, H, cap)
+    dst = vit.KVPlane(dst_c, side, S, H, cap, signs)
+    sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
+    for p0 in range(0, cap, 16384):
+        n = min(16384, cap - p0)
+        vit.vit_kv_append_quant(src, _device_rows(torch, gen, (S, n, H, D), "lognormal", sc), [p0] * S)
+    torch.cuda.synchronize()
+    print(f"# transcode {src_c} -> {dst_c}, side {side}: S={S} Hkv={H} rows={cap}", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    call = vit.prepare_transcode(src, dst, [cap] * S, stream=stream)
+    arm = vit.vit_arm_kernel_events
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
+            call()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            arm(a, b)
+            call()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    rows = S * H * cap
+    per_launch = rows * (_row_bytes(src_c) + _row_bytes(dst_c))
+    return dict(src_c=src_c, dst_c=dst_c, side=side, S=S, H=H, cap=cap, rows=rows, ms_per_step=ms_per_step,
+                mean_ms=float(np.mean(ms)), min_ms=float(np.min(ms)), per_launch_bytes=per_launch,
+                achieved_gbs=per_launch / (float(np.mean(ms)) * 1e-3) / 1e9)
+
+
+def cpu_baseline_transcode(r, budget_s=15.0):
+    """oracle.vbr.transcode on the host for rows of one (sequence, KV head)
+    stream (its source codes prepared untimed), scaled to the step."""
+    import numpy as np
+
+    from oracle import codecs, vbr
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    n = 16384
+    rows = synth.kv_rows(5, r["side"], 0, 0, 0, 0, n)
+    q_src = codecs.quantize(r["src_c"], rows)
+    signs = synth.sign_mask(5, 0, r["side"]) if r["dst_c"] == "rot4" else None
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        vbr.transcode(r["src_c"], r["dst_c"], q_src, dst_signs=signs)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} rows ({r['src_c']} -> {r['dst_c']}) of one (sequence, KV head) stream in "
+                       f"{n}-row calls, {el:.1f} s on 1 thread; step = {r['rows']} rows")}
+
+
+def main_transcode(args):
+    r = run_transcode(args)
+    tag = f"{r['src_c']}_to_{r['dst_c']}_{r['side']}"
+    line = {
+        "metric": "VBR degrade step: rows re-encoded per second + effective GB/s (% of HBM peak), 1 GPU",
+        "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{r['src_c']} decoded exactly to fp32, encoded to {r['dst_c']}",
+        "data": "synthetic (seeded device normals with log-normal channel scales; no model weights or dataset)",
+        "config": {"workload": f"transcode_{tag}", "n_seqs": r["S"], "n_kv_heads": r["H"], "head_dim": D,
+                   "rows_per_stream": r["cap"], "side": r["side"], "src_codec": r["src_c"], "dst_codec": r["dst_c"],
+                   "launch": "eager (pre-marshalled C call)"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "transcode_kernel",
+            "achieved": round(r["achieved_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("transcode", tag),
+            "algorithmic_bytes_per_launch": r["per_launch_bytes"],
+            "mean_launch_ms": round(r["mean_ms"], 5),
+            "min_launch_ms": round(r["min_ms"], 5),
+        },
+        "kernel_source_hash": kernel_source_hash("transcode"),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_transcode(r, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def run_copy_calibration(steps):
     """A plain device copy of known size, for scaling rocprofv3 counters."""
     import torch
@@ -362,15 +494,16 @@ def profile_tag(workload, q_len):
     return workload if q_len == 1 else f"{workload}_verify{q_len}"
 
 
-def load_traffic(workload, n_splits):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    only if they were taken on the current decode sources at this split count."""
-    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+def load_traffic(kind, tag, n_splits=None):
+    """HBM bytes per launch of the measured kernel from the committed rocprofv3
+    counter runs, only if they were taken on its current sources (and, for
+    decode, at this split count)."""
+    p = os.path.join(ROOT, "profiles", f"{kind}_{tag}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("n_splits") != n_splits:
+    if t.get("kernel_source_hash") != kernel_source_hash(kind) or t.get("n_splits") != n_splits:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -393,12 +526,13 @@ def _counter_kib(d, counter, name_part):
     return sum(v) / len(v), len(v)
 
 
-def summarize_profiles(workload, prof, commands):
+def summarize_profiles(kind, workload, prof, commands):
     """Turn one workload's rocprofv3 runs into the committed summaries:
-    profiles/decode_<workload>_kernel_stats.md (kernel-trace statistics beside
-    the bench line of the same run) and profiles/decode_<workload>_traffic.json
-    (HBM bytes per decode launch from FETCH_SIZE and WRITE_SIZE, each scaled by
-    what the counter reads for a plain 1 GiB device copy)."""
+    profiles/<kind>_<workload>_kernel_stats.md (kernel-trace statistics beside
+    the bench line of the same run) and profiles/<kind>_<workload>_traffic.json
+    (HBM bytes per launch of <kind>_kernel from FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the counter reads for a plain 1 GiB device copy)."""
+    kernel = f"{kind}_kernel"
     stats = _read_csv(os.path.join(prof, workload, "trace", "run_kernel_stats.csv"))
     def bench_line(name):
         with open(os.path.join(prof, workload, name)) as f:
@@ -410,15 +544,15 @@ def summarize_profiles(workload, prof, commands):
     copy_write, _ = _counter_kib(os.path.join(prof, "copy_write"), "WRITE_SIZE", "copy")
     f_fetch = (1 << 30) / (copy_fetch * 1024)
     f_write = (1 << 30) / (copy_write * 1024)
-    fetch, n_f = _counter_kib(os.path.join(prof, workload, "fetch"), "FETCH_SIZE", "decode_kernel")
-    write, n_w = _counter_kib(os.path.join(prof, workload, "write"), "WRITE_SIZE", "decode_kernel")
+    fetch, n_f = _counter_kib(os.path.join(prof, workload, "fetch"), "FETCH_SIZE", kernel)
+    write, n_w = _counter_kib(os.path.join(prof, workload, "write"), "WRITE_SIZE", kernel)
     hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
     alg = line["roofline"]["algorithmic_bytes_per_launch"]
-    dec = [r for r in stats if "decode_kernel" in r["Name"]]
+    dec = [r for r in stats if kernel in r["Name"]]
     calls = sum(int(r["Calls"]) for r in dec)
     avg_us = sum(float(r["TotalDurationNs"]) for r in dec) / calls / 1e3
     traffic = {
-        "workload": workload, "kernel": "decode_kernel",
+        "workload": workload, "kernel": kernel,
         "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
         "dispatches": [n_f, n_w],
         "copy_calibration": {"fetch_kib_per_gib": round(copy_fetch, 1), "write_kib_per_gib": round(copy_write, 1),
@@ -427,14 +561,14 @@ def summarize_profiles(workload, prof, commands):
         "algorithmic_bytes_per_launch": alg,
         "hbm_over_algorithmic": round(hbm / alg, 4),
         "kernel_source_hash": line["kernel_source_hash"],
-        "n_splits": line["config"]["n_splits"],
+        "n_splits": line["config"].get("n_splits"),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
-    md = [f"# decode_kernel, workload {workload}: rocprofv3 kernel statistics", "",
-          f"Kernel sources: {line['kernel_source_hash']} (sha256 prefix over the decode kernel's csrc/ files, as bench.py computes it).", "",
+    md = [f"# {kernel}, workload {workload}: rocprofv3 kernel statistics", "",
+          f"Kernel sources: {line['kernel_source_hash']} (sha256 prefix over the {kind} kernel's csrc/ files, as bench.py computes it).", "",
           "Commands (from the repository root, with TMPDIR=/tmp):", "", "```"] + commands + ["```", "",
           "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
@@ -443,20 +577,22 @@ def summarize_profiles(workload, prof, commands):
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     rl = line["roofline"]
     trl = traced["roofline"]
-    md += ["", f"rocprofv3: decode_kernel average over all {calls} calls of the traced run (warmup included): "
+    splits = line["config"].get("n_splits")
+    md += ["", f"rocprofv3: {kernel} average over all {calls} calls of the traced run (warmup included): "
            f"{avg_us:.2f} us.", "",
-           f"bench.py, same command without a profiler attached: mean over its timed decode launches "
+           f"bench.py, same command without a profiler attached: mean over its timed {kind} launches "
            f"{1e3 * rl['mean_launch_ms']:.2f} us (min {1e3 * rl['min_launch_ms']:.2f} us), from HIP events recorded "
-           f"by the decode dispatch itself; value {line['value']} {line['unit']}, {line['ms_per_step']} ms/step, "
+           f"by the {kind} dispatch itself; value {line['value']} {line['unit']}, {line['ms_per_step']} ms/step, "
            f"roofline achieved {rl['achieved']} GB/s = {rl['frac']} of {rl['peak']} GB/s "
-           f"({rl['algorithmic_bytes_per_launch']} algorithmic bytes per launch), n_splits {line['config']['n_splits']}.", "",
+           f"({rl['algorithmic_bytes_per_launch']} algorithmic bytes per launch)"
+           + (f", n_splits {splits}." if splits is not None else "."), "",
            f"(Inside the traced run the tracer perturbs those events: bench.py read "
            f"{1e3 * trl['mean_launch_ms']:.2f} us there.)", "",
-           "HBM traffic per decode launch (separate --pmc runs, one counter each):", "",
+           f"HBM traffic per {kind} launch (separate --pmc runs, one counter each):", "",
            f"- FETCH_SIZE {fetch:.1f} KiB x {f_fetch:.3f} (1 GiB copy reads {copy_fetch:.0f} KiB) "
            f"+ WRITE_SIZE {write:.1f} KiB x {f_write:.3f} (1 GiB copy writes {copy_write:.0f} KiB)",
            f"- = {hbm / 1e6:.2f} MB per launch vs {alg / 1e6:.2f} MB algorithmic ({hbm / alg:.3f}x)", ""]
-    with open(os.path.join(ROOT, "profiles", f"decode_{workload}_kernel_stats.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{kind}_{workload}_kernel_stats.md"), "w") as f:
         f.write("\n".join(md))
     print("\n".join(md))
 
@@ -471,6 +607,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence verified per step (vit_attn_decode_mq when > 1)")
+    ap.add_argument("--transcode", default=None, choices=TRANSCODE_PAIRS,
+                    help="time a VBR degrade step (vit_kv_transcode) of one ladder-slot tensor instead")
+    ap.add_argument("--side", default="k", choices=("k", "v"), help="plane side for --transcode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps as HIP graph replays (one captured graph per replica)")
@@ -480,8 +619,15 @@ def main():
                     help="write profiles/ summaries for --workload from rocprofv3 output under PROF_DIR (no GPU)")
     args = ap.parse_args()
     if args.summarize:
-        w = profile_tag(args.workload, args.q_len)
-        b = f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
+        if args.transcode:
+            kind = "transcode"
+            sc, dc = args.transcode.split(":")
+            w = f"{sc}_to_{dc}_{args.side}"
+            b = f"python3 bench.py --transcode {args.transcode} --side {args.side}"
+        else:
+            kind = "decode"
+            w = profile_tag(args.workload, args.q_len)
+            b = f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
         cmds = [f"{b} --no-cpu-baseline > PROF/{w}/bench.json",
                 f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{w}/trace -o run -- "
                 f"{b} --no-cpu-baseline > PROF/{w}/bench_traced.json",
@@ -492,7 +638,7 @@ def main():
                 "rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/copy_fetch -o run -- python3 bench.py --calib-copy 4",
                 "rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/copy_write -o run -- python3 bench.py --calib-copy 4",
                 f"{b} --summarize PROF"]
-        summarize_profiles(w, args.summarize, cmds)
+        summarize_profiles(kind, w, args.summarize, cmds)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -502,10 +648,13 @@ def main():
     if args.calib_copy:
         run_copy_calibration(args.calib_copy)
         return
+    if args.transcode:
+        main_transcode(args)
+        return
     r = run_gpu(args)
     cfg = r["cfg"]
     tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
-    traffic = load_traffic(profile_tag(args.workload, r["QL"]), r["n_splits"])
+    traffic = load_traffic("decode", profile_tag(args.workload, r["QL"]), r["n_splits"])
     line = {
         "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(tok_s, 1),

@@ -272,11 +272,12 @@ int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_h
                            float *out, void *stream);
 
 /* Measurement aid (no operation of the method): arm two caller-created
- * hipEvent_t handles (timing enabled) so that the decode kernel of this host
- * thread's next vit_attn_decode call records `start_event` when its dispatch
- * begins and `stop_event` when it ends (hipExtLaunchKernel), i.e. the pair
- * brackets that one kernel and nothing else.  One-shot: the next
- * vit_attn_decode call consumes the arming whether or not it launches.
+ * hipEvent_t handles (timing enabled) so that the kernel of this host
+ * thread's next vit_attn_decode, vit_attn_decode_mq or vit_kv_transcode call
+ * records `start_event` when its dispatch begins and `stop_event` when it
+ * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and
+ * nothing else.  One-shot: that next call consumes the arming whether or
+ * not it launches.
  * Both NULL disarms; exactly one NULL returns VIT_E_ARG.  The events stay
  * owned by the caller. */
 int vit_arm_kernel_events(void *start_event, void *stop_event);

@@ -257,8 +257,9 @@ def _event_handle(ev):
 
 
 def vit_arm_kernel_events(start, stop):
-    """Make the next decode kernel record torch.cuda.Event ``start``/``stop``
-    at its own dispatch start and end (both None disarms)."""
+    """Make the kernel of the next decode or transcode call record
+    torch.cuda.Event ``start``/``stop`` at its own dispatch start and end
+    (both None disarms)."""
     st = _lib.load().vit_arm_kernel_events(_event_handle(start), _event_handle(stop))
     return _lib.check("vit_arm_kernel_events", st)
 
@@ -283,6 +284,14 @@ def prepare_append(plane, src, pos0, n_tokens=None, stream=None):
     p = plane.struct()
     args = (ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
     return _Prepared("vit_kv_append_quant", lib.vit_kv_append_quant, args, (p, p0, src, plane))
+
+
+def prepare_transcode(src, dst, n_rows, stream=None):
+    lib = _lib.load()
+    nr = (ctypes.c_int64 * len(n_rows))(*[int(x) for x in n_rows])
+    sp, dp = src.struct(), dst.struct()
+    args = (ctypes.byref(sp), ctypes.byref(dp), nr, _stream_handle(stream))
+    return _Prepared("vit_kv_transcode", lib.vit_kv_transcode, args, (sp, dp, nr, src, dst))
 
 
 def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, scale=None, n_splits=1,

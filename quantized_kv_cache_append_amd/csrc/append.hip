@@ -234,13 +234,15 @@ hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, con
 #define VIT_TRANSCODE_CASE(S, D)                                                                         \
   case (S)*4 + (D):                                                                                      \
     if (side == 0)                                                                                       \
-      hipLaunchKernelGGL((transcode_kernel<S, D, 0>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
+      hipExtLaunchKernelGGL((transcode_kernel<S, D, 0>), grid, dim3(64 * kAppendWaves), 0, stream,      \
+                            ev.start, ev.stop, 0, args);                                                 \
     else                                                                                                 \
-      hipLaunchKernelGGL((transcode_kernel<S, D, 1>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
+      hipExtLaunchKernelGGL((transcode_kernel<S, D, 1>), grid, dim3(64 * kAppendWaves), 0, stream,      \
+                            ev.start, ev.stop, 0, args);                                                 \
     break;
 
 hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
-                            const TranscodeArgs& args) {
+                            const TranscodeArgs& args, const KernelEvents& ev) {
   switch (src_codec * 4 + dst_codec) {
     VIT_TRANSCODE_CASE(F16, Q8_0)
     VIT_TRANSCODE_CASE(F16, Q4_0)

@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kRowBytes[4] = {256, 128, 64, 64};
 
-// events armed by vit_arm_kernel_events for this host thread's next decode
+// events armed by vit_arm_kernel_events for this host thread's next decode or transcode
 thread_local vit::KernelEvents g_armed;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -117,6 +117,8 @@ int vit_kv_append_quant(const vit_kv_plane* dst, const float* src, const int64_t
 }
 
 int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int64_t* n_rows, void* stream) {
+  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
+  g_armed = vit::KernelEvents{};
   int st = check_plane(src);
   if (st != VIT_OK) return st;
   st = check_plane(dst);
@@ -160,7 +162,7 @@ int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int
   for (int s = 0; s < src->n_seqs; ++s) a.n_rows[s] = n_rows[s];
   const dim3 grid(static_cast<unsigned>((max_rows + 31) / 32), static_cast<unsigned>(dst->n_kv_heads),
                   static_cast<unsigned>(dst->n_seqs));
-  return vit::launch_transcode(src->codec, dst->codec, dst->side, grid, static_cast<hipStream_t>(stream), a) ==
+  return vit::launch_transcode(src->codec, dst->codec, dst->side, grid, static_cast<hipStream_t>(stream), a, ev) ==
                  hipSuccess
              ? VIT_OK
              : VIT_E_HIP;

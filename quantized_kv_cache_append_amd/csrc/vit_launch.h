@@ -81,7 +81,7 @@ struct KernelEvents {
 
 hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
 hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
-                            const TranscodeArgs& args);
+                            const TranscodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args,
                          const KernelEvents& ev);
 hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
