@@ -20,6 +20,8 @@ What it computes (numpy, written for a reader to check by eye):
 * ``bytes_model``-- bits/value, bytes per row and the per-token KV arithmetic.
 * ``vbr``        -- a VBR degrade step (stored rows decoded and re-encoded one
                     rung down) and the classic ladder's strictly banded order.
+* ``probe``      -- attention-probe cell scores (per-cell softmax mass with
+                    exponential decay) and the choice of cells to evict.
 
 Sources.  The codec family (f16, q8_0, q4_0 with 32-value blocks; bits per
 value 16 / 8.5 / 4.5; rotated "turbo" scalar codecs) is the "Codecs" table of
@@ -34,6 +36,6 @@ against closed forms, brute force, textbook values or invariants.  The one
 function without an independent pin is listed in its own docstring.
 """
 
-from . import attention, bytes_model, codecs, fp, lloyd_max, vbr, wht  # noqa: F401
+from . import attention, bytes_model, codecs, fp, lloyd_max, probe, vbr, wht  # noqa: F401
 
-__all__ = ["attention", "bytes_model", "codecs", "fp", "lloyd_max", "vbr", "wht"]
+__all__ = ["attention", "bytes_model", "codecs", "fp", "lloyd_max", "probe", "vbr", "wht"]

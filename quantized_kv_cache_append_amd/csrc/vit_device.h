@@ -286,15 +286,16 @@ __device__ inline void encode_q4_0(const float (&x0)[R], const float (&x1)[R], i
   }
 }
 
+// idx = #{k : th_k < t} + #{k : th_k == t and t >= 0} (a tie goes to the
+// level farther from zero).  The thresholds are symmetric (th_k = -th_{14-k},
+// th_7 = 0), so with c = #{k >= 8 : th_k <= |t|} this is 8 + c for t >= 0
+// (-0 included) and 7 - c for t < 0.
 __device__ inline uint32_t rot4_index(float t) {
-  uint32_t idx = 0;
+  const float a = fabsf(t);
+  uint32_t c = 0;
 #pragma unroll
-  for (int k = 0; k < 15; ++k) {
-    const float th = kThresholds[k];
-    idx += (t > th) ? 1u : 0u;
-    idx += (t == th && t >= 0.0f) ? 1u : 0u;
-  }
-  return idx;
+  for (int k = 8; k < 15; ++k) c += kThresholds[k] <= a ? 1u : 0u;
+  return t >= 0.0f ? 8u + c : 7u - c;
 }
 
 // One Walsh-Hadamard stage across lanes for every row: lanes with bit h set
