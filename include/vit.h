@@ -271,9 +271,54 @@ int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_h
                            int32_t head_dim, int32_t n_splits, const vit_kv_plane *v,
                            float *out, void *stream);
 
+/* Workspace bytes of vit_attn_probe_scores: fp32 logits [n_seqs][n_q_heads]
+ * [capacity] (256-byte padded) followed by softmax partials [n_seqs]
+ * [n_q_heads][64][2].  Returns 0 for invalid sizes (n_q_heads up to 256). */
+size_t vit_attn_probe_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int64_t capacity);
+
+/* Attention-probe cell scores for sparse KV eviction (Randozart/VITRIOL page:
+ * "What sets VITRIOL apart" -- probe scoring decides which KV cells earn
+ * their keep; "How It Works -- Resident mode" -- a probe graph of a q.K
+ * softmax with exponential decay, run every 16 steps; draft tokens are
+ * excluded).  For every sequence s and every query head, the softmax of
+ * scale * q . k over its KV head's cells 0 .. seq_len[s]-1 (keys dequantized
+ * on the fly, as decode does) gives one probability per cell; a cell is a
+ * token position holding every KV head, so its mass is the sum over all
+ * n_q_heads query heads (a sequence's masses sum to n_q_heads).  Then
+ *     scores[s][j] = decay * scores[s][j] + mass[s][j]   for j < seq_len[s];
+ * cells at or past seq_len[s] are not touched.  The cadence of scoring events
+ * is the caller's; for several layers in one event, pass the decay with the
+ * first and 1 with the others.
+ *  k          a K-side plane (any codec).
+ *  q          fp32 [n_seqs][n_q_heads][128]: the current token's query rows,
+ *             model domain, 16-B aligned; G = n_q_heads / n_kv_heads <= 16.
+ *  seq_len    [host] int64 [n_seqs], 1 .. capacity.
+ *  workspace  vit_attn_probe_workspace_bytes(n_seqs, n_q_heads, capacity)
+ *             bytes, 256-B aligned.
+ *  scores     fp32 [n_seqs][capacity], in/out, 16-B aligned.
+ * The masses equal the fp64 definition to fp32 accumulation accuracy. */
+int vit_attn_probe_scores(const vit_kv_plane *k, const float *q, int32_t n_q_heads, const int64_t *seq_len,
+                          float scale, float decay, float *workspace, float *scores, void *stream);
+
+/* The cells to evict (same page and section: the lowest-scored middle cells
+ * go first; sinks and recent cells are protected).  For each sequence s, the
+ * middle cells are n_sink <= j < seq_len[s] - n_recent; the n_evict lowest
+ * (score, cell) pairs among them (equal scores: lower cell first, so the
+ * choice is unique) are written in increasing cell order.
+ *  scores     fp32 [n_seqs][capacity] (device), e.g. from vit_attn_probe_scores.
+ *  seq_len    [host] int64 [n_seqs], 0 .. capacity.
+ *  n_sink, n_recent, n_evict  >= 0.
+ *  rows_out   int64 [n_seqs][n_evict] (device): the chosen cells, then -1.
+ *  n_out      int32 [n_seqs] (device): how many were chosen,
+ *             min(n_evict, middle cells). */
+int vit_probe_select_evictions(const float *scores, int32_t n_seqs, int64_t capacity, const int64_t *seq_len,
+                               int64_t n_sink, int64_t n_recent, int32_t n_evict, int64_t *rows_out,
+                               int32_t *n_out, void *stream);
+
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
- * thread's next vit_attn_decode, vit_attn_decode_mq or vit_kv_transcode call
+ * thread's next vit_attn_decode, vit_attn_decode_mq, vit_kv_transcode or
+ * vit_attn_probe_scores call (for the latter: its logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it
  * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and
  * nothing else.  One-shot: that next call consumes the arming whether or

@@ -14,10 +14,11 @@ protected; draft tokens are excluded from probe scoring).
 Readings (the page prints no formula):
 
 * A scoring event takes the current token's query rows (the n_q_heads query
-  heads of one sequence; no draft tokens) and, for every KV head, the softmax
-  over that head's cells 0 .. L-1 of scale * q . k, per query head, exactly
-  as in decode attention.  A cell's mass is the sum of its probabilities over
-  the query heads sharing the KV head (so the masses of one KV head sum to G).
+  heads of one sequence; no draft tokens) and, per query head, the softmax of
+  scale * q . k over its KV head's cells 0 .. L-1, exactly as in decode
+  attention.  A cell is a token position (it holds every KV head), so its
+  mass is the sum of its probabilities over all n_q_heads query heads (the
+  masses of one sequence sum to n_q_heads).
 * Exponential decay: score <- decay * score + mass, applied per scoring event
   (scores of cells at or past L are not touched).  The event cadence (every
   16 steps) is the caller's.
@@ -41,6 +42,15 @@ def probe_mass(q_rows, k_rows, k_codec, scale, k_signs=None):
     p = np.exp(s)
     p /= p.sum(axis=1, keepdims=True)
     return p.sum(axis=0)
+
+
+def cell_mass(q_rows, k_rows, k_codec, scale, k_signs=None):
+    """Mass per cell [L] of one sequence: q_rows [Hq, 128] (query head h uses
+    KV head h // G), k_rows [Hkv, L, 128]; the sum over the KV heads of
+    probe_mass of their G query rows."""
+    hkv = len(k_rows)
+    g = len(q_rows) // hkv
+    return sum(probe_mass(q_rows[h * g:(h + 1) * g], k_rows[h], k_codec, scale, k_signs) for h in range(hkv))
 
 
 def decay_update(prev, mass, decay):

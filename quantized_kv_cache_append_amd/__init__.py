@@ -8,7 +8,9 @@ names mirror the C entry points:
     vit_kv_plane_sizes, vit_kv_append_quant, vit_kv_transcode,
     vit_vbr_classic_next_step, vit_attn_workspace_bytes,
     vit_attn_default_splits, vit_attn_decode, vit_attn_decode_mq,
-    vit_attn_splitk_reduce, vit_arm_kernel_events (a measurement aid)
+    vit_attn_splitk_reduce, vit_attn_probe_workspace_bytes,
+    vit_attn_probe_scores, vit_probe_select_evictions,
+    vit_arm_kernel_events (a measurement aid)
 
 ``KVPlane`` allocates the three arrays of one (layer, side) cache tensor.
 """
@@ -25,6 +27,7 @@ __all__ = [
     "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_kv_transcode", "vit_vbr_classic_next_step",
     "vit_attn_workspace_bytes",
     "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_splitk_reduce",
+    "vit_attn_probe_workspace_bytes", "vit_attn_probe_scores", "vit_probe_select_evictions",
     "vit_arm_kernel_events",
 ]
 
@@ -247,6 +250,48 @@ def decode(k, v, q, n_q_heads, seq_len, k_new=None, v_new=None, scale=None, n_sp
     return out
 
 
+def vit_attn_probe_workspace_bytes(n_seqs, n_q_heads, capacity):
+    return int(_lib.load().vit_attn_probe_workspace_bytes(int(n_seqs), int(n_q_heads), int(capacity)))
+
+
+def vit_attn_probe_scores(k, q, n_q_heads, seq_len, scores, scale=None, decay=1.0, workspace=None, stream=None):
+    """One probe scoring event: scores fp32 [S, capacity] (in/out) <- decay *
+    scores + per-cell softmax mass of q fp32 [S, Hq, 128] over K plane ``k``."""
+    import torch
+
+    lib = _lib.load()
+    scale = 1.0 / np.sqrt(HEAD_DIM) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(vit_attn_probe_workspace_bytes(k.n_seqs, n_q_heads, k.capacity),
+                                dtype=torch.uint8, device=q.device)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp = k.struct()
+    st = lib.vit_attn_probe_scores(ctypes.byref(kp), _fptr(q, "q"), int(n_q_heads), sl, ctypes.c_float(scale),
+                                   ctypes.c_float(decay), _fptr(workspace, "workspace", "uint8"),
+                                   _fptr(scores, "scores"), _stream_handle(stream))
+    _lib.check("vit_attn_probe_scores", st)
+    return scores
+
+
+def vit_probe_select_evictions(scores, seq_len, n_sink, n_recent, n_evict, rows_out=None, n_out=None, stream=None):
+    """The cells to evict per sequence: (rows_out int64 [S, n_evict], -1
+    padded; n_out int32 [S]) from scores fp32 [S, capacity]."""
+    import torch
+
+    lib = _lib.load()
+    S, cap = scores.shape
+    if rows_out is None:
+        rows_out = torch.empty((S, max(1, n_evict)), dtype=torch.int64, device=scores.device)
+    if n_out is None:
+        n_out = torch.empty((S,), dtype=torch.int32, device=scores.device)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    st = lib.vit_probe_select_evictions(_fptr(scores, "scores"), int(S), int(cap), sl, int(n_sink), int(n_recent),
+                                        int(n_evict), _fptr(rows_out, "rows_out", "int64"),
+                                        _fptr(n_out, "n_out", "int32"), _stream_handle(stream))
+    _lib.check("vit_probe_select_evictions", st)
+    return rows_out[:, :n_evict], n_out
+
+
 def _event_handle(ev):
     if ev is None:
         return None
@@ -257,7 +302,7 @@ def _event_handle(ev):
 
 
 def vit_arm_kernel_events(start, stop):
-    """Make the kernel of the next decode or transcode call record
+    """Make the kernel of the next decode, transcode or probe call record
     torch.cuda.Event ``start``/``stop`` at its own dispatch start and end
     (both None disarms)."""
     st = _lib.load().vit_arm_kernel_events(_event_handle(start), _event_handle(stop))

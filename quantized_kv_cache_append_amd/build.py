@@ -32,6 +32,7 @@ SOURCES = {
     "decode_k2.hip": [],
     "decode_k3.hip": [],
     "reduce.hip": [],
+    "probe.hip": [],
     "vit_host.cpp": [],
 }
 

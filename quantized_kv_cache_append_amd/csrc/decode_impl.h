@@ -100,6 +100,25 @@ struct Lut {
   uint32_t lane4;         // 4 * lane: the lane's byte offset within an entry
 };
 
+// Fill the lane-replicated table (entry b = level pair (b & 15, b >> 4) of
+// lane l at word 64 b + l) with NTHREADS threads, a multiple of 256; lv is
+// kLevelBits[lane & 15], loaded early by the caller.  Word 4 (tid + NTHREADS
+// i) + j (j < 4) is entry e = (tid + NTHREADS i) / 16 of lane 4 (tid % 16) + j:
+// low level (tid / 16) % 16, high level tid / 256 + (NTHREADS / 256) i, the
+// same for the whole wave.
+template <int NTHREADS>
+__device__ inline void fill_rot4_lut(uint32_t* lut, int tid, uint32_t lv) {
+  static_assert(NTHREADS % 256 == 0 && NTHREADS <= 4096, "table fill: whole 256-thread groups");
+  const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(lv), (tid >> 4) & 15));
+  const int hb = __builtin_amdgcn_readfirstlane(tid >> 8);
+#pragma unroll
+  for (int i = 0; i < 4096 / NTHREADS; ++i) {
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lv), hb + (NTHREADS / 256) * i));
+    const uint32_t e = lo | (hi << 16);
+    *reinterpret_cast<u32x4*>(&lut[4 * (tid + NTHREADS * i)]) = u32x4{e, e, e, e};
+  }
+}
+
 // eight rot4 indices -> fp16 levels, element order (lo b0, hi b0, lo b1,
 // hi b1, ...).  One v_perm_b32 per byte builds its table address
 // 256 * byte + 4 * lane.
@@ -398,8 +417,8 @@ struct QOperands<4> {
 
 // K factors of the lane's tile row 16h + n16 for blocks 0..3: the fp16 block
 // scale (rot4: times the row norm); 1 for f16 planes.
-template <int KC, int VC, int NT>
-__device__ __forceinline__ void k_block_factors(const TileRegs<KC, VC, NT>& cur, float (&kf)[2][4]) {
+template <int KC, class Regs>
+__device__ __forceinline__ void k_block_factors(const Regs& cur, float (&kf)[2][4]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -461,7 +480,7 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
   // ---- S^T: lane (n16, qg) gets the 4 block partials of query row 4*nt + qg
   //      at tile row 16h + n16, for both halves h ----
   float kf[2][4];
-  k_block_factors(cur, kf);
+  k_block_factors<KC>(cur, kf);
   float s[NT][2];
   half8 bk[2][4];
 #pragma unroll
@@ -656,7 +675,7 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
 
   // ---- S^T: lane (n16, qg) gets queries 2qg + jj at tile row 16h + n16 ----
   float kf[2][4];
-  k_block_factors(cur, kf);
+  k_block_factors<KC>(cur, kf);
   float s[2][2];  // [query 2qg + jj][half]
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -796,7 +815,7 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
 
   // ---- S^T ----
   float kf[2][4];
-  k_block_factors(cur, kf);
+  k_block_factors<KC>(cur, kf);
   float s[4][2];  // [query 4qg + i][half]
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1020,19 +1039,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   load_slot(ta, wave);
   load_slot(tb, wave + kDecodeWaves);
 
-  if constexpr (kRot4) {
-    // word 4 (tid + 512 i) + j (j < 4) is entry e = tid / 16 + 32 i of lane
-    // 4 (tid % 16) + j: low level (e & 15) = (tid / 16) % 16, high level
-    // (e >> 4) = tid / 256 + 2 i, the same for the whole wave
-    const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(lv), (tid >> 4) & 15));
-    const int hb = __builtin_amdgcn_readfirstlane(tid >> 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lv), hb + 2 * i));
-      const uint32_t e = lo | (hi << 16);
-      *reinterpret_cast<u32x4*>(&lut[4 * (tid + 512 * i)]) = u32x4{e, e, e, e};
-    }
-  }
+  if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
   const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
   QOperands<NT> aq;
   // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query

@@ -1,0 +1,357 @@
+// Attention-probe cell scoring for sparse KV eviction, and the eviction
+// choice (Randozart/VITRIOL page: "How It Works -- Resident mode" runs a
+// probe graph -- a q.K softmax with exponential decay -- every 16 steps and
+// evicts the lowest-scored middle cells, sinks and recent cells protected).
+//
+// probe_logits_kernel: one 8-wave workgroup per (chunk, KV head, sequence).
+// Chunk c owns tiles c, c + n_chunks, ...; wave w takes the chunk's tile
+// slots w, w + 8, ..., prefetching the next one.  S^T = Q K^T runs on MFMA
+// exactly as in decode's 16-row layout (query rows, fp16 hi and lo parts in
+// two chained MFMAs, K codes exact in fp16, block scales in fp32); each
+// lane writes its base-2 logits and keeps an online (max, sum of 2^(s - max))
+// per query row; the waves merge into one partial per (query head, chunk).
+// probe_mass_kernel: merges a sequence's partials per query head, then for
+// every cell adds the query heads' probabilities and applies the decay.
+// select_kernel: one workgroup per sequence; a 4-pass radix select over the
+// middle cells' keys finds the n_evict-th smallest (score, cell), then a
+// pass in cell order writes the chosen cells.
+#include "decode_impl.h"
+
+namespace vit {
+
+// K registers of one 32-row tile for one lane (the K half of TileRegs).
+template <int KC>
+struct KTile {
+  u32x4 kd[2][units_per_block(KC)];
+  u32x2 ks[2];
+  uint32_t kn[2];
+};
+
+template <int KC>
+__device__ inline void load_k_tile(KTile<KC>& r, int t, int lane, const uint8_t* kbase, const uint16_t* ksb,
+                                   const uint16_t* knb) {
+  constexpr int KCB = units_per_block(KC);
+  const uint8_t* kt = kbase + static_cast<int64_t>(t) * tile_code_bytes(KC);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < KCB; ++c)
+      r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
+  const int64_t row0 = static_cast<int64_t>(t) * kTile + (lane & 15);
+  if constexpr (has_scales(KC)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.ks[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ksb + (row0 + 16 * h) * 4));
+  }
+  if constexpr (has_norms(KC)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.kn[h] = __builtin_nontemporal_load(knb + row0 + 16 * h);
+  }
+}
+
+template <int KC>
+__global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void probe_logits_kernel(
+    ProbeArgs a) {
+  constexpr int kThreads = 64 * kProbeWaves;
+  constexpr bool kRot4 = KC == ROT4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n16 = lane & 15;
+  const int qg = lane >> 4;
+  const int chunk = blockIdx.x;
+  const int head = blockIdx.y;
+  const int seq = blockIdx.z;
+  const int L = a.seq_len[seq];
+  const int G = a.gqa;
+  const int n_tiles = (L + kTile - 1) / kTile;
+
+  __shared__ float sq[16][kD];
+  __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
+  __shared__ float s_m[kProbeWaves][16], s_l[kProbeWaves][16];
+
+  const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
+  const uint8_t* kbase = a.kcodes + ph * a.capacity * row_code_bytes(KC);
+  const uint16_t* ksb = has_scales(KC) ? a.kscales + ph * a.capacity * 4 : nullptr;
+  const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
+
+  // this chunk's tiles; loads past the last are clamped to it (a chunk
+  // without tiles re-reads tile 0, which always exists, and processes none)
+  const int n_mine = chunk < n_tiles ? (n_tiles - 1 - chunk) / a.n_chunks + 1 : 0;
+  const int t_last = chunk < n_tiles ? chunk + a.n_chunks * (n_mine - 1) : 0;
+  auto tile_of = [&](int k) { return chunk + a.n_chunks * k; };
+  KTile<KC> ta, tb;
+  load_k_tile<KC>(ta, min(tile_of(wave), t_last), lane, kbase, ksb, knb);
+  load_k_tile<KC>(tb, min(tile_of(wave + kProbeWaves), t_last), lane, kbase, ksb, knb);
+
+  // ---- query rows of this KV head (G <= 16, zero rows past G) in LDS ----
+  [[maybe_unused]] uint32_t lv = 0;
+  if constexpr (kRot4) lv = kLevelBits[lane & 15];
+  const float* qhead = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
+  if (tid < 256) {
+    const int r = (8 * tid) >> 7, c0 = (8 * tid) & 127;
+    const float* src = qhead + static_cast<int64_t>(min(r, G - 1)) * kD + c0;
+    const float4v v0 = *reinterpret_cast<const float4v*>(src);
+    const float4v v1 = *reinterpret_cast<const float4v*>(src + 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = r < G ? (j < 4 ? v0[j] : v1[j - 4]) : 0.0f;
+      if constexpr (kRot4) v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
+      sq[r][c0 + j] = v;
+    }
+  }
+  if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
+  __syncthreads();
+  float qs = a.qscale;
+  if constexpr (kRot4) {
+    // rotate the query rows like the keys (unnormalised WHT; 1/128 folded in)
+    for (int h = 1; h < kD; h <<= 1) {
+      for (int i = tid; i < 16 * 64; i += kThreads) {
+        const int g = i >> 6, k = i & 63;
+        const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
+        const float x = sq[g][lo], y = sq[g][lo + h];
+        sq[g][lo] = x + y;
+        sq[g][lo + h] = x - y;
+      }
+      __syncthreads();
+    }
+    qs *= 1.0f / 128.0f;
+  }
+  // A operand of MFMA b: row n16 = query n16, chunk qg of block b, hi and lo
+  half8 aqh[4], aql[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = sq[n16][k_chan<KC>(qg, b, j)] * qs;
+    split8(v, aqh[b], aql[b]);
+  }
+  const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
+
+  float m_run[4], l_run[4];  // queries 4qg + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -__FLT_MAX__;  // finite: a fully masked first tile leaves l = 0, no NaN
+    l_run[i] = 0.0f;
+  }
+  float* lg = a.logits + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * a.capacity;
+  auto proc = [&](const KTile<KC>& cur, int t) {
+    float kf[2][4];
+    k_block_factors<KC>(cur, kf);
+    float s[4][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4v acc[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const half8 kb = unpack_k<KC>(cur.kd[h], b, lutr);
+        acc[b] = mfma16(aqh[b], kb, float4v{0.0f, 0.0f, 0.0f, 0.0f});
+        acc[b] = mfma16(aql[b], kb, acc[b]);
+      }
+      const int row = t * kTile + 16 * h + n16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v;
+        if constexpr (KC == F16) v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+        else v = (acc[0][i] * kf[h][0] + acc[1][i] * kf[h][1]) + (acc[2][i] * kf[h][2] + acc[3][i] * kf[h][3]);
+        s[i][h] = row < L ? v : -INFINITY;
+        if (row < L && 4 * qg + i < G) lg[static_cast<int64_t>(4 * qg + i) * a.capacity + row] = v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mnew = fmaxf(m_run[i], row16_max(fmaxf(s[i][0], s[i][1])));
+      l_run[i] = l_run[i] * __builtin_amdgcn_exp2f(m_run[i] - mnew) + __builtin_amdgcn_exp2f(s[i][0] - mnew) +
+                 __builtin_amdgcn_exp2f(s[i][1] - mnew);
+      m_run[i] = mnew;
+    }
+  };
+  // two buffers: wave slots w + 16 j in ta, w + 8 + 16 j in tb
+  for (int k = wave; k < n_mine; k += 2 * kProbeWaves) {
+    proc(ta, tile_of(k));
+    load_k_tile<KC>(ta, min(tile_of(k + 2 * kProbeWaves), t_last), lane, kbase, ksb, knb);
+    if (k + kProbeWaves >= n_mine) break;
+    proc(tb, tile_of(k + kProbeWaves));
+    load_k_tile<KC>(tb, min(tile_of(k + 3 * kProbeWaves), t_last), lane, kbase, ksb, knb);
+  }
+
+  // ---- merge the waves: one (max, sum) per query head of this chunk ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float l = row16_sum(l_run[i]);
+    if (n16 == 0) {
+      s_m[wave][4 * qg + i] = m_run[i];
+      s_l[wave][4 * qg + i] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -__FLT_MAX__;
+    for (int w = 0; w < kProbeWaves; ++w) M = fmaxf(M, s_m[w][tid]);
+    float Ls = 0.0f;
+    for (int w = 0; w < kProbeWaves; ++w)
+      if (s_l[w][tid] > 0.0f) Ls += s_l[w][tid] * __builtin_amdgcn_exp2f(s_m[w][tid] - M);
+    float* p = a.part + ((static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G + tid) * a.n_chunks + chunk) * 2;
+    p[0] = M;
+    p[1] = Ls;
+  }
+}
+
+// One workgroup per (1024-cell block, sequence): merge every query head's
+// chunk partials into (max, 1 / sum), then score <- decay * score + the sum
+// over the query heads of 2^(logit - max) / sum for each cell below L.
+__global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
+  const int tid = threadIdx.x;
+  const int seq = blockIdx.y;
+  const int L = a.seq_len[seq];
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 1024;
+  if (j0 >= L) return;  // uniform per workgroup
+  __shared__ float s_max[kProbeMaxHeads], s_inv[kProbeMaxHeads];
+  for (int h = tid; h < a.n_q_heads; h += 256) {
+    const float* p = a.part + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.n_chunks * 2;
+    float M = -__FLT_MAX__;
+    for (int c = 0; c < a.n_chunks; ++c)
+      if (p[2 * c + 1] > 0.0f) M = fmaxf(M, p[2 * c]);
+    float Ls = 0.0f;
+    for (int c = 0; c < a.n_chunks; ++c)
+      if (p[2 * c + 1] > 0.0f) Ls += p[2 * c + 1] * __builtin_amdgcn_exp2f(p[2 * c] - M);
+    s_max[h] = M;
+    s_inv[h] = 1.0f / Ls;  // every head sees L >= 1 cells: Ls >= 1
+  }
+  __syncthreads();
+  const float* lg = a.logits + static_cast<int64_t>(seq) * a.n_q_heads * a.capacity;
+  float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t j = j0 + r * 256 + tid;
+    if (j < L) {
+      float mass = 0.0f;
+      for (int h = 0; h < a.n_q_heads; ++h)
+        mass += __builtin_amdgcn_exp2f(lg[static_cast<int64_t>(h) * a.capacity + j] - s_max[h]) * s_inv[h];
+      sc[j] = a.decay * sc[j] + mass;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ select
+constexpr int kSelectThreads = 1024;
+
+// order-preserving key of an fp32 score (larger key = larger score; -0 and
+// +0 are one key; NaN is outside the domain)
+__device__ inline uint32_t score_key(float f) {
+  const uint32_t u = f == 0.0f ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// inclusive sum over the workgroup's threads of v (every thread gets its
+// prefix); `tot` receives the workgroup total
+__device__ inline int block_scan(int v, int tid, int* s_wave, int& tot) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kSelectThreads / 64; ++w) {
+    const int t = s_wave[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();  // s_wave is reused by the next call
+  tot = all;
+  return before + x;
+}
+
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
+  const int tid = threadIdx.x;
+  const int seq = blockIdx.x;
+  const int64_t L = a.seq_len[seq];
+  const int64_t lo = a.n_sink < L ? a.n_sink : L;
+  const int64_t hi = L - a.n_recent > lo ? L - a.n_recent : lo;
+  const int64_t k = (hi - lo) < a.n_evict ? (hi - lo) : a.n_evict;
+  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+  int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
+  for (int64_t i = k + tid; i < a.n_evict; i += kSelectThreads) out[i] = -1;
+  if (tid == 0) a.n_out[seq] = static_cast<int32_t>(k);
+  if (k == 0) return;  // uniform per workgroup
+
+  __shared__ int hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int64_t s_rank;
+  __shared__ int s_wave[kSelectThreads / 64];
+  // ---- radix select, 8 bits per pass from the top: the key T of the k-th
+  //      smallest middle cell and its rank among the cells with key T ----
+  uint32_t prefix = 0, mask = 0;
+  int64_t rank = k;  // 1-based, among the keys matching prefix under mask
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t j = lo + tid; j < hi; j += kSelectThreads) {
+      const uint32_t key = score_key(sc[j]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t before = 0;
+      int d = 0;
+      while (d < 255 && before + hist[d] < rank) before += hist[d++];
+      s_prefix = prefix | (static_cast<uint32_t>(d) << shift);
+      s_rank = rank - before;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    rank = s_rank;
+    mask |= 255u << shift;
+  }
+  // ---- in cell order: every key below T, and the first `rank` keys equal to T ----
+  const uint32_t T = prefix;
+  int64_t eq_seen = 0, taken = 0;
+  for (int64_t base = lo; base < hi && taken < k; base += kSelectThreads) {
+    const int64_t j = base + tid;
+    const uint32_t key = j < hi ? score_key(sc[j]) : 0xFFFFFFFFu;
+    const int is_eq = j < hi && key == T ? 1 : 0;
+    int n_eq;
+    const int eq_incl = block_scan(is_eq, tid, s_wave, n_eq);
+    const int sel = (j < hi && key < T) || (is_eq && eq_seen + eq_incl <= rank) ? 1 : 0;
+    int n_sel;
+    const int pos = block_scan(sel, tid, s_wave, n_sel);
+    if (sel && taken + pos - 1 < k) out[taken + pos - 1] = j;  // exactly k are selected; the bound is a guard
+    eq_seen += n_eq;
+    taken += n_sel;
+  }
+}
+
+#define VIT_PROBE_CASE(KC)                                                                                  \
+  case KC:                                                                                                  \
+    hipExtLaunchKernelGGL((probe_logits_kernel<KC>), grid, dim3(64 * kProbeWaves), 0, stream, ev.start,    \
+                          ev.stop, 0, args);                                                                \
+    break;
+
+hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream, const ProbeArgs& args,
+                        const KernelEvents& ev) {
+  const dim3 grid(static_cast<unsigned>(args.n_chunks), static_cast<unsigned>(args.n_kv_heads),
+                  static_cast<unsigned>(n_seqs));
+  switch (kc) {
+    VIT_PROBE_CASE(F16)
+    VIT_PROBE_CASE(Q8_0)
+    VIT_PROBE_CASE(Q4_0)
+    VIT_PROBE_CASE(ROT4)
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid(static_cast<unsigned>((max_seq_len + 1023) / 1024), static_cast<unsigned>(n_seqs));
+  hipLaunchKernelGGL(probe_mass_kernel, mgrid, dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(int n_seqs, hipStream_t stream, const SelectArgs& args) {
+  hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(kSelectThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace vit

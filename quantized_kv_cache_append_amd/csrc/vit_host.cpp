@@ -207,6 +207,89 @@ int vit_vbr_classic_next_step(int32_t n_tensors, const int32_t* codecs, const in
   return VIT_OK;
 }
 
+size_t vit_attn_probe_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int64_t capacity) {
+  if (n_seqs < 1 || n_seqs > VIT_MAX_SEQS || n_q_heads < 1 || n_q_heads > vit::kProbeMaxHeads || capacity < 1 ||
+      capacity > VIT_MAX_CAPACITY)
+    return 0;
+  const size_t logits = (static_cast<size_t>(n_seqs) * n_q_heads * capacity * sizeof(float) + 255) & ~size_t{255};
+  return logits + static_cast<size_t>(n_seqs) * n_q_heads * vit::kProbeMaxChunks * 2 * sizeof(float);
+}
+
+int vit_attn_probe_scores(const vit_kv_plane* k, const float* q, int32_t n_q_heads, const int64_t* seq_len,
+                          float scale, float decay, float* workspace, float* scores, void* stream) {
+  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
+  g_armed = vit::KernelEvents{};
+  int st = check_plane(k);
+  if (st != VIT_OK) return st;
+  if (k->side != VIT_SIDE_K) return VIT_E_ARG;
+  if (!q || !seq_len || !workspace || !scores) return VIT_E_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return VIT_E_ARG;
+  const int32_t gqa = n_q_heads / k->n_kv_heads;
+  if (gqa > VIT_MAX_GQA || n_q_heads > vit::kProbeMaxHeads) return VIT_E_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(decay)) return VIT_E_ARG;
+  int64_t max_len = 0;
+  for (int s = 0; s < k->n_seqs; ++s) {
+    if (seq_len[s] < 1) return VIT_E_ARG;
+    if (seq_len[s] > k->capacity) return VIT_E_CAPACITY;
+    if (seq_len[s] > max_len) max_len = seq_len[s];
+  }
+  if (!aligned(q, 16) || !aligned(workspace, 256) || !aligned(scores, 16)) return VIT_E_ALIGN;
+
+  vit::ProbeArgs a{};
+  a.kcodes = static_cast<const uint8_t*>(k->codes);
+  a.kscales = k->scales;
+  a.knorms = k->norms;
+  a.q = q;
+  a.logits = workspace;
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                    ((static_cast<size_t>(k->n_seqs) * n_q_heads * k->capacity * sizeof(float) + 255) &
+                                     ~size_t{255}));
+  a.scores = scores;
+  a.capacity = k->capacity;
+  a.n_kv_heads = k->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.gqa = gqa;
+  // chunks per (sequence, KV head): about two 8-wave workgroups per compute
+  // unit in all, at most one per tile
+  const int64_t units = static_cast<int64_t>(k->n_seqs) * k->n_kv_heads;
+  int64_t chunks = (512 + units - 1) / units;
+  const int64_t tiles = (max_len + 31) / 32;
+  if (chunks > tiles) chunks = tiles;
+  if (chunks > vit::kProbeMaxChunks) chunks = vit::kProbeMaxChunks;
+  a.n_chunks = static_cast<int32_t>(chunks < 1 ? 1 : chunks);
+  a.qscale = scale * 1.4426950408889634f;
+  a.decay = decay;
+  load_signs(k, a.ksigns);
+  for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
+  return vit::launch_probe(k->codec, k->n_seqs, static_cast<int>(max_len), static_cast<hipStream_t>(stream), a, ev) ==
+                 hipSuccess
+             ? VIT_OK
+             : VIT_E_HIP;
+}
+
+int vit_probe_select_evictions(const float* scores, int32_t n_seqs, int64_t capacity, const int64_t* seq_len,
+                               int64_t n_sink, int64_t n_recent, int32_t n_evict, int64_t* rows_out, int32_t* n_out,
+                               void* stream) {
+  if (!scores || !seq_len || !n_out) return VIT_E_ARG;
+  if (n_seqs < 1 || capacity < 1 || n_sink < 0 || n_recent < 0 || n_evict < 0) return VIT_E_ARG;
+  if (n_evict > 0 && !rows_out) return VIT_E_ARG;
+  if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
+  if (capacity > VIT_MAX_CAPACITY) return VIT_E_UNSUPPORTED;
+  for (int s = 0; s < n_seqs; ++s)
+    if (seq_len[s] < 0 || seq_len[s] > capacity) return VIT_E_CAPACITY;
+  if (!aligned(scores, 4) || (rows_out && !aligned(rows_out, 8)) || !aligned(n_out, 4)) return VIT_E_ALIGN;
+  vit::SelectArgs a{};
+  a.scores = scores;
+  a.rows_out = rows_out;
+  a.n_out = n_out;
+  a.capacity = capacity;
+  a.n_sink = n_sink;
+  a.n_recent = n_recent;
+  a.n_evict = n_evict;
+  for (int s = 0; s < n_seqs; ++s) a.seq_len[s] = seq_len[s];
+  return vit::launch_select(n_seqs, static_cast<hipStream_t>(stream), a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+}
+
 size_t vit_attn_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t head_dim, int32_t n_splits) {
   if (head_dim != VIT_HEAD_DIM || n_seqs < 1 || n_q_heads < 1 || n_splits < 1 || n_splits > VIT_MAX_SPLITS)
     return 0;

@@ -37,6 +37,44 @@ struct TranscodeArgs {
   int64_t n_rows[kMaxSeqs];    // rows 0 .. n_rows[s]-1 of sequence s
 };
 
+// Attention-probe cell scores: per-cell logits of the current token's query
+// rows and per-chunk softmax partials (probe_logits_kernel), then the per-cell
+// mass with exponential decay (probe_mass_kernel).
+constexpr int kProbeWaves = 8;
+constexpr int kProbeMaxChunks = 64;
+constexpr int kProbeMaxHeads = 256;  // n_q_heads
+struct ProbeArgs {
+  const uint8_t* kcodes;
+  const uint16_t* kscales;
+  const uint16_t* knorms;
+  const float* q;        // [S][Hq][128]
+  float* logits;         // [S][Hq][capacity], base-2 scaled
+  float* part;           // [S][Hq][n_chunks][2]: (max, sum of 2^(logit - max))
+  float* scores;         // [S][capacity]
+  int64_t capacity;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t gqa;
+  int32_t n_chunks;
+  float qscale;          // softmax scale * log2(e)
+  float decay;
+  uint32_t ksigns[4];
+  int32_t seq_len[kMaxSeqs];
+};
+
+// The cells to evict: a radix select of the n_evict lowest (score, cell)
+// keys among each sequence's middle cells, then their compaction in cell order.
+struct SelectArgs {
+  const float* scores;   // [S][capacity]
+  int64_t* rows_out;     // [S][n_evict]
+  int32_t* n_out;        // [S]
+  int64_t capacity;
+  int64_t n_sink;
+  int64_t n_recent;
+  int32_t n_evict;
+  int64_t seq_len[kMaxSeqs];
+};
+
 struct DecodeArgs {
   const uint8_t* kcodes;
   const uint16_t* kscales;
@@ -89,5 +127,10 @@ hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const
 hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
+// both probe kernels (logits over grid (n_chunks, Hkv, S), then the mass);
+// ev brackets the logits kernel
+hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream, const ProbeArgs& args,
+                        const KernelEvents& ev);
+hipError_t launch_select(int n_seqs, hipStream_t stream, const SelectArgs& args);
 
 }  // namespace vit

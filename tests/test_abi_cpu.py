@@ -234,6 +234,45 @@ def test_classic_next_step_validation(lib):
     assert call([2, 2], [0, 1]) == _lib.VIT_OK and t.value == -1  # nothing left to degrade
 
 
+def test_probe_validation(lib):
+    """Attention-probe scores: K plane only, G <= 16, 1 <= seq_len <= capacity,
+    finite scale and decay, aligned buffers (no compute: every case fails)."""
+    K = _plane(side=0)
+
+    def call(k=K, hq=4, seq_len=(10, 10), scale=0.088, decay=0.9, ws=FAKE, scores=FAKE, q=FAKE):
+        arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+        return lib.vit_attn_probe_scores(ctypes.byref(k), q, hq, arr, scale, decay, ws, scores, None)
+
+    assert call(k=_plane(side=1)) == _lib.VIT_E_ARG
+    assert call(hq=3) == _lib.VIT_E_ARG
+    assert call(hq=34) == _lib.VIT_E_UNSUPPORTED          # G = 17
+    assert call(seq_len=(0, 10)) == _lib.VIT_E_ARG
+    assert call(seq_len=(513, 10)) == _lib.VIT_E_CAPACITY
+    assert call(scale=float("inf")) == _lib.VIT_E_ARG
+    assert call(decay=float("nan")) == _lib.VIT_E_ARG
+    assert call(ws=None) == _lib.VIT_E_ARG
+    assert call(ws=FAKE + 16) == _lib.VIT_E_ALIGN
+    assert call(scores=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert lib.vit_attn_probe_workspace_bytes(2, 4, 512) == 2 * 4 * 512 * 4 + 2 * 4 * 64 * 2 * 4
+    assert lib.vit_attn_probe_workspace_bytes(2, 300, 512) == 0
+
+
+def test_select_evictions_validation(lib):
+    def call(seq_len=(10, 10), ns=2, nr=2, ne=3, rows=FAKE, nout=FAKE, scores=FAKE, cap=512):
+        arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+        return lib.vit_probe_select_evictions(scores, len(seq_len), cap, arr, ns, nr, ne, rows, nout, None)
+
+    assert call(seq_len=(513, 1)) == _lib.VIT_E_CAPACITY
+    assert call(seq_len=(-1, 1)) == _lib.VIT_E_CAPACITY
+    assert call(ns=-1) == _lib.VIT_E_ARG
+    assert call(ne=-2) == _lib.VIT_E_ARG
+    assert call(rows=None) == _lib.VIT_E_ARG
+    assert call(nout=None) == _lib.VIT_E_ARG
+    assert call(scores=None) == _lib.VIT_E_ARG
+    assert call(rows=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert call(seq_len=(1,) * 65) == _lib.VIT_E_UNSUPPORTED
+
+
 def test_reduce_validation(lib):
     V = _plane(side=1)
     r = lib.vit_attn_splitk_reduce

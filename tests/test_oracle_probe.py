@@ -62,6 +62,15 @@ def test_probe_mass_is_the_decode_weighting():
     assert np.allclose(out.sum(axis=0), m @ vd, rtol=1e-10, atol=1e-10)
 
 
+def test_cell_mass_sums_over_kv_heads():
+    q = _rows(13, 6) * 0.2            # 6 query heads on 3 KV heads (G = 2)
+    k = np.stack([_rows(14 + h, 40) for h in range(3)])
+    m = probe.cell_mass(q, k, "q4_0", SCALE)
+    assert m.sum() == pytest.approx(6.0, rel=1e-12)
+    per_head = [probe.probe_mass(q[2 * h:2 * h + 2], k[h], "q4_0", SCALE) for h in range(3)]
+    assert np.allclose(m, per_head[0] + per_head[1] + per_head[2], rtol=0, atol=0)
+
+
 def test_decay_update_closed_form():
     prev0 = np.array([0.5, 2.0, 0.0])
     mass = np.array([0.25, 0.0, 1.0])
