@@ -59,6 +59,7 @@ D = 128
 KERNEL_SOURCES = {
     "decode": ("decode_impl.h", "decode_k*.hip", "vit_device.h", "vit_launch.h"),
     "transcode": ("append.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
+    "probe_logits": ("probe.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
 }
 TRANSCODE_PAIRS = ("f16:q8_0", "f16:q4_0", "f16:rot4", "q8_0:q4_0", "q8_0:rot4")
 
@@ -380,6 +381,157 @@ def cpu_baseline_transcode(r, budget_s=15.0):
                        f"{n}-row calls, {el:.1f} s on 1 thread; step = {r['rows']} rows")}
 
 
+def run_probe(args):
+    """One attention-probe scoring event over a workload's K plane (layer 0):
+    per-cell softmax mass of every query head with decay 0.9, then the
+    eviction choice (4 sink and 256 recent cells protected, L/16 evicted).
+    Cold-cache replicas as for decode."""
+    import numpy as np
+    import torch
+
+    import quantized_kv_cache_append_amd as vit
+    import synth
+
+    cfgno = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[cfgno]
+    S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
+    kc = synth.codec_map(cfgno)[0][0]
+    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED2026 + 99 + cfgno)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    k_bytes = S * H * L * _row_bytes(kc)
+    replicas = args.replicas if args.replicas else min(256, max(1, math.ceil((1 << 30) / (S * H * cap * _row_bytes(kc)))))
+    planes = [vit.KVPlane(kc, "k", S, H, cap, ks)]
+    sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda")) if cfg["dist"] == "lognormal" else None
+    for p0 in range(0, L, 16384):
+        n = min(16384, L - p0)
+        vit.vit_kv_append_quant(planes[0], _device_rows(torch, gen, (S, n, H, D), cfg["dist"], sc), [p0] * S)
+    for _ in range(replicas - 1):
+        k = vit.KVPlane.like(planes[0])
+        k.copy_from(planes[0])
+        planes.append(k)
+    q = _device_rows(torch, gen, (S, Hq, D), cfg["dist"])
+    scores = torch.zeros((S, cap), dtype=torch.float32, device="cuda")
+    ws = torch.empty(vit.vit_attn_probe_workspace_bytes(S, Hq, cap), dtype=torch.uint8, device="cuda")
+    n_evict = L // 16
+    rows_out = torch.empty((S, n_evict), dtype=torch.int64, device="cuda")
+    n_out = torch.empty((S,), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    print(f"# probe {cfg['name']}: K={kc} S={S} Hq={Hq} Hkv={H} L={L} replicas={replicas}", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    calls = [(vit.prepare_probe(kp, q, Hq, [L] * S, scores, ws, decay=0.9, stream=stream),
+              vit.prepare_select(scores, [L] * S, 4, 256, n_evict, rows_out, n_out, stream=stream)) for kp in planes]
+    arm = vit.vit_arm_kernel_events
+
+    def step(i, ev=None):
+        pr, sel = calls[i % replicas]
+        if ev is not None:
+            arm(ev[0], ev[1])
+        pr()
+        sel()
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    assert np.isfinite(scores.cpu().numpy()).all(), "non-finite probe scores"
+    per_launch = k_bytes + S * Hq * L * 4  # K read + logits written
+    return dict(cfg=cfg, cfgno=cfgno, kc=kc, S=S, Hq=Hq, H=H, L=L, replicas=replicas, ms_per_step=ms_per_step,
+                mean_ms=float(np.mean(ms)), min_ms=float(np.min(ms)), per_launch_bytes=per_launch,
+                achieved_gbs=per_launch / (float(np.mean(ms)) * 1e-3) / 1e9, n_evict=n_evict)
+
+
+def cpu_baseline_probe(r, budget_s=15.0):
+    """oracle.probe (cell_mass, decay_update, select_evictions) as it stands,
+    over one sequence's first 8192 cells, scaled to the step."""
+    import numpy as np
+
+    from oracle import probe
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    cfgno, H, Hq, L, kc = r["cfgno"], r["H"], r["Hq"], r["L"], r["kc"]
+    n = min(L, 8192)
+    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
+    keys = np.stack([synth.kv_rows(cfgno, "k", 0, 0, h, 0, n) for h in range(H)])
+    q = synth.q_rows(cfgno, 0, 0, Hq)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        mass = probe.cell_mass(q, keys, kc, 1.0 / math.sqrt(D), ks)
+        sc = probe.decay_update(np.zeros(n), mass, 0.9)
+        probe.select_evictions(sc, n, 4, 256, n // 16)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    per_seq = el / done * (L / n)
+    return {"value": 1.0 / (per_seq * r["S"]), "unit": "scoring events/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} passes over sequence 0 ({H} KV heads x {n} cells), {el:.1f} s on 1 thread, scaled "
+                       f"to {r['S']} sequences x {L} cells; pass = oracle cell mass of {Hq} query heads (its key "
+                       "quantization included) + decay + eviction choice")}
+
+
+def main_probe(args):
+    r = run_probe(args)
+    line = {
+        "metric": "attention-probe scoring events per second + effective K-read GB/s (% of HBM peak), 1 GPU",
+        "value": round(1e3 / r["ms_per_step"], 1),
+        "unit": "scoring events/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{r['kc']} K codes, fp16 MFMA operands (hi+lo query), fp32 logits and masses",
+        "data": "synthetic (seeded device normals shaped like the workload; no model weights or dataset)",
+        "config": {"workload": f"probe_{r['cfg']['name']}", "n_seqs": r["S"], "n_q_heads": r["Hq"],
+                   "n_kv_heads": r["H"], "head_dim": D, "context": r["L"], "k_codec": r["kc"], "decay": 0.9,
+                   "n_sink": 4, "n_recent": 256, "n_evict": r["n_evict"], "cold_cache_replicas": r["replicas"],
+                   "launch": "eager (pre-marshalled C calls)"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "probe_logits_kernel",
+            "achieved": round(r["achieved_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("probe_logits", r["cfg"]["name"]),
+            "algorithmic_bytes_per_launch": r["per_launch_bytes"],
+            "mean_launch_ms": round(r["mean_ms"], 5),
+            "min_launch_ms": round(r["min_ms"], 5),
+        },
+        "kernel_source_hash": kernel_source_hash("probe_logits"),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_probe(r, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main_transcode(args):
     r = run_transcode(args)
     tag = f"{r['src_c']}_to_{r['dst_c']}_{r['side']}"
@@ -526,16 +678,17 @@ def _counter_kib(d, counter, name_part):
     return sum(v) / len(v), len(v)
 
 
-def summarize_profiles(kind, workload, prof, commands):
+def summarize_profiles(kind, workload, prof, commands, subdir=None):
     """Turn one workload's rocprofv3 runs into the committed summaries:
     profiles/<kind>_<workload>_kernel_stats.md (kernel-trace statistics beside
     the bench line of the same run) and profiles/<kind>_<workload>_traffic.json
     (HBM bytes per launch of <kind>_kernel from FETCH_SIZE and WRITE_SIZE,
     each scaled by what the counter reads for a plain 1 GiB device copy)."""
     kernel = f"{kind}_kernel"
-    stats = _read_csv(os.path.join(prof, workload, "trace", "run_kernel_stats.csv"))
+    subdir = subdir or workload
+    stats = _read_csv(os.path.join(prof, subdir, "trace", "run_kernel_stats.csv"))
     def bench_line(name):
-        with open(os.path.join(prof, workload, name)) as f:
+        with open(os.path.join(prof, subdir, name)) as f:
             return json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
 
     line = bench_line("bench.json")          # plain run (no profiler attached)
@@ -544,8 +697,8 @@ def summarize_profiles(kind, workload, prof, commands):
     copy_write, _ = _counter_kib(os.path.join(prof, "copy_write"), "WRITE_SIZE", "copy")
     f_fetch = (1 << 30) / (copy_fetch * 1024)
     f_write = (1 << 30) / (copy_write * 1024)
-    fetch, n_f = _counter_kib(os.path.join(prof, workload, "fetch"), "FETCH_SIZE", kernel)
-    write, n_w = _counter_kib(os.path.join(prof, workload, "write"), "WRITE_SIZE", kernel)
+    fetch, n_f = _counter_kib(os.path.join(prof, subdir, "fetch"), "FETCH_SIZE", kernel)
+    write, n_w = _counter_kib(os.path.join(prof, subdir, "write"), "WRITE_SIZE", kernel)
     hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
     alg = line["roofline"]["algorithmic_bytes_per_launch"]
     dec = [r for r in stats if kernel in r["Name"]]
@@ -610,6 +763,8 @@ def main():
     ap.add_argument("--transcode", default=None, choices=TRANSCODE_PAIRS,
                     help="time a VBR degrade step (vit_kv_transcode) of one ladder-slot tensor instead")
     ap.add_argument("--side", default="k", choices=("k", "v"), help="plane side for --transcode")
+    ap.add_argument("--probe", action="store_true",
+                    help="time an attention-probe scoring event (+ eviction choice) on --workload's K plane instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps as HIP graph replays (one captured graph per replica)")
@@ -624,21 +779,26 @@ def main():
             sc, dc = args.transcode.split(":")
             w = f"{sc}_to_{dc}_{args.side}"
             b = f"python3 bench.py --transcode {args.transcode} --side {args.side}"
+        elif args.probe:
+            kind = "probe_logits"
+            w = args.workload
+            b = f"python3 bench.py --probe --workload {args.workload}"
         else:
             kind = "decode"
             w = profile_tag(args.workload, args.q_len)
             b = f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
-        cmds = [f"{b} --no-cpu-baseline > PROF/{w}/bench.json",
-                f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{w}/trace -o run -- "
-                f"{b} --no-cpu-baseline > PROF/{w}/bench_traced.json",
-                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/{w}/fetch -o run -- "
+        d = f"probe_{w}" if args.probe else w  # directory under PROF
+        cmds = [f"{b} --no-cpu-baseline > PROF/{d}/bench.json",
+                f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{d}/trace -o run -- "
+                f"{b} --no-cpu-baseline > PROF/{d}/bench_traced.json",
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/{d}/fetch -o run -- "
                 f"{b} --steps 20 --warmup 3 --no-cpu-baseline",
-                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/{w}/write -o run -- "
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/{d}/write -o run -- "
                 f"{b} --steps 20 --warmup 3 --no-cpu-baseline",
                 "rocprofv3 --pmc FETCH_SIZE --output-format csv -d PROF/copy_fetch -o run -- python3 bench.py --calib-copy 4",
                 "rocprofv3 --pmc WRITE_SIZE --output-format csv -d PROF/copy_write -o run -- python3 bench.py --calib-copy 4",
                 f"{b} --summarize PROF"]
-        summarize_profiles(kind, w, args.summarize, cmds)
+        summarize_profiles(kind, w, args.summarize, cmds, subdir=d)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -650,6 +810,9 @@ def main():
         return
     if args.transcode:
         main_transcode(args)
+        return
+    if args.probe:
+        main_probe(args)
         return
     r = run_gpu(args)
     cfg = r["cfg"]

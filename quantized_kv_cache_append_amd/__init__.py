@@ -339,6 +339,25 @@ def prepare_transcode(src, dst, n_rows, stream=None):
     return _Prepared("vit_kv_transcode", lib.vit_kv_transcode, args, (sp, dp, nr, src, dst))
 
 
+def prepare_probe(k, q, n_q_heads, seq_len, scores, workspace, scale=None, decay=1.0, stream=None):
+    lib = _lib.load()
+    scale = 1.0 / np.sqrt(HEAD_DIM) if scale is None else scale
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp = k.struct()
+    args = (ctypes.byref(kp), _fptr(q, "q"), int(n_q_heads), sl, ctypes.c_float(scale), ctypes.c_float(decay),
+            _fptr(workspace, "workspace", "uint8"), _fptr(scores, "scores"), _stream_handle(stream))
+    return _Prepared("vit_attn_probe_scores", lib.vit_attn_probe_scores, args, (kp, sl, q, workspace, scores, k))
+
+
+def prepare_select(scores, seq_len, n_sink, n_recent, n_evict, rows_out, n_out, stream=None):
+    lib = _lib.load()
+    S, cap = scores.shape
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    args = (_fptr(scores, "scores"), int(S), int(cap), sl, int(n_sink), int(n_recent), int(n_evict),
+            _fptr(rows_out, "rows_out", "int64"), _fptr(n_out, "n_out", "int32"), _stream_handle(stream))
+    return _Prepared("vit_probe_select_evictions", lib.vit_probe_select_evictions, args, (sl, scores, rows_out, n_out))
+
+
 def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, scale=None, n_splits=1,
                    workspace=None, stream=None, q_len=None):
     lib = _lib.load()
