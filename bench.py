@@ -417,11 +417,13 @@ def run_probe(args):
     n_evict = L // 16
     rows_out = torch.empty((S, n_evict), dtype=torch.int64, device="cuda")
     n_out = torch.empty((S,), dtype=torch.int32, device="cuda")
+    sel_ws = torch.empty(vit.vit_probe_select_workspace_bytes(S), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     print(f"# probe {cfg['name']}: K={kc} S={S} Hq={Hq} Hkv={H} L={L} replicas={replicas}", file=sys.stderr, flush=True)
     stream = torch.cuda.Stream()
     calls = [(vit.prepare_probe(kp, q, Hq, [L] * S, scores, ws, decay=0.9, stream=stream),
-              vit.prepare_select(scores, [L] * S, 4, 256, n_evict, rows_out, n_out, stream=stream)) for kp in planes]
+              vit.prepare_select(scores, [L] * S, 4, 256, n_evict, rows_out, n_out, sel_ws, stream=stream))
+             for kp in planes]
     arm = vit.vit_arm_kernel_events
 
     def step(i, ev=None):

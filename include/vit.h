@@ -310,10 +310,17 @@ int vit_attn_probe_scores(const vit_kv_plane *k, const float *q, int32_t n_q_hea
  *  n_sink, n_recent, n_evict  >= 0.
  *  rows_out   int64 [n_seqs][n_evict] (device): the chosen cells, then -1.
  *  n_out      int32 [n_seqs] (device): how many were chosen,
- *             min(n_evict, middle cells). */
+ *             min(n_evict, middle cells).
+ *  workspace  vit_probe_select_workspace_bytes(n_seqs) bytes (device).
+ * Scores are finite (NaN is outside the domain); -0 and +0 are equal. */
 int vit_probe_select_evictions(const float *scores, int32_t n_seqs, int64_t capacity, const int64_t *seq_len,
                                int64_t n_sink, int64_t n_recent, int32_t n_evict, int64_t *rows_out,
-                               int32_t *n_out, void *stream);
+                               int32_t *n_out, void *workspace, void *stream);
+
+/* Workspace bytes of vit_probe_select_evictions (radix histograms and block
+ * counts; 256-B aligned; no state is kept between calls).  0 for invalid
+ * n_seqs. */
+size_t vit_probe_select_workspace_bytes(int32_t n_seqs);
 
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host

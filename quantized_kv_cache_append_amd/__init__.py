@@ -28,6 +28,7 @@ __all__ = [
     "vit_attn_workspace_bytes",
     "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_splitk_reduce",
     "vit_attn_probe_workspace_bytes", "vit_attn_probe_scores", "vit_probe_select_evictions",
+    "vit_probe_select_workspace_bytes",
     "vit_arm_kernel_events",
 ]
 
@@ -273,7 +274,12 @@ def vit_attn_probe_scores(k, q, n_q_heads, seq_len, scores, scale=None, decay=1.
     return scores
 
 
-def vit_probe_select_evictions(scores, seq_len, n_sink, n_recent, n_evict, rows_out=None, n_out=None, stream=None):
+def vit_probe_select_workspace_bytes(n_seqs):
+    return int(_lib.load().vit_probe_select_workspace_bytes(int(n_seqs)))
+
+
+def vit_probe_select_evictions(scores, seq_len, n_sink, n_recent, n_evict, rows_out=None, n_out=None,
+                               workspace=None, stream=None):
     """The cells to evict per sequence: (rows_out int64 [S, n_evict], -1
     padded; n_out int32 [S]) from scores fp32 [S, capacity]."""
     import torch
@@ -284,10 +290,13 @@ def vit_probe_select_evictions(scores, seq_len, n_sink, n_recent, n_evict, rows_
         rows_out = torch.empty((S, max(1, n_evict)), dtype=torch.int64, device=scores.device)
     if n_out is None:
         n_out = torch.empty((S,), dtype=torch.int32, device=scores.device)
+    if workspace is None:
+        workspace = torch.empty(vit_probe_select_workspace_bytes(S), dtype=torch.uint8, device=scores.device)
     sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
     st = lib.vit_probe_select_evictions(_fptr(scores, "scores"), int(S), int(cap), sl, int(n_sink), int(n_recent),
                                         int(n_evict), _fptr(rows_out, "rows_out", "int64"),
-                                        _fptr(n_out, "n_out", "int32"), _stream_handle(stream))
+                                        _fptr(n_out, "n_out", "int32"), _fptr(workspace, "workspace", "uint8"),
+                                        _stream_handle(stream))
     _lib.check("vit_probe_select_evictions", st)
     return rows_out[:, :n_evict], n_out
 
@@ -349,13 +358,15 @@ def prepare_probe(k, q, n_q_heads, seq_len, scores, workspace, scale=None, decay
     return _Prepared("vit_attn_probe_scores", lib.vit_attn_probe_scores, args, (kp, sl, q, workspace, scores, k))
 
 
-def prepare_select(scores, seq_len, n_sink, n_recent, n_evict, rows_out, n_out, stream=None):
+def prepare_select(scores, seq_len, n_sink, n_recent, n_evict, rows_out, n_out, workspace, stream=None):
     lib = _lib.load()
     S, cap = scores.shape
     sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
     args = (_fptr(scores, "scores"), int(S), int(cap), sl, int(n_sink), int(n_recent), int(n_evict),
-            _fptr(rows_out, "rows_out", "int64"), _fptr(n_out, "n_out", "int32"), _stream_handle(stream))
-    return _Prepared("vit_probe_select_evictions", lib.vit_probe_select_evictions, args, (sl, scores, rows_out, n_out))
+            _fptr(rows_out, "rows_out", "int64"), _fptr(n_out, "n_out", "int32"),
+            _fptr(workspace, "workspace", "uint8"), _stream_handle(stream))
+    return _Prepared("vit_probe_select_evictions", lib.vit_probe_select_evictions, args,
+                     (sl, scores, rows_out, n_out, workspace))
 
 
 def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, scale=None, n_splits=1,

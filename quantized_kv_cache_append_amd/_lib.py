@@ -34,6 +34,7 @@ EXPORTS = (
     "vit_attn_probe_workspace_bytes",
     "vit_attn_probe_scores",
     "vit_probe_select_evictions",
+    "vit_probe_select_workspace_bytes",
     "vit_arm_kernel_events",
     "vit_status_string",
 )
@@ -102,8 +103,10 @@ def load():
     lib.vit_attn_probe_workspace_bytes.restype = sz
     lib.vit_attn_probe_scores.argtypes = [plane_p, vp, i32, P(i64), f32, f32, vp, vp, vp]
     lib.vit_attn_probe_scores.restype = ctypes.c_int
-    lib.vit_probe_select_evictions.argtypes = [vp, i32, i64, P(i64), i64, i64, i32, vp, vp, vp]
+    lib.vit_probe_select_evictions.argtypes = [vp, i32, i64, P(i64), i64, i64, i32, vp, vp, vp, vp]
     lib.vit_probe_select_evictions.restype = ctypes.c_int
+    lib.vit_probe_select_workspace_bytes.argtypes = [i32]
+    lib.vit_probe_select_workspace_bytes.restype = sz
     lib.vit_status_string.argtypes = [ctypes.c_int]
     lib.vit_status_string.restype = ctypes.c_char_p
     _lib = lib

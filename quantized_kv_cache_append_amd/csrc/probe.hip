@@ -12,9 +12,10 @@
 // per query row; the waves merge into one partial per (query head, chunk).
 // probe_mass_kernel: merges a sequence's partials per query head, then for
 // every cell adds the query heads' probabilities and applies the decay.
-// select_kernel: one workgroup per sequence; a 4-pass radix select over the
-// middle cells' keys finds the n_evict-th smallest (score, cell), then a
-// pass in cell order writes the chosen cells.
+// select_*_kernel: a 3-pass radix select over the middle cells' keys, by
+// blocks of cells, finds the n_evict-th smallest (score, cell); then each
+// block writes its chosen cells in cell order after those of the blocks
+// before it.
 #include "decode_impl.h"
 
 namespace vit {
@@ -206,16 +207,25 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 1024;
   if (j0 >= L) return;  // uniform per workgroup
   __shared__ float s_max[kProbeMaxHeads], s_inv[kProbeMaxHeads];
-  for (int h = tid; h < a.n_q_heads; h += 256) {
+  // one wave per query head, one lane per chunk partial (n_chunks <= 64)
+  const int lane = tid & 63;
+  for (int h = tid >> 6; h < a.n_q_heads; h += 4) {
     const float* p = a.part + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.n_chunks * 2;
-    float M = -__FLT_MAX__;
-    for (int c = 0; c < a.n_chunks; ++c)
-      if (p[2 * c + 1] > 0.0f) M = fmaxf(M, p[2 * c]);
-    float Ls = 0.0f;
-    for (int c = 0; c < a.n_chunks; ++c)
-      if (p[2 * c + 1] > 0.0f) Ls += p[2 * c + 1] * __builtin_amdgcn_exp2f(p[2 * c] - M);
-    s_max[h] = M;
-    s_inv[h] = 1.0f / Ls;  // every head sees L >= 1 cells: Ls >= 1
+    float m = -__FLT_MAX__, l = 0.0f;
+    if (lane < a.n_chunks) {
+      m = p[2 * lane];
+      l = p[2 * lane + 1];
+    }
+    float M = l > 0.0f ? m : -__FLT_MAX__;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    float Ls = l > 0.0f ? l * __builtin_amdgcn_exp2f(m - M) : 0.0f;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) Ls += __shfl_xor(Ls, d, 64);
+    if (lane == 0) {
+      s_max[h] = M;
+      s_inv[h] = 1.0f / Ls;  // every head sees L >= 1 cells: Ls >= 1
+    }
   }
   __syncthreads();
   const float* lg = a.logits + static_cast<int64_t>(seq) * a.n_q_heads * a.capacity;
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
 }
 
 // ------------------------------------------------------------------ select
-constexpr int kSelectThreads = 1024;
+constexpr int kSelectThreads = 256;
 
 // order-preserving key of an fp32 score (larger key = larger score; -0 and
 // +0 are one key; NaN is outside the domain)
@@ -255,6 +265,7 @@ __device__ inline int block_scan(int v, int tid, int* s_wave, int& tot) {
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
+#pragma unroll
   for (int w = 0; w < kSelectThreads / 64; ++w) {
     const int t = s_wave[w];
     before += w < wave ? t : 0;
@@ -265,60 +276,179 @@ __device__ inline int block_scan(int v, int tid, int* s_wave, int& tot) {
   return before + x;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-  const int tid = threadIdx.x;
-  const int seq = blockIdx.x;
-  const int64_t L = a.seq_len[seq];
-  const int64_t lo = a.n_sink < L ? a.n_sink : L;
-  const int64_t hi = L - a.n_recent > lo ? L - a.n_recent : lo;
-  const int64_t k = (hi - lo) < a.n_evict ? (hi - lo) : a.n_evict;
-  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
-  int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
-  for (int64_t i = k + tid; i < a.n_evict; i += kSelectThreads) out[i] = -1;
-  if (tid == 0) a.n_out[seq] = static_cast<int32_t>(k);
-  if (k == 0) return;  // uniform per workgroup
+// digit p of a key: bits 31..21, 20..10, 9..0
+__device__ constexpr int kDigitShift[3] = {21, 10, 0};
+__device__ constexpr uint32_t kDigitMask[3] = {0x7FFu, 0x7FFu, 0x3FFu};
 
-  __shared__ int hist[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_rank;
-  __shared__ int s_wave[kSelectThreads / 64];
-  // ---- radix select, 8 bits per pass from the top: the key T of the k-th
-  //      smallest middle cell and its rank among the cells with key T ----
-  uint32_t prefix = 0, mask = 0;
-  int64_t rank = k;  // 1-based, among the keys matching prefix under mask
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelectThreads) hist[i] = 0;
-    __syncthreads();
-    for (int64_t j = lo + tid; j < hi; j += kSelectThreads) {
-      const uint32_t key = score_key(sc[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+// A sequence's middle cells and the number to choose.
+struct SelectRange {
+  int64_t lo, hi, k;
+};
+__device__ inline SelectRange select_range(const SelectArgs& a, int seq) {
+  const int64_t L = a.seq_len[seq];
+  SelectRange r;
+  r.lo = a.n_sink < L ? a.n_sink : L;
+  r.hi = L - a.n_recent > r.lo ? L - a.n_recent : r.lo;
+  r.k = (r.hi - r.lo) < a.n_evict ? (r.hi - r.lo) : a.n_evict;
+  return r;
+}
+
+// The key prefix after `passes` finished passes and the 1-based rank of the
+// target among the keys carrying it (the same in every workgroup).
+__device__ inline void select_state(const SelectArgs& a, int seq, int passes, int64_t k, int tid, uint32_t& prefix,
+                                    uint32_t& mask, int64_t& rank, int* s_wave, int* s_pick) {
+  prefix = 0;
+  mask = 0;
+  rank = k;
+  for (int p = 0; p < passes; ++p) {
+    const int* h = a.hist + (static_cast<int64_t>(p) * a.n_seqs + seq) * kSelectBins;
+    constexpr int per = kSelectBins / kSelectThreads;  // 8 bins per thread
+    int c[per], sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      c[i] = h[tid * per + i];
+      sum += c[i];
     }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t before = 0;
+    int tot;
+    const int incl = block_scan(sum, tid, s_wave, tot);
+    int64_t before = incl - sum;
+    if (before < rank && rank <= before + sum) {  // exactly one thread holds the target's bin
       int d = 0;
-      while (d < 255 && before + hist[d] < rank) before += hist[d++];
-      s_prefix = prefix | (static_cast<uint32_t>(d) << shift);
-      s_rank = rank - before;
+      while (d < per - 1 && before + c[d] < rank) before += c[d++];
+      s_pick[0] = tid * per + d;
+      s_pick[1] = static_cast<int>(rank - before);
     }
     __syncthreads();
-    prefix = s_prefix;
-    rank = s_rank;
-    mask |= 255u << shift;
+    prefix |= static_cast<uint32_t>(s_pick[0]) << kDigitShift[p];
+    mask |= kDigitMask[p] << kDigitShift[p];
+    rank = s_pick[1];
+    __syncthreads();
   }
-  // ---- in cell order: every key below T, and the first `rank` keys equal to T ----
-  const uint32_t T = prefix;
-  int64_t eq_seen = 0, taken = 0;
-  for (int64_t base = lo; base < hi && taken < k; base += kSelectThreads) {
+}
+
+__global__ __launch_bounds__(kSelectThreads) void select_zero_kernel(SelectArgs a) {
+  const int seq = blockIdx.x;
+  for (int p = 0; p < 3; ++p)
+    for (int i = threadIdx.x; i < kSelectBins; i += kSelectThreads)
+      a.hist[(static_cast<int64_t>(p) * a.n_seqs + seq) * kSelectBins + i] = 0;
+}
+
+// Pass P: histogram of digit P over the block's keys that carry the prefix
+// of passes 0 .. P-1.  Lanes of a wave that share a bin are counted with one
+// LDS add by a leader (scores cluster, so most keys share the top digits).
+template <int P>
+__global__ __launch_bounds__(kSelectThreads) void select_hist_kernel(SelectArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int seq = blockIdx.y;
+  const SelectRange r = select_range(a, seq);
+  const int64_t b0 = r.lo + static_cast<int64_t>(blockIdx.x) * a.cells_per_block;
+  if (r.k == 0 || b0 >= r.hi) return;  // uniform per workgroup
+  const int64_t b1 = b0 + a.cells_per_block < r.hi ? b0 + a.cells_per_block : r.hi;
+  __shared__ int hist[kSelectBins];
+  __shared__ int s_wave[kSelectThreads / 64];
+  __shared__ int s_pick[2];
+  uint32_t prefix, mask;
+  int64_t rank;
+  select_state(a, seq, P, r.k, tid, prefix, mask, rank, s_wave, s_pick);
+  for (int i = tid; i < kSelectBins; i += kSelectThreads) hist[i] = 0;
+  __syncthreads();
+  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+  for (int64_t base = b0; base < b1; base += kSelectThreads) {  // uniform trip count
     const int64_t j = base + tid;
-    const uint32_t key = j < hi ? score_key(sc[j]) : 0xFFFFFFFFu;
-    const int is_eq = j < hi && key == T ? 1 : 0;
+    const uint32_t key = j < b1 ? score_key(sc[j]) : 0u;
+    bool pending = j < b1 && (key & mask) == prefix;
+    const uint32_t bin = (key >> kDigitShift[P]) & kDigitMask[P];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const uint64_t act = __builtin_amdgcn_ballot_w64(pending);
+      if (act == 0) break;
+      const int leader = __builtin_ctzll(act);
+      const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+      const uint64_t same = __builtin_amdgcn_ballot_w64(pending && bin == lb);
+      if (lane == leader) atomicAdd(&hist[lb], __builtin_popcountll(same));
+      pending = pending && bin != lb;
+    }
+    if (pending) atomicAdd(&hist[bin], 1);
+  }
+  __syncthreads();
+  int* g = a.hist + (static_cast<int64_t>(P) * a.n_seqs + seq) * kSelectBins;
+  for (int i = tid; i < kSelectBins; i += kSelectThreads)
+    if (hist[i] != 0) atomicAdd(&g[i], hist[i]);
+}
+
+// Per block: its cells below the target key T and equal to it.
+__global__ __launch_bounds__(kSelectThreads) void select_count_kernel(SelectArgs a) {
+  const int tid = threadIdx.x;
+  const int seq = blockIdx.y;
+  const SelectRange r = select_range(a, seq);
+  const int64_t b0 = r.lo + static_cast<int64_t>(blockIdx.x) * a.cells_per_block;
+  if (r.k == 0 || b0 >= r.hi) return;  // uniform per workgroup
+  const int64_t b1 = b0 + a.cells_per_block < r.hi ? b0 + a.cells_per_block : r.hi;
+  __shared__ int s_wave[kSelectThreads / 64];
+  __shared__ int s_pick[2];
+  uint32_t T, mask;
+  int64_t rank;
+  select_state(a, seq, 3, r.k, tid, T, mask, rank, s_wave, s_pick);
+  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+  int lt = 0, eq = 0;
+  for (int64_t j = b0 + tid; j < b1; j += kSelectThreads) {
+    const uint32_t key = score_key(sc[j]);
+    lt += key < T ? 1 : 0;
+    eq += key == T ? 1 : 0;
+  }
+  int n_lt, n_eq;
+  block_scan(lt, tid, s_wave, n_lt);
+  block_scan(eq, tid, s_wave, n_eq);
+  if (tid == 0) {
+    int* c = a.counts + (static_cast<int64_t>(seq) * kSelectMaxBlocks + blockIdx.x) * 2;
+    c[0] = n_lt;
+    c[1] = n_eq;
+  }
+}
+
+// Per block, in cell order: every key below T and, of the keys equal to T,
+// those whose rank among all of them (in cell order) is at most `rank`.
+// The blocks before this one give the output offset.
+__global__ __launch_bounds__(kSelectThreads) void select_write_kernel(SelectArgs a) {
+  const int tid = threadIdx.x;
+  const int seq = blockIdx.y;
+  const SelectRange r = select_range(a, seq);
+  int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
+  if (blockIdx.x == 0) {
+    for (int64_t i = r.k + tid; i < a.n_evict; i += kSelectThreads) out[i] = -1;
+    if (tid == 0) a.n_out[seq] = static_cast<int32_t>(r.k);
+  }
+  const int64_t b0 = r.lo + static_cast<int64_t>(blockIdx.x) * a.cells_per_block;
+  if (r.k == 0 || b0 >= r.hi) return;  // uniform per workgroup
+  const int64_t b1 = b0 + a.cells_per_block < r.hi ? b0 + a.cells_per_block : r.hi;
+  __shared__ int s_wave[kSelectThreads / 64];
+  __shared__ int s_pick[2];
+  uint32_t T, mask;
+  int64_t rank;
+  select_state(a, seq, 3, r.k, tid, T, mask, rank, s_wave, s_pick);
+  // cells chosen and keys equal to T in the blocks before this one
+  const int* c = a.counts + static_cast<int64_t>(seq) * kSelectMaxBlocks * 2;
+  int e_b = 0, l_b = 0;
+  for (int b = tid; b < static_cast<int>(blockIdx.x); b += kSelectThreads) {
+    l_b += c[2 * b];
+    e_b += c[2 * b + 1];
+  }
+  int lt_before, eq_before;
+  block_scan(l_b, tid, s_wave, lt_before);
+  block_scan(e_b, tid, s_wave, eq_before);
+  int64_t taken = lt_before + (eq_before < rank ? eq_before : rank);  // chosen before this block
+  int64_t eq_seen = eq_before;
+  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+  for (int64_t base = b0; base < b1; base += kSelectThreads) {  // uniform trip count
+    const int64_t j = base + tid;
+    const uint32_t key = j < b1 ? score_key(sc[j]) : 0xFFFFFFFFu;
+    const int is_eq = j < b1 && key == T ? 1 : 0;
     int n_eq;
     const int eq_incl = block_scan(is_eq, tid, s_wave, n_eq);
-    const int sel = (j < hi && key < T) || (is_eq && eq_seen + eq_incl <= rank) ? 1 : 0;
+    const int sel = (j < b1 && key < T) || (is_eq && eq_seen + eq_incl <= rank) ? 1 : 0;
     int n_sel;
     const int pos = block_scan(sel, tid, s_wave, n_sel);
-    if (sel && taken + pos - 1 < k) out[taken + pos - 1] = j;  // exactly k are selected; the bound is a guard
+    if (sel && taken + pos - 1 < r.k) out[taken + pos - 1] = j;  // exactly k are chosen; the bound is a guard
     eq_seen += n_eq;
     taken += n_sel;
   }
@@ -350,7 +480,13 @@ hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream,
 }
 
 hipError_t launch_select(int n_seqs, hipStream_t stream, const SelectArgs& args) {
-  hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(kSelectThreads), 0, stream, args);
+  const dim3 block(kSelectThreads), grid(static_cast<unsigned>(args.n_blocks), static_cast<unsigned>(n_seqs));
+  hipLaunchKernelGGL(select_zero_kernel, dim3(static_cast<unsigned>(n_seqs)), block, 0, stream, args);
+  hipLaunchKernelGGL(select_hist_kernel<0>, grid, block, 0, stream, args);
+  hipLaunchKernelGGL(select_hist_kernel<1>, grid, block, 0, stream, args);
+  hipLaunchKernelGGL(select_hist_kernel<2>, grid, block, 0, stream, args);
+  hipLaunchKernelGGL(select_count_kernel, grid, block, 0, stream, args);
+  hipLaunchKernelGGL(select_write_kernel, grid, block, 0, stream, args);
   return hipGetLastError();
 }
 

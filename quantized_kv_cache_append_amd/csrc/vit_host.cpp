@@ -267,26 +267,47 @@ int vit_attn_probe_scores(const vit_kv_plane* k, const float* q, int32_t n_q_hea
              : VIT_E_HIP;
 }
 
+size_t vit_probe_select_workspace_bytes(int32_t n_seqs) {
+  if (n_seqs < 1 || n_seqs > VIT_MAX_SEQS) return 0;
+  return static_cast<size_t>(n_seqs) * (3 * vit::kSelectBins + vit::kSelectMaxBlocks * 2) * sizeof(int32_t);
+}
+
 int vit_probe_select_evictions(const float* scores, int32_t n_seqs, int64_t capacity, const int64_t* seq_len,
                                int64_t n_sink, int64_t n_recent, int32_t n_evict, int64_t* rows_out, int32_t* n_out,
-                               void* stream) {
-  if (!scores || !seq_len || !n_out) return VIT_E_ARG;
+                               void* workspace, void* stream) {
+  if (!scores || !seq_len || !n_out || !workspace) return VIT_E_ARG;
   if (n_seqs < 1 || capacity < 1 || n_sink < 0 || n_recent < 0 || n_evict < 0) return VIT_E_ARG;
   if (n_evict > 0 && !rows_out) return VIT_E_ARG;
   if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
   if (capacity > VIT_MAX_CAPACITY) return VIT_E_UNSUPPORTED;
   for (int s = 0; s < n_seqs; ++s)
     if (seq_len[s] < 0 || seq_len[s] > capacity) return VIT_E_CAPACITY;
-  if (!aligned(scores, 4) || (rows_out && !aligned(rows_out, 8)) || !aligned(n_out, 4)) return VIT_E_ALIGN;
+  if (!aligned(scores, 4) || (rows_out && !aligned(rows_out, 8)) || !aligned(n_out, 4) || !aligned(workspace, 256))
+    return VIT_E_ALIGN;
   vit::SelectArgs a{};
   a.scores = scores;
   a.rows_out = rows_out;
   a.n_out = n_out;
+  a.hist = static_cast<int32_t*>(workspace);
+  a.counts = a.hist + static_cast<size_t>(n_seqs) * 3 * vit::kSelectBins;
   a.capacity = capacity;
   a.n_sink = n_sink;
   a.n_recent = n_recent;
   a.n_evict = n_evict;
-  for (int s = 0; s < n_seqs; ++s) a.seq_len[s] = seq_len[s];
+  a.n_seqs = n_seqs;
+  int64_t max_mid = 0;  // middle cells of the longest middle range
+  for (int s = 0; s < n_seqs; ++s) {
+    a.seq_len[s] = seq_len[s];
+    const int64_t lo = n_sink < seq_len[s] ? n_sink : seq_len[s];
+    const int64_t hi = seq_len[s] - n_recent > lo ? seq_len[s] - n_recent : lo;
+    if (hi - lo > max_mid) max_mid = hi - lo;
+  }
+  // blocks of >= 4096 cells, at most kSelectMaxBlocks per sequence
+  int64_t cpb = 4096;
+  while ((max_mid + cpb - 1) / cpb > vit::kSelectMaxBlocks) cpb *= 2;
+  const int64_t nb = (max_mid + cpb - 1) / cpb;
+  a.cells_per_block = static_cast<int32_t>(cpb);
+  a.n_blocks = static_cast<int32_t>(nb < 1 ? 1 : nb);
   return vit::launch_select(n_seqs, static_cast<hipStream_t>(stream), a) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 

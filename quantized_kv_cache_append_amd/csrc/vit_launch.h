@@ -62,16 +62,24 @@ struct ProbeArgs {
   int32_t seq_len[kMaxSeqs];
 };
 
-// The cells to evict: a radix select of the n_evict lowest (score, cell)
-// keys among each sequence's middle cells, then their compaction in cell order.
+// The cells to evict: a 3-pass radix select (11, 11, 10 bits) of the n_evict
+// lowest (score, cell) keys among each sequence's middle cells, by blocks of
+// cells_per_block cells, then their compaction in cell order.
+constexpr int kSelectMaxBlocks = 256;  // blocks per sequence
+constexpr int kSelectBins = 2048;      // bins of an 11-bit digit
 struct SelectArgs {
   const float* scores;   // [S][capacity]
   int64_t* rows_out;     // [S][n_evict]
   int32_t* n_out;        // [S]
+  int32_t* hist;         // [3][S][kSelectBins], zeroed by the first kernel
+  int32_t* counts;       // [S][kSelectMaxBlocks][2]: block's cells below T, equal to T
   int64_t capacity;
   int64_t n_sink;
   int64_t n_recent;
   int32_t n_evict;
+  int32_t n_seqs;
+  int32_t cells_per_block;
+  int32_t n_blocks;
   int64_t seq_len[kMaxSeqs];
 };
 

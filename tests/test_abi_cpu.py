@@ -258,9 +258,9 @@ def test_probe_validation(lib):
 
 
 def test_select_evictions_validation(lib):
-    def call(seq_len=(10, 10), ns=2, nr=2, ne=3, rows=FAKE, nout=FAKE, scores=FAKE, cap=512):
+    def call(seq_len=(10, 10), ns=2, nr=2, ne=3, rows=FAKE, nout=FAKE, scores=FAKE, cap=512, ws=FAKE):
         arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
-        return lib.vit_probe_select_evictions(scores, len(seq_len), cap, arr, ns, nr, ne, rows, nout, None)
+        return lib.vit_probe_select_evictions(scores, len(seq_len), cap, arr, ns, nr, ne, rows, nout, ws, None)
 
     assert call(seq_len=(513, 1)) == _lib.VIT_E_CAPACITY
     assert call(seq_len=(-1, 1)) == _lib.VIT_E_CAPACITY
@@ -270,7 +270,11 @@ def test_select_evictions_validation(lib):
     assert call(nout=None) == _lib.VIT_E_ARG
     assert call(scores=None) == _lib.VIT_E_ARG
     assert call(rows=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert call(ws=None) == _lib.VIT_E_ARG
+    assert call(ws=FAKE + 64) == _lib.VIT_E_ALIGN
     assert call(seq_len=(1,) * 65) == _lib.VIT_E_UNSUPPORTED
+    assert lib.vit_probe_select_workspace_bytes(3) == 3 * (3 * 2048 + 256 * 2) * 4
+    assert lib.vit_probe_select_workspace_bytes(0) == 0
 
 
 def test_reduce_validation(lib):

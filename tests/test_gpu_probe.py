@@ -184,3 +184,25 @@ def test_select_evictions_edges_and_full_slot():
     for s in range(2):
         ref = probe.select_evictions(sc[s].astype(np.float64), lens[s], 4, 256, 5000)
         assert n[s] == 5000 and rows[s].tolist() == ref
+
+
+@pytest.mark.gpu
+def test_select_evictions_ties_across_blocks():
+    """Several 4096-cell blocks per sequence; the tied target key's cells span
+    blocks, so each block's share of them depends on the blocks before it."""
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    rng = np.random.default_rng(47)
+    cap = 30000
+    sc = np.ones((3, cap), np.float32)                               # all equal
+    sc[1] = (rng.integers(0, 3, cap) / 4.0).astype(np.float32)       # three values
+    sc[2] = rng.random(cap).astype(np.float32)
+    sc[2, 5000:21000:3] = 0.125                                       # a tie run across blocks
+    lens = [cap, 29999, 25001]
+    for ne in (1, 4095, 4097, 9000, 12000, 30000):
+        rows, n = _select(torch, vit, sc, lens, 17, 5, ne)
+        for s in range(3):
+            ref = probe.select_evictions(sc[s].astype(np.float64), lens[s], 17, 5, ne)
+            assert n[s] == len(ref), (ne, s)
+            assert rows[s, :len(ref)].tolist() == ref, (ne, s)
