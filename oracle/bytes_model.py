@@ -4,7 +4,7 @@ Closed forms that the pages print and that this model must reproduce:
 * bits/value: f16 16, q8_0 8.5, q4_0 4.5, turbo4 4.125, turbo8 8.125
   (buun-llama-cpp page, "Codecs" table);
 * tq3_0 at 3.5 bits is "~22% smaller than q4_0" (Randozart/VITRIOL page,
-  "What sets VITRIOL apart" table);
+  "What sets VITRIOL apart" table); rot3 is that 3.5 bits/value class;
 * VBR aggregate bits/value 15.75 then 15.51 for the first two degrade steps
   and 160 / 600 steps for 16 / 60 attention layers (buun-llama-cpp page,
   "VBR -- Variable Bit-Rate KV Cache");
@@ -22,6 +22,7 @@ BPV = {
     "q8_0": 8.0 + 16.0 / BLOCK,                     # 8.5
     "q4_0": 4.0 + 16.0 / BLOCK,                     # 4.5
     "rot4": 4.0 + 16.0 / BLOCK + 16.0 / HEAD_DIM,   # 4.625: scale per 32 + norm per row
+    "rot3": 3.0 + 16.0 / BLOCK,                     # 3.5: scale per 32, no norm
     # rotated codecs of the pages' ladder that carry one fp16 norm per 128 values
     "turbo8": 8.0 + 16.0 / HEAD_DIM,                # 8.125
     "turbo4": 4.0 + 16.0 / HEAD_DIM,                # 4.125

@@ -23,6 +23,7 @@ Logical outputs (what parity compares, bit for bit):
   q8_0  codes int8[N,128], scales uint16[N,4]
   q4_0  codes uint8[N,128] in 0..15, scales uint16[N,4]
   rot4  idx uint8[N,128] in 0..15, scales uint16[N,4], norms uint16[N]
+  rot3  idx uint8[N,128] in 0..7, scales uint16[N,4]
 For q4_0 and rot4 the canonical byte packing of block b is
 byte j (0..15) = code[32b + j] | code[32b + j + 16] << 4   (``pack_nibbles``).
 """
@@ -37,7 +38,7 @@ D = 128
 QK = 32
 NB = D // QK
 
-CODECS = ("f16", "q8_0", "q4_0", "rot4")
+CODECS = ("f16", "q8_0", "q4_0", "rot4", "rot3")
 
 
 MIN_BLOCK_MAX = np.float32(2.0 ** -100)
@@ -176,6 +177,54 @@ def dequant_rot4(q, signs16):
     return s * wht(y, np.float64) / np.sqrt(128.0)
 
 
+# ---------------------------------------------------------------------- rot3
+def quantize_rot3(x, signs16):
+    """Rotated 3-bit codec, 3.5 bits/value (the "tq3_0 / turbo3" class of the
+    Randozart/VITRIOL page's "What sets VITRIOL apart" table and the
+    buun-llama-cpp page's "Codecs" table: WHT-rotated, 3-bit scalar codes).
+
+    Steps, all fp32, in this order:
+      1. r_j = s_j x_j;  w = WHT(r)          (as rot4, unnormalised)
+      2. per block b: r_b = sqrt(tree32(w_j * w_j) * 0.03125);  S_b = fp16(r_b)
+      3. ib = 1/r_b (0 if r_b == 0);  t_j = w_j * ib
+      4. idx_j = #{k: t_j > th_k} + #{k: t_j == th_k and t_j >= 0}
+         (7 thresholds of the 8-level codebook; a tie goes to the level
+         farther from zero; 0 -> 4)
+    Reading: with one fp16 per 32 values (3 + 16/32 = 3.5 bits/value) the
+    block scale is the RMS of the rotated block itself (no row norm), so the
+    rotated-domain reconstruction is S_b * level, i.e. y = w / sqrt(128)
+    reconstructs as S_b * level / sqrt(128), the domain rot4 uses.
+    """
+    x = _rows(x)
+    s = sign_vector(signs16)
+    r = np.where(s < 0, -x, x).astype(np.float32)
+    w = wht(r, np.float32)
+    wb = w.reshape(-1, NB, QK)
+    ms = (tree_sum((wb * wb).astype(np.float32)) * F32(0.03125)).astype(np.float32)
+    rb = np.sqrt(ms).astype(np.float32)
+    ib = safe_recip(rb)
+    t = (wb * ib[..., None]).astype(np.float32)
+    _, thr, _ = codebook(8)
+    tt = t[..., None]
+    idx = (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+    return {"codes": idx.astype(np.uint8).reshape(-1, D), "scales": f16_bits(rb)}
+
+
+def dequant_rot3_rotated(q):
+    """Rotated-domain reconstruction y_j = S_b * level[idx_j] / sqrt(128)."""
+    lv, _, _ = codebook(8)
+    S = f16_value(q["scales"]).astype(np.float64)
+    c = lv.astype(np.float64)[q["codes"].astype(np.int64)].reshape(-1, NB, QK)
+    return (c * S[..., None] / np.sqrt(128.0)).reshape(-1, D)
+
+
+def dequant_rot3(q, signs16):
+    """Model-domain reconstruction x = s * (H y) / sqrt(128), in fp64."""
+    y = dequant_rot3_rotated(q)
+    s = sign_vector(signs16).astype(np.float64)
+    return s * wht(y, np.float64) / np.sqrt(128.0)
+
+
 # ------------------------------------------------------------------ dispatch
 def quantize(codec, x, signs16=None):
     if codec == "f16":
@@ -186,6 +235,8 @@ def quantize(codec, x, signs16=None):
         return quantize_q4_0(x)
     if codec == "rot4":
         return quantize_rot4(x, signs16)
+    if codec == "rot3":
+        return quantize_rot3(x, signs16)
     raise ValueError(codec)
 
 
@@ -198,6 +249,8 @@ def dequant(codec, q, signs16=None):
         return dequant_q4_0(q)
     if codec == "rot4":
         return dequant_rot4(q, signs16)
+    if codec == "rot3":
+        return dequant_rot3(q, signs16)
     raise ValueError(codec)
 
 

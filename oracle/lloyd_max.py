@@ -1,16 +1,17 @@
-"""16-level Lloyd-Max quantizer for a standard normal source.
+"""Lloyd-Max quantizers (16 and 8 levels) for a standard normal source.
 
 The rot4 codec stores, per value, the index of one of 16 reconstruction
-levels.  The pages name a scalar quantizer applied after the random-sign FWHT
+levels; the rot3 codec one of 8.  The pages name a scalar quantizer applied after the random-sign FWHT
 rotation (buun-llama-cpp page, "How it works", step 1, and the rotated
 "turbo4" row of its "Codecs" table); the rotation makes entries close to
 i.i.d. N(0,1), and the minimum-MSE scalar quantizer for that source is the
 Lloyd-Max quantizer (J. Max, "Quantizing for minimum distortion", IRE Trans.
 Inf. Theory 6(1), 1960; S. Lloyd, "Least squares quantization in PCM", 1957/1982).
 
-Reading taken (the pages give no codebook): levels are the 16-level Lloyd-Max
-levels for N(0,1), solved here in fp64, then stored at fp16 precision (the
-same precision as every other stored rot4 field).  The encoder's decision
+Reading taken (the pages give no codebook): levels are the 16-level (rot4) or
+8-level (rot3, the 3-bit "tq3_0 / turbo3" class) Lloyd-Max levels for N(0,1),
+solved here in fp64, then stored at fp16 precision (the same precision as
+every other stored field).  The encoder's decision
 thresholds are the fp32 midpoints of adjacent stored levels, so nearest-level
 coding and threshold counting agree.
 """
@@ -68,7 +69,7 @@ def solve_positive_half(n_levels=16, tol=1e-15, max_iter=2_000_000):
 
 
 def full_levels_fp64(n_levels=16):
-    """All 16 levels in increasing order (fp64): c[15-k] = -c[k]."""
+    """All n_levels levels in increasing order (fp64): c[n-1-k] = -c[k]."""
     pos, _, _ = solve_positive_half(n_levels)
     return np.concatenate([-pos[::-1], pos])
 
@@ -93,17 +94,17 @@ def mse_fp64(levels, thresholds):
     return total
 
 
-def codebook():
-    """The stored rot4 codebook and thresholds.
+def codebook(n_levels=16):
+    """The stored codebook and thresholds (16 levels: rot4; 8 levels: rot3).
 
     Returns (levels_f32, thresholds_f32, levels_fp16_bits):
       levels_f32[k]     -- level k rounded to fp16 (RNE), as its exact fp32 value
-      thresholds_f32[k] -- fp32((levels_f32[k] + levels_f32[k+1]) * 0.5), k < 15
+      thresholds_f32[k] -- fp32((levels_f32[k] + levels_f32[k+1]) * 0.5), k < n-1
       levels_fp16_bits  -- the fp16 bit patterns of the levels
     The fp32 sum of two fp16 values is exact and * 0.5 is exact, so every
     threshold is the exact midpoint of its two stored levels.
     """
-    lv = full_levels_fp64(16)
+    lv = full_levels_fp64(n_levels)
     bits = lv.astype(np.float32).astype(np.float16).view(np.uint16)
     # fp64 -> fp16 through fp32: the two roundings cannot differ from a direct
     # fp64 -> fp16 rounding for these values (checked by a test).

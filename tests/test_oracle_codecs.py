@@ -287,6 +287,78 @@ def test_rot4_decoder_inverts_rotation_exactly():
     assert np.allclose(xh, x * n16 / np.sqrt(128.0), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------- rot3
+def test_rot3_impulse_closed_form():
+    """x = a e_j rotates to w = +-a on every channel: each block's RMS is |a|,
+    every t is +-1 (index 5 or 2), and the decode is exactly L5 * a * e_j
+    with L5 the stored level 0.756 (a fp16-exact, any signs)."""
+    lv, _, _ = lloyd_max.codebook(8)
+    rng = np.random.default_rng(8)
+    for j, a in ((0, 3.0), (77, -0.375), (127, 1.25)):
+        s = rng.integers(0, 256, 16, dtype=np.uint8)
+        x = np.zeros((1, D), np.float32)
+        x[0, j] = a
+        q = codecs.quantize_rot3(x, s)
+        assert np.all(fp.f16_value(q["scales"]) == abs(a))
+        assert set(np.unique(q["codes"]).tolist()) <= {2, 5}
+        xh = codecs.dequant_rot3(q, s)
+        expect = np.zeros((1, D))
+        expect[0, j] = float(lv[5]) * a
+        assert np.allclose(xh, expect, rtol=0, atol=1e-12)
+
+
+def test_rot3_zero_row():
+    q = codecs.quantize_rot3(np.zeros((1, D), np.float32), np.zeros(16, np.uint8))
+    assert np.all(q["scales"] == 0) and np.all(q["codes"] == 4) and "norms" not in q
+
+
+def test_rot3_index_is_nearest_level(rng):
+    x = rng.standard_normal((512, D)).astype(np.float32)
+    s = _signs(rng)
+    q = codecs.quantize_rot3(x, s)
+    from oracle.wht import sign_vector, sylvester
+
+    H = sylvester(D).astype(np.float64)
+    wb = ((x.astype(np.float64) * sign_vector(s)) @ H.T).reshape(-1, 4, 32)
+    t = wb / np.sqrt((wb * wb).mean(-1, keepdims=True))
+    lv, thr, _ = lloyd_max.codebook(8)
+    near = np.argmin(np.abs(t[..., None] - lv.astype(np.float64)), axis=-1)
+    gap = np.min(np.abs(t[..., None] - thr.astype(np.float64)), axis=-1)
+    safe = gap > 1e-5
+    assert safe.mean() > 0.99
+    assert np.array_equal(q["codes"].reshape(-1, 4, 32)[safe], near[safe])
+
+
+def test_rot3_ties_go_away_from_zero():
+    lv, thr, _ = lloyd_max.codebook(8)
+    assert thr[3] == 0.0 and all(thr[k] == -thr[6 - k] for k in range(7))  # symmetric
+    t = np.concatenate([thr, -thr]).astype(np.float32)
+    idx = (t[:, None] > thr).sum(-1) + ((t[:, None] == thr) & (t[:, None] >= 0)).sum(-1)
+    for v, i in zip(t, idx):
+        if v > 0:
+            assert lv[i] > v and lv[i - 1] < v
+        elif v < 0:
+            assert lv[i] < v and lv[i + 1] > v
+        else:
+            assert i == 4
+
+
+def test_rot3_statistics_match_lloyd_max_mse(rng):
+    x = rng.standard_normal((20000, D)).astype(np.float32)
+    s = _signs(rng)
+    q = codecs.quantize_rot3(x, s)
+    xh = codecs.dequant_rot3(q, s)
+    rel = ((xh - x) ** 2).sum(1) / (x.astype(np.float64) ** 2).sum(1)
+    assert 0.030 < rel.mean() < 0.040  # the 8-level Lloyd-Max MSE is 0.0345
+
+
+def test_rot3_bits_per_value():
+    from oracle import bytes_model
+
+    assert bytes_model.BPV["rot3"] == 3.5
+    assert 1.0 - bytes_model.BPV["rot3"] / bytes_model.BPV["q4_0"] == pytest.approx(0.2222, abs=1e-4)  # ~22% smaller
+
+
 # -------------------------------------------------- planted mistakes (oracle)
 def test_planted_fp32_floor_rounding_is_caught(monkeypatch):
     """A plausible mistake (fp32 floor(x + 0.5)) must fail the q8 tie pin."""

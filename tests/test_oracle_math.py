@@ -65,9 +65,10 @@ def test_sign_mask_bit_order():
 
 
 # --------------------------------------------------------------- Lloyd-Max
-def test_lloyd_max_matches_max_1960_table():
-    lv, thr, _ = lloyd_max.solve_positive_half()
-    for kind, k, sval in _golden("max1960_gaussian_16level.txt"):
+@pytest.mark.parametrize("n_levels", [16, 8])
+def test_lloyd_max_matches_max_1960_table(n_levels):
+    lv, thr, _ = lloyd_max.solve_positive_half(n_levels)
+    for kind, k, sval in _golden(f"max1960_gaussian_{n_levels}level.txt"):
         k, val = int(k), float(sval)
         # the table is rounded to its last printed digit (3 or 4 decimals)
         tol = 0.5 * 10.0 ** -len(sval.split(".")[1]) + 1e-4
@@ -81,13 +82,14 @@ def test_lloyd_max_matches_max_1960_table():
             assert abs(lloyd_max.mse_fp64(full, ths) - val) <= 1e-5
 
 
-def test_lloyd_max_optimality_by_independent_integration():
+@pytest.mark.parametrize("n_levels", [16, 8])
+def test_lloyd_max_optimality_by_independent_integration(n_levels):
     """Centroid and midpoint conditions, checked with scipy's adaptive
     quadrature (independent of the closed forms the solver uses)."""
     from scipy import integrate
     from scipy.stats import norm
 
-    lv, thr, _ = lloyd_max.solve_positive_half()
+    lv, thr, _ = lloyd_max.solve_positive_half(n_levels)
     edges = [0.0] + list(thr) + [np.inf]
     for i, y in enumerate(lv):
         a, b = edges[i], edges[i + 1]
