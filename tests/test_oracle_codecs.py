@@ -386,8 +386,13 @@ def test_planted_q4_sign_mistake_is_caught(rng, monkeypatch):
         return q
 
     bad = codecs.dequant_q4_0(bad_quant(x))
-    assert np.max(np.abs(good - x)) < 0.3
-    assert np.max(np.abs(bad - x)) > 1.0
+    # a correct round trip errs by at most |d| per block (|d|/2 from rounding,
+    # |d| at the clamped -m), plus the fp16 rounding of d times |code| <= 8;
+    # a sign-flipped scale errs by ~2|x| at the block maximum |x| = 8|d|
+    d = np.abs(fp.f16_value(codecs.quantize_q4_0(x)["scales"]).astype(np.float64))  # [16, 4]
+    bound = np.repeat(d * (1.0 + 8 * 2.0 ** -10), 32, axis=1)
+    assert np.all(np.abs(good - x) <= bound)
+    assert np.all(np.max(np.abs(bad - x).reshape(-1, 4, 32), axis=-1) >= 15.0 * d)
     del orig, monkeypatch
 
 
