@@ -8,8 +8,10 @@
  * ("Configuration" flag table) and the per-(layer, side) degrade ladder of
  * the buun-llama-cpp page ("VBR -- Variable Bit-Rate KV Cache").  Codecs:
  * f16, q8_0 and q4_0 with 32-value blocks (buun-llama-cpp page, "Codecs"
- * table) and rot4, a Walsh-Hadamard-rotated 4-bit scalar codec (same table's
- * rotated "turbo4" row; step 1 of its "How it works" list).  Decode is
+ * table), rot4, a Walsh-Hadamard-rotated 4-bit scalar codec (same table's
+ * rotated "turbo4" row; step 1 of its "How it works" list), and rot3, its
+ * 3-bit, 3.5 bits/value sibling (the "tq3_0" class of the Randozart/VITRIOL
+ * page's "What sets VITRIOL apart" table, the buun-llama-cpp page's "turbo3").  Decode is
  * flash attention only (buun-llama-cpp page, "Requirements" paragraph), for
  * grouped-query heads, over a context whose per-sequence capacity is a
  * multiple of 256 (serverAppConfigs commit log, tests/frank_small_unit.bats
@@ -46,6 +48,12 @@
  *        midpoints of adjacent levels.  Reconstruction in the rotated domain
  *        is norm * scale_b * level[idx_j] / sqrt(128); the model-domain row is
  *        s .* (WHT(that) / sqrt(128)).
+ *  ROT3  y = WHT(s .* x) as ROT4; per block b: r_b = sqrt(mean(y_j^2))
+ *        (stride-halving fp32 sum, then * (1/32)); t_j = y_j * (1 / r_b);
+ *        idx_j = number of the 7 thresholds below t_j (ties go to the level
+ *        farther from zero; 0 -> 4); scale_b = fp16(r_b); no norm.  Levels:
+ *        the 8-level Lloyd-Max quantizer for N(0,1) as fp16.  Reconstruction
+ *        in the rotated domain is scale_b * level[idx_j] / sqrt(128).
  *
  * ------------------------------------------------------------------------
  * Physical layout of one cache plane (one (layer, side) tensor).
@@ -53,7 +61,7 @@
  * tiles of 32 positions; plane index ph = seq * n_kv_heads + head.
  *
  *  codes   ph * capacity * RB bytes per stream, RB = 256 (F16), 128 (Q8_0),
- *          64 (Q4_0, ROT4) bytes per row; a tile is 32 * RB bytes.
+ *          64 (Q4_0, ROT4), 48 (ROT3) bytes per row; a tile is 32 * RB bytes.
  *  scales  fp16, 4 per row (one per 32-value block); NULL for F16.
  *          K side: [S][H][capacity][4] (row-major);  V side:
  *          [S][H][capacity/32][4][32], scale of (tile t, block b, row p) at
@@ -70,6 +78,9 @@
  *  (((h*CB + c)*4 + g)*16 + r)*16; unit U[c][g][r] holds chunk g of blocks
  *  c*BPU .. c*BPU+BPU-1 of row r in block order, BPU = 4/CB (F16: 1 block,
  *  16 B; Q8_0: 2 blocks, 8 B each; Q4_0/ROT4: 4 blocks, 4 B each).
+ *  ROT3 K tiles use 12-byte units instead: unit (h, g, r) at byte
+ *  ((h*4 + g)*16 + r)*12 holds, for b = 0..3 at bytes 3b .. 3b+2, the 24-bit
+ *  group of channels 32b + 8g + j (j < 8), code j at bits 3j.
  *  A V-side tile ("column units") stores, for each channel ch (N-tile
  *  nt = ch>>4, n = ch&15) and each group of 8 positions g8 = p>>3, the 8
  *  codes of positions 8*g8 .. 8*g8+7 of that channel:
@@ -78,7 +89,9 @@
  *          P8[j], P8 = {0,2,1,3,4,6,5,7};
  *    Q4_0: 4 B at ((nt>>2)*4 + g8)*16 + n)*16 + 4*(nt&3), position j in byte
  *          Q4B[j] = {0,2,1,3,0,2,1,3}[j], low nibble for j < 4, high for j >= 4;
- *    ROT4: 4 B as Q4_0, position j in byte j>>1, low nibble for even j.
+ *    ROT4: 4 B as Q4_0, position j in byte j>>1, low nibble for even j;
+ *    ROT3: 24 bits at byte (((ch>>6)*4 + g8)*16 + n)*12 + 3*((ch>>4)&3)
+ *          (12-byte units of 4 channels), position j at bits 3j.
  *  K and V planes of the same codec differ only in this code layout (the
  *  plane's side field); their sizes are equal.
  *
@@ -87,8 +100,8 @@
  * stored fp16 scales and norms stay below 65504.  Outside it the codes are
  * deterministic but unspecified.
  *
- * Sign mask (ROT4): 16 bytes, bit (j & 7) of byte (j >> 3) set => channel j
- * is negated before the transform.  One mask per (layer, side).
+ * Sign mask (ROT4, ROT3): 16 bytes, bit (j & 7) of byte (j >> 3) set =>
+ * channel j is negated before the transform.  One mask per (layer, side).
  */
 #ifndef VIT_H
 #define VIT_H
@@ -104,7 +117,8 @@ typedef enum vit_codec {
   VIT_CODEC_F16 = 0,
   VIT_CODEC_Q8_0 = 1,
   VIT_CODEC_Q4_0 = 2,
-  VIT_CODEC_ROT4 = 3
+  VIT_CODEC_ROT4 = 3,
+  VIT_CODEC_ROT3 = 4
 } vit_codec;
 
 typedef enum vit_side { VIT_SIDE_K = 0, VIT_SIDE_V = 1 } vit_side;
@@ -128,7 +142,7 @@ typedef enum vit_status {
 #define VIT_MAX_CAPACITY (1 << 30) /* rows per (sequence, KV head) */
 
 /* One (layer, side) cache tensor: caller-owned device memory in the layout
- * above.  `signs` is a [host] pointer to 16 bytes (ROT4 only, else NULL),
+ * above.  `signs` is a [host] pointer to 16 bytes (ROT4 and ROT3, else NULL),
  * read during the call. */
 typedef struct vit_kv_plane {
   int32_t codec;       /* vit_codec */

@@ -84,9 +84,9 @@ class KVPlane:
         self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
         self.scales = torch.empty(sb // 2, dtype=torch.int16, device=device) if sb else None
         self.norms = torch.empty(nb // 2, dtype=torch.int16, device=device) if nb else None
-        if codec == "rot4":
+        if codec in ("rot4", "rot3"):
             if signs is None:
-                raise ValueError("rot4 planes need a 16-byte sign mask")
+                raise ValueError(f"{codec} planes need a 16-byte sign mask")
             self.signs = np.ascontiguousarray(signs, dtype=np.uint8).reshape(16).copy()
         else:
             self.signs = None

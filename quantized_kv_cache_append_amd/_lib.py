@@ -17,7 +17,7 @@ VIT_E_CAPACITY = -3
 VIT_E_ALIGN = -4
 VIT_E_HIP = -5
 
-CODEC_IDS = {"f16": 0, "q8_0": 1, "q4_0": 2, "rot4": 3}
+CODEC_IDS = {"f16": 0, "q8_0": 1, "q4_0": 2, "rot4": 3, "rot3": 4}
 SIDE_IDS = {"k": 0, "v": 1}
 
 # every symbol include/vit.h declares

@@ -31,6 +31,7 @@ SOURCES = {
     "decode_k1.hip": [],
     "decode_k2.hip": [],
     "decode_k3.hip": [],
+    "decode_k4.hip": [],
     "reduce.hip": [],
     "probe.hip": [],
     "vit_host.cpp": [],

@@ -20,7 +20,7 @@ namespace vit {
 // to their tile units one by one.  On the V side a channel's 8 rows form one
 // column unit: a whole group is assembled in registers and written whole; a
 // group cut by the range edge keeps the rows outside it (per-row stores,
-// read-modify-write of the shared 4-bit words).
+// read-modify-write of the shared 4-bit and 3-bit words).
 template <int CODEC, int SIDE>
 __device__ inline void store_group(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t g0,
                                    const RowCodes (&rc)[8], const bool (&live)[8], int lane, uint8_t (*rowbuf)[256]) {
@@ -37,30 +37,59 @@ __device__ inline void store_group(uint8_t* codes, uint16_t* scales, uint16_t* n
   const int64_t tile = g0 >> 5;
   const int pbase = static_cast<int>(g0 & 31);  // 0, 8, 16 or 24
   uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+  if constexpr (CODEC == ROT3) {
+    // lane l: the 24-bit groups of channels l and l + 64 over the 8 rows;
+    // lane n16 < 16 writes units (u, g8, n16), channels 64u + 16c + n16
+    uint32_t gv[2] = {0u, 0u};
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int ch = lane + 64 * half;
-    uint32_t c[8];
+    for (int r = 0; r < 8; ++r) {
+      gv[0] |= (rc[r].c0 & 7u) << (3 * r);
+      gv[1] |= (rc[r].c1 & 7u) << (3 * r);
+    }
+    uint32_t g[2][4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) c[r] = half ? rc[r].c1 : rc[r].c0;
-    int sh;
-    const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
-    if constexpr (CODEC == F16) {
-      const u32x4 u = {c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
-      *reinterpret_cast<u32x4*>(tbase + off0) = u;
-    } else if constexpr (CODEC == Q8_0) {
-      // row r goes to byte P8[r] = {0,2,1,3,4,6,5,7}[r] of the 8-byte unit
-      const uint32_t lo = (c[0] & 0xFFu) | ((c[2] & 0xFFu) << 8) | ((c[1] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
-      const uint32_t hi = (c[4] & 0xFFu) | ((c[6] & 0xFFu) << 8) | ((c[5] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
-      *reinterpret_cast<u32x2*>(tbase + off0) = u32x2{lo, hi};
-    } else {
-      uint32_t w = 0;
+    for (int c = 0; c < 4; ++c) {
+      g[0][c] = static_cast<uint32_t>(__shfl(static_cast<int>(gv[0]), 16 * c + (lane & 15), kWave));
+      g[1][c] = static_cast<uint32_t>(__shfl(static_cast<int>(gv[1]), 16 * c + (lane & 15), kWave));
+    }
+    if (lane < 16) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
-        w |= (c[r] & 0xFu) << (((off & 3) << 3) + sh);
+      for (int u = 0; u < 2; ++u) {
+        uint32_t w[3];
+        rot3_unit_words(g[u], w);
+        int bit;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tbase + v3_group_offset(pbase, 64 * u + lane, &bit));
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
       }
-      *reinterpret_cast<uint32_t*>(tbase + (off0 & ~3)) = w;
+    }
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ch = lane + 64 * half;
+      uint32_t c[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) c[r] = half ? rc[r].c1 : rc[r].c0;
+      int sh;
+      const int off0 = v_code_offset(CODEC, pbase, ch, &sh);
+      if constexpr (CODEC == F16) {
+        const u32x4 u = {c[0] | (c[1] << 16), c[2] | (c[3] << 16), c[4] | (c[5] << 16), c[6] | (c[7] << 16)};
+        *reinterpret_cast<u32x4*>(tbase + off0) = u;
+      } else if constexpr (CODEC == Q8_0) {
+        // row r goes to byte P8[r] = {0,2,1,3,4,6,5,7}[r] of the 8-byte unit
+        const uint32_t lo = (c[0] & 0xFFu) | ((c[2] & 0xFFu) << 8) | ((c[1] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
+        const uint32_t hi = (c[4] & 0xFFu) | ((c[6] & 0xFFu) << 8) | ((c[5] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
+        *reinterpret_cast<u32x2*>(tbase + off0) = u32x2{lo, hi};
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int off = v_code_offset(CODEC, pbase + r, ch, &sh);
+          w |= (c[r] & 0xFu) << (((off & 3) << 3) + sh);
+        }
+        *reinterpret_cast<uint32_t*>(tbase + (off0 & ~3)) = w;
+      }
     }
   }
   if constexpr (has_scales(CODEC)) {
@@ -224,15 +253,18 @@ hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, con
     VIT_APPEND_CASE(Q4_0, 1)
     VIT_APPEND_CASE(ROT4, 0)
     VIT_APPEND_CASE(ROT4, 1)
+    VIT_APPEND_CASE(ROT3, 0)
+    VIT_APPEND_CASE(ROT3, 1)
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// The degrade steps: f16 -> q8_0 / q4_0 / rot4, q8_0 -> q4_0 / rot4.
+// The degrade steps: f16 -> q8_0 / q4_0 / rot4 / rot3, q8_0 -> q4_0 / rot4 /
+// rot3, q4_0 -> rot3.
 #define VIT_TRANSCODE_CASE(S, D)                                                                         \
-  case (S)*4 + (D):                                                                                      \
+  case (S)*8 + (D):                                                                                      \
     if (side == 0)                                                                                       \
       hipExtLaunchKernelGGL((transcode_kernel<S, D, 0>), grid, dim3(64 * kAppendWaves), 0, stream,      \
                             ev.start, ev.stop, 0, args);                                                 \
@@ -243,12 +275,15 @@ hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, con
 
 hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
                             const TranscodeArgs& args, const KernelEvents& ev) {
-  switch (src_codec * 4 + dst_codec) {
+  switch (src_codec * 8 + dst_codec) {
     VIT_TRANSCODE_CASE(F16, Q8_0)
     VIT_TRANSCODE_CASE(F16, Q4_0)
     VIT_TRANSCODE_CASE(F16, ROT4)
+    VIT_TRANSCODE_CASE(F16, ROT3)
     VIT_TRANSCODE_CASE(Q8_0, Q4_0)
     VIT_TRANSCODE_CASE(Q8_0, ROT4)
+    VIT_TRANSCODE_CASE(Q8_0, ROT3)
+    VIT_TRANSCODE_CASE(Q4_0, ROT3)
     default:
       return hipErrorInvalidValue;
   }

@@ -96,8 +96,9 @@ __device__ inline half8 q4_unpack(uint32_t w) {
 // lane l at word 64 b + l), so the 64 lookups of one instruction always fall
 // in distinct banks however the code bytes are distributed.
 struct Lut {
-  const uint32_t* words;  // 256 * 64 words
-  uint32_t lane4;         // 4 * lane: the lane's byte offset within an entry
+  const uint32_t* words;   // rot4: 256 * 64 words
+  const uint32_t* words3;  // rot3: 64 * 64 words
+  uint32_t lane4;          // 4 * lane: the lane's byte offset within an entry
 };
 
 // Fill the lane-replicated table (entry b = level pair (b & 15, b >> 4) of
@@ -117,6 +118,41 @@ __device__ inline void fill_rot4_lut(uint32_t* lut, int tid, uint32_t lv) {
     const uint32_t e = lo | (hi << 16);
     *reinterpret_cast<u32x4*>(&lut[4 * (tid + NTHREADS * i)]) = u32x4{e, e, e, e};
   }
+}
+
+// The rot3 table: entry e (6 bits) = level pair (e & 7, e >> 3) of lane l at
+// word 64 e + l, filled with NTHREADS threads (a multiple of 128); lv3 is
+// kLevelBits3[lane & 7].  Word 4 (tid + NTHREADS i) + j is entry
+// (tid + NTHREADS i) / 16: low level (tid / 16) % 8, high level
+// tid / 128 + (NTHREADS / 128) i, the same for the whole wave.
+template <int NTHREADS>
+__device__ inline void fill_rot3_lut(uint32_t* lut3, int tid, uint32_t lv3) {
+  static_assert(NTHREADS % 128 == 0 && NTHREADS <= 1024, "table fill: whole 128-thread groups");
+  const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(lv3), (tid >> 4) & 7));
+  const int hb = __builtin_amdgcn_readfirstlane(tid >> 7);
+#pragma unroll
+  for (int i = 0; i < 1024 / NTHREADS; ++i) {
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lv3), hb + (NTHREADS / 128) * i));
+    const uint32_t e = lo | (hi << 16);
+    *reinterpret_cast<u32x4*>(&lut3[4 * (tid + NTHREADS * i)]) = u32x4{e, e, e, e};
+  }
+}
+
+// eight rot3 indices (a 24-bit group, code j at bits 3j) -> fp16 levels in
+// order j: four 6-bit fields, each one lookup at 256 * field + 4 * lane.
+__device__ inline half8 rot3_unpack(uint32_t g, const Lut& lut) {
+  const char* base = reinterpret_cast<const char*>(lut.words3);
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    r[p] = *reinterpret_cast<const uint32_t*>(base + ((__builtin_amdgcn_ubfe(g, 6 * p, 6) << 8) | lut.lane4));
+  return __builtin_bit_cast(half8, r);
+}
+
+// 24-bit group i (< 4) of a 12-byte rot3 unit held in u[0..2]
+__device__ inline uint32_t rot3_group(const u32x4& u, int i) {
+  return i == 0 ? u[0] : i == 1 ? __builtin_amdgcn_alignbit(u[1], u[0], 24)
+                       : i == 2 ? __builtin_amdgcn_alignbit(u[2], u[1], 16) : u[2] >> 8;
 }
 
 // eight rot4 indices -> fp16 levels, element order (lo b0, hi b0, lo b1,
@@ -144,8 +180,10 @@ __device__ inline int k_chan(int g, int m, int j) {
   } else if constexpr (KC == Q4_0) {
     const int byte = ((j & 1) << 1) | ((j >> 1) & 1);
     return 32 * m + 4 * g + byte + ((j >> 2) << 4);
-  } else {
+  } else if constexpr (KC == ROT4) {
     return 32 * m + 4 * g + (j >> 1) + ((j & 1) << 4);
+  } else {  // ROT3: chunk g of block m is channels 32m + 8g .. 32m + 8g + 7
+    return 32 * m + 8 * g + j;
   }
 }
 
@@ -158,8 +196,10 @@ __device__ inline half8 unpack_k(const u32x4* units, int m, const Lut& lut) {
     return (m & 1) ? q8_unpack(u[2], u[3]) : q8_unpack(u[0], u[1]);
   } else if constexpr (KC == Q4_0) {
     return q4_unpack(units[0][m]);
-  } else {
+  } else if constexpr (KC == ROT4) {
     return rot4_unpack(units[0][m], lut);
+  } else {
+    return rot3_unpack(rot3_group(units[0], m), lut);
   }
 }
 
@@ -173,9 +213,18 @@ __device__ inline half8 unpack_v(const u32x4* vd, int nt, const Lut& lut) {
     return (nt & 1) ? q8_unpack(u[2], u[3]) : q8_unpack(u[0], u[1]);
   } else if constexpr (VC == Q4_0) {
     return q4_unpack(vd[nt >> 2][nt & 3]);
-  } else {
+  } else if constexpr (VC == ROT4) {
     return rot4_unpack(vd[nt >> 2][nt & 3], lut);
+  } else {  // ROT3: 12-byte unit nt / 4, group nt % 4
+    return rot3_unpack(rot3_group(vd[nt >> 2], nt & 3), lut);
   }
+}
+
+// one 12-byte rot3 unit (4-byte aligned) into components 0..2; nothing past
+// it is read
+__device__ inline u32x4 load_unit12(const uint8_t* p) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+  return u32x4{__builtin_nontemporal_load(w), __builtin_nontemporal_load(w + 1), __builtin_nontemporal_load(w + 2), 0u};
 }
 
 template <int C>
@@ -253,13 +302,20 @@ __device__ inline void load_tile(TileRegs<KC, VC, NT>& r, int t, int lane, const
   const uint8_t* kt = kbase + static_cast<int64_t>(t) * tile_code_bytes(KC);
   const uint8_t* vt = vbase + static_cast<int64_t>(t) * tile_code_bytes(VC);
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (KC == ROT3) {
+      r.kd[h][0] = load_unit12(kt + (h * 64 + lane) * 12);
+    } else {
 #pragma unroll
-    for (int c = 0; c < KCB; ++c)
-      r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
+      for (int c = 0; c < KCB; ++c)
+        r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
+    }
+  }
 #pragma unroll
-  for (int i = 0; i < v_loads<VC>(); ++i)
-    r.vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16));
+  for (int i = 0; i < v_loads<VC>(); ++i) {
+    if constexpr (VC == ROT3) r.vd[i] = load_unit12(vt + (i * 64 + lane) * 12);
+    else r.vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vt + (i * 64 + lane) * 16));
+  }
   const int n16 = lane & 15, qg = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(t) * kTile;
   if constexpr (has_scales(KC)) {
@@ -288,6 +344,23 @@ constexpr int prefetch_depth() {
   return (NT == 1 && tile_code_bytes(KC) + tile_code_bytes(VC) <= 4096) ? 2 : 1;
 }
 
+// rot3: the 24-bit group of 8 consecutive lanes' 3-bit codes (lane 8k + j
+// contributes code j at bits 3j); every lane of the 8 gets the group.
+__device__ inline uint32_t rot3_group8(uint32_t code, int lane) {
+  uint32_t v = (code & 7u) << (3 * (lane & 7));
+  v |= xshfl<1>(v);
+  v |= xshfl<2>(v);
+  v |= xshfl<4>(v);
+  return v;
+}
+
+// rot3: three dwords of a 12-byte unit from its four 24-bit groups
+__device__ inline void rot3_unit_words(const uint32_t (&g)[4], uint32_t (&w)[3]) {
+  w[0] = g[0] | (g[1] << 24);
+  w[1] = (g[1] >> 8) | (g[2] << 16);
+  w[2] = (g[2] >> 16) | (g[3] << 8);
+}
+
 // Store one encoded row p of a (sequence, KV head) stream from a single wave:
 // scales, norm and codes (K: canonical bytes staged in `rowbuf`, 256 bytes of
 // LDS private to the wave, then 16-byte units; V: the row's code in each
@@ -313,6 +386,60 @@ __device__ inline void store_row(uint8_t* codes, uint16_t* scales, uint16_t* nor
     if (lane == 0) norms[p] = rc.norm;
   }
   uint8_t* tbase = codes + tile * tile_code_bytes(C);
+  if constexpr (C == ROT3) {
+    if constexpr (SIDE == 0) {
+      // channel groups of 8: lane l holds channels l (blocks 0, 1) and l + 64
+      // (blocks 2, 3); lanes 8k .. 8k+7 form group k of each half.  Unit
+      // (p, g): blocks 0..3 of chunk g = groups of lanes 8g (c0, c1) and
+      // 8g + 32 (c0, c1)
+      const uint32_t g0 = rot3_group8(rc.c0, lane);
+      const uint32_t g1 = rot3_group8(rc.c1, lane);
+      const uint32_t h0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(g0), 32, kWave));
+      const uint32_t h1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(g1), 32, kWave));
+      if (lane < 32 && (lane & 7) == 0) {
+        const uint32_t g[4] = {g0, h0, g1, h1};
+        uint32_t w[3];
+        rot3_unit_words(g, w);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tbase + k3_unit_offset(pt, lane >> 3));
+        dst[0] = w[0];
+        dst[1] = w[1];
+        dst[2] = w[2];
+      }
+    } else {
+      // one lane per unit (u, pt / 8, n16) rewrites row pt's four fields:
+      // channels 64u + 16c + n16, c < 4 (several channels share its words)
+      uint32_t cc[2][4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        cc[0][c] = static_cast<uint32_t>(__shfl(static_cast<int>(rc.c0), 16 * c + (lane & 15), kWave));
+        cc[1][c] = static_cast<uint32_t>(__shfl(static_cast<int>(rc.c1), 16 * c + (lane & 15), kWave));
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          int bit;
+          const int off = v3_group_offset(pt, 64 * u + lane, &bit);  // group c = 0 of the unit
+          uint32_t* wp = reinterpret_cast<uint32_t*>(tbase + off);
+          uint32_t d[3] = {wp[0], wp[1], wp[2]};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int P = 24 * c + bit;  // bit position in the 96-bit unit
+            const int lo = P >> 5, sh = P & 31;
+            const uint32_t v = cc[u][c] & 7u;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+              if (k == lo) d[k] = (d[k] & ~(7u << sh)) | (v << sh);
+              if (k == lo + 1 && sh > 29) d[k] = (d[k] & ~(7u >> (32 - sh))) | (v >> (32 - sh));
+            }
+          }
+          wp[0] = d[0];
+          wp[1] = d[1];
+          wp[2] = d[2];
+        }
+      }
+    }
+    return;
+  }
   if constexpr (SIDE == 0) {
     // canonical row bytes in LDS, then 16-byte units to their tile slots
     if constexpr (C == F16) {
@@ -949,9 +1076,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   __shared__ float sq[GMAX][kD];
   constexpr bool kRot4 = KC == ROT4 || VC == ROT4;
+  constexpr bool kRot3 = KC == ROT3 || VC == ROT3;
   __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
+  __shared__ uint32_t lut3[kRot3 ? 64 * 64 : 1];
   __shared__ float s_p[kDecodeWaves][NT][4][kTile];
-  __shared__ float s_o[kDecodeWaves][RW][kD];
+  // the waves' outputs for the merge; with both tables (rot4 and rot3) they
+  // reuse the 64 KB rot4 table once every wave is past its tiles
+  constexpr bool kOutInLut = kRot4 && kRot3;
+  static_assert(!kOutInLut || kDecodeWaves * RW * kD <= 256 * 64, "outputs fit the rot4 table");
+  __shared__ float s_o_own[kOutInLut ? 1 : kDecodeWaves * RW * kD];
+  float (*const s_o)[RW][kD] = reinterpret_cast<float (*)[RW][kD]>(kOutInLut ? static_cast<void*>(lut) : s_o_own);
   __shared__ float s_m[kDecodeWaves][RW];
   __shared__ float s_l[kDecodeWaves][RW];
   __shared__ int s_next;  // next tile slot to hand out
@@ -1013,12 +1147,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     const float* qsrc = a.q + qrow_index(min(qs_row, G - 1)) * kD + ((8 * tid) & 127);
     q0 = *reinterpret_cast<const float4v*>(qsrc);
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
-    if constexpr (KC == ROT4) ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
+    if constexpr (rotated(KC)) ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
   }
   // rot4 levels: lane l (< 16) fetches level l; issued before the tile loads
   // so that building the table below does not wait for them
-  [[maybe_unused]] uint32_t lv = 0;
+  [[maybe_unused]] uint32_t lv = 0, lv3 = 0;
   if constexpr (kRot4) lv = kLevelBits[lane & 15];
+  if constexpr (kRot3) lv3 = kLevelBits3[lane & 7];
 
   // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
   // k = 0, 1, ... (so at any moment the splits of one stream read one
@@ -1040,7 +1175,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   load_slot(tb, wave + kDecodeWaves);
 
   if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
-  const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
+  if constexpr (kRot3) fill_rot3_lut<kThreads>(lut3, tid, lv3);
+  const Lut lutr{lut, lut3, 4u * static_cast<uint32_t>(lane)};
   QOperands<NT> aq;
   // ---- A operands of S^T = Q K^T for this wave's rows: row n16 = 4*(query
   //      row) + block slot; MFMA m covers block m (lane group qg its chunk
@@ -1051,15 +1187,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float v = live ? (j < 4 ? q0[j] : q1[j - 4]) : 0.0f;
-      if constexpr (KC == ROT4) v = ((ksw >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
+      if constexpr (rotated(KC)) v = ((ksw >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
       sq[qs_row][c0 + j] = v;
     }
   }
   __syncthreads();
   float qs = a.qscale;
-  if constexpr (KC == ROT4) {
+  if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (WHT); the keys reconstruct as
-    // N*S*level/sqrt(128) against q~ = H(s.q)/sqrt(128)
+    // N*S*level/sqrt(128) (rot3: S*level/sqrt(128)) against q~ = H(s.q)/sqrt(128)
     for (int h = 1; h < kD; h <<= 1) {
       for (int i = tid; i < RW * 64; i += kThreads) {
         const int g = i >> 6, k = i & 63;
@@ -1184,6 +1320,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   }
 
   // ---- per-wave state to LDS: row r of the wave's RW query rows ----
+  if constexpr (kOutInLut) __syncthreads();  // no wave reads the rot4 table any more
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = state_row(nt);
@@ -1232,7 +1369,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   }
   if (final_out) {
     __syncthreads();
-    if constexpr (VC == ROT4) {
+    if constexpr (rotated(VC)) {
       for (int h = 1; h < kD; h <<= 1) {
         for (int i = tid; i < RW * 64; i += kThreads) {
           const int g = i >> 6, k = i & 63;
@@ -1247,7 +1384,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     for (int i = tid; i < G * kD; i += kThreads) {
       const int g = i >> 7, c = i & 127;
       float v = sq[g][c];
-      if constexpr (VC == ROT4) {
+      if constexpr (rotated(VC)) {
         v *= (1.0f / 128.0f);
         v = ((a.vsigns[c >> 5] >> (c & 31)) & 1u) ? -v : v;
       }
@@ -1272,6 +1409,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       case Q8_0: VIT_DECODE_NT(KC, Q8_0) break;                                       \
       case Q4_0: VIT_DECODE_NT(KC, Q4_0) break;                                       \
       case ROT4: VIT_DECODE_NT(KC, ROT4) break;                                       \
+      case ROT3: VIT_DECODE_NT(KC, ROT3) break;                                       \
       default: return hipErrorInvalidValue;                                           \
     }                                                                                 \
     return hipGetLastError();                                                         \

@@ -1,5 +1,5 @@
 // Decode kernels with K codec 3 (see decode_impl.h); one file per K codec so
-// the 16 codec pairs x 3 row-group counts compile in parallel.
+// the 25 codec pairs x 3 row layouts compile in parallel.
 #include "decode_impl.h"
 
 namespace vit {

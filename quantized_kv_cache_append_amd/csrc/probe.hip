@@ -34,10 +34,15 @@ __device__ inline void load_k_tile(KTile<KC>& r, int t, int lane, const uint8_t*
   constexpr int KCB = units_per_block(KC);
   const uint8_t* kt = kbase + static_cast<int64_t>(t) * tile_code_bytes(KC);
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (KC == ROT3) {
+      r.kd[h][0] = load_unit12(kt + (h * 64 + lane) * 12);
+    } else {
 #pragma unroll
-    for (int c = 0; c < KCB; ++c)
-      r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
+      for (int c = 0; c < KCB; ++c)
+        r.kd[h][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + ((h * KCB + c) * 64 + lane) * 16));
+    }
+  }
   const int64_t row0 = static_cast<int64_t>(t) * kTile + (lane & 15);
   if constexpr (has_scales(KC)) {
 #pragma unroll
@@ -54,6 +59,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
     ProbeArgs a) {
   constexpr int kThreads = 64 * kProbeWaves;
   constexpr bool kRot4 = KC == ROT4;
+  constexpr bool kRot3 = KC == ROT3;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -68,6 +74,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
 
   __shared__ float sq[16][kD];
   __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
+  __shared__ uint32_t lut3[kRot3 ? 64 * 64 : 1];
   __shared__ float s_m[kProbeWaves][16], s_l[kProbeWaves][16];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
@@ -85,8 +92,9 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
   load_k_tile<KC>(tb, min(tile_of(wave + kProbeWaves), t_last), lane, kbase, ksb, knb);
 
   // ---- query rows of this KV head (G <= 16, zero rows past G) in LDS ----
-  [[maybe_unused]] uint32_t lv = 0;
+  [[maybe_unused]] uint32_t lv = 0, lv3 = 0;
   if constexpr (kRot4) lv = kLevelBits[lane & 15];
+  if constexpr (kRot3) lv3 = kLevelBits3[lane & 7];
   const float* qhead = a.q + (static_cast<int64_t>(seq) * a.n_q_heads + static_cast<int64_t>(head) * G) * kD;
   if (tid < 256) {
     const int r = (8 * tid) >> 7, c0 = (8 * tid) & 127;
@@ -96,14 +104,15 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float v = r < G ? (j < 4 ? v0[j] : v1[j - 4]) : 0.0f;
-      if constexpr (kRot4) v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
+      if constexpr (rotated(KC)) v = ((a.ksigns[(c0 + j) >> 5] >> ((c0 + j) & 31)) & 1u) ? -v : v;  // the keys' sign flip
       sq[r][c0 + j] = v;
     }
   }
   if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
+  if constexpr (kRot3) fill_rot3_lut<kThreads>(lut3, tid, lv3);
   __syncthreads();
   float qs = a.qscale;
-  if constexpr (kRot4) {
+  if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (unnormalised WHT; 1/128 folded in)
     for (int h = 1; h < kD; h <<= 1) {
       for (int i = tid; i < 16 * 64; i += kThreads) {
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
     for (int j = 0; j < 8; ++j) v[j] = sq[n16][k_chan<KC>(qg, b, j)] * qs;
     split8(v, aqh[b], aql[b]);
   }
-  const Lut lutr{lut, 4u * static_cast<uint32_t>(lane)};
+  const Lut lutr{lut, lut3, 4u * static_cast<uint32_t>(lane)};
 
   float m_run[4], l_run[4];  // queries 4qg + i
 #pragma unroll
@@ -469,6 +478,7 @@ hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream,
     VIT_PROBE_CASE(Q8_0)
     VIT_PROBE_CASE(Q4_0)
     VIT_PROBE_CASE(ROT4)
+    VIT_PROBE_CASE(ROT3)
     default:
       return hipErrorInvalidValue;
   }

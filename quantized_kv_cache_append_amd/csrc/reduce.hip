@@ -113,6 +113,7 @@ hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, 
     case Q8_0: return launch_decode_k1(vc, nt, grid, stream, args, ev);
     case Q4_0: return launch_decode_k2(vc, nt, grid, stream, args, ev);
     case ROT4: return launch_decode_k3(vc, nt, grid, stream, args, ev);
+    case ROT3: return launch_decode_k4(vc, nt, grid, stream, args, ev);
     default: return hipErrorInvalidValue;
   }
 }

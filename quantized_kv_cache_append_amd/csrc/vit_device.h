@@ -14,18 +14,24 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Codec { F16 = 0, Q8_0 = 1, Q4_0 = 2, ROT4 = 3 };
+enum Codec { F16 = 0, Q8_0 = 1, Q4_0 = 2, ROT4 = 3, ROT3 = 4 };
 
 constexpr int kD = 128;      // head_dim
 constexpr int kTile = 32;    // rows per tile
 constexpr int kWave = 64;
 
-// code bytes per row and 16-byte units per 32-value block ("CB")
-__host__ __device__ constexpr int row_code_bytes(int c) { return c == F16 ? 256 : (c == Q8_0 ? 128 : 64); }
-__host__ __device__ constexpr int units_per_block(int c) { return row_code_bytes(c) / 64; }
+// code bytes per row and 16-byte units per 32-value block ("CB"; rot3 rows
+// of 48 bytes use 12-byte units instead, see below)
+__host__ __device__ constexpr int row_code_bytes(int c) {
+  return c == F16 ? 256 : (c == Q8_0 ? 128 : (c == ROT3 ? 48 : 64));
+}
+__host__ __device__ constexpr int units_per_block(int c) { return c == ROT3 ? 1 : row_code_bytes(c) / 64; }
 __host__ __device__ constexpr int tile_code_bytes(int c) { return kTile * row_code_bytes(c); }
 __host__ __device__ constexpr bool has_scales(int c) { return c != F16; }
 __host__ __device__ constexpr bool has_norms(int c) { return c == ROT4; }
+// codes in the Walsh-Hadamard-rotated domain (queries rotate with the keys,
+// outputs rotate back)
+__host__ __device__ constexpr bool rotated(int c) { return c == ROT4 || c == ROT3; }
 
 // ---------------------------------------------------------------------------
 // The rot4 levels: the 16-level Lloyd-Max quantizer for N(0,1) (J. Max 1960),
@@ -38,6 +44,12 @@ __device__ constexpr float kThresholds[15] = {
     -0x1.334p+1f, -0x1.d7ep+0f, -0x1.6fep+0f, -0x1.196p+0f, -0x1.996p-1f,
     -0x1.0b7p-1f, -0x1.086p-2f, 0.0f, 0x1.086p-2f, 0x1.0b7p-1f,
     0x1.996p-1f, 0x1.196p+0f, 0x1.6fep+0f, 0x1.d7ep+0f, 0x1.334p+1f};
+
+// The rot3 levels: the 8-level Lloyd-Max quantizer for N(0,1) (Max 1960) as
+// fp16 bit patterns, increasing, and the fp32 midpoints of adjacent levels.
+__device__ constexpr uint16_t kLevelBits3[8] = {0xc04e, 0xbd60, 0xba0c, 0xb3d8, 0x33d8, 0x3a0c, 0x3d60, 0x404e};
+__device__ constexpr float kThresholds3[7] = {-0x1.bf8p+0f, -0x1.0ccp+0f, -0x1.004p-1f, 0.0f,
+                                              0x1.004p-1f,  0x1.0ccp+0f,  0x1.bf8p+0f};
 
 // ---------------------------------------------------------------------------
 // Physical layout (see include/vit.h).  Offsets are within one 32-row tile.
@@ -63,8 +75,26 @@ __host__ __device__ inline int k_canon_offset(int codec, int p, int k) {
   return k_unit_offset(codec, p, off / chb, blk / bpu) + (blk % bpu) * chb + off % chb;
 }
 
+// rot3 K side: the 12-byte unit of (row p, chunk g): 24-bit groups of blocks
+// 0..3 at bytes 3b; group (b, g) holds channels 32b + 8g + j (j < 8), code j
+// at bits 3j.  Rows 16h .. 16h+15 form half h; lane 16g + r of a wave-wide
+// 12-byte load of half h reads row 16h + r, chunk g.
+__host__ __device__ inline int k3_unit_offset(int p, int g) {
+  return (((p >> 4) * 4 + g) * 16 + (p & 15)) * 12;
+}
+
+// rot3 V side: the 12-byte unit (u, 8-row group g8, n16) holds the 24-bit
+// groups of channels 64u + 16c + n16 (c < 4) at bytes 3c, the code of row
+// 8 g8 + j at bits 3j.  Lane 16 g8 + n16 of a wave-wide 12-byte load u reads
+// unit (u, g8, n16).  Returns the group's byte offset; *bit = 3j.
+__host__ __device__ inline int v3_group_offset(int p, int ch, int* bit) {
+  *bit = 3 * (p & 7);
+  return (((ch >> 6) * 4 + (p >> 3)) * 16 + (ch & 15)) * 12 + 3 * ((ch >> 4) & 3);
+}
+
 // V side: byte offset of the code of (row p, channel ch) and, for 4-bit
 // codecs, the nibble shift (0 or 4).  F16 codes take 2 bytes at the offset.
+// (rot3: v3_group_offset.)
 __host__ __device__ inline int v_code_offset(int codec, int p, int ch, int* shift) {
   const int nt = ch >> 4, n = ch & 15, g8 = p >> 3, j = p & 7;
   *shift = 0;
@@ -317,15 +347,15 @@ __device__ inline void wht_stage(float (&w0)[R], float (&w1)[R], int lane) {
   }
 }
 
+// Sign flip and unnormalised Walsh-Hadamard transform of R rows: w = H (s . x).
 // signs: the 128-bit mask as 4 words; bit j set => channel j negated.
 template <int R>
-__device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
-                                   RowCodes (&rc)[R]) {
+__device__ inline void rotate_rows(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
+                                   float (&w0)[R], float (&w1)[R]) {
 #pragma clang fp contract(off)
   const int ch0 = lane, ch1 = lane + 64;
   const bool neg0 = ((signs[ch0 >> 5] >> (ch0 & 31)) & 1u) != 0;
   const bool neg1 = ((signs[ch1 >> 5] >> (ch1 & 31)) & 1u) != 0;
-  float w0[R], w1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     w0[r] = neg0 ? -x0[r] : x0[r];
@@ -344,6 +374,14 @@ __device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], i
     w0[r] = a;
     w1[r] = b;
   }
+}
+
+template <int R>
+__device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
+                                   RowCodes (&rc)[R]) {
+#pragma clang fp contract(off)
+  float w0[R], w1[R];
+  rotate_rows(x0, x1, lane, signs, w0, w1);
   // row norm: stride-halving tree of the squares of the input row
   float ss[R];
 #pragma unroll
@@ -390,13 +428,58 @@ __device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], i
   }
 }
 
+// The rot3 index: #{k : th_k < t} + #{k : th_k == t and t >= 0} over the 7
+// symmetric thresholds (th_3 = 0), i.e. 4 + #{k >= 4 : th_k <= |t|} for
+// t >= 0 (-0 included) and 3 minus that count for t < 0.
+__device__ inline uint32_t rot3_index(float t) {
+  const float a = fabsf(t);
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 4; k < 7; ++k) c += kThresholds3[k] <= a ? 1u : 0u;
+  return t >= 0.0f ? 4u + c : 3u - c;
+}
+
+// rot3: rotate, then per block the RMS of the rotated values is the fp16
+// scale and t = w / RMS picks one of 8 levels (no row norm).
+template <int R>
+__device__ inline void encode_rot3(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
+                                   RowCodes (&rc)[R]) {
+#pragma clang fp contract(off)
+  float w0[R], w1[R];
+  rotate_rows(x0, x1, lane, signs, w0, w1);
+  float b[2 * R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    b[2 * r] = w0[r] * w0[r];
+    b[2 * r + 1] = w1[r] * w1[r];
+  }
+  sum_step<16>(b);
+  sum_step<8>(b);
+  sum_step<4>(b);
+  sum_step<2>(b);
+  sum_step<1>(b);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float r0 = sqrt_rn(b[2 * r] * 0.03125f);
+    const float r1 = sqrt_rn(b[2 * r + 1] * 0.03125f);
+    rc[r] = RowCodes{};
+    rc[r].s0 = f16_bits(r0);
+    rc[r].s1 = f16_bits(r1);
+    const float ib0 = r0 > 0.0f ? 1.0f / r0 : 0.0f;
+    const float ib1 = r1 > 0.0f ? 1.0f / r1 : 0.0f;
+    rc[r].c0 = rot3_index(w0[r] * ib0);
+    rc[r].c1 = rot3_index(w1[r] * ib1);
+  }
+}
+
 template <int CODEC, int R>
 __device__ inline void encode_rows(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
                                    RowCodes (&rc)[R]) {
   if constexpr (CODEC == F16) encode_f16(x0, x1, rc);
   else if constexpr (CODEC == Q8_0) encode_q8_0(x0, x1, rc);
   else if constexpr (CODEC == Q4_0) encode_q4_0(x0, x1, lane, rc);
-  else encode_rot4(x0, x1, lane, signs, rc);
+  else if constexpr (CODEC == ROT4) encode_rot4(x0, x1, lane, signs, rc);
+  else encode_rot3(x0, x1, lane, signs, rc);
 }
 
 template <int CODEC>

@@ -10,7 +10,9 @@
 
 namespace {
 
-constexpr int kRowBytes[4] = {256, 128, 64, 64};
+constexpr int kRowBytes[5] = {256, 128, 64, 64, 48};
+
+bool is_rotated(int32_t codec) { return codec == VIT_CODEC_ROT4 || codec == VIT_CODEC_ROT3; }
 
 // events armed by vit_arm_kernel_events for this host thread's next decode or transcode
 thread_local vit::KernelEvents g_armed;
@@ -19,7 +21,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int check_plane(const vit_kv_plane* p) {
   if (!p) return VIT_E_ARG;
-  if (p->codec < VIT_CODEC_F16 || p->codec > VIT_CODEC_ROT4) return VIT_E_UNSUPPORTED;
+  if (p->codec < VIT_CODEC_F16 || p->codec > VIT_CODEC_ROT3) return VIT_E_UNSUPPORTED;
   if (p->side != VIT_SIDE_K && p->side != VIT_SIDE_V) return VIT_E_ARG;
   if (p->head_dim != VIT_HEAD_DIM) return VIT_E_UNSUPPORTED;
   if (p->reserved != 0) return VIT_E_ARG;
@@ -29,7 +31,8 @@ int check_plane(const vit_kv_plane* p) {
   if (p->capacity % VIT_CAPACITY_ALIGN != 0) return VIT_E_CAPACITY;
   if (!p->codes) return VIT_E_ARG;
   if (p->codec != VIT_CODEC_F16 && !p->scales) return VIT_E_ARG;
-  if (p->codec == VIT_CODEC_ROT4 && (!p->norms || !p->signs)) return VIT_E_ARG;
+  if (p->codec == VIT_CODEC_ROT4 && !p->norms) return VIT_E_ARG;
+  if (is_rotated(p->codec) && !p->signs) return VIT_E_ARG;
   if (!aligned(p->codes, 256) || (p->scales && !aligned(p->scales, 256)) ||
       (p->norms && !aligned(p->norms, 256)))
     return VIT_E_ALIGN;
@@ -38,7 +41,7 @@ int check_plane(const vit_kv_plane* p) {
 
 void load_signs(const vit_kv_plane* p, uint32_t out[4]) {
   memset(out, 0, 4 * sizeof(uint32_t));
-  if (p->codec == VIT_CODEC_ROT4 && p->signs) {
+  if (is_rotated(p->codec) && p->signs) {
     for (int j = 0; j < 16; ++j) out[j >> 2] |= static_cast<uint32_t>(p->signs[j]) << (8 * (j & 3));
   }
 }
@@ -90,7 +93,7 @@ const char* vit_status_string(int status) {
 int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_t head_dim,
                        int64_t capacity, size_t* codes_bytes, size_t* scales_bytes,
                        size_t* norms_bytes) {
-  if (codec < VIT_CODEC_F16 || codec > VIT_CODEC_ROT4) return VIT_E_UNSUPPORTED;
+  if (codec < VIT_CODEC_F16 || codec > VIT_CODEC_ROT3) return VIT_E_UNSUPPORTED;
   if (head_dim != VIT_HEAD_DIM) return VIT_E_UNSUPPORTED;
   if (n_seqs < 1 || n_kv_heads < 1 || capacity <= 0) return VIT_E_ARG;
   if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
@@ -127,9 +130,11 @@ int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int
   if (src->side != dst->side || src->n_seqs != dst->n_seqs || src->n_kv_heads != dst->n_kv_heads ||
       src->capacity != dst->capacity)
     return VIT_E_ARG;
-  // the degrade steps: f16 -> q8_0 / q4_0 / rot4, q8_0 -> q4_0 / rot4
+  // the degrade steps: f16 -> q8_0 / q4_0 / rot4 / rot3, q8_0 -> q4_0 / rot4
+  // / rot3, q4_0 -> rot3 (sources whose values decode exactly to fp32)
   const bool step = (src->codec == VIT_CODEC_F16 && dst->codec != VIT_CODEC_F16) ||
-                    (src->codec == VIT_CODEC_Q8_0 && (dst->codec == VIT_CODEC_Q4_0 || dst->codec == VIT_CODEC_ROT4));
+                    (src->codec == VIT_CODEC_Q8_0 && (dst->codec == VIT_CODEC_Q4_0 || is_rotated(dst->codec))) ||
+                    (src->codec == VIT_CODEC_Q4_0 && dst->codec == VIT_CODEC_ROT3);
   if (!step) return VIT_E_UNSUPPORTED;
   // the two planes' arrays must be disjoint
   const void* sp[3] = {src->codes, src->scales, src->norms};
@@ -411,8 +416,8 @@ int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_h
   if (!workspace || !out || !v) return VIT_E_ARG;
   if (n_seqs < 1 || n_q_heads < 1 || n_splits < 2 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
   if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
-  if (v->codec < VIT_CODEC_F16 || v->codec > VIT_CODEC_ROT4) return VIT_E_UNSUPPORTED;
-  if (v->codec == VIT_CODEC_ROT4 && !v->signs) return VIT_E_ARG;
+  if (v->codec < VIT_CODEC_F16 || v->codec > VIT_CODEC_ROT3) return VIT_E_UNSUPPORTED;
+  if (is_rotated(v->codec) && !v->signs) return VIT_E_ARG;
   if (!aligned(workspace, 16) || !aligned(out, 16)) return VIT_E_ALIGN;
   vit::ReduceArgs a{};
   a.ws_o = workspace;
@@ -421,7 +426,7 @@ int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_h
   a.out = out;
   a.n_q_heads = n_q_heads;
   a.n_splits = n_splits;
-  a.rotate = v->codec == VIT_CODEC_ROT4 ? 1 : 0;
+  a.rotate = is_rotated(v->codec) ? 1 : 0;
   load_signs(v, a.vsigns);
   const dim3 grid(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(n_seqs));
   return vit::launch_reduce(grid, static_cast<hipStream_t>(stream), a) == hipSuccess ? VIT_OK : VIT_E_HIP;

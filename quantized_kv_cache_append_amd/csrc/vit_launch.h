@@ -134,6 +134,7 @@ hipError_t launch_decode_k0(int vc, int nt, dim3 grid, hipStream_t stream, const
 hipError_t launch_decode_k1(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
+hipError_t launch_decode_k4(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
 // both probe kernels (logits over grid (n_chunks, Hkv, S), then the mass);
 // ev brackets the logits kernel

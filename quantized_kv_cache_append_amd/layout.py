@@ -10,7 +10,7 @@ the plane arrays; nothing here is on the decode path.
 
 import numpy as np
 
-ROW_BYTES = {"f16": 256, "q8_0": 128, "q4_0": 64, "rot4": 64}
+ROW_BYTES = {"f16": 256, "q8_0": 128, "q4_0": 64, "rot4": 64, "rot3": 48}
 TILE = 32
 D = 128
 
@@ -57,6 +57,37 @@ def _v_map(codec):
     return np.broadcast_to(off, (TILE, D)), np.broadcast_to(shift, (TILE, D))
 
 
+def _rot3_bitpos(side):
+    """Bit offset (within a tile) of the 3-bit code of (row p, channel ch)
+    [32, 128], code bit k at offset + k (little-endian bit order)."""
+    p = np.arange(TILE)[:, None]
+    ch = np.arange(D)[None, :]
+    if side == "k":
+        # unit (h, g, r) of 12 bytes; block b's group at byte 3b, code j at bit 3j
+        h, r, b, g, j = p >> 4, p & 15, ch >> 5, (ch & 31) >> 3, ch & 7
+        return ((((h * 4 + g) * 16 + r) * 12 + 3 * b) * 8 + 3 * j).astype(np.int64)
+    # unit (u, g8, n16) of 12 bytes; N-tile (ch >> 4) & 3 at byte 3c, row j at bit 3j
+    u, g8, n16, c, j = ch >> 6, p >> 3, ch & 15, (ch >> 4) & 3, p & 7
+    return (((((u * 4 + g8) * 16 + n16) * 12) + 3 * c) * 8 + 3 * j).astype(np.int64)
+
+
+def _rot3_unpack(side, tiles):
+    bits = np.unpackbits(tiles, axis=-1, bitorder="little")
+    pos = _rot3_bitpos(side)
+    c = bits[..., pos] | (bits[..., pos + 1] << 1) | (bits[..., pos + 2] << 2)
+    return c.astype(np.uint8)
+
+
+def _rot3_pack(side, codes_tiles, tiles):
+    """codes_tiles [..., 32, 128] -> tiles [..., 32 * 48] (every bit rewritten)."""
+    pos = _rot3_bitpos(side)
+    bits = np.zeros(tiles.shape[:-1] + (tiles.shape[-1] * 8,), dtype=np.uint8)
+    c = np.asarray(codes_tiles, dtype=np.uint8)
+    for k in range(3):
+        bits[..., pos + k] = (c >> k) & 1
+    tiles[...] = np.packbits(bits, axis=-1, bitorder="little")
+
+
 def _canon_to_codes(codec, rows):
     """Canonical row bytes [..., RB] -> logical codes [..., 128]."""
     if codec == "f16":
@@ -78,9 +109,12 @@ def _codes_to_canon(codec, codes):
 
 def unpack_codes(codec, side, raw, n_seqs, n_kv_heads, capacity):
     """Physical code bytes -> logical codes [S, H, capacity, 128]
-    (uint16 fp16 bits for f16, int8 for q8_0, 0..15 for q4_0 / rot4)."""
+    (uint16 fp16 bits for f16, int8 for q8_0, 0..15 for q4_0 / rot4, 0..7
+    for rot3)."""
     rb = ROW_BYTES[codec]
     tiles = np.asarray(raw, dtype=np.uint8).reshape(n_seqs, n_kv_heads, capacity // TILE, TILE * rb)
+    if codec == "rot3":
+        return _rot3_unpack(side, tiles).reshape(n_seqs, n_kv_heads, capacity, D)
     if side == "k":
         rows = tiles[..., _k_perm(codec)].reshape(n_seqs, n_kv_heads, capacity, rb)
         return _canon_to_codes(codec, rows)
@@ -101,6 +135,9 @@ def pack_codes(codec, side, codes, raw):
     S, H, cap, _ = codes.shape
     rb = ROW_BYTES[codec]
     tiles = raw.reshape(S, H, cap // TILE, TILE * rb)
+    if codec == "rot3":
+        _rot3_pack(side, codes.reshape(S, H, cap // TILE, TILE, D), tiles)
+        return raw
     if side == "k":
         canon = _codes_to_canon(codec, codes).reshape(S, H, cap // TILE, TILE, rb)
         tiles[..., _k_perm(codec)] = canon

@@ -42,20 +42,20 @@ def test_status_strings(lib):
     assert _lib.status_string(7) == "unknown status"
 
 
-@pytest.mark.parametrize("codec,rb,sb,nb", [(0, 256, 0, 0), (1, 128, 8, 0), (2, 64, 8, 0), (3, 64, 8, 2)])
+@pytest.mark.parametrize("codec,rb,sb,nb", [(0, 256, 0, 0), (1, 128, 8, 0), (2, 64, 8, 0), (3, 64, 8, 2), (4, 48, 8, 0)])
 def test_plane_sizes(lib, codec, rb, sb, nb):
     c, s, n = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.vit_kv_plane_sizes(codec, 2, 8, 128, 200704, ctypes.byref(c), ctypes.byref(s), ctypes.byref(n)) == 0
     rows = 2 * 8 * 200704
     assert (c.value, s.value, n.value) == (rows * rb, rows * sb, rows * nb)
     # bits per value of the plane = the codec's bits per value
-    assert 8 * (c.value + s.value + n.value) / (rows * 128) == {0: 16, 1: 8.5, 2: 4.5, 3: 4.625}[codec]
+    assert 8 * (c.value + s.value + n.value) / (rows * 128) == {0: 16, 1: 8.5, 2: 4.5, 3: 4.625, 4: 3.5}[codec]
 
 
 def test_plane_size_errors(lib):
     z = ctypes.c_size_t()
     r = ctypes.byref(z)
-    assert lib.vit_kv_plane_sizes(4, 1, 1, 128, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
+    assert lib.vit_kv_plane_sizes(5, 1, 1, 128, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
     assert lib.vit_kv_plane_sizes(0, 1, 1, 64, 256, r, r, r) == _lib.VIT_E_UNSUPPORTED
     assert lib.vit_kv_plane_sizes(0, 1, 1, 128, 300, r, r, r) == _lib.VIT_E_CAPACITY
     assert lib.vit_kv_plane_sizes(0, 0, 1, 128, 256, r, r, r) == _lib.VIT_E_ARG
@@ -299,7 +299,7 @@ def test_arm_kernel_events_validation(lib):
 
 
 # ------------------------------------------------------------- host layout
-@pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4", "rot3"])
 @pytest.mark.parametrize("side", ["k", "v"])
 def test_layout_is_a_bijection(codec, side):
     rng = np.random.default_rng(3)
@@ -309,7 +309,7 @@ def test_layout_is_a_bijection(codec, side):
     elif codec == "q8_0":
         codes = rng.integers(-127, 128, (S, H, cap, 128)).astype(np.int8)
     else:
-        codes = rng.integers(0, 16, (S, H, cap, 128)).astype(np.uint8)
+        codes = rng.integers(0, 8 if codec == "rot3" else 16, (S, H, cap, 128)).astype(np.uint8)
     raw = np.zeros(S * H * cap * layout.ROW_BYTES[codec], np.uint8)
     layout.pack_codes(codec, side, codes, raw)
     back = layout.unpack_codes(codec, side, raw, S, H, cap)

@@ -8,7 +8,7 @@ import pytest
 
 from gpu_helpers import append_rows, compare_plane_rows, make_plane, say, torch_cuda
 
-CODECS = ["f16", "q8_0", "q4_0", "rot4"]
+CODECS = ["f16", "q8_0", "q4_0", "rot4", "rot3"]
 D = 128
 
 
@@ -51,7 +51,7 @@ def test_append_bit_exact(codec, side):
     say(f"[append] codec={codec} side={side}")
     S, H, cap = 3, 2, 512
     rng = np.random.default_rng(1000 + 10 * CODECS.index(codec) + (side == "v"))
-    signs = rng.integers(0, 256, 16, dtype=np.uint8) if codec == "rot4" else None
+    signs = rng.integers(0, 256, 16, dtype=np.uint8) if codec in ("rot4", "rot3") else None
     plane = make_plane(codec, side, S, H, cap, signs)
     edge = _edge_rows()
     written = {}
@@ -82,13 +82,13 @@ def test_append_bit_exact(codec, side):
             elif codec == "q8_0":
                 assert np.all(untouched.astype(np.int8) == -1)
             else:
-                assert np.all(untouched == 15)
+                assert np.all(untouched == (7 if codec == "rot3" else 15))  # every code bit set
             if "scales" in view:
                 assert np.all(view["scales"][s, h, mask] == 0xFFFF)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("codec", ["q4_0", "rot4", "q8_0"])
+@pytest.mark.parametrize("codec", ["q4_0", "rot4", "q8_0", "rot3"])
 def test_append_many_random_rows(codec):
     """20k seeded rows per codec (heavy tails, outliers, tiny rows) through
     the K and V layouts; exercises the correctly rounded sqrt of rot4."""
@@ -96,7 +96,7 @@ def test_append_many_random_rows(codec):
     say(f"[append-many] codec={codec}")
     S, H, cap = 2, 4, 2560
     rng = np.random.default_rng(77 + CODECS.index(codec))
-    signs = rng.integers(0, 256, 16, dtype=np.uint8) if codec == "rot4" else None
+    signs = rng.integers(0, 256, 16, dtype=np.uint8) if codec in ("rot4", "rot3") else None
     x = rng.standard_normal((S, cap, H, D)).astype(np.float32)
     hit = rng.random(x.shape) < 0.01
     x[hit] = rng.standard_t(3, int(hit.sum())).astype(np.float32)

@@ -15,7 +15,7 @@ import pytest
 import synth
 from gpu_helpers import append_rows, check_close, fill_plane_synth, make_plane, ref_unit, say, torch_cuda
 
-CODECS = ["f16", "q8_0", "q4_0", "rot4"]
+CODECS = ["f16", "q8_0", "q4_0", "rot4", "rot3"]
 D = 128
 
 
@@ -32,8 +32,8 @@ def _run_small(kc, vc, G, lens, n_splits, seed, S=2, H=2, cap=512, vmul=1.0, kmu
     import quantized_kv_cache_append_amd as vit
 
     rng = np.random.default_rng(seed)
-    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
-    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc == "rot4" else None
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc in ("rot4", "rot3") else None
+    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc in ("rot4", "rot3") else None
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     Lmax = max(lens)
@@ -77,7 +77,7 @@ def test_gqa_widths(G):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("vc", ["q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("vc", ["q8_0", "q4_0", "rot4", "rot3"])
 @pytest.mark.parametrize("vmul", [1e-5, 1e-3, 1e2])
 def test_v_magnitude_range(vc, vmul):
     """V rows far from unit scale: the P.V operand (probability times V block
@@ -145,7 +145,7 @@ def test_kernel_events_bracket_the_decode_kernel():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kc,vc", [("q8_0", "q8_0"), ("rot4", "q4_0"), ("f16", "rot4")])
+@pytest.mark.parametrize("kc,vc", [("q8_0", "q8_0"), ("rot4", "q4_0"), ("f16", "rot4"), ("rot3", "rot3")])
 def test_fused_append_matches_separate_append(kc, vc):
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
@@ -160,8 +160,8 @@ def test_fused_append_matches_separate_append(kc, vc):
     q = torch.from_numpy(_rand_rows(rng, (S, H * G, D))).cuda()
     planes = []
     for fused in (False, True):
-        K = make_plane(kc, "k", S, H, cap, ks if kc == "rot4" else None)
-        V = make_plane(vc, "v", S, H, cap, ks if vc == "rot4" else None)
+        K = make_plane(kc, "k", S, H, cap, ks if kc in ("rot4", "rot3") else None)
+        V = make_plane(vc, "v", S, H, cap, ks if vc in ("rot4", "rot3") else None)
         # rows 0 .. max(len)-2 of every sequence; the new row then lands at len-1
         T = max(lens) - 1
         append_rows(K, kx[:, :T], [0] * S)
@@ -202,8 +202,8 @@ def _run_workload(cfg, units, layers=(0,)):
     scale = 1.0 / math.sqrt(D)
     for layer in layers:
         kc, vc = cmap[layer]
-        ks = synth.sign_mask(cfg, layer, "k") if kc == "rot4" else None
-        vs = synth.sign_mask(cfg, layer, "v") if vc == "rot4" else None
+        ks = synth.sign_mask(cfg, layer, "k") if kc in ("rot4", "rot3") else None
+        vs = synth.sign_mask(cfg, layer, "v") if vc in ("rot4", "rot3") else None
         say(f"[workload {c['name']}] layer {layer} K={kc} V={vc} units={units}")
         K = make_plane(kc, "k", S, H, cap, ks)
         V = make_plane(vc, "v", S, H, cap, vs)

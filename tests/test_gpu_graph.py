@@ -28,8 +28,8 @@ def test_captured_step_replays_match_eager(kc, vc, G):
     rng = np.random.default_rng(2024 + G)
     S, H, cap, n_splits = 2, 2, 512, 3
     lens = [300, 97]
-    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
-    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc == "rot4" else None
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc in ("rot4", "rot3") else None
+    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc in ("rot4", "rot3") else None
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     kx = rng.standard_normal((S, max(lens), H, D)).astype(np.float32)

@@ -34,8 +34,8 @@ def _run(kc, vc, G, q_len, lens, n_splits, fused, seed, S=2, H=2, cap=512):
     import quantized_kv_cache_append_amd as vit
 
     rng = np.random.default_rng(seed)
-    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
-    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc == "rot4" else None
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc in ("rot4", "rot3") else None
+    vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc in ("rot4", "rot3") else None
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     Lmax = max(lens)
@@ -87,6 +87,8 @@ CASES = [
     ("f16", "rot4", 1, 4, [5, 260], 5, True),      # 4 rows: narrow layout; a 5-row sequence
     ("q8_0", "f16", 8, 2, [70, 200], 1, False),   # 16 rows, one split (normalised output straight from decode)
     ("rot4", "rot4", 4, 3, [31, 97], 4, True),     # 12 rows
+    ("rot3", "rot3", 2, 4, [64, 130], 3, True),    # 8 rows, 3-bit rotated K and V
+    ("rot3", "q8_0", 4, 4, [40, 300], 2, True),    # 16 rows
 ]
 
 
@@ -138,8 +140,8 @@ def _run_workload_verify(cfg, q_len, units):
     S, Hq, H, cap, L = c["seqs"], c["hq"], c["hkv"], c["capacity"], c["ctx"]
     G = Hq // H
     kc, vc = synth.codec_map(cfg)[0]
-    ks = synth.sign_mask(cfg, 0, "k") if kc == "rot4" else None
-    vs = synth.sign_mask(cfg, 0, "v") if vc == "rot4" else None
+    ks = synth.sign_mask(cfg, 0, "k") if kc in ("rot4", "rot3") else None
+    vs = synth.sign_mask(cfg, 0, "v") if vc in ("rot4", "rot3") else None
     say(f"[verify {c['name']}] K={kc} V={vc} q_len={q_len} units={units}")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1000 + cfg)

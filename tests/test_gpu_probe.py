@@ -39,17 +39,17 @@ def _check_scores(got, prev, mass, decay, L, what):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kc", ["f16", "q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("kc", ["f16", "q8_0", "q4_0", "rot4", "rot3"])
 @pytest.mark.parametrize("G", [1, 4, 16])
 def test_probe_scores_match_oracle(kc, G):
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
 
     say(f"[probe] K={kc} G={G}")
-    rng = np.random.default_rng(300 + 10 * G + ["f16", "q8_0", "q4_0", "rot4"].index(kc))
+    rng = np.random.default_rng(300 + 10 * G + ["f16", "q8_0", "q4_0", "rot4", "rot3"].index(kc))
     S, H, cap = 3, 2, 512
     lens = [300, 37, 1]
-    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc == "rot4" else None
+    ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc in ("rot4", "rot3") else None
     K = make_plane(kc, "k", S, H, cap, ks)
     kx = _rows(rng, (S, cap, H, D))
     append_rows(K, kx, [0] * S)
@@ -98,7 +98,7 @@ def _run_probe_workload(cfg, seqs):
     c = synth.CONFIGS[cfg]
     S, Hq, H, cap, L = c["seqs"], c["hq"], c["hkv"], c["capacity"], c["ctx"]
     kc = synth.codec_map(cfg)[0][0]
-    ks = synth.sign_mask(cfg, 0, "k") if kc == "rot4" else None
+    ks = synth.sign_mask(cfg, 0, "k") if kc in ("rot4", "rot3") else None
     say(f"[probe {c['name']}] K={kc} S={S} Hq={Hq} L={L} sampled seqs {seqs}")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2000 + cfg)

@@ -15,7 +15,8 @@ from gpu_helpers import append_rows, fill_plane_synth, make_plane, say, torch_cu
 from oracle import codecs, vbr
 
 D = 128
-PAIRS = [("f16", "q8_0"), ("f16", "q4_0"), ("f16", "rot4"), ("q8_0", "q4_0"), ("q8_0", "rot4")]
+PAIRS = [("f16", "q8_0"), ("f16", "q4_0"), ("f16", "rot4"), ("q8_0", "q4_0"), ("q8_0", "rot4"),
+         ("f16", "rot3"), ("q8_0", "rot3"), ("q4_0", "rot3")]
 
 
 def _rows(rng, shape):
@@ -50,7 +51,7 @@ def test_transcode_matches_oracle(src_c, dst_c, side):
     rng = np.random.default_rng(900 + 10 * PAIRS.index((src_c, dst_c)) + (side == "v"))
     S, H, cap = 3, 2, 512
     n_rows = [300, 37, 512]  # ragged: a partial tile, a partial 8-row group, every row
-    dsigns = rng.integers(0, 256, 16, dtype=np.uint8) if dst_c == "rot4" else None
+    dsigns = rng.integers(0, 256, 16, dtype=np.uint8) if dst_c in ("rot4", "rot3") else None
     src = make_plane(src_c, side, S, H, cap)
     x = _rows(rng, (S, cap, H, D))
     append_rows(src, x, [0] * S)

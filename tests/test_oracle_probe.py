@@ -34,9 +34,9 @@ def test_probe_mass_bruteforce_tiny():
     assert np.allclose(got, expect, rtol=1e-12, atol=1e-15)
 
 
-@pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("codec", ["f16", "q8_0", "q4_0", "rot4", "rot3"])
 def test_probe_mass_sums_to_the_query_heads(codec):
-    signs = np.full(16, 0x5A, dtype=np.uint8) if codec == "rot4" else None
+    signs = np.full(16, 0x5A, dtype=np.uint8) if codec in ("rot4", "rot3") else None
     m = probe.probe_mass(_rows(2, 4) * 0.5, _rows(3, 300), codec, SCALE, signs)
     assert m.shape == (300,) and np.all(m > 0)
     assert m.sum() == pytest.approx(4.0, rel=1e-12)

@@ -30,11 +30,11 @@ def test_transcode_to_own_codec_is_identity(codec):
         assert np.array_equal(t[key], q[key]), key
 
 
-@pytest.mark.parametrize("dst", ["q8_0", "q4_0", "rot4"])
+@pytest.mark.parametrize("dst", ["q8_0", "q4_0", "rot4", "rot3"])
 def test_transcode_from_f16_equals_encoding_the_values(dst):
     # rows that are already fp16 values come out of an f16 plane unchanged
     x = _rows(2).astype(np.float16).astype(np.float32)
-    signs = (np.arange(16) * 37 % 256).astype(np.uint8) if dst == "rot4" else None
+    signs = (np.arange(16) * 37 % 256).astype(np.uint8) if dst in ("rot4", "rot3") else None
     t = vbr.transcode("f16", dst, codecs.quantize("f16", x), dst_signs=signs)
     ref = codecs.quantize(dst, x, signs)
     for key in ref:
