@@ -61,7 +61,9 @@ KERNEL_SOURCES = {
     "transcode": ("append.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
     "probe_logits": ("probe.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
 }
-TRANSCODE_PAIRS = ("f16:q8_0", "f16:q4_0", "f16:rot4", "q8_0:q4_0", "q8_0:rot4")
+TRANSCODE_PAIRS = ("f16:q8_0", "f16:q4_0", "f16:rot4", "f16:rot3", "q8_0:q4_0", "q8_0:rot4", "q8_0:rot3", "q4_0:rot3")
+CODEC_NAMES = ("f16", "q8_0", "q4_0", "rot4", "rot3")
+ROTATED = ("rot4", "rot3")
 
 
 def kernel_source_hash(kind="decode"):
@@ -76,7 +78,7 @@ def kernel_source_hash(kind="decode"):
 
 
 def _row_bytes(codec):
-    return {"f16": 256, "q8_0": 136, "q4_0": 72, "rot4": 74}[codec]
+    return {"f16": 256, "q8_0": 136, "q4_0": 72, "rot4": 74, "rot3": 56}[codec]
 
 
 def _device_rows(torch, gen, shape, dist, scales=None):
@@ -128,6 +130,10 @@ def run_gpu(args):
     if QL > 1 and ("ubatch" in cfg or (Hq // H) * QL > 16 or QL > 4):
         raise SystemExit(f"--q-len {QL} needs a single-layer workload with (n_q_heads / n_kv_heads) x q_len <= 16")
     cmap = synth.codec_map(cfgno)
+    if args.codecs:
+        if cfg["layers"] != 1:
+            raise SystemExit("--codecs needs a single-layer workload")
+        cmap = [tuple(args.codecs.split(":"))]
     n_layers = cfg["layers"]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0x5EED2026 + cfgno)
@@ -147,8 +153,8 @@ def run_gpu(args):
     layers = []
     chan_scale = {}
     for li, (kc, vc) in enumerate(cmap):
-        ks = synth.sign_mask(cfgno, li, "k") if kc == "rot4" else None
-        vs = synth.sign_mask(cfgno, li, "v") if vc == "rot4" else None
+        ks = synth.sign_mask(cfgno, li, "k") if kc in ROTATED else None
+        vs = synth.sign_mask(cfgno, li, "v") if vc in ROTATED else None
         lay = Layer(vit, cfg, kc, vc, replicas, ks, vs)
         for side, plane in (("k", lay.K[0]), ("v", lay.V[0])):
             sc = None
@@ -310,7 +316,7 @@ def run_transcode(args):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0x5EED2026 + 77)
     torch.cuda.set_device(torch.device("cuda:0"))
-    signs = synth.sign_mask(5, 0, side) if dst_c == "rot4" else None
+    signs = synth.sign_mask(5, 0, side) if dst_c in ROTATED else None
     src = vit.KVPlane(src_c, side, S, H, cap)
     dst = vit.KVPlane(dst_c, side, S, H, cap, signs)
     sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
@@ -365,7 +371,7 @@ def cpu_baseline_transcode(r, budget_s=15.0):
     n = 16384
     rows = synth.kv_rows(5, r["side"], 0, 0, 0, 0, n)
     q_src = codecs.quantize(r["src_c"], rows)
-    signs = synth.sign_mask(5, 0, r["side"]) if r["dst_c"] == "rot4" else None
+    signs = synth.sign_mask(5, 0, r["side"]) if r["dst_c"] in ROTATED else None
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -395,8 +401,8 @@ def run_probe(args):
     cfgno = WORKLOADS[args.workload]
     cfg = synth.CONFIGS[cfgno]
     S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
-    kc = synth.codec_map(cfgno)[0][0]
-    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
+    kc = args.codecs.split(":")[0] if args.codecs else synth.codec_map(cfgno)[0][0]
+    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0x5EED2026 + 99 + cfgno)
     torch.cuda.set_device(torch.device("cuda:0"))
@@ -474,7 +480,7 @@ def cpu_baseline_probe(r, budget_s=15.0):
         limiter = None
     cfgno, H, Hq, L, kc = r["cfgno"], r["H"], r["Hq"], r["L"], r["kc"]
     n = min(L, 8192)
-    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
+    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
     keys = np.stack([synth.kv_rows(cfgno, "k", 0, 0, h, 0, n) for h in range(H)])
     q = synth.q_rows(cfgno, 0, 0, Hq)
     done = 0
@@ -604,8 +610,8 @@ def cpu_baseline(r, budget_s=15.0):
     cfgno, L, S, H, Hq, QL = r["cfgno"], r["L"], r["S"], r["H"], r["Hq"], r["QL"]
     G = Hq // H
     kc, vc = r["cmap"][0]
-    ks = synth.sign_mask(cfgno, 0, "k") if kc == "rot4" else None
-    vs = synth.sign_mask(cfgno, 0, "v") if vc == "rot4" else None
+    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
+    vs = synth.sign_mask(cfgno, 0, "v") if vc in ROTATED else None
     units = [(s, h) for s in range(S) for h in range(H)]
     rows_unit = min(L, 8192)  # longer contexts are timed on an 8192-row slice and scaled
     prep = []
@@ -643,9 +649,11 @@ def cpu_baseline(r, budget_s=15.0):
                        "dequantize cache + fp64 attention")}
 
 
-def profile_tag(workload, q_len):
-    """Name of a workload's profiles: the workload, plus the verify width."""
-    return workload if q_len == 1 else f"{workload}_verify{q_len}"
+def profile_tag(workload, q_len, codecs=None):
+    """Name of a workload's bench line and profiles: the workload, its codec
+    pair when overridden, and the verify width."""
+    tag = workload if not codecs else f"{workload}_{codecs.replace(':', '_')}"
+    return tag if q_len == 1 else f"{tag}_verify{q_len}"
 
 
 def load_traffic(kind, tag, n_splits=None):
@@ -762,6 +770,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence verified per step (vit_attn_decode_mq when > 1)")
+    ap.add_argument("--codecs", default=None, metavar="K:V",
+                    help="override a single-layer workload's codec pair, e.g. rot3:rot3 ("
+                    + ", ".join(CODEC_NAMES) + ")")
     ap.add_argument("--transcode", default=None, choices=TRANSCODE_PAIRS,
                     help="time a VBR degrade step (vit_kv_transcode) of one ladder-slot tensor instead")
     ap.add_argument("--side", default="k", choices=("k", "v"), help="plane side for --transcode")
@@ -787,8 +798,9 @@ def main():
             b = f"python3 bench.py --probe --workload {args.workload}"
         else:
             kind = "decode"
-            w = profile_tag(args.workload, args.q_len)
-            b = f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
+            w = profile_tag(args.workload, args.q_len, args.codecs)
+            b = (f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
+                 + (f" --codecs {args.codecs}" if args.codecs else ""))
         d = f"probe_{w}" if args.probe else w  # directory under PROF
         cmds = [f"{b} --no-cpu-baseline > PROF/{d}/bench.json",
                 f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{d}/trace -o run -- "
@@ -802,6 +814,9 @@ def main():
                 f"{b} --summarize PROF"]
         summarize_profiles(kind, w, args.summarize, cmds, subdir=d)
         return
+    if args.codecs and any(c not in CODEC_NAMES for c in args.codecs.split(":")) or \
+            (args.codecs and len(args.codecs.split(":")) != 2):
+        raise SystemExit(f"--codecs takes K:V with codecs from {CODEC_NAMES}")
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path shards by (sequence, KV head) with no exchange; see DESIGN.md)",
@@ -819,7 +834,7 @@ def main():
     r = run_gpu(args)
     cfg = r["cfg"]
     tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
-    traffic = load_traffic("decode", profile_tag(args.workload, r["QL"]), r["n_splits"])
+    traffic = load_traffic("decode", profile_tag(args.workload, r["QL"], args.codecs), r["n_splits"])
     line = {
         "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(tok_s, 1),
@@ -831,10 +846,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/q4_0/rot4/f16 codes, fp16 MFMA operands (hi+lo split), fp32 accumulate",
+        "dtype": "q8_0/q4_0/rot4/rot3/f16 codes, fp16 MFMA operands (hi+lo split), fp32 accumulate",
         "data": "synthetic (seeded device normals shaped like the workload; no model weights or dataset)",
         "config": {
-            "workload": profile_tag(cfg["name"], r["QL"]),
+            "workload": profile_tag(cfg["name"], r["QL"], args.codecs),
             "n_seqs": r["S"], "n_q_heads": r["Hq"], "n_kv_heads": r["H"], "head_dim": D,
             "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"], "query_tokens_per_seq": r["QL"],
             "codecs": "ladder (seeded per layer/side)" if r["n_layers"] > 1 else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",

@@ -26,6 +26,15 @@ def test_help_and_one_gpu_only():
 def test_profile_tags():
     assert bench.profile_tag("batched", 1) == "batched"
     assert bench.profile_tag("batched", 4) == "batched_verify4"
+    assert bench.profile_tag("lowbit", 1, "rot3:rot3") == "lowbit_rot3_rot3"
+    assert bench.profile_tag("lowbit", 3, "rot3:q4_0") == "lowbit_rot3_q4_0_verify3"
+
+
+def test_codec_override_is_checked():
+    r = _run("--codecs", "rot3")
+    assert r.returncode != 0 and "K:V" in r.stderr
+    r = _run("--codecs", "rot5:rot3")
+    assert r.returncode != 0
 
 
 def test_traffic_is_taken_only_on_current_sources(tmp_path, monkeypatch):
