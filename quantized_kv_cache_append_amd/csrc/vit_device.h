@@ -205,6 +205,50 @@ __device__ inline void block_max_abs(float (&a)[N]) {
   max_step<1>(a);
 }
 
+// Per lane: b where lane bit set in `mask` (a constant lane pattern), else a.
+__device__ inline float lane_select(uint64_t mask, float a, float b) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+
+// N block quantities v[i] that every lane of a half-wave holds (the same
+// value on all 32 lanes, e.g. after a block reduction) mapped through f once
+// per slot instead of on every lane: lane i (and i + 16) of each half-wave
+// evaluates slot i, and ds_bpermute hands both results back to every lane.
+// f(v, a, b) writes two results; for other slot counts than 8 and 16 the
+// direct per-lane evaluation is used.  The arithmetic of f is unchanged,
+// only where it runs.  (A full-wave quantity, the same on all 64 lanes,
+// works too.)
+template <int N, class F>
+__device__ inline void per_slot(const float (&v)[N], int lane, F f, float (&a)[N], float (&b)[N]) {
+  if constexpr (N != 8 && N != 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f(v[i], a[i], b[i]);
+  } else {
+    // v[lane % N] by a binary tree of selects on the bits of lane % N
+    // (explicit v_cndmask with constant lane masks: written as ?:, the
+    // selects become a lane-indexed stack array in scratch memory)
+    constexpr uint64_t kBit[4] = {0xAAAAAAAAAAAAAAAAull, 0xCCCCCCCCCCCCCCCCull, 0xF0F0F0F0F0F0F0F0ull,
+                                  0xFF00FF00FF00FF00ull};
+    float t[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) t[i] = v[i];
+#pragma unroll
+    for (int level = 0, n = N; n > 1; ++level, n >>= 1)
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) t[i] = lane_select(kBit[level], t[2 * i], t[2 * i + 1]);
+    float A, B;
+    f(t[0], A, B);
+    const int base = lane & 32;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      a[i] = __shfl(A, base | i, kWave);
+      b[i] = __shfl(B, base | i, kWave);
+    }
+  }
+}
+
 template <int R>
 __device__ inline void encode_f16(const float (&x0)[R], const float (&x1)[R], RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
@@ -224,7 +268,7 @@ __device__ inline int8_t q8_code(float x, float inv) {
 }
 
 template <int R>
-__device__ inline void encode_q8_0(const float (&x0)[R], const float (&x1)[R], RowCodes (&rc)[R]) {
+__device__ inline void encode_q8_0(const float (&x0)[R], const float (&x1)[R], int lane, RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
   float m[2 * R];
 #pragma unroll
@@ -233,60 +277,48 @@ __device__ inline void encode_q8_0(const float (&x0)[R], const float (&x1)[R], R
     m[2 * r + 1] = x1[r];
   }
   block_max_abs(m);
+  // d = amax / 127 and 1/d once per (row, block); the fp16 bits of d travel
+  // as a float
+  float sb[2 * R], inv[2 * R];
+  per_slot(m, lane, [](float amax, float& bits, float& iv) {
+#pragma clang fp contract(off)
+    const float d = amax / 127.0f;
+    bits = __uint_as_float(f16_bits(d));
+    iv = recip_or_zero(d);
+  }, sb, inv);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float d0 = m[2 * r] / 127.0f;
-    const float d1 = m[2 * r + 1] / 127.0f;
-    const float i0 = recip_or_zero(d0), i1 = recip_or_zero(d1);
     rc[r] = RowCodes{};
-    rc[r].c0 = static_cast<uint8_t>(q8_code(x0[r], i0));
-    rc[r].c1 = static_cast<uint8_t>(q8_code(x1[r], i1));
-    rc[r].s0 = f16_bits(d0);
-    rc[r].s1 = f16_bits(d1);
+    rc[r].c0 = static_cast<uint8_t>(q8_code(x0[r], inv[2 * r]));
+    rc[r].c1 = static_cast<uint8_t>(q8_code(x1[r], inv[2 * r + 1]));
+    rc[r].s0 = static_cast<uint16_t>(__float_as_uint(sb[2 * r]));
+    rc[r].s1 = static_cast<uint16_t>(__float_as_uint(sb[2 * r + 1]));
   }
 }
 
-// q4_0 block scales d = m / -8 from the first element of largest magnitude.
-// key: |x| bits (monotone for non-negative floats) high, inverted index low,
-// so the max picks the largest magnitude and, among equals, the first index.
-template <int M, int N>
-__device__ inline void key_max_step(uint32_t (&hi)[N], uint32_t (&lo)[N]) {
-  uint32_t oh[N], ol[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    oh[i] = xshfl<M>(hi[i]);
-    ol[i] = xshfl<M>(lo[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const bool take = oh[i] > hi[i] || (oh[i] == hi[i] && ol[i] > lo[i]);
-    hi[i] = take ? oh[i] : hi[i];
-    lo[i] = take ? ol[i] : lo[i];
-  }
-}
+// q4_0: the signed value m of the first element of largest magnitude in
+// each block (channel order = lane order within the half-wave): the block
+// max |x|, then a ballot of the lanes holding it and the first of them.
 template <int N>
-__device__ inline void q4_block_scales(const float (&x)[N], int lane, float (&d)[N]) {
-#pragma clang fp contract(off)
-  uint32_t hi[N], lo[N];
-  const uint32_t j = static_cast<uint32_t>(lane & 31);
+__device__ inline void q4_block_signed_max(const float (&x)[N], int lane, float (&m)[N]) {
+  float a[N], mx[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    hi[i] = __float_as_uint(fabsf(x[i]));
-    lo[i] = 31u - j;
+    a[i] = fabsf(x[i]);
+    mx[i] = a[i];
   }
-  key_max_step<16>(hi, lo);
-  key_max_step<8>(hi, lo);
-  key_max_step<4>(hi, lo);
-  key_max_step<2>(hi, lo);
-  key_max_step<1>(hi, lo);
-  float m[N];
+  max_step<16>(mx);
+  max_step<8>(mx);
+  max_step<4>(mx);
+  max_step<2>(mx);
+  max_step<1>(mx);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const int src = (lane & 32) | static_cast<int>(31u - lo[i]);
-    m[i] = __shfl(x[i], src, kWave);
+    const uint64_t eq = __builtin_amdgcn_ballot_w64(a[i] == mx[i]);
+    // a half-wave's mask is never 0: its maximum is one of its values
+    const uint32_t half = lane < 32 ? static_cast<uint32_t>(eq) : static_cast<uint32_t>(eq >> 32);
+    m[i] = __shfl(x[i], (lane & 32) | static_cast<int>(__builtin_ctz(half)), kWave);
   }
-#pragma unroll
-  for (int i = 0; i < N; ++i) d[i] = hi[i] == 0u ? 0.0f : m[i] / -8.0f;
 }
 
 __device__ inline uint32_t q4_code(float x, float inv) {
@@ -299,20 +331,29 @@ __device__ inline uint32_t q4_code(float x, float inv) {
 template <int R>
 __device__ inline void encode_q4_0(const float (&x0)[R], const float (&x1)[R], int lane, RowCodes (&rc)[R]) {
 #pragma clang fp contract(off)
-  float x[2 * R], d[2 * R];
+  float x[2 * R], m[2 * R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     x[2 * r] = x0[r];
     x[2 * r + 1] = x1[r];
   }
-  q4_block_scales(x, lane, d);
+  q4_block_signed_max(x, lane, m);
+  // d = m / -8 (+0 for a zero block, where m is +-0) and 1/d once per
+  // (row, block); the fp16 bits of d travel as a float
+  float sb[2 * R], inv[2 * R];
+  per_slot(m, lane, [](float mm, float& bits, float& iv) {
+#pragma clang fp contract(off)
+    const float d = mm == 0.0f ? 0.0f : mm / -8.0f;
+    bits = __uint_as_float(f16_bits(d));
+    iv = recip_or_zero(d);
+  }, sb, inv);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     rc[r] = RowCodes{};
-    rc[r].c0 = q4_code(x0[r], recip_or_zero(d[2 * r]));
-    rc[r].c1 = q4_code(x1[r], recip_or_zero(d[2 * r + 1]));
-    rc[r].s0 = f16_bits(d[2 * r]);
-    rc[r].s1 = f16_bits(d[2 * r + 1]);
+    rc[r].c0 = q4_code(x0[r], inv[2 * r]);
+    rc[r].c1 = q4_code(x1[r], inv[2 * r + 1]);
+    rc[r].s0 = static_cast<uint16_t>(__float_as_uint(sb[2 * r]));
+    rc[r].s1 = static_cast<uint16_t>(__float_as_uint(sb[2 * r + 1]));
   }
 }
 
@@ -345,6 +386,15 @@ __device__ inline void wht_stage(float (&w0)[R], float (&w1)[R], int lane) {
     w0[r] = upper ? p0[r] - w0[r] : w0[r] + p0[r];
     w1[r] = upper ? p1[r] - w1[r] : w1[r] + p1[r];
   }
+}
+
+// A block's RMS r = sqrt(sum * (1/32)) as fp16 bits and its reciprocal
+// (0 for r == 0), the per-block step of rot4 and rot3.
+__device__ inline void block_rms(float sum, float& bits, float& ib) {
+#pragma clang fp contract(off)
+  const float r = sqrt_rn(sum * 0.03125f);
+  bits = __uint_as_float(f16_bits(r));
+  ib = r > 0.0f ? 1.0f / r : 0.0f;
 }
 
 // Sign flip and unnormalised Walsh-Hadamard transform of R rows: w = H (s . x).
@@ -396,15 +446,21 @@ __device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], i
   sum_step<4>(ss);
   sum_step<2>(ss);
   sum_step<1>(ss);
+  // n = ||x||, its fp16 bits and g = 1/n once per row
+  float nb[R], gr[R];
+  per_slot(ss, lane, [](float s2, float& bits, float& g) {
+#pragma clang fp contract(off)
+    const float n = sqrt_rn(s2);
+    bits = __uint_as_float(f16_bits(n));
+    g = n > 0.0f ? 1.0f / n : 0.0f;
+  }, nb, gr);
   float u[2 * R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float n = sqrt_rn(ss[r]);
     rc[r] = RowCodes{};
-    rc[r].norm = f16_bits(n);
-    const float g = n > 0.0f ? 1.0f / n : 0.0f;
-    u[2 * r] = w0[r] * g;
-    u[2 * r + 1] = w1[r] * g;
+    rc[r].norm = static_cast<uint16_t>(__float_as_uint(nb[r]));
+    u[2 * r] = w0[r] * gr[r];
+    u[2 * r + 1] = w1[r] * gr[r];
   }
   // per-block RMS of the whitened values
   float b[2 * R];
@@ -415,16 +471,14 @@ __device__ inline void encode_rot4(const float (&x0)[R], const float (&x1)[R], i
   sum_step<4>(b);
   sum_step<2>(b);
   sum_step<1>(b);
+  float sb[2 * R], ib[2 * R];
+  per_slot(b, lane, block_rms, sb, ib);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float r0 = sqrt_rn(b[2 * r] * 0.03125f);
-    const float r1 = sqrt_rn(b[2 * r + 1] * 0.03125f);
-    rc[r].s0 = f16_bits(r0);
-    rc[r].s1 = f16_bits(r1);
-    const float ib0 = r0 > 0.0f ? 1.0f / r0 : 0.0f;
-    const float ib1 = r1 > 0.0f ? 1.0f / r1 : 0.0f;
-    rc[r].c0 = rot4_index(u[2 * r] * ib0);
-    rc[r].c1 = rot4_index(u[2 * r + 1] * ib1);
+    rc[r].s0 = static_cast<uint16_t>(__float_as_uint(sb[2 * r]));
+    rc[r].s1 = static_cast<uint16_t>(__float_as_uint(sb[2 * r + 1]));
+    rc[r].c0 = rot4_index(u[2 * r] * ib[2 * r]);
+    rc[r].c1 = rot4_index(u[2 * r + 1] * ib[2 * r + 1]);
   }
 }
 
@@ -458,17 +512,15 @@ __device__ inline void encode_rot3(const float (&x0)[R], const float (&x1)[R], i
   sum_step<4>(b);
   sum_step<2>(b);
   sum_step<1>(b);
+  float sb[2 * R], ib[2 * R];
+  per_slot(b, lane, block_rms, sb, ib);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float r0 = sqrt_rn(b[2 * r] * 0.03125f);
-    const float r1 = sqrt_rn(b[2 * r + 1] * 0.03125f);
     rc[r] = RowCodes{};
-    rc[r].s0 = f16_bits(r0);
-    rc[r].s1 = f16_bits(r1);
-    const float ib0 = r0 > 0.0f ? 1.0f / r0 : 0.0f;
-    const float ib1 = r1 > 0.0f ? 1.0f / r1 : 0.0f;
-    rc[r].c0 = rot3_index(w0[r] * ib0);
-    rc[r].c1 = rot3_index(w1[r] * ib1);
+    rc[r].s0 = static_cast<uint16_t>(__float_as_uint(sb[2 * r]));
+    rc[r].s1 = static_cast<uint16_t>(__float_as_uint(sb[2 * r + 1]));
+    rc[r].c0 = rot3_index(w0[r] * ib[2 * r]);
+    rc[r].c1 = rot3_index(w1[r] * ib[2 * r + 1]);
   }
 }
 
@@ -476,7 +528,7 @@ template <int CODEC, int R>
 __device__ inline void encode_rows(const float (&x0)[R], const float (&x1)[R], int lane, const uint32_t signs[4],
                                    RowCodes (&rc)[R]) {
   if constexpr (CODEC == F16) encode_f16(x0, x1, rc);
-  else if constexpr (CODEC == Q8_0) encode_q8_0(x0, x1, rc);
+  else if constexpr (CODEC == Q8_0) encode_q8_0(x0, x1, lane, rc);
   else if constexpr (CODEC == Q4_0) encode_q4_0(x0, x1, lane, rc);
   else if constexpr (CODEC == ROT4) encode_rot4(x0, x1, lane, signs, rc);
   else encode_rot3(x0, x1, lane, signs, rc);
