@@ -60,6 +60,7 @@ KERNEL_SOURCES = {
     "decode": ("decode_impl.h", "decode_k*.hip", "vit_device.h", "vit_launch.h"),
     "transcode": ("append.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
     "probe_logits": ("probe.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
+    "append": ("append.hip", "decode_impl.h", "vit_device.h", "vit_launch.h"),
 }
 TRANSCODE_PAIRS = ("f16:q8_0", "f16:q4_0", "f16:rot4", "f16:rot3", "q8_0:q4_0", "q8_0:rot4", "q8_0:rot3", "q4_0:rot3")
 CODEC_NAMES = ("f16", "q8_0", "q4_0", "rot4", "rot3")
@@ -540,6 +541,126 @@ def main_probe(args):
     print(json.dumps(line), flush=True)
 
 
+def run_append(args):
+    """One ubatch append of the ladder workload: 2048 new rows for each of
+    2 sequences x 8 KV heads (fp32 in, one codec, one side), at rows
+    198,656 .. 200,703 of its 200,704-row slots."""
+    import numpy as np
+    import torch
+
+    import quantized_kv_cache_append_amd as vit
+    import synth
+
+    codec, side = args.append, args.side
+    cfg = synth.CONFIGS[5]
+    S, H, cap, pre, ub = cfg["seqs"], cfg["hkv"], cfg["capacity"], cfg["prefill"], cfg["ubatch"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED2026 + 55)
+    torch.cuda.set_device(torch.device("cuda:0"))
+    signs = synth.sign_mask(5, 0, side) if codec in ROTATED else None
+    plane = vit.KVPlane(codec, side, S, H, cap, signs)
+    sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
+    # distinct source buffers, round-robin, so the 16.8 MB fp32 ubatch is not served from the cache
+    n_src = 16
+    srcs = [_device_rows(torch, gen, (S, ub, H, D), "lognormal", sc) for _ in range(n_src)]
+    torch.cuda.synchronize()
+    print(f"# append {codec} side {side}: S={S} Hkv={H} rows={ub} at {pre}", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    calls = [vit.prepare_append(plane, src, [pre] * S, stream=stream) for src in srcs]
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            calls[i % n_src]()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            calls[i % n_src]()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    for pair in evs:  # create the HIP events (torch does so on first record)
+        for e in pair:
+            e.record(stream)
+    torch.cuda.synchronize()
+    # the append dispatch itself records each pair at its kernel's start and end
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            vit.vit_arm_kernel_events(evs[i][0], evs[i][1])
+            calls[i % n_src]()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    rows = S * H * ub
+    per_launch = rows * (4 * D + _row_bytes(codec))  # fp32 row read + encoded row written
+    return dict(codec=codec, side=side, S=S, H=H, ub=ub, rows=rows, ms_per_step=ms_per_step,
+                mean_ms=float(np.mean(ms)), min_ms=float(np.min(ms)), per_launch_bytes=per_launch,
+                achieved_gbs=per_launch / (float(np.mean(ms)) * 1e-3) / 1e9)
+
+
+def cpu_baseline_append(r, budget_s=15.0):
+    """oracle.codecs.quantize on the host for rows of one stream, scaled."""
+    from oracle import codecs
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    n = 2048
+    rows = synth.kv_rows(5, r["side"], 0, 0, 0, 0, n)
+    signs = synth.sign_mask(5, 0, r["side"]) if r["codec"] in ROTATED else None
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        codecs.quantize(r["codec"], rows, signs)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return {"value": done / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows ({r['codec']}) in {n}-row calls, {el:.1f} s on 1 thread; step = {r['rows']} rows"}
+
+
+def main_append(args):
+    r = run_append(args)
+    tag = f"{r['codec']}_{r['side']}"
+    line = {
+        "metric": "KV append: rows quantized and stored per second + effective GB/s (% of HBM peak), 1 GPU",
+        "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"fp32 rows encoded to {r['codec']}",
+        "data": "synthetic (seeded device normals with log-normal channel scales; no model weights or dataset)",
+        "config": {"workload": f"append_{tag}", "n_seqs": r["S"], "n_kv_heads": r["H"], "head_dim": D,
+                   "ubatch": r["ub"], "codec": r["codec"], "side": r["side"],
+                   "launch": "eager (pre-marshalled C call)"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "append_kernel",
+            "achieved": round(r["achieved_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("append", tag),
+            "algorithmic_bytes_per_launch": r["per_launch_bytes"],
+            "mean_launch_ms": round(r["mean_ms"], 5),
+            "min_launch_ms": round(r["min_ms"], 5),
+        },
+        "kernel_source_hash": kernel_source_hash("append"),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_append(r, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main_transcode(args):
     r = run_transcode(args)
     tag = f"{r['src_c']}_to_{r['dst_c']}_{r['side']}"
@@ -775,7 +896,9 @@ def main():
                     + ", ".join(CODEC_NAMES) + ")")
     ap.add_argument("--transcode", default=None, choices=TRANSCODE_PAIRS,
                     help="time a VBR degrade step (vit_kv_transcode) of one ladder-slot tensor instead")
-    ap.add_argument("--side", default="k", choices=("k", "v"), help="plane side for --transcode")
+    ap.add_argument("--side", default="k", choices=("k", "v"), help="plane side for --transcode / --append")
+    ap.add_argument("--append", default=None, choices=CODEC_NAMES,
+                    help="time one ladder ubatch append (vit_kv_append_quant) of this codec instead")
     ap.add_argument("--probe", action="store_true",
                     help="time an attention-probe scoring event (+ eviction choice) on --workload's K plane instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -792,6 +915,10 @@ def main():
             sc, dc = args.transcode.split(":")
             w = f"{sc}_to_{dc}_{args.side}"
             b = f"python3 bench.py --transcode {args.transcode} --side {args.side}"
+        elif args.append:
+            kind = "append"
+            w = f"{args.append}_{args.side}"
+            b = f"python3 bench.py --append {args.append} --side {args.side}"
         elif args.probe:
             kind = "probe_logits"
             w = args.workload
@@ -801,7 +928,7 @@ def main():
             w = profile_tag(args.workload, args.q_len, args.codecs)
             b = (f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
                  + (f" --codecs {args.codecs}" if args.codecs else ""))
-        d = f"probe_{w}" if args.probe else w  # directory under PROF
+        d = f"probe_{w}" if args.probe else (f"append_{w}" if args.append else w)  # directory under PROF
         cmds = [f"{b} --no-cpu-baseline > PROF/{d}/bench.json",
                 f"rocprofv3 --kernel-trace --stats --output-format csv -d PROF/{d}/trace -o run -- "
                 f"{b} --no-cpu-baseline > PROF/{d}/bench_traced.json",
@@ -830,6 +957,9 @@ def main():
         return
     if args.probe:
         main_probe(args)
+        return
+    if args.append:
+        main_append(args)
         return
     r = run_gpu(args)
     cfg = r["cfg"]

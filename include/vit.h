@@ -338,8 +338,9 @@ size_t vit_probe_select_workspace_bytes(int32_t n_seqs);
 
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
- * thread's next vit_attn_decode, vit_attn_decode_mq, vit_kv_transcode or
- * vit_attn_probe_scores call (for the latter: its logits kernel)
+ * thread's next vit_kv_append_quant, vit_attn_decode, vit_attn_decode_mq,
+ * vit_kv_transcode or vit_attn_probe_scores call (for the latter: its
+ * logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it
  * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and
  * nothing else.  One-shot: that next call consumes the arming whether or

@@ -240,10 +240,12 @@ __global__ __launch_bounds__(64 * kAppendWaves) void transcode_kernel(TranscodeA
 
 #define VIT_APPEND_CASE(C, S)                                                   \
   case (C)*2 + (S):                                                             \
-    hipLaunchKernelGGL((append_kernel<C, S>), grid, dim3(64 * kAppendWaves), 0, stream, args); \
+    hipExtLaunchKernelGGL((append_kernel<C, S>), grid, dim3(64 * kAppendWaves), 0, stream, ev.start, ev.stop, 0, \
+                          args);                                                \
     break;
 
-hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args) {
+hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args,
+                         const KernelEvents& ev) {
   switch (codec * 2 + side) {
     VIT_APPEND_CASE(F16, 0)
     VIT_APPEND_CASE(F16, 1)

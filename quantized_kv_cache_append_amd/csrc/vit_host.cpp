@@ -14,7 +14,8 @@ constexpr int kRowBytes[5] = {256, 128, 64, 64, 48};
 
 bool is_rotated(int32_t codec) { return codec == VIT_CODEC_ROT4 || codec == VIT_CODEC_ROT3; }
 
-// events armed by vit_arm_kernel_events for this host thread's next decode or transcode
+// events armed by vit_arm_kernel_events for this host thread's next append, decode, transcode
+// or probe call
 thread_local vit::KernelEvents g_armed;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -52,7 +53,7 @@ size_t ws_o_bytes(int32_t s, int32_t hq, int32_t ns) {
 }
 
 int enqueue_append(const vit_kv_plane* dst, const float* src, const int64_t* pos0, int32_t n_tokens,
-                   hipStream_t stream) {
+                   hipStream_t stream, const vit::KernelEvents& ev) {
   vit::AppendArgs a{};
   a.codes = dst->codes;
   a.scales = dst->scales;
@@ -71,7 +72,7 @@ int enqueue_append(const vit_kv_plane* dst, const float* src, const int64_t* pos
   const dim3 grid(static_cast<unsigned>((groups + vit::kAppendWaves - 1) / vit::kAppendWaves),
                   static_cast<unsigned>(dst->n_kv_heads),
                   static_cast<unsigned>(dst->n_seqs));
-  return vit::launch_append(dst->codec, dst->side, grid, stream, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  return vit::launch_append(dst->codec, dst->side, grid, stream, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 
 }  // namespace
@@ -108,6 +109,8 @@ int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_
 
 int vit_kv_append_quant(const vit_kv_plane* dst, const float* src, const int64_t* pos0,
                         int32_t n_tokens, void* stream) {
+  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
+  g_armed = vit::KernelEvents{};
   int st = check_plane(dst);
   if (st != VIT_OK) return st;
   if (n_tokens < 0 || !pos0) return VIT_E_ARG;
@@ -116,7 +119,7 @@ int vit_kv_append_quant(const vit_kv_plane* dst, const float* src, const int64_t
   if (!aligned(src, 16)) return VIT_E_ALIGN;
   for (int s = 0; s < dst->n_seqs; ++s)
     if (pos0[s] < 0 || pos0[s] + n_tokens > dst->capacity) return VIT_E_CAPACITY;
-  return enqueue_append(dst, src, pos0, n_tokens, static_cast<hipStream_t>(stream));
+  return enqueue_append(dst, src, pos0, n_tokens, static_cast<hipStream_t>(stream), ev);
 }
 
 int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int64_t* n_rows, void* stream) {

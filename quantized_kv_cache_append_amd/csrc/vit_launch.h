@@ -118,14 +118,15 @@ struct ReduceArgs {
   uint32_t vsigns[4];
 };
 
-// Optional events recorded by the decode dispatch itself (kernel start and
+// Optional events recorded by a kernel's dispatch itself (kernel start and
 // end, via hipExtLaunchKernel); null members record nothing.
 struct KernelEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args);
+hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, const AppendArgs& args,
+                         const KernelEvents& ev);
 hipError_t launch_transcode(int src_codec, int dst_codec, int side, dim3 grid, hipStream_t stream,
                             const TranscodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode(int kc, int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args,

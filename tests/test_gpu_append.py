@@ -111,3 +111,36 @@ def test_append_many_random_rows(codec):
         for s in range(S):
             for h in range(H):
                 compare_plane_rows(plane, view, s, h, np.arange(cap), x[s, :, h])
+
+
+@pytest.mark.gpu
+def test_kernel_events_bracket_the_append_kernel():
+    """vit_arm_kernel_events before vit_kv_append_quant: the append dispatch
+    records both events, the stored planes equal an unarmed append's, and the
+    arming is one-shot."""
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    say("[append-events]")
+    rng = np.random.default_rng(19)
+    S, H, cap = 2, 2, 512
+    x = rng.standard_normal((S, 300, H, D)).astype(np.float32)
+    plain = make_plane("q4_0", "v", S, H, cap)
+    timed = make_plane("q4_0", "v", S, H, cap)
+    append_rows(plain, x, [5, 100])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    vit.vit_arm_kernel_events(e0, e1)
+    append_rows(timed, x, [5, 100])
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0, ms
+    a, b = plain.host_view(), timed.host_view()
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+    # consumed: a second append does not touch the events again
+    append_rows(timed, x, [5, 100])
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
