@@ -12,7 +12,10 @@ Other workloads (tiny, lowbit, rotated, ladder) are available with
 --workload.  ``--q-len N`` (2 .. 4, single-layer workloads) makes each step
 verify N new tokens per sequence at once, causal among themselves
 (vit_attn_decode_mq, all N rows appended by the decode call); ``value`` then
-counts the N tokens of every sequence.
+counts the N tokens of every sequence.  The ladder's step appends a
+2048-row ubatch to every (layer, side) plane with vit_kv_append_quant on a
+second stream: decode l waits for layer l's two appends only, and each
+step's appends wait for the previous step's decodes.
 
 Inputs are synthetic (seeded device normals shaped like the workload) and
 resident in HBM before timing starts.  Because the batched cache (143 MB)
@@ -192,21 +195,28 @@ def run_gpu(args):
     lens = [L] * S
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
+    # The ladder's ubatch appends go to a second stream (default priority too):
+    # decode l waits only for layer l's appends, so the later layers' appends
+    # run beside the first decodes; each step's appends wait for the previous
+    # step's decodes (they rewrite the rows those read).
+    fused = "ubatch" not in cfg
+    astream = stream if fused else torch.cuda.Stream()
+    app_done = [torch.cuda.Event() for _ in range(n_layers)]
+    fork = torch.cuda.Event()
 
     # every call of a step, marshalled once per replica (the host then only
     # issues the C calls, so the GPU queue never runs dry).  One (or q_len)
     # new token(s) per sequence: their K/V rows go through the decode call's
     # fused append.  A ubatch of new rows (the ladder) is appended by
     # vit_kv_append_quant first.
-    fused = "ubatch" not in cfg
     calls = []
     for r in range(replicas):
         app, dec = [], []
         for li, lay in enumerate(layers):
             kn, vn = new_rows[li]
             if not fused:
-                app.append(vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=stream))
-                app.append(vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=stream))
+                app.append((vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=astream),
+                            vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=astream)))
             # [S][H][128] rows for one token, [S][q_len][H][128] for several
             k_in = (kn[:, 0].contiguous() if QL == 1 else kn) if fused else None
             v_in = (vn[:, 0].contiguous() if QL == 1 else vn) if fused else None
@@ -220,9 +230,16 @@ def run_gpu(args):
 
     def step(i, ev=None):
         app, dec = calls[i % replicas]
-        for c in app:
-            c()
+        if app:
+            fork.record(stream)  # everything issued on the decode stream before this step
+            astream.wait_event(fork)
+            for li, (ck, cv) in enumerate(app):
+                ck()
+                cv()
+                app_done[li].record(astream)
         for li, (d, red) in enumerate(dec):
+            if app:
+                stream.wait_event(app_done[li])
             if ev is not None:
                 # the decode dispatch itself records this pair at its start and end
                 arm(ev[0][li], ev[1][li])
