@@ -15,28 +15,136 @@
 
 namespace vit {
 
+// K side, a whole 8-row group (not rot3): the 8 rows' canonical bytes go to
+// LDS together (4-bit codecs pair their nibbles by a lane exchange first),
+// one wave fence, then lane l stores unit l % (4 CB) of row l / (4 CB), so one
+// 16-byte store instruction covers 4 (f16), 8 (q8_0) or all 8 (4-bit) rows.
+// The 8 rows' 32 fp16 scales (K: [row][block], contiguous) go out as four
+// 16-byte stores from lanes 0 and 32, the rot4 norms as one from lane 0.
+template <int CODEC>
+__device__ inline void store_k_group(uint8_t* tbase, uint16_t* scales, uint16_t* norms, int64_t g0, int pbase,
+                                     const RowCodes (&rc)[8], int lane, uint8_t (*rowbuf)[256]) {
+  // row r's canonical bytes at kb + r * KS: the padding makes the unit reads
+  // of a store instruction (several rows at once) fall in distinct LDS banks
+  // (4-bit: all 32 lanes of a half-wave; q8_0: at most 2 lanes per bank)
+  constexpr int KS = CODEC == F16 ? 256 : (CODEC == Q8_0 ? 144 : 80);
+  uint8_t* kb = &rowbuf[0][0];
+  if constexpr (CODEC == Q4_0 || CODEC == ROT4) {
+    // canonical byte 16b + j = code j | code j + 16 << 4 of block b: lane
+    // 32h + j (j < 16) holds channel j of blocks h (c0) and 2 + h (c1), and
+    // its xor-16 partner channel j + 16
+    uint32_t hi0[8], hi1[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      hi0[r] = xshfl<16>(rc[r].c0);
+      hi1[r] = xshfl<16>(rc[r].c1);
+    }
+    if ((lane & 16) == 0) {
+      const int j = lane & 15, h = lane >> 5;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        kb[r * KS + 16 * h + j] = static_cast<uint8_t>((rc[r].c0 & 15u) | ((hi0[r] & 15u) << 4));
+        kb[r * KS + 16 * (2 + h) + j] = static_cast<uint8_t>((rc[r].c1 & 15u) | ((hi1[r] & 15u) << 4));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if constexpr (CODEC == F16) {
+        reinterpret_cast<uint16_t*>(kb + r * KS)[lane] = static_cast<uint16_t>(rc[r].c0);
+        reinterpret_cast<uint16_t*>(kb + r * KS)[lane + 64] = static_cast<uint16_t>(rc[r].c1);
+      } else {
+        kb[r * KS + lane] = static_cast<uint8_t>(rc[r].c0);
+        kb[r * KS + lane + 64] = static_cast<uint8_t>(rc[r].c1);
+      }
+    }
+  }
+  wave_lds_fence();
+  // unit (c, g): chunk g (CHB bytes) of each of the BPU blocks of unit c
+  constexpr int CB = units_per_block(CODEC);
+  constexpr int BPU = 4 / CB, CHB = 4 * CB, LPR = 4 * CB;  // LPR: lanes (units) per row
+  constexpr int RPP = 64 / LPR;                               // rows per store instruction
+#pragma unroll
+  for (int r0 = 0; r0 < 8; r0 += RPP) {
+    const int r = r0 + lane / LPR;
+    if (r < 8) {
+      const int u = lane % LPR;
+      const int g = u / CB, c = u % CB;
+      uint32_t w[4];
+#pragma unroll
+      for (int bb = 0; bb < BPU; ++bb)
+#pragma unroll
+        for (int k = 0; k < CHB / 4; ++k)
+          w[bb * (CHB / 4) + k] =
+              *reinterpret_cast<const uint32_t*>(kb + r * KS + (c * BPU + bb) * 16 * CB + g * CHB + 4 * k);
+      *reinterpret_cast<u32x4*>(tbase + k_unit_offset(CODEC, pbase + r, g, c)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+  if constexpr (has_scales(CODEC)) {
+    // lane 0 holds blocks 0 and 2 of every row, lane 32 blocks 1 and 3
+    uint32_t own0[8], own1[8], oth0[8], oth1[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      own0[r] = rc[r].s0;
+      own1[r] = rc[r].s1;
+      oth0[r] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(own0[r]), 32, kWave));
+      oth1[r] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(own1[r]), 32, kWave));
+    }
+    if ((lane & 31) == 0) {
+      const bool upper = lane != 0;  // lane 32: rows 4..7, and its own blocks are 1 and 3
+      uint32_t row[4][2];            // [row i of this lane's four][word]: blocks (0, 1), (2, 3)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = upper ? own0[4 + i] : own0[i], a1 = upper ? own1[4 + i] : own1[i];
+        const uint32_t b0 = upper ? oth0[4 + i] : oth0[i], b1 = upper ? oth1[4 + i] : oth1[i];
+        const uint32_t blk0 = upper ? b0 : a0, blk1 = upper ? a0 : b0;
+        const uint32_t blk2 = upper ? b1 : a1, blk3 = upper ? a1 : b1;
+        row[i][0] = blk0 | (blk1 << 16);
+        row[i][1] = blk2 | (blk3 << 16);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(scales + k_scale_index(g0 + (upper ? 4 : 0), 0));
+      dst[0] = u32x4{row[0][0], row[0][1], row[1][0], row[1][1]};
+      dst[1] = u32x4{row[2][0], row[2][1], row[3][0], row[3][1]};
+    }
+  }
+  if constexpr (has_norms(CODEC)) {
+    if (lane == 0) {
+      uint32_t nv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) nv[r] = rc[r].norm;
+      const u32x4 u = {nv[0] | (nv[1] << 16), nv[2] | (nv[3] << 16), nv[4] | (nv[5] << 16), nv[6] | (nv[7] << 16)};
+      *reinterpret_cast<u32x4*>(norms + g0) = u;
+    }
+  }
+}
+
 // Store the encoded rows g0 .. g0+7 (one 8-row group, g0 % 8 == 0) of one
-// (sequence, KV head) stream; only rows with live[r] are written.  K rows go
-// to their tile units one by one.  On the V side a channel's 8 rows form one
-// column unit: a whole group is assembled in registers and written whole; a
-// group cut by the range edge keeps the rows outside it (per-row stores,
-// read-modify-write of the shared 4-bit and 3-bit words).
+// (sequence, KV head) stream; only rows with live[r] are written.  A whole
+// group goes out together: K rows through LDS (store_k_group; rot3 K rows one
+// by one); on the V side a channel's 8 rows form one column unit, assembled
+// in registers and written whole.  A group cut by the range edge goes row by
+// row and keeps the rows outside it (read-modify-write of the shared 4-bit
+// and 3-bit V words).
 template <int CODEC, int SIDE>
 __device__ inline void store_group(uint8_t* codes, uint16_t* scales, uint16_t* norms, int64_t g0,
                                    const RowCodes (&rc)[8], const bool (&live)[8], int lane, uint8_t (*rowbuf)[256]) {
   bool all = true;
 #pragma unroll
   for (int r = 0; r < 8; ++r) all = all && live[r];
-  if (SIDE == 0 || !all) {
+  if (!all || (SIDE == 0 && CODEC == ROT3)) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
       if (live[r]) store_row<CODEC, SIDE>(codes, scales, norms, g0 + r, rc[r], lane, rowbuf[r]);
     return;
   }
-  // the whole group is in range: write column units, scales and norms whole
+  // the whole group is in range: write units, scales and norms whole
   const int64_t tile = g0 >> 5;
   const int pbase = static_cast<int>(g0 & 31);  // 0, 8, 16 or 24
   uint8_t* tbase = codes + tile * tile_code_bytes(CODEC);
+  if constexpr (SIDE == 0) {
+    store_k_group<CODEC>(tbase, scales, norms, g0, pbase, rc, lane, rowbuf);
+    return;
+  }
   if constexpr (CODEC == ROT3) {
     // lane l: the 24-bit groups of channels l and l + 64 over the 8 rows;
     // lane n16 < 16 writes units (u, g8, n16), channels 64u + 16c + n16
