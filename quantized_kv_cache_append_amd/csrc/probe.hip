@@ -20,6 +20,8 @@
 
 namespace vit {
 
+constexpr int kMassCells = 256;  // cells per probe_mass_kernel workgroup (one per thread)
+
 // K registers of one 32-row tile for one lane (the K half of TileRegs).
 template <int KC>
 struct KTile {
@@ -206,32 +208,34 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
   }
 }
 
-// One workgroup per (1024-cell block, sequence): merge every query head's
+// One workgroup per (256-cell block, sequence): merge every query head's
 // chunk partials into (max, 1 / sum), then score <- decay * score + the sum
-// over the query heads of 2^(logit - max) / sum for each cell below L.
+// over the query heads (in head order) of 2^(logit - max) / sum for each
+// cell below L, one cell per thread.
 __global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
   const int tid = threadIdx.x;
   const int seq = blockIdx.y;
   const int L = a.seq_len[seq];
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 1024;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kMassCells;
   if (j0 >= L) return;  // uniform per workgroup
   __shared__ float s_max[kProbeMaxHeads], s_inv[kProbeMaxHeads];
-  // one wave per query head, one lane per chunk partial (n_chunks <= 64)
-  const int lane = tid & 63;
-  for (int h = tid >> 6; h < a.n_q_heads; h += 4) {
+  // a group of W lanes (W = n_chunks rounded up to a power of two, <= 64)
+  // per query head, one lane per chunk partial: 256 / W heads per round
+  int W = 1;
+  while (W < a.n_chunks) W <<= 1;
+  const int sub = tid & (W - 1);
+  for (int h = tid / W; h < a.n_q_heads; h += kMassCells / W) {  // uniform per W-lane group
     const float* p = a.part + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.n_chunks * 2;
     float m = -__FLT_MAX__, l = 0.0f;
-    if (lane < a.n_chunks) {
-      m = p[2 * lane];
-      l = p[2 * lane + 1];
+    if (sub < a.n_chunks) {
+      m = p[2 * sub];
+      l = p[2 * sub + 1];
     }
     float M = l > 0.0f ? m : -__FLT_MAX__;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    for (int d = W >> 1; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
     float Ls = l > 0.0f ? l * __builtin_amdgcn_exp2f(m - M) : 0.0f;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) Ls += __shfl_xor(Ls, d, 64);
-    if (lane == 0) {
+    for (int d = W >> 1; d >= 1; d >>= 1) Ls += __shfl_xor(Ls, d, 64);
+    if (sub == 0) {
       s_max[h] = M;
       s_inv[h] = 1.0f / Ls;  // every head sees L >= 1 cells: Ls >= 1
     }
@@ -239,15 +243,22 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
   __syncthreads();
   const float* lg = a.logits + static_cast<int64_t>(seq) * a.n_q_heads * a.capacity;
   float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity;
+  const int64_t j = j0 + tid;
+  if (j < L) {
+    const float prev = sc[j];
+    float mass = 0.0f;
+    int h = 0;
+    // eight heads' logits in flight at a time, summed in head order
+    for (; h + 8 <= a.n_q_heads; h += 8) {
+      float v[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t j = j0 + r * 256 + tid;
-    if (j < L) {
-      float mass = 0.0f;
-      for (int h = 0; h < a.n_q_heads; ++h)
-        mass += __builtin_amdgcn_exp2f(lg[static_cast<int64_t>(h) * a.capacity + j] - s_max[h]) * s_inv[h];
-      sc[j] = a.decay * sc[j] + mass;
+      for (int i = 0; i < 8; ++i) v[i] = lg[static_cast<int64_t>(h + i) * a.capacity + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mass += __builtin_amdgcn_exp2f(v[i] - s_max[h + i]) * s_inv[h + i];
     }
+    for (; h < a.n_q_heads; ++h)
+      mass += __builtin_amdgcn_exp2f(lg[static_cast<int64_t>(h) * a.capacity + j] - s_max[h]) * s_inv[h];
+    sc[j] = a.decay * prev + mass;
   }
 }
 
@@ -484,7 +495,7 @@ hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 mgrid(static_cast<unsigned>((max_seq_len + 1023) / 1024), static_cast<unsigned>(n_seqs));
+  const dim3 mgrid(static_cast<unsigned>((max_seq_len + kMassCells - 1) / kMassCells), static_cast<unsigned>(n_seqs));
   hipLaunchKernelGGL(probe_mass_kernel, mgrid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }

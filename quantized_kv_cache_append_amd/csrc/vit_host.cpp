@@ -310,8 +310,9 @@ int vit_probe_select_evictions(const float* scores, int32_t n_seqs, int64_t capa
     const int64_t hi = seq_len[s] - n_recent > lo ? seq_len[s] - n_recent : lo;
     if (hi - lo > max_mid) max_mid = hi - lo;
   }
-  // blocks of >= 4096 cells, at most kSelectMaxBlocks per sequence
-  int64_t cpb = 4096;
+  // blocks of >= 1024 cells (4 rounds of the workgroup's 256 threads in the
+  // ordered write), at most kSelectMaxBlocks per sequence
+  int64_t cpb = 1024;
   while ((max_mid + cpb - 1) / cpb > vit::kSelectMaxBlocks) cpb *= 2;
   const int64_t nb = (max_mid + cpb - 1) / cpb;
   a.cells_per_block = static_cast<int32_t>(cpb);

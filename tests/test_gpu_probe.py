@@ -188,7 +188,7 @@ def test_select_evictions_edges_and_full_slot():
 
 @pytest.mark.gpu
 def test_select_evictions_ties_across_blocks():
-    """Several 4096-cell blocks per sequence; the tied target key's cells span
+    """Several 1024-cell blocks per sequence; the tied target key's cells span
     blocks, so each block's share of them depends on the blocks before it."""
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
