@@ -183,26 +183,42 @@ struct RowCodes {
 };
 
 template <int M, int N>
-__device__ inline void max_step(float (&a)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] = fmaxf(a[i], xshfl<M>(a[i]));
-}
-template <int M, int N>
 __device__ inline void sum_step(float (&a)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) a[i] = a[i] + xshfl<M>(a[i]);
 }
 
+// Maxima of non-negative floats as unsigned integers: for x, y >= +0 the
+// bit patterns order like the values, so max(bits) is the bits of the float
+// maximum (the encoders' inputs are finite).  The float form would first
+// quiet each exchanged operand (an extra max per value in IEEE mode), and the
+// integer max takes the lane exchange as a DPP operand.
+template <int M, int N>
+__device__ inline void umax_step(uint32_t (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t o = xshfl<M>(a[i]);
+    a[i] = a[i] > o ? a[i] : o;
+  }
+}
+template <int N>
+__device__ inline void half_wave_umax(uint32_t (&a)[N]) {
+  umax_step<16>(a);
+  umax_step<8>(a);
+  umax_step<4>(a);
+  umax_step<2>(a);
+  umax_step<1>(a);
+}
+
 // |x| maxima of the blocks: a[i] <- max over the lane's 32-lane half-wave
 template <int N>
 __device__ inline void block_max_abs(float (&a)[N]) {
+  uint32_t u[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) a[i] = fabsf(a[i]);
-  max_step<16>(a);
-  max_step<8>(a);
-  max_step<4>(a);
-  max_step<2>(a);
-  max_step<1>(a);
+  for (int i = 0; i < N; ++i) u[i] = __float_as_uint(a[i]) & 0x7FFFFFFFu;  // |x|
+  half_wave_umax(u);
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = __uint_as_float(u[i]);
 }
 
 // Per lane: b where lane bit set in `mask` (a constant lane pattern), else a.
@@ -301,17 +317,13 @@ __device__ inline void encode_q8_0(const float (&x0)[R], const float (&x1)[R], i
 // max |x|, then a ballot of the lanes holding it and the first of them.
 template <int N>
 __device__ inline void q4_block_signed_max(const float (&x)[N], int lane, float (&m)[N]) {
-  float a[N], mx[N];
+  uint32_t a[N], mx[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    a[i] = fabsf(x[i]);
+    a[i] = __float_as_uint(x[i]) & 0x7FFFFFFFu;  // |x| as bits
     mx[i] = a[i];
   }
-  max_step<16>(mx);
-  max_step<8>(mx);
-  max_step<4>(mx);
-  max_step<2>(mx);
-  max_step<1>(mx);
+  half_wave_umax(mx);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const uint64_t eq = __builtin_amdgcn_ballot_w64(a[i] == mx[i]);
@@ -370,21 +382,17 @@ __device__ inline uint32_t rot4_index(float t) {
 }
 
 // One Walsh-Hadamard stage across lanes for every row: lanes with bit h set
-// take (partner - own), the others (own + partner).
+// take (partner - own), the others (own + partner), both written as
+// partner + (+-own): x - y and x + (-y) are the same IEEE operation, signed
+// zeros included, and the sum takes the lane exchange as a DPP operand.
 template <int H, int R>
 __device__ inline void wht_stage(float (&w0)[R], float (&w1)[R], int lane) {
 #pragma clang fp contract(off)
-  float p0[R], p1[R];
+  const uint32_t neg = (lane & H) != 0 ? 0x80000000u : 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    p0[r] = xshfl<H>(w0[r]);
-    p1[r] = xshfl<H>(w1[r]);
-  }
-  const bool upper = (lane & H) != 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    w0[r] = upper ? p0[r] - w0[r] : w0[r] + p0[r];
-    w1[r] = upper ? p1[r] - w1[r] : w1[r] + p1[r];
+    w0[r] = xshfl<H>(w0[r]) + __uint_as_float(__float_as_uint(w0[r]) ^ neg);
+    w1[r] = xshfl<H>(w1[r]) + __uint_as_float(__float_as_uint(w1[r]) ^ neg);
   }
 }
 
