@@ -304,6 +304,41 @@ def run_gpu(args):
         graph_ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
         assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output (graph replay)"
         del graphs
+    if not fused:
+        # The two-stream step must compute what a serial one does.  The timed
+        # steps append the same rows every time, which would hide a decode
+        # that ran before its layer's appends; so the ubatch rows are scaled
+        # by 8 first (their logits then dominate the softmax, and a stale read
+        # would move the output by O(1)), then one overlapped step and the
+        # same calls serially (every append done before the first decode) must
+        # agree to fp32 rounding (the decode's tile-to-wave order, and so its
+        # summation order, may differ between the two runs).
+        for kv in new_rows:
+            for x in kv:
+                x.mul_(8.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        overlapped = [o.clone() for o in out]
+        app, dec = calls[0]
+        for ck, cv in app:
+            ck()
+            cv()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for d, red in dec:
+                d()
+                if red is not None:
+                    red()
+        torch.cuda.synchronize()
+        worst = 0.0
+        for a, b in zip(overlapped, out):
+            rms = float(torch.sqrt(torch.mean(b * b)))
+            err = float(torch.max(torch.abs(a - b)))
+            worst = max(worst, err / rms)
+            assert err <= 1e-3 * rms, f"overlapped step differs from the serial step: {err} vs rms {rms}"
+        print(f"# overlap check: overlapped vs serial step, max |diff| / rms = {worst:.2e}", file=sys.stderr, flush=True)
     dec_mean_ms = float(np.mean(dec_ms))
     per_launch_bytes = kv_bytes / n_layers
     # algorithmic bytes of all timed decode launches / their summed duration
