@@ -104,6 +104,9 @@ def test_split_counts_and_empty_splits():
 
 @pytest.mark.gpu
 def test_deterministic_bitwise():
+    """Bitwise repeatable where every split holds at most 16 tiles (each of
+    the 8 waves then has its two tiles assigned up front); beyond that the
+    tile-to-wave order follows timing and only fp32 rounding may differ."""
     say("[decode-determinism]")
     a, _ = _run_small("q8_0", "q8_0", 4, [480, 512], 5, seed=9)
     b, _ = _run_small("q8_0", "q8_0", 4, [480, 512], 5, seed=9)
