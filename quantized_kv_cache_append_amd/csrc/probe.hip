@@ -274,6 +274,7 @@ __device__ inline uint32_t score_key(float f) {
 
 // inclusive sum over the workgroup's threads of v (every thread gets its
 // prefix); `tot` receives the workgroup total
+template <int NT = kSelectThreads>
 __device__ inline int block_scan(int v, int tid, int* s_wave, int& tot) {
   const int lane = tid & 63, wave = tid >> 6;
   int x = v;
@@ -286,7 +287,7 @@ __device__ inline int block_scan(int v, int tid, int* s_wave, int& tot) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kSelectThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int t = s_wave[w];
     before += w < wave ? t : 0;
     all += t;
@@ -500,7 +501,104 @@ hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream,
   return hipGetLastError();
 }
 
+// A sequence whose middle range fits in LDS: one workgroup does the three
+// radix passes on an LDS histogram and the ordered write, in one launch.  In
+// the write each thread owns a contiguous run of cells, so two block scans
+// (keys below T, keys equal to T) give every thread its output offset.
+constexpr int kSmallThreads = 1024;  // threads of the one-workgroup select
+
+__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(SelectArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int seq = blockIdx.x;
+  const SelectRange r = select_range(a, seq);
+  int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
+  for (int64_t i = r.k + tid; i < a.n_evict; i += kSmallThreads) out[i] = -1;
+  if (tid == 0) a.n_out[seq] = static_cast<int32_t>(r.k);
+  if (r.k == 0) return;  // uniform per workgroup
+  const int n = static_cast<int>(r.hi - r.lo);  // <= kSelectSmallCells
+  __shared__ uint32_t keys[kSelectSmallCells];
+  __shared__ int hist[kSelectBins];
+  __shared__ int s_wave[kSmallThreads / 64];
+  __shared__ int s_pick[2];
+  const float* sc = a.scores + static_cast<int64_t>(seq) * a.capacity + r.lo;
+  for (int i = tid; i < n; i += kSmallThreads) keys[i] = score_key(sc[i]);
+  uint32_t prefix = 0, mask = 0;
+  int64_t rank = r.k;
+  for (int p = 0; p < 3; ++p) {
+    for (int i = tid; i < kSelectBins; i += kSmallThreads) hist[i] = 0;
+    __syncthreads();  // (pass 0: also the key loads)
+    for (int base = 0; base < n; base += kSmallThreads) {  // uniform trip count
+      const int j = base + tid;
+      const uint32_t key = j < n ? keys[j] : 0u;
+      bool pending = j < n && (key & mask) == prefix;
+      const uint32_t bin = (key >> kDigitShift[p]) & kDigitMask[p];
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const uint64_t act = __builtin_amdgcn_ballot_w64(pending);
+        if (act == 0) break;
+        const int leader = __builtin_ctzll(act);
+        const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+        const uint64_t same = __builtin_amdgcn_ballot_w64(pending && bin == lb);
+        if (lane == leader) atomicAdd(&hist[lb], __builtin_popcountll(same));
+        pending = pending && bin != lb;
+      }
+      if (pending) atomicAdd(&hist[bin], 1);
+    }
+    __syncthreads();
+    // the bin of the rank-th key and its rank among the keys in that bin
+    constexpr int per = kSelectBins / kSmallThreads;
+    int c[per], sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      c[i] = hist[tid * per + i];
+      sum += c[i];
+    }
+    int tot;
+    const int incl = block_scan<kSmallThreads>(sum, tid, s_wave, tot);
+    int64_t before = incl - sum;
+    if (before < rank && rank <= before + sum) {
+      int d = 0;
+      while (d < per - 1 && before + c[d] < rank) before += c[d++];
+      s_pick[0] = tid * per + d;
+      s_pick[1] = static_cast<int>(rank - before);
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(s_pick[0]) << kDigitShift[p];
+    mask |= kDigitMask[p] << kDigitShift[p];
+    rank = s_pick[1];
+    __syncthreads();
+  }
+  // every key below T, and the first `rank` keys equal to T in cell order
+  const uint32_t T = prefix;
+  const int run = (n + kSmallThreads - 1) / kSmallThreads;
+  const int c0 = min(tid * run, n), c1 = min(c0 + run, n);
+  int lt = 0, eq = 0;
+  for (int j = c0; j < c1; ++j) {
+    lt += keys[j] < T ? 1 : 0;
+    eq += keys[j] == T ? 1 : 0;
+  }
+  int n_lt, n_eq;
+  const int lt_incl = block_scan<kSmallThreads>(lt, tid, s_wave, n_lt);
+  const int eq_incl = block_scan<kSmallThreads>(eq, tid, s_wave, n_eq);
+  int64_t eq_seen = eq_incl - eq;                                       // equal keys before this run
+  int64_t pos = (lt_incl - lt) + (eq_seen < rank ? eq_seen : rank);     // chosen cells before this run
+  for (int j = c0; j < c1; ++j) {
+    const uint32_t key = keys[j];
+    bool sel = key < T;
+    if (key == T) sel = eq_seen++ < rank;
+    if (sel) {
+      if (pos < r.k) out[pos] = r.lo + j;  // exactly k are chosen; the bound is a guard
+      ++pos;
+    }
+  }
+}
+
 hipError_t launch_select(int n_seqs, hipStream_t stream, const SelectArgs& args) {
+  if (args.max_mid <= kSelectSmallCells) {
+    hipLaunchKernelGGL(select_small_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(kSmallThreads), 0, stream,
+                       args);
+    return hipGetLastError();
+  }
   const dim3 block(kSelectThreads), grid(static_cast<unsigned>(args.n_blocks), static_cast<unsigned>(n_seqs));
   hipLaunchKernelGGL(select_zero_kernel, dim3(static_cast<unsigned>(n_seqs)), block, 0, stream, args);
   hipLaunchKernelGGL(select_hist_kernel<0>, grid, block, 0, stream, args);

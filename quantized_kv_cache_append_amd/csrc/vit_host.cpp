@@ -317,6 +317,7 @@ int vit_probe_select_evictions(const float* scores, int32_t n_seqs, int64_t capa
   const int64_t nb = (max_mid + cpb - 1) / cpb;
   a.cells_per_block = static_cast<int32_t>(cpb);
   a.n_blocks = static_cast<int32_t>(nb < 1 ? 1 : nb);
+  a.max_mid = max_mid;
   return vit::launch_select(n_seqs, static_cast<hipStream_t>(stream), a) == hipSuccess ? VIT_OK : VIT_E_HIP;
 }
 

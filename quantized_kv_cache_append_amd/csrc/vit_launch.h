@@ -65,8 +65,11 @@ struct ProbeArgs {
 // The cells to evict: a 3-pass radix select (11, 11, 10 bits) of the n_evict
 // lowest (score, cell) keys among each sequence's middle cells, by blocks of
 // cells_per_block cells, then their compaction in cell order.
-constexpr int kSelectMaxBlocks = 256;  // blocks per sequence
-constexpr int kSelectBins = 2048;      // bins of an 11-bit digit
+// A longest middle range of at most kSelectSmallCells cells takes the
+// one-workgroup-per-sequence form (keys in LDS, one launch).
+constexpr int kSelectMaxBlocks = 256;     // blocks per sequence
+constexpr int kSelectBins = 2048;         // bins of an 11-bit digit
+constexpr int kSelectSmallCells = 8192;
 struct SelectArgs {
   const float* scores;   // [S][capacity]
   int64_t* rows_out;     // [S][n_evict]
@@ -80,6 +83,7 @@ struct SelectArgs {
   int32_t n_seqs;
   int32_t cells_per_block;
   int32_t n_blocks;
+  int64_t max_mid;       // middle cells of the longest middle range
   int64_t seq_len[kMaxSeqs];
 };
 

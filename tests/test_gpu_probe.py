@@ -206,3 +206,25 @@ def test_select_evictions_ties_across_blocks():
             ref = probe.select_evictions(sc[s].astype(np.float64), lens[s], 17, 5, ne)
             assert n[s] == len(ref), (ne, s)
             assert rows[s, :len(ref)].tolist() == ref, (ne, s)
+
+
+@pytest.mark.gpu
+def test_select_evictions_both_forms_at_the_threshold():
+    """A longest middle range of 8192 cells takes the one-workgroup form
+    (keys in LDS), 8193 the multi-block form; both must equal the oracle."""
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    rng = np.random.default_rng(53)
+    cap = 8704
+    sc = (rng.integers(0, 50, (2, cap)) / 16.0).astype(np.float32)  # many ties
+    sc[1] = rng.standard_normal(cap).astype(np.float32)
+    for lens in ([8192, 5000], [8193, 5000]):
+        for ne in (1, 700, 4096, 9000):
+            say(f"[select-threshold] lens={lens} evict={ne}")
+            rows, n = _select(torch, vit, sc, lens, 0, 0, ne)
+            for s in range(2):
+                ref = probe.select_evictions(sc[s].astype(np.float64), lens[s], 0, 0, ne)
+                assert n[s] == len(ref), (lens, ne, s)
+                assert rows[s, :len(ref)].tolist() == ref, (lens, ne, s)
+                assert np.all(rows[s, len(ref):] == -1)
