@@ -54,7 +54,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-WORKLOADS = {"tiny": 1, "batched": 2, "lowbit": 3, "rotated": 4, "ladder": 5}
+WORKLOADS = ("tiny", "batched", "lowbit", "rotated", "ladder")
 D = 128
 
 
@@ -127,20 +127,20 @@ def run_gpu(args):
     import quantized_kv_cache_append_amd as vit
     import synth
 
-    cfgno = WORKLOADS[args.workload]
-    cfg = synth.CONFIGS[cfgno]
+    wl = args.workload
+    cfg = synth.CONFIGS[wl]
     S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
     QL = args.q_len
     if QL > 1 and ("ubatch" in cfg or (Hq // H) * QL > 16 or QL > 4):
         raise SystemExit(f"--q-len {QL} needs a single-layer workload with (n_q_heads / n_kv_heads) x q_len <= 16")
-    cmap = synth.codec_map(cfgno)
+    cmap = synth.codec_map(wl)
     if args.codecs:
         if cfg["layers"] != 1:
             raise SystemExit("--codecs needs a single-layer workload")
         cmap = [tuple(args.codecs.split(":"))]
     n_layers = cfg["layers"]
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(0x5EED2026 + cfgno)
+    gen.manual_seed(0x5EED2026 + synth.SEED_ID[wl])
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -157,8 +157,8 @@ def run_gpu(args):
     layers = []
     chan_scale = {}
     for li, (kc, vc) in enumerate(cmap):
-        ks = synth.sign_mask(cfgno, li, "k") if kc in ROTATED else None
-        vs = synth.sign_mask(cfgno, li, "v") if vc in ROTATED else None
+        ks = synth.sign_mask(wl, li, "k") if kc in ROTATED else None
+        vs = synth.sign_mask(wl, li, "v") if vc in ROTATED else None
         lay = Layer(vit, cfg, kc, vc, replicas, ks, vs)
         for side, plane in (("k", lay.K[0]), ("v", lay.V[0])):
             sc = None
@@ -343,7 +343,7 @@ def run_gpu(args):
     per_launch_bytes = kv_bytes / n_layers
     # algorithmic bytes of all timed decode launches / their summed duration
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
-    return dict(cfg=cfg, cfgno=cfgno, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
+    return dict(cfg=cfg, wl=wl, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
                 dec_mean_ms=dec_mean_ms,
                 dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
@@ -363,13 +363,13 @@ def run_transcode(args):
     import synth
 
     src_c, dst_c = args.transcode.split(":")
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS["ladder"]
     S, H, cap = cfg["seqs"], cfg["hkv"], cfg["capacity"]
     side = args.side
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0x5EED2026 + 77)
     torch.cuda.set_device(torch.device("cuda:0"))
-    signs = synth.sign_mask(5, 0, side) if dst_c in ROTATED else None
+    signs = synth.sign_mask("ladder", 0, side) if dst_c in ROTATED else None
     src = vit.KVPlane(src_c, side, S, H, cap)
     dst = vit.KVPlane(dst_c, side, S, H, cap, signs)
     sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
@@ -422,9 +422,9 @@ def cpu_baseline_transcode(r, budget_s=15.0):
     except Exception:  # pragma: no cover
         limiter = None
     n = 16384
-    rows = synth.kv_rows(5, r["side"], 0, 0, 0, 0, n)
+    rows = synth.kv_rows("ladder", r["side"], 0, 0, 0, 0, n)
     q_src = codecs.quantize(r["src_c"], rows)
-    signs = synth.sign_mask(5, 0, r["side"]) if r["dst_c"] in ROTATED else None
+    signs = synth.sign_mask("ladder", 0, r["side"]) if r["dst_c"] in ROTATED else None
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -451,13 +451,13 @@ def run_probe(args):
     import quantized_kv_cache_append_amd as vit
     import synth
 
-    cfgno = WORKLOADS[args.workload]
-    cfg = synth.CONFIGS[cfgno]
+    wl = args.workload
+    cfg = synth.CONFIGS[wl]
     S, Hq, H, cap, L = cfg["seqs"], cfg["hq"], cfg["hkv"], cfg["capacity"], cfg["ctx"]
-    kc = args.codecs.split(":")[0] if args.codecs else synth.codec_map(cfgno)[0][0]
-    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
+    kc = args.codecs.split(":")[0] if args.codecs else synth.codec_map(wl)[0][0]
+    ks = synth.sign_mask(wl, 0, "k") if kc in ROTATED else None
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(0x5EED2026 + 99 + cfgno)
+    gen.manual_seed(0x5EED2026 + 99 + synth.SEED_ID[wl])
     torch.cuda.set_device(torch.device("cuda:0"))
     k_bytes = S * H * L * _row_bytes(kc)
     replicas = args.replicas if args.replicas else min(256, max(1, math.ceil((1 << 30) / (S * H * cap * _row_bytes(kc)))))
@@ -513,7 +513,7 @@ def run_probe(args):
     ms = [a.elapsed_time(b) for a, b in evs]
     assert np.isfinite(scores.cpu().numpy()).all(), "non-finite probe scores"
     per_launch = k_bytes + S * Hq * L * 4  # K read + logits written
-    return dict(cfg=cfg, cfgno=cfgno, kc=kc, S=S, Hq=Hq, H=H, L=L, replicas=replicas, ms_per_step=ms_per_step,
+    return dict(cfg=cfg, wl=wl, kc=kc, S=S, Hq=Hq, H=H, L=L, replicas=replicas, ms_per_step=ms_per_step,
                 mean_ms=float(np.mean(ms)), min_ms=float(np.min(ms)), per_launch_bytes=per_launch,
                 achieved_gbs=per_launch / (float(np.mean(ms)) * 1e-3) / 1e9, n_evict=n_evict)
 
@@ -531,11 +531,11 @@ def cpu_baseline_probe(r, budget_s=15.0):
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    cfgno, H, Hq, L, kc = r["cfgno"], r["H"], r["Hq"], r["L"], r["kc"]
+    wl, H, Hq, L, kc = r["wl"], r["H"], r["Hq"], r["L"], r["kc"]
     n = min(L, 8192)
-    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
-    keys = np.stack([synth.kv_rows(cfgno, "k", 0, 0, h, 0, n) for h in range(H)])
-    q = synth.q_rows(cfgno, 0, 0, Hq)
+    ks = synth.sign_mask(wl, 0, "k") if kc in ROTATED else None
+    keys = np.stack([synth.kv_rows(wl, "k", 0, 0, h, 0, n) for h in range(H)])
+    q = synth.q_rows(wl, 0, 0, Hq)
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -604,12 +604,12 @@ def run_append(args):
     import synth
 
     codec, side = args.append, args.side
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS["ladder"]
     S, H, cap, pre, ub = cfg["seqs"], cfg["hkv"], cfg["capacity"], cfg["prefill"], cfg["ubatch"]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0x5EED2026 + 55)
     torch.cuda.set_device(torch.device("cuda:0"))
-    signs = synth.sign_mask(5, 0, side) if codec in ROTATED else None
+    signs = synth.sign_mask("ladder", 0, side) if codec in ROTATED else None
     plane = vit.KVPlane(codec, side, S, H, cap, signs)
     sc = torch.exp(torch.randn((1, 1, H, D), generator=gen, device="cuda"))
     # distinct source buffers, round-robin, so the 16.8 MB fp32 ubatch is not served from the cache
@@ -659,8 +659,8 @@ def cpu_baseline_append(r, budget_s=15.0):
     except Exception:  # pragma: no cover
         limiter = None
     n = 2048
-    rows = synth.kv_rows(5, r["side"], 0, 0, 0, 0, n)
-    signs = synth.sign_mask(5, 0, r["side"]) if r["codec"] in ROTATED else None
+    rows = synth.kv_rows("ladder", r["side"], 0, 0, 0, 0, n)
+    signs = synth.sign_mask("ladder", 0, r["side"]) if r["codec"] in ROTATED else None
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -780,18 +780,18 @@ def cpu_baseline(r, budget_s=15.0):
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    cfgno, L, S, H, Hq, QL = r["cfgno"], r["L"], r["S"], r["H"], r["Hq"], r["QL"]
+    wl, L, S, H, Hq, QL = r["wl"], r["L"], r["S"], r["H"], r["Hq"], r["QL"]
     G = Hq // H
     kc, vc = r["cmap"][0]
-    ks = synth.sign_mask(cfgno, 0, "k") if kc in ROTATED else None
-    vs = synth.sign_mask(cfgno, 0, "v") if vc in ROTATED else None
+    ks = synth.sign_mask(wl, 0, "k") if kc in ROTATED else None
+    vs = synth.sign_mask(wl, 0, "v") if vc in ROTATED else None
     units = [(s, h) for s in range(S) for h in range(H)]
     rows_unit = min(L, 8192)  # longer contexts are timed on an 8192-row slice and scaled
     prep = []
     for (s, h) in units[:4]:
-        kx = synth.kv_rows(cfgno, "k", 0, s, h, 0, rows_unit)
-        vx = synth.kv_rows(cfgno, "v", 0, s, h, 0, rows_unit)
-        qx = synth.q_rows(cfgno, 0, s, Hq)[h * G:(h + 1) * G]
+        kx = synth.kv_rows(wl, "k", 0, s, h, 0, rows_unit)
+        vx = synth.kv_rows(wl, "v", 0, s, h, 0, rows_unit)
+        qx = synth.q_rows(wl, 0, s, Hq)[h * G:(h + 1) * G]
         prep.append((codecs.quantize(kc, kx[:-QL], ks), codecs.quantize(vc, vx[:-QL], vs),
                      kx[-QL:], vx[-QL:], qx))
     scale = 1.0 / math.sqrt(D)
@@ -938,7 +938,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="batched", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="batched", choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -997,8 +997,8 @@ def main():
             (args.codecs and len(args.codecs.split(":")) != 2):
         raise SystemExit(f"--codecs takes K:V with codecs from {CODEC_NAMES}")
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path shards by (sequence, KV head) with no exchange; see DESIGN.md)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path would shard by (sequence, KV head) with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     if args.calib_copy:

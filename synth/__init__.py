@@ -39,25 +39,28 @@ KIND_K, KIND_V, KIND_Q, KIND_SIGNS, KIND_CODECMAP, KIND_OUTLIER, KIND_SCALES, KI
 SIDE_KIND = {"k": KIND_K, "v": KIND_V}
 
 CONFIGS = {
-    1: dict(name="tiny", layers=1, seqs=1, hq=4, hkv=1, ctx=512, capacity=512,
+    "tiny": dict(name="tiny", layers=1, seqs=1, hq=4, hkv=1, ctx=512, capacity=512,
             k_codec="f16", v_codec="q8_0", dist="outlier", fused_append=False),
-    2: dict(name="batched", layers=1, seqs=8, hq=32, hkv=8, ctx=8192, capacity=8192,
+    "batched": dict(name="batched", layers=1, seqs=8, hq=32, hkv=8, ctx=8192, capacity=8192,
             k_codec="q8_0", v_codec="q8_0", dist="lognormal", fused_append=True),
-    3: dict(name="lowbit", layers=1, seqs=4, hq=40, hkv=8, ctx=32768, capacity=32768,
+    "lowbit": dict(name="lowbit", layers=1, seqs=4, hq=40, hkv=8, ctx=32768, capacity=32768,
             k_codec="q4_0", v_codec="q4_0", dist="heavy", fused_append=False),
-    4: dict(name="rotated", layers=1, seqs=1, hq=16, hkv=2, ctx=131072, capacity=131072,
+    "rotated": dict(name="rotated", layers=1, seqs=1, hq=16, hkv=2, ctx=131072, capacity=131072,
             k_codec="rot4", v_codec="rot4", dist="outlier", fused_append=False),
-    5: dict(name="ladder", layers=16, seqs=2, hq=32, hkv=8, ctx=200704, capacity=200704,
+    "ladder": dict(name="ladder", layers=16, seqs=2, hq=32, hkv=8, ctx=200704, capacity=200704,
             k_codec=None, v_codec=None, dist="lognormal", fused_append=False,
             prefill=198656, ubatch=2048),
 }
+
+# each workload's number in the seed derivation (fixes every generated value)
+SEED_ID = {"tiny": 1, "batched": 2, "lowbit": 3, "rotated": 4, "ladder": 5}
 
 LADDER_CODECS = ("f16", "q8_0", "rot4", "q4_0")
 
 
 def rng(cfg, kind, layer, seq, head, chunk):
     """The PCG64 generator of one (config, kind, layer, seq, head, chunk)."""
-    ss = np.random.SeedSequence(BASE_SEED, spawn_key=(cfg, kind, layer, seq, head, chunk))
+    ss = np.random.SeedSequence(BASE_SEED, spawn_key=(SEED_ID[cfg], kind, layer, seq, head, chunk))
     return np.random.Generator(np.random.PCG64(ss))
 
 

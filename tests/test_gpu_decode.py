@@ -201,7 +201,7 @@ def _run_workload(cfg, units, layers=(0,)):
     G = Hq // H
     cmap = synth.codec_map(cfg)
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(cfg)
+    gen.manual_seed(synth.SEED_ID[cfg])
     scale = 1.0 / math.sqrt(D)
     for layer in layers:
         kc, vc = cmap[layer]
@@ -251,31 +251,31 @@ def _run_workload(cfg, units, layers=(0,)):
 
 @pytest.mark.gpu
 def test_workload_tiny():
-    _run_workload(1, [(0, 0)])
+    _run_workload("tiny", [(0, 0)])
 
 
 @pytest.mark.gpu
 def test_workload_batched():
-    _run_workload(2, [(0, 0), (3, 5), (7, 7)])
+    _run_workload("batched", [(0, 0), (3, 5), (7, 7)])
 
 
 @pytest.mark.gpu
 def test_workload_lowbit():
-    _run_workload(3, [(0, 1), (3, 6)])
+    _run_workload("lowbit", [(0, 1), (3, 6)])
 
 
 @pytest.mark.gpu
 def test_workload_rotated():
-    _run_workload(4, [(0, 0), (0, 1)])
+    _run_workload("rotated", [(0, 0), (0, 1)])
 
 
 @pytest.mark.gpu
 def test_workload_ladder_layers():
-    cmap = synth.codec_map(5)
+    cmap = synth.codec_map("ladder")
     # one layer per distinct (K, V) pair present, up to four layers
     seen, layers = set(), []
     for i, pair in enumerate(cmap):
         if pair not in seen and len(layers) < 4:
             seen.add(pair)
             layers.append(i)
-    _run_workload(5, [(1, 6)], layers=layers)
+    _run_workload("ladder", [(1, 6)], layers=layers)

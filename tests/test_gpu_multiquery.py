@@ -144,7 +144,7 @@ def _run_workload_verify(cfg, q_len, units):
     vs = synth.sign_mask(cfg, 0, "v") if vc in ("rot4", "rot3") else None
     say(f"[verify {c['name']}] K={kc} V={vc} q_len={q_len} units={units}")
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(1000 + cfg)
+    gen.manual_seed(1000 + synth.SEED_ID[cfg])
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     fill_plane_synth(K, cfg, 0, "k", 0, L - q_len, units, torch, gen)
@@ -154,7 +154,7 @@ def _run_workload_verify(cfg, q_len, units):
     for (s, h) in units:
         k_new[s, :, h] = torch.from_numpy(synth.kv_rows(cfg, "k", 0, s, h, L - q_len, q_len)).cuda()
         v_new[s, :, h] = torch.from_numpy(synth.kv_rows(cfg, "v", 0, s, h, L - q_len, q_len)).cuda()
-    q = np.random.default_rng(4242 + cfg).standard_normal((S, q_len, Hq, D)).astype(np.float32)
+    q = np.random.default_rng(4242 + synth.SEED_ID[cfg]).standard_normal((S, q_len, Hq, D)).astype(np.float32)
     ns = vit.vit_attn_default_splits(S, H, Hq, L)
     out = vit.decode(K, V, torch.from_numpy(q).cuda(), Hq, [L] * S, k_new=k_new, v_new=v_new, n_splits=ns,
                      q_len=q_len)
@@ -174,14 +174,14 @@ def _run_workload_verify(cfg, q_len, units):
 
 @pytest.mark.gpu
 def test_workload_batched_verify4():
-    _run_workload_verify(2, 4, [(0, 0), (5, 3)])
+    _run_workload_verify("batched", 4, [(0, 0), (5, 3)])
 
 
 @pytest.mark.gpu
 def test_workload_lowbit_verify3():
-    _run_workload_verify(3, 3, [(2, 6)])
+    _run_workload_verify("lowbit", 3, [(2, 6)])
 
 
 @pytest.mark.gpu
 def test_workload_rotated_verify2():
-    _run_workload_verify(4, 2, [(0, 1)])
+    _run_workload_verify("rotated", 2, [(0, 1)])

@@ -101,7 +101,7 @@ def _run_probe_workload(cfg, seqs):
     ks = synth.sign_mask(cfg, 0, "k") if kc in ("rot4", "rot3") else None
     say(f"[probe {c['name']}] K={kc} S={S} Hq={Hq} L={L} sampled seqs {seqs}")
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(2000 + cfg)
+    gen.manual_seed(2000 + synth.SEED_ID[cfg])
     K = make_plane(kc, "k", S, H, cap, ks)
     fill_plane_synth(K, cfg, 0, "k", 0, L, [(s, h) for s in seqs for h in range(H)], torch, gen)
     torch.cuda.empty_cache()
@@ -120,12 +120,12 @@ def _run_probe_workload(cfg, seqs):
 
 @pytest.mark.gpu
 def test_probe_batched_workload():
-    _run_probe_workload(2, [0, 5])
+    _run_probe_workload("batched", [0, 5])
 
 
 @pytest.mark.gpu
 def test_probe_rotated_workload():
-    _run_probe_workload(4, [0])
+    _run_probe_workload("rotated", [0])
 
 
 # ------------------------------------------------------------------ select

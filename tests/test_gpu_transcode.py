@@ -102,21 +102,21 @@ def test_transcode_ladder_tensor_full_size():
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
 
-    c = synth.CONFIGS[5]
+    c = synth.CONFIGS["ladder"]
     S, H, cap = c["seqs"], c["hkv"], c["capacity"]
     units = [(1, 6)]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(55)
     say(f"[transcode ladder] f16 -> q8_0, {S} x {H} x {cap} rows, units {units}")
     src = make_plane("f16", "k", S, H, cap, poison=False)
-    fill_plane_synth(src, 5, 0, "k", 0, cap, units, torch, gen)
+    fill_plane_synth(src, "ladder", 0, "k", 0, cap, units, torch, gen)
     torch.cuda.empty_cache()
     dst = make_plane("q8_0", "k", S, H, cap, poison=False)
     vit.vit_kv_transcode(src, dst, [cap] * S)
     torch.cuda.synchronize()
     for (s, h) in units:
         view = unit_view(dst, s, h)
-        rows = synth.kv_rows(5, "k", 0, s, h, 0, cap)
+        rows = synth.kv_rows("ladder", "k", 0, s, h, 0, cap)
         expect = vbr.transcode("f16", "q8_0", codecs.quantize("f16", rows))
         assert np.array_equal(view["codes"].astype(np.int8), expect["codes"])
         assert np.array_equal(view["scales"], expect["scales"])
