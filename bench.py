@@ -861,6 +861,35 @@ def _counter_kib(d, counter, name_part):
     return sum(v) / len(v), len(v)
 
 
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS",
+               "SQ_WAIT_INST_ANY", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(workload, prof, command, subdir):
+    """profiles/decode_<workload>_sq_counters.md: per-dispatch means of the
+    issue counters of decode_kernel from one rocprofv3 --pmc run, and the
+    counters' ratios to SQ_WAVE_CYCLES (how the waves' time splits)."""
+    d = os.path.join(prof, subdir, "sq")
+    vals = {c: _counter_kib(d, c, "decode_kernel")[0] for c in SQ_COUNTERS}
+    n = _counter_kib(d, "SQ_WAVE_CYCLES", "decode_kernel")[1]
+    md = [f"# decode_kernel, workload {workload}: issue counters (rocprofv3 --pmc)", "",
+          f"Kernel sources: {kernel_source_hash('decode')} (sha256 prefix over the decode kernel's csrc/ files, "
+          "as bench.py computes it).", "", "Command (from the repository root, with TMPDIR=/tmp):", "", "```", command, "```", "",
+          f"Means over {n} decode_kernel dispatches (warmup included):", "", "| counter | per dispatch | / SQ_WAVE_CYCLES |",
+          "|---|---:|---:|"]
+    for c in SQ_COUNTERS:
+        ratio = f"{vals[c] / vals['SQ_WAVE_CYCLES']:.3f}" if c.startswith("SQ_") and c != "SQ_WAVE_CYCLES" else ""
+        md.append(f"| `{c}` | {vals[c]:.4g} | {ratio} |")
+    md += ["", "The ratios compare each counter with the cycles the kernel's waves were resident "
+           "(SQ_WAVE_CYCLES); they are read across workloads, not as absolute utilisations.  On this stack "
+           "SQ_ACTIVE_INST_VMEM reads 0 and SQ_VALU_MFMA_BUSY_CYCLES reads exact powers of two for every "
+           "workload, so neither is used; the MFMA work is 1-3 GFLOP per launch, far below the matrix peak."]
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_sq_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def summarize_profiles(kind, workload, prof, commands, subdir=None):
     """Turn one workload's rocprofv3 runs into the committed summaries:
     profiles/<kind>_<workload>_kernel_stats.md (kernel-trace statistics beside
@@ -958,9 +987,18 @@ def main():
                     help="also time the steps as HIP graph replays (one captured graph per replica)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", type=int, default=0, help="only run N plain 1 GiB copies")
+    ap.add_argument("--summarize-sq", metavar="PROF_DIR", default=None,
+                    help="write the decode issue-counter summary for --workload from PROF_DIR/<tag>/sq (no GPU)")
     ap.add_argument("--summarize", metavar="PROF_DIR", default=None,
                     help="write profiles/ summaries for --workload from rocprofv3 output under PROF_DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize_sq:
+        w = profile_tag(args.workload, args.q_len, args.codecs)
+        b = (f"python3 bench.py --workload {args.workload}" + (f" --q-len {args.q_len}" if args.q_len > 1 else "")
+             + (f" --codecs {args.codecs}" if args.codecs else ""))
+        summarize_sq(w, args.summarize_sq, f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv "
+                     f"-d PROF/{w}/sq -o run -- {b} --steps 20 --warmup 3 --no-cpu-baseline", w)
+        return
     if args.summarize:
         if args.transcode:
             kind = "transcode"
