@@ -120,23 +120,24 @@ def dequant_q4_0(q):
 
 
 # ---------------------------------------------------------------------- rot4
-def quantize_rot4(x, signs16):
-    """Rotated 4-bit codec (random signs, WHT, fp16 norm, per-32 fp16 RMS scale,
-    16-level Lloyd-Max indices).
+def level_index(t, thr):
+    """Level index of whitened fp32 values ``t`` against ascending thresholds
+    ``thr`` (the midpoints of adjacent levels): the number of thresholds below
+    t, where a value lying exactly on a threshold goes to the level farther
+    from zero, and 0 (either sign) to the first non-negative level.
 
-    Steps, all fp32, in this order:
-      1. r_j = s_j x_j                      (s = +-1 from the 16-byte sign mask)
-      2. w = WHT(r)                         (unnormalised; stages h = 1..64)
-      3. n = sqrt(tree(x_j * x_j))          (norm of the model-domain row)
-      4. N = fp16(n)
-      5. g = 1/n (0 if n == 0);  u_j = w_j * g        (u has mean square ~1)
-      6. per block b: r_b = sqrt(tree32(u_j * u_j) * 0.03125);  S_b = fp16(r_b)
-      7. ib = 1/r_b (0 if r_b == 0);  t_j = u_j * ib
-      8. idx_j = #{k: t_j > th_k} + #{k: t_j == th_k and t_j >= 0}
-         (15 thresholds; a tie goes to the level farther from zero; 0 -> 8)
-    Reading for the two fp16 fields: the norm is ||x||_2 of the input row and
-    the block scale is the RMS of the norm-whitened rotated block, so N*S_b is
-    the per-block magnitude and the Lloyd-Max levels see unit-variance input.
+    Equivalently: the nearest level, exact midpoints resolved away from zero.
+    Both rotated codecs (rot4 with 15 thresholds, rot3 with 7) use this rule.
+    """
+    tt = np.asarray(t, dtype=np.float32)[..., None]
+    return (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+
+
+def whiten_rot4(x, signs16):
+    """Steps 1-7 of the rot4 encoder (see ``quantize_rot4``), all fp32.
+
+    Returns (t [N,4,32], r_b [N,4], n [N]): the whitened values whose level
+    index is stored, the per-block RMS and the row norm before fp16 rounding.
     """
     x = _rows(x)
     s = sign_vector(signs16)
@@ -150,9 +151,30 @@ def quantize_rot4(x, signs16):
     rb = np.sqrt(ms).astype(np.float32)
     ib = safe_recip(rb)
     t = (ub * ib[..., None]).astype(np.float32)
+    return t, rb, n
+
+
+def quantize_rot4(x, signs16):
+    """Rotated 4-bit codec (random signs, WHT, fp16 norm, per-32 fp16 RMS scale,
+    16-level Lloyd-Max indices).
+
+    Steps, all fp32, in this order:
+      1. r_j = s_j x_j                      (s = +-1 from the 16-byte sign mask)
+      2. w = WHT(r)                         (unnormalised; stages h = 1..64)
+      3. n = sqrt(tree(x_j * x_j))          (norm of the model-domain row)
+      4. N = fp16(n)
+      5. g = 1/n (0 if n == 0);  u_j = w_j * g        (u has mean square ~1)
+      6. per block b: r_b = sqrt(tree32(u_j * u_j) * 0.03125);  S_b = fp16(r_b)
+      7. ib = 1/r_b (0 if r_b == 0);  t_j = u_j * ib
+      8. idx_j = level_index(t_j) over the 15 thresholds
+         (a tie goes to the level farther from zero; 0 -> 8)
+    Reading for the two fp16 fields: the norm is ||x||_2 of the input row and
+    the block scale is the RMS of the norm-whitened rotated block, so N*S_b is
+    the per-block magnitude and the Lloyd-Max levels see unit-variance input.
+    """
+    t, rb, n = whiten_rot4(x, signs16)
     _, thr, _ = codebook()
-    tt = t[..., None]
-    idx = (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+    idx = level_index(t, thr)
     return {
         "codes": idx.astype(np.uint8).reshape(-1, D),
         "scales": f16_bits(rb),
@@ -178,22 +200,10 @@ def dequant_rot4(q, signs16):
 
 
 # ---------------------------------------------------------------------- rot3
-def quantize_rot3(x, signs16):
-    """Rotated 3-bit codec, 3.5 bits/value (the "tq3_0 / turbo3" class of the
-    Randozart/VITRIOL page's "What sets VITRIOL apart" table and the
-    buun-llama-cpp page's "Codecs" table: WHT-rotated, 3-bit scalar codes).
+def whiten_rot3(x, signs16):
+    """Steps 1-3 of the rot3 encoder (see ``quantize_rot3``), all fp32.
 
-    Steps, all fp32, in this order:
-      1. r_j = s_j x_j;  w = WHT(r)          (as rot4, unnormalised)
-      2. per block b: r_b = sqrt(tree32(w_j * w_j) * 0.03125);  S_b = fp16(r_b)
-      3. ib = 1/r_b (0 if r_b == 0);  t_j = w_j * ib
-      4. idx_j = #{k: t_j > th_k} + #{k: t_j == th_k and t_j >= 0}
-         (7 thresholds of the 8-level codebook; a tie goes to the level
-         farther from zero; 0 -> 4)
-    Reading: with one fp16 per 32 values (3 + 16/32 = 3.5 bits/value) the
-    block scale is the RMS of the rotated block itself (no row norm), so the
-    rotated-domain reconstruction is S_b * level, i.e. y = w / sqrt(128)
-    reconstructs as S_b * level / sqrt(128), the domain rot4 uses.
+    Returns (t [N,4,32], r_b [N,4]).
     """
     x = _rows(x)
     s = sign_vector(signs16)
@@ -204,9 +214,28 @@ def quantize_rot3(x, signs16):
     rb = np.sqrt(ms).astype(np.float32)
     ib = safe_recip(rb)
     t = (wb * ib[..., None]).astype(np.float32)
+    return t, rb
+
+
+def quantize_rot3(x, signs16):
+    """Rotated 3-bit codec, 3.5 bits/value (the "tq3_0 / turbo3" class of the
+    Randozart/VITRIOL page's "What sets VITRIOL apart" table and the
+    buun-llama-cpp page's "Codecs" table: WHT-rotated, 3-bit scalar codes).
+
+    Steps, all fp32, in this order:
+      1. r_j = s_j x_j;  w = WHT(r)          (as rot4, unnormalised)
+      2. per block b: r_b = sqrt(tree32(w_j * w_j) * 0.03125);  S_b = fp16(r_b)
+      3. ib = 1/r_b (0 if r_b == 0);  t_j = w_j * ib
+      4. idx_j = level_index(t_j) over the 7 thresholds of the 8-level
+         codebook (a tie goes to the level farther from zero; 0 -> 4)
+    Reading: with one fp16 per 32 values (3 + 16/32 = 3.5 bits/value) the
+    block scale is the RMS of the rotated block itself (no row norm), so the
+    rotated-domain reconstruction is S_b * level, i.e. y = w / sqrt(128)
+    reconstructs as S_b * level / sqrt(128), the domain rot4 uses.
+    """
+    t, rb = whiten_rot3(x, signs16)
     _, thr, _ = codebook(8)
-    tt = t[..., None]
-    idx = (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+    idx = level_index(t, thr)
     return {"codes": idx.astype(np.uint8).reshape(-1, D), "scales": f16_bits(rb)}
 
 

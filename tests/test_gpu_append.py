@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from gpu_helpers import append_rows, compare_plane_rows, make_plane, say, torch_cuda
+from test_oracle_crafted import ROWS as CRAFTED, SIGNS as CRAFTED_SIGNS
 
 CODECS = ["f16", "q8_0", "q4_0", "rot4", "rot3"]
 D = 128
@@ -40,6 +41,9 @@ def _edge_rows():
     r[:] = np.float32(1.0e-25)                                # tiny rows (squares underflow)
     r[::3] = np.float32(-3.0e-25)
     rows.append(r)
+    # rows on which the reciprocal rule, a tie rule or the operation order
+    # decides a stored field (tests/golden/crafted_rows.txt)
+    rows += [c["x"] for c in CRAFTED]
     return np.stack(rows).astype(np.float32)
 
 
@@ -144,3 +148,42 @@ def test_kernel_events_bracket_the_append_kernel():
     append_rows(timed, x, [5, 100])
     torch.cuda.synchronize()
     assert e0.elapsed_time(e1) == ms
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("side", ["k", "v"])
+def test_append_crafted_rows(codec, side):
+    """The crafted rows (tests/golden/crafted_rows.txt) with the sign mask
+    they were found for: whitened values exactly on rot4 / rot3 thresholds,
+    q8_0 / q4_0 elements where x * (1/d) and x / d round differently, and
+    rows where the WHT stage order or the summation order moves a field.
+    Bit-exact against the oracle; the tie channels also against their
+    hand-stated index (the level farther from zero)."""
+    torch_cuda()
+    say(f"[append-crafted] codec={codec} side={side}")
+    S, H, cap = 2, 2, 256
+    rng = np.random.default_rng(4242)
+    x = rng.standard_normal((S, len(CRAFTED), H, D)).astype(np.float32)
+    for i, c in enumerate(CRAFTED):
+        x[0, i, 0] = c["x"]
+        x[1, i, 1] = c["x"]
+    signs = CRAFTED_SIGNS if codec in ("rot4", "rot3") else None
+    plane = make_plane(codec, side, S, H, cap, signs)
+    pos0 = [3, 200 - len(CRAFTED)]
+    append_rows(plane, x, pos0)
+    view = plane.host_view()
+    for s in range(S):
+        for h in range(H):
+            idx = np.arange(pos0[s], pos0[s] + len(CRAFTED))
+            compare_plane_rows(plane, view, s, h, idx, x[s, :, h])
+    if codec in ("rot4", "rot3"):
+        from oracle import lloyd_max
+
+        lv, _, _ = lloyd_max.codebook(16 if codec == "rot4" else 8)
+        for i, c in enumerate(CRAFTED):
+            if c["kind"] == "tie" and c["codec"] == codec:
+                k = int(c["detail"][3:])
+                want = k + 1 if lv[k] + lv[k + 1] > 0 else k
+                for s, h in ((0, 0), (1, 1)):
+                    assert int(view["codes"][s, h, pos0[s] + i, c["ch"]]) == want, (codec, k)
