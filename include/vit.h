@@ -19,15 +19,18 @@
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked [host].  The library never
- *    allocates or frees device memory; the caller owns every buffer.
+ *    allocates or frees device memory; the caller owns every buffer.  (The
+ *    one exception is the static scratch array of vit_attn_decode_noalloc,
+ *    part of the library's code object on each GPU.)
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.
  *  - Arguments are validated on the host before anything is enqueued.  On a
  *    failed validation the call returns a negative vit_status and enqueues
  *    nothing.  After a launch, a HIP launch error maps to VIT_E_HIP.  Faults
  *    inside kernels surface at the caller's next synchronisation.
- *  - The library keeps no state between calls and is re-entrant.  Two calls
- *    that write the same cache rows must not run concurrently.
+ *  - The library keeps no state between calls and is re-entrant (except
+ *    vit_attn_decode_noalloc's per-GPU scratch, see there).  Two calls that
+ *    write the same cache rows must not run concurrently.
  *  - head_dim must be 128.  Capacity must be a multiple of 256.  At most 64
  *    sequences per call; query heads per KV head (G) at most 16.
  *
@@ -130,7 +133,8 @@ typedef enum vit_status {
                              capacity > VIT_MAX_CAPACITY */
   VIT_E_CAPACITY = -3,    /* rows outside 0..capacity-1, capacity % 256 != 0 */
   VIT_E_ALIGN = -4,       /* plane pointer not 256-B aligned, other pointer not 16-B aligned */
-  VIT_E_HIP = -5          /* a HIP launch failed */
+  VIT_E_HIP = -5,         /* a HIP launch failed */
+  VIT_E_SCRATCH = -6      /* vit_attn_decode_noalloc: split partials larger than its static scratch */
 } vit_status;
 
 #define VIT_HEAD_DIM 128
@@ -338,10 +342,41 @@ int vit_probe_select_evictions(const float *scores, int32_t n_seqs, int64_t capa
  * n_seqs. */
 size_t vit_probe_select_workspace_bytes(int32_t n_seqs);
 
+/* Bytes of device memory vit_attn_decode_noalloc holds for split partials
+ * on every GPU it runs on (a file-scope static array, kept until the process
+ * ends). */
+#define VIT_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * result as vit_attn_decode_mq followed, when n_splits > 1, by
+ * vit_attn_splitk_reduce into `out`, with the split partials kept in a
+ * static device array of VIT_NOALLOC_SCRATCH_BYTES bytes instead of a
+ * caller's workspace.  The call allocates and frees nothing; the array is
+ * the library's, one per GPU, held until the process ends.  Its device
+ * address is looked up once per GPU, on the first call made with that GPU
+ * current.
+ *  Arguments as vit_attn_decode_mq (q, out fp32 [n_seqs][q_len][n_q_heads]
+ *  [128]); there is no workspace argument.
+ *  Errors: those of vit_attn_decode_mq; VIT_E_SCRATCH when
+ *  vit_attn_workspace_bytes(n_seqs, n_q_heads * q_len, 128, n_splits) >
+ *  VIT_NOALLOC_SCRATCH_BYTES (checked on the host before anything is
+ *  enqueued); VIT_E_HIP if the array's address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that may overlap on one GPU (different streams, or
+ * host threads, without an order between them) race on it and may return
+ * wrong results.  Nothing in it needs clearing: the decode writes every
+ * partial the merge reads.  Kernel events armed by vit_arm_kernel_events
+ * bracket the decode kernel of this call. */
+int vit_attn_decode_noalloc(const vit_kv_plane *k, const vit_kv_plane *v, const float *q,
+                            int32_t n_q_heads, int32_t q_len, const int64_t *seq_len,
+                            const float *k_new, const float *v_new, float scale, int32_t n_splits,
+                            float *out, void *stream);
+
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
  * thread's next vit_kv_append_quant, vit_attn_decode, vit_attn_decode_mq,
- * vit_kv_transcode or vit_attn_probe_scores call (for the latter: its
+ * vit_attn_decode_noalloc, vit_kv_transcode or vit_attn_probe_scores call (for the latter: its
  * logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it
  * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and

@@ -8,7 +8,7 @@ names mirror the C entry points:
     vit_kv_plane_sizes, vit_kv_append_quant, vit_kv_transcode,
     vit_vbr_classic_next_step, vit_attn_workspace_bytes,
     vit_attn_default_splits, vit_attn_decode, vit_attn_decode_mq,
-    vit_attn_splitk_reduce, vit_attn_probe_workspace_bytes,
+    vit_attn_decode_noalloc, vit_attn_splitk_reduce, vit_attn_probe_workspace_bytes,
     vit_attn_probe_scores, vit_probe_select_evictions,
     vit_arm_kernel_events (a measurement aid)
 
@@ -26,7 +26,8 @@ __all__ = [
     "KVPlane", "VitError", "layout",
     "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_kv_transcode", "vit_vbr_classic_next_step",
     "vit_attn_workspace_bytes",
-    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_splitk_reduce",
+    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_decode_noalloc",
+    "vit_attn_splitk_reduce",
     "vit_attn_probe_workspace_bytes", "vit_attn_probe_scores", "vit_probe_select_evictions",
     "vit_probe_select_workspace_bytes",
     "vit_arm_kernel_events",
@@ -217,6 +218,23 @@ def vit_attn_decode_mq(k, v, q, n_q_heads, q_len, seq_len, k_new=None, v_new=Non
                                 _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
                                 _fptr(out, "out"), _stream_handle(stream))
     _lib.check("vit_attn_decode_mq", st)
+    return out
+
+
+def vit_attn_decode_noalloc(k, v, q, n_q_heads, q_len, seq_len, out, k_new=None, v_new=None, scale=None,
+                            n_splits=1, stream=None):
+    """Decode attention (+ split-K merge) with the split partials in the
+    library's static device scratch: q, out fp32 [S, q_len, Hq, 128] (out is
+    caller-allocated; the call allocates nothing)."""
+    lib = _lib.load()
+    if scale is None:
+        scale = 1.0 / np.sqrt(HEAD_DIM)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    st = lib.vit_attn_decode_noalloc(ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len),
+                                     sl, _fptr(k_new, "k_new"), _fptr(v_new, "v_new"), ctypes.c_float(scale),
+                                     int(n_splits), _fptr(out, "out"), _stream_handle(stream))
+    _lib.check("vit_attn_decode_noalloc", st)
     return out
 
 

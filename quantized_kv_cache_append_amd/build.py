@@ -33,6 +33,7 @@ SOURCES = {
     "decode_k3.hip": [],
     "decode_k4.hip": [],
     "reduce.hip": [],
+    "noalloc.hip": [],
     "probe.hip": [],
     "vit_host.cpp": [],
 }

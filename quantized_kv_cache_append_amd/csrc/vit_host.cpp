@@ -77,6 +77,107 @@ int enqueue_append(const vit_kv_plane* dst, const float* src, const int64_t* pos
 
 }  // namespace
 
+namespace vit {
+
+KernelEvents take_armed_events() {
+  const KernelEvents ev = g_armed;
+  g_armed = KernelEvents{};
+  return ev;
+}
+
+int check_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
+                 const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
+                 bool have_workspace, const void* workspace, const float* out) {
+  int st = check_plane(k);
+  if (st != VIT_OK) return st;
+  st = check_plane(v);
+  if (st != VIT_OK) return st;
+  if (k->side != VIT_SIDE_K || v->side != VIT_SIDE_V) return VIT_E_ARG;
+  if (k->n_seqs != v->n_seqs || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity) return VIT_E_ARG;
+  if (!q || !out || !seq_len) return VIT_E_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return VIT_E_ARG;
+  if (q_len < 1) return VIT_E_ARG;
+  const int32_t gqa = n_q_heads / k->n_kv_heads;
+  if (q_len > VIT_MAX_QLEN || gqa * q_len > VIT_MAX_GQA) return VIT_E_UNSUPPORTED;
+  if ((k_new == nullptr) != (v_new == nullptr)) return VIT_E_ARG;
+  if (n_splits < 1 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
+  if (n_splits > 1 && !have_workspace) return VIT_E_ARG;
+  if (!isfinite(scale)) return VIT_E_ARG;
+  for (int s = 0; s < k->n_seqs; ++s) {
+    if (seq_len[s] < q_len) return VIT_E_ARG;
+    if (seq_len[s] > k->capacity) return VIT_E_CAPACITY;
+  }
+  if (!aligned(q, 16) || !aligned(out, 16) || (workspace && !aligned(workspace, 16)) ||
+      (k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
+    return VIT_E_ALIGN;
+  return VIT_OK;
+}
+
+int enqueue_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
+                   const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
+                   float* workspace, float* out, hipStream_t stream, const KernelEvents& ev) {
+  const int32_t gqa = n_q_heads / k->n_kv_heads;
+  DecodeArgs a{};
+  a.kcodes = static_cast<const uint8_t*>(k->codes);
+  a.kscales = k->scales;
+  a.knorms = k->norms;
+  a.vcodes = static_cast<const uint8_t*>(v->codes);
+  a.vscales = v->scales;
+  a.vnorms = v->norms;
+  a.q = q;
+  a.k_new = k_new;  // quantized and stored in-kernel by the owning workgroup
+  a.v_new = v_new;
+  a.ws_o = workspace;
+  a.ws_ml = workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                                 ws_o_bytes(k->n_seqs, n_q_heads * q_len, n_splits))
+                      : nullptr;
+  a.out = out;
+  a.capacity = k->capacity;
+  a.n_kv_heads = k->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.gqa = gqa;
+  a.q_len = q_len;
+  a.n_splits = n_splits;
+  a.qscale = scale * 1.4426950408889634f;
+  load_signs(k, a.ksigns);
+  load_signs(v, a.vsigns);
+  for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
+  const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
+                  static_cast<unsigned>(k->n_seqs));
+  const int rows = gqa * q_len;  // query rows per KV head, all in every wave
+  const int nt = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;  // query rows per wave: 4, 8 or 16
+  return launch_decode(k->codec, v->codec, nt, grid, stream, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
+}
+
+int check_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim, int32_t n_splits,
+                 const vit_kv_plane* v, const float* out) {
+  if (head_dim != VIT_HEAD_DIM) return VIT_E_UNSUPPORTED;
+  if (!workspace || !out || !v) return VIT_E_ARG;
+  if (n_seqs < 1 || n_q_heads < 1 || n_splits < 2 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
+  if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
+  if (v->codec < VIT_CODEC_F16 || v->codec > VIT_CODEC_ROT3) return VIT_E_UNSUPPORTED;
+  if (is_rotated(v->codec) && !v->signs) return VIT_E_ARG;
+  if (!aligned(workspace, 16) || !aligned(out, 16)) return VIT_E_ALIGN;
+  return VIT_OK;
+}
+
+int enqueue_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t n_splits,
+                   const vit_kv_plane* v, float* out, hipStream_t stream) {
+  ReduceArgs a{};
+  a.ws_o = workspace;
+  a.ws_ml = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
+                                           ws_o_bytes(n_seqs, n_q_heads, n_splits));
+  a.out = out;
+  a.n_q_heads = n_q_heads;
+  a.n_splits = n_splits;
+  a.rotate = is_rotated(v->codec) ? 1 : 0;
+  load_signs(v, a.vsigns);
+  const dim3 grid(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(n_seqs));
+  return launch_reduce(grid, stream, a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+}
+
+}  // namespace vit
+
 extern "C" {
 
 const char* vit_status_string(int status) {
@@ -87,6 +188,7 @@ const char* vit_status_string(int status) {
     case VIT_E_CAPACITY: return "row outside the plane capacity (or capacity not a multiple of 256)";
     case VIT_E_ALIGN: return "misaligned pointer";
     case VIT_E_HIP: return "HIP launch error";
+    case VIT_E_SCRATCH: return "split partials larger than the static scratch (VIT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -349,63 +451,12 @@ int vit_attn_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q
 int vit_attn_decode_mq(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads,
                        int32_t q_len, const int64_t* seq_len, const float* k_new, const float* v_new, float scale,
                        int32_t n_splits, float* workspace, float* out, void* stream) {
-  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
-  g_armed = vit::KernelEvents{};
-  int st = check_plane(k);
+  const vit::KernelEvents ev = vit::take_armed_events();  // one-shot, whatever the outcome
+  const int st = vit::check_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits,
+                                   workspace != nullptr, workspace, out);
   if (st != VIT_OK) return st;
-  st = check_plane(v);
-  if (st != VIT_OK) return st;
-  if (k->side != VIT_SIDE_K || v->side != VIT_SIDE_V) return VIT_E_ARG;
-  if (k->n_seqs != v->n_seqs || k->n_kv_heads != v->n_kv_heads || k->capacity != v->capacity) return VIT_E_ARG;
-  if (!q || !out || !seq_len) return VIT_E_ARG;
-  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads != 0) return VIT_E_ARG;
-  if (q_len < 1) return VIT_E_ARG;
-  const int32_t gqa = n_q_heads / k->n_kv_heads;
-  if (q_len > VIT_MAX_QLEN || gqa * q_len > VIT_MAX_GQA) return VIT_E_UNSUPPORTED;
-  if ((k_new == nullptr) != (v_new == nullptr)) return VIT_E_ARG;
-  if (n_splits < 1 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
-  if (n_splits > 1 && !workspace) return VIT_E_ARG;
-  if (!isfinite(scale)) return VIT_E_ARG;
-  for (int s = 0; s < k->n_seqs; ++s) {
-    if (seq_len[s] < q_len) return VIT_E_ARG;
-    if (seq_len[s] > k->capacity) return VIT_E_CAPACITY;
-  }
-  if (!aligned(q, 16) || !aligned(out, 16) || (workspace && !aligned(workspace, 16)) ||
-      (k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
-    return VIT_E_ALIGN;
-
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-
-  vit::DecodeArgs a{};
-  a.kcodes = static_cast<const uint8_t*>(k->codes);
-  a.kscales = k->scales;
-  a.knorms = k->norms;
-  a.vcodes = static_cast<const uint8_t*>(v->codes);
-  a.vscales = v->scales;
-  a.vnorms = v->norms;
-  a.q = q;
-  a.k_new = k_new;  // quantized and stored in-kernel by the owning workgroup
-  a.v_new = v_new;
-  a.ws_o = workspace;
-  a.ws_ml = workspace ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                                 ws_o_bytes(k->n_seqs, n_q_heads * q_len, n_splits))
-                      : nullptr;
-  a.out = out;
-  a.capacity = k->capacity;
-  a.n_kv_heads = k->n_kv_heads;
-  a.n_q_heads = n_q_heads;
-  a.gqa = gqa;
-  a.q_len = q_len;
-  a.n_splits = n_splits;
-  a.qscale = scale * 1.4426950408889634f;
-  load_signs(k, a.ksigns);
-  load_signs(v, a.vsigns);
-  for (int s = 0; s < k->n_seqs; ++s) a.seq_len[s] = static_cast<int32_t>(seq_len[s]);
-  const dim3 grid(static_cast<unsigned>(n_splits), static_cast<unsigned>(k->n_kv_heads),
-                  static_cast<unsigned>(k->n_seqs));
-  const int rows = gqa * q_len;  // query rows per KV head, all in every wave
-  const int nt = rows <= 4 ? 1 : rows <= 8 ? 2 : 4;  // query rows per wave: 4, 8 or 16
-  return vit::launch_decode(k->codec, v->codec, nt, grid, hs, a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  return vit::enqueue_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, workspace, out,
+                             static_cast<hipStream_t>(stream), ev);
 }
 
 int vit_arm_kernel_events(void* start_event, void* stop_event) {
@@ -417,24 +468,9 @@ int vit_arm_kernel_events(void* start_event, void* stop_event) {
 
 int vit_attn_splitk_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,
                            int32_t n_splits, const vit_kv_plane* v, float* out, void* stream) {
-  if (head_dim != VIT_HEAD_DIM) return VIT_E_UNSUPPORTED;
-  if (!workspace || !out || !v) return VIT_E_ARG;
-  if (n_seqs < 1 || n_q_heads < 1 || n_splits < 2 || n_splits > VIT_MAX_SPLITS) return VIT_E_ARG;
-  if (n_seqs > VIT_MAX_SEQS) return VIT_E_UNSUPPORTED;
-  if (v->codec < VIT_CODEC_F16 || v->codec > VIT_CODEC_ROT3) return VIT_E_UNSUPPORTED;
-  if (is_rotated(v->codec) && !v->signs) return VIT_E_ARG;
-  if (!aligned(workspace, 16) || !aligned(out, 16)) return VIT_E_ALIGN;
-  vit::ReduceArgs a{};
-  a.ws_o = workspace;
-  a.ws_ml = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
-                                           ws_o_bytes(n_seqs, n_q_heads, n_splits));
-  a.out = out;
-  a.n_q_heads = n_q_heads;
-  a.n_splits = n_splits;
-  a.rotate = is_rotated(v->codec) ? 1 : 0;
-  load_signs(v, a.vsigns);
-  const dim3 grid(static_cast<unsigned>(n_q_heads), static_cast<unsigned>(n_seqs));
-  return vit::launch_reduce(grid, static_cast<hipStream_t>(stream), a) == hipSuccess ? VIT_OK : VIT_E_HIP;
+  const int st = vit::check_reduce(workspace, n_seqs, n_q_heads, head_dim, n_splits, v, out);
+  if (st != VIT_OK) return st;
+  return vit::enqueue_reduce(workspace, n_seqs, n_q_heads, n_splits, v, out, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

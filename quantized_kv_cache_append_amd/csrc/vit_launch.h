@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/vit.h"
+
 namespace vit {
 
 constexpr int kMaxSeqs = 64;
@@ -146,5 +148,20 @@ hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
 hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream, const ProbeArgs& args,
                         const KernelEvents& ev);
 hipError_t launch_select(int n_seqs, hipStream_t stream, const SelectArgs& args);
+
+// Host-side pieces of the decode and reduce entry points (vit_host.cpp),
+// shared with the entry point that keeps the split partials in static device
+// memory (noalloc.hip).
+KernelEvents take_armed_events();  // this thread's armed events, disarming them
+int check_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
+                 const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
+                 bool have_workspace, const void* workspace, const float* out);
+int enqueue_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
+                   const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
+                   float* workspace, float* out, hipStream_t stream, const KernelEvents& ev);
+int check_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim, int32_t n_splits,
+                 const vit_kv_plane* v, const float* out);
+int enqueue_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t n_splits,
+                   const vit_kv_plane* v, float* out, hipStream_t stream);
 
 }  // namespace vit

@@ -37,8 +37,8 @@ def test_header_declarations_are_all_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5):
-        assert _lib.status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert _lib.status_string(s) != "unknown status"
     assert _lib.status_string(7) == "unknown status"
 
 
@@ -154,6 +154,35 @@ def test_decode_mq_validation(lib):
     assert _decode_mq(lib, K, V, q_len=3, seq_len=(10, 2)) == _lib.VIT_E_ARG  # shorter than q_len
     assert _decode_mq(lib, K, V, q_len=2, seq_len=(513, 10)) == _lib.VIT_E_CAPACITY
     assert _decode_mq(lib, K, V, q_len=2, ns=3, ws=None) == _lib.VIT_E_ARG
+
+
+def _decode_noalloc(lib, k, v, hq=4, q_len=1, seq_len=(10, 10), ns=1, k_new=None, v_new=None, out=FAKE):
+    arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+    return lib.vit_attn_decode_noalloc(ctypes.byref(k), ctypes.byref(v), FAKE, hq, q_len, arr, k_new, v_new, 0.088,
+                                       ns, out, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks its arguments like vit_attn_decode_mq
+    and rejects split partials larger than its static scratch, on the host,
+    before it looks up the scratch or enqueues anything (no GPU here)."""
+    K, V = _plane(side=0, cap=1 << 20), _plane(side=1, cap=1 << 20)
+    assert _decode_noalloc(lib, K, V, seq_len=(0, 1)) == _lib.VIT_E_ARG
+    assert _decode_noalloc(lib, K, V, hq=3) == _lib.VIT_E_ARG
+    assert _decode_noalloc(lib, K, V, q_len=5) == _lib.VIT_E_UNSUPPORTED
+    assert _decode_noalloc(lib, K, V, k_new=FAKE) == _lib.VIT_E_ARG
+    assert _decode_noalloc(lib, K, V, ns=0) == _lib.VIT_E_ARG
+    assert _decode_noalloc(lib, K, V, out=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert _decode_noalloc(lib, V, K) == _lib.VIT_E_ARG
+    # partials of 2 x 32 rows x n_splits x 520 B against the 4 MiB array
+    limit = _lib.NOALLOC_SCRATCH_BYTES
+    need = lambda ns: lib.vit_attn_workspace_bytes(2, 32, 128, ns)
+    ns_max = max(n for n in range(2, 4097) if need(n) <= limit)
+    assert need(ns_max) <= limit < need(ns_max + 1)
+    assert _decode_noalloc(lib, K, V, hq=32, ns=ns_max + 1) == _lib.VIT_E_SCRATCH
+    assert _decode_noalloc(lib, K, V, hq=32, ns=4096) == _lib.VIT_E_SCRATCH
+    assert _decode_noalloc(lib, K, V, hq=16, q_len=2, ns=ns_max + 1) == _lib.VIT_E_SCRATCH  # 16 x 2 rows
+    assert _lib.status_string(_lib.VIT_E_SCRATCH).startswith("split partials larger than the static scratch")
 
 
 def _transcode(lib, src, dst, n_rows=(10, 10)):
