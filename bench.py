@@ -1,29 +1,32 @@
 #!/usr/bin/env python3
 """Decode-attention throughput of the quantized KV path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ladder]
 
-A step is one pass of the whole hot path over one batch: quantize-and-append
-the new token's K and V rows of every (sequence, KV head), flash-decode
-attention over the quantized cache, and the split-K merge.  The default
-workload is "batched": 8 sequences x 1 new token, 32 query heads on 8 KV
-heads, head_dim 128, 8192 cached rows per sequence, K and V both q8_0.
-Other workloads (tiny, lowbit, rotated, ladder) are available with
---workload.  ``--q-len N`` (2 .. 4, single-layer workloads) makes each step
-verify N new tokens per sequence at once, causal among themselves
-(vit_attn_decode_mq, all N rows appended by the decode call); ``value`` then
-counts the N tokens of every sequence.  The ladder's step appends a
-2048-row ubatch to every (layer, side) plane with vit_kv_append_quant on a
-second stream: decode l waits for layer l's two appends only, and each
-step's appends wait for the previous step's decodes.
+A step is one pass of the whole hot path over one batch.  The default
+workload is the ladder, the largest configuration: 16 layers whose K and V
+tensors each carry a codec from a seeded map over {f16, q8_0, q4_0, rot4},
+2 sequences, 32 query heads on 8 KV heads, head_dim 128, 200,704-row slots;
+a step appends a 2048-row ubatch to every (layer, side) plane with
+vit_kv_append_quant on a second stream and decodes one token per sequence
+through all 16 layers (decode + split-K merge per layer; decode l waits for
+layer l's two appends only, and each step's appends wait for the previous
+step's decodes).  The single-layer workloads (tiny, batched, lowbit,
+rotated) are available with --workload: a step there is the fused append of
+the new token's K/V rows, the decode and the merge.  ``--q-len N`` (2 .. 4,
+single-layer workloads) makes each step verify N new tokens per sequence at
+once, causal among themselves (vit_attn_decode_mq, all N rows appended by
+the decode call); ``value`` then counts the N tokens of every sequence.
 
 Inputs are synthetic (seeded device normals shaped like the workload) and
 resident in HBM before timing starts.  Because the batched cache (143 MB)
 fits in the 256 MB last-level cache, each timed step reads a different one of
 R device replicas (R * footprint >= 1 GiB), round-robin.
 
-The timed steps are eager C calls with pre-marshalled arguments, run twice.
-Pass 1 gives the step time.  In pass 2 every decode dispatch records a pair of
+The timed steps are eager C calls with pre-marshalled arguments.  Pass 1
+gives the step time: ``--repeats`` blocks of exactly K steps, each between
+device synchronisations; ``ms_per_step`` is the median block, with the
+fastest and slowest blocks beside it.  In pass 2 every decode dispatch records a pair of
 HIP events at its own start and end (vit_arm_kernel_events ->
 hipExtLaunchKernel), so the duration covers the kernel alone, as rocprofv3's
 kernel trace does; recording them costs the host about 16 us per launch,
@@ -37,7 +40,9 @@ launch / its mean duration, against the 8 TB/s HBM peak.  ``traffic``
 is the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
 a copy-kernel calibration), read from profiles/ only when it was measured on
 the current kernel sources.  ``cpu_baseline`` times the numpy oracle on the
-host for the same step (a baseline, not a target).
+host for the same step on every core this process may use, with the 1-core
+time and the CPU model (a baseline, not a target); it runs before the GPU
+is touched.
 """
 
 import argparse
@@ -195,51 +200,46 @@ def run_gpu(args):
     lens = [L] * S
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
-    # The ladder's ubatch appends go to a second stream (default priority too):
+    # The ladder's ubatch appends go to a second stream (default priority
+    # too), scheduled by the step driver (quantized_kv_cache_append_amd.step):
     # decode l waits only for layer l's appends, so the later layers' appends
     # run beside the first decodes; each step's appends wait for the previous
     # step's decodes (they rewrite the rows those read).
     fused = "ubatch" not in cfg
-    astream = stream if fused else torch.cuda.Stream()
-    app_done = [torch.cuda.Event() for _ in range(n_layers)]
-    fork = torch.cuda.Event()
+    astream = None if fused else torch.cuda.Stream()
 
     # every call of a step, marshalled once per replica (the host then only
     # issues the C calls, so the GPU queue never runs dry).  One (or q_len)
     # new token(s) per sequence: their K/V rows go through the decode call's
-    # fused append.  A ubatch of new rows (the ladder) is appended by
-    # vit_kv_append_quant first.
+    # fused append.
     calls = []
     for r in range(replicas):
-        app, dec = [], []
+        if not fused:
+            from quantized_kv_cache_append_amd.step import DecodeStep
+
+            calls.append(DecodeStep([(lay.K[r], lay.V[r]) for lay in layers], q, new_rows, out, lens, p_new, Hq,
+                                    n_splits, ws, stream, astream))
+            continue
+        dec = []
         for li, lay in enumerate(layers):
             kn, vn = new_rows[li]
-            if not fused:
-                app.append((vit.prepare_append(lay.K[r], kn, [p_new] * S, stream=astream),
-                            vit.prepare_append(lay.V[r], vn, [p_new] * S, stream=astream)))
             # [S][H][128] rows for one token, [S][q_len][H][128] for several
-            k_in = (kn[:, 0].contiguous() if QL == 1 else kn) if fused else None
-            v_in = (vn[:, 0].contiguous() if QL == 1 else vn) if fused else None
+            k_in = kn[:, 0].contiguous() if QL == 1 else kn
+            v_in = vn[:, 0].contiguous() if QL == 1 else vn
             d = vit.prepare_decode(lay.K[r], lay.V[r], q[li], Hq, lens, out[li], n_splits=n_splits,
                                    k_new=k_in, v_new=v_in, workspace=ws if n_splits > 1 else None,
                                    stream=stream, q_len=QL if QL > 1 else None)
             red = (vit.prepare_reduce(ws, S, Hq * QL, n_splits, lay.V[r], out[li], stream=stream)
                    if n_splits > 1 else None)
             dec.append((d, red))
-        calls.append((app, dec))
+        calls.append(dec)
 
     def step(i, ev=None):
-        app, dec = calls[i % replicas]
-        if app:
-            fork.record(stream)  # everything issued on the decode stream before this step
-            astream.wait_event(fork)
-            for li, (ck, cv) in enumerate(app):
-                ck()
-                cv()
-                app_done[li].record(astream)
-        for li, (d, red) in enumerate(dec):
-            if app:
-                stream.wait_event(app_done[li])
+        c = calls[i % replicas]
+        if not fused:
+            c(ev)
+            return
+        for li, (d, red) in enumerate(c):
             if ev is not None:
                 # the decode dispatch itself records this pair at its start and end
                 arm(ev[0][li], ev[1][li])
@@ -258,14 +258,19 @@ def run_gpu(args):
         for e in pair[0] + pair[1]:
             e.record(stream)
     arm = vit.vit_arm_kernel_events
-    # Pass 1, the step throughput: the timed steps as eager C calls.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            step(args.warmup + i)
-    torch.cuda.synchronize()
-    eager_ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    # Pass 1, the step throughput: the timed steps as eager C calls, in
+    # `repeats` blocks of exactly K steps, each bracketed by a device
+    # synchronisation; the median block gives ms_per_step.
+    block_ms = []
+    for rep in range(args.repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                step(args.warmup + rep * args.steps + i)
+        torch.cuda.synchronize()
+        block_ms.append(1e3 * (time.perf_counter() - t0) / args.steps)
+    eager_ms_per_step = float(np.median(block_ms))
     assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output"
     # Pass 2, the decode kernel's duration: the same steps again, each decode
     # dispatch recording its own start/stop events.  (Recording them costs the
@@ -321,17 +326,8 @@ def run_gpu(args):
             step(0)
         torch.cuda.synchronize()
         overlapped = [o.clone() for o in out]
-        app, dec = calls[0]
-        for ck, cv in app:
-            ck()
-            cv()
-        torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            for d, red in dec:
-                d()
-                if red is not None:
-                    red()
-        torch.cuda.synchronize()
+            calls[0].run_serial()
         worst = 0.0
         for a, b in zip(overlapped, out):
             rms = float(torch.sqrt(torch.mean(b * b)))
@@ -345,6 +341,7 @@ def run_gpu(args):
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
     return dict(cfg=cfg, wl=wl, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
+                block_ms=block_ms,
                 dec_mean_ms=dec_mean_ms,
                 dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
                 achieved_gbs=achieved)
@@ -766,60 +763,193 @@ def run_copy_calibration(steps):
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": steps}))
 
 
-def cpu_baseline(r, budget_s=15.0):
-    """The numpy oracle on the host: for each (sequence, KV head) of the step,
-    quantize the new rows, dequantize the cache and attend in fp64 (each of
-    q_len new tokens over the rows up to its own)."""
-    import numpy as np
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
 
-    from oracle import attention, codecs
+    return platform.processor() or "unknown"
+
+
+def _cpu_items(wl, q_len):
+    """The sampled (layer, sequence, KV head) units of a workload's step for
+    the CPU baseline: one unit of every layer for the ladder (so every codec
+    pair of its map is timed), up to 16 units of a single-layer workload."""
     import synth
+
+    cfg = synth.CONFIGS[wl]
+    S, H = cfg["seqs"], cfg["hkv"]
+    if cfg["layers"] > 1:
+        return [(li, (li // H) % S, (3 * li + 1) % H) for li in range(cfg["layers"])]
+    units = [(0, s, h) for s in range(S) for h in range(H)]
+    return units[:: max(1, len(units) // 16)][:16]
+
+
+_CPU_ITEMS = None
+
+
+def _cpu_prepare(wl, q_len, rows, n_new, items):
+    """Untimed set-up of the sampled units: each unit's cached rows encoded by
+    the oracle, its new rows and its query heads."""
+    global _CPU_ITEMS
+    from oracle import codecs
+    import synth
+
+    cfg = synth.CONFIGS[wl]
+    Hq, H = cfg["hq"], cfg["hkv"]
+    G = Hq // H
+    cmap = synth.codec_map(wl)
+    prep = []
+    for (li, s, h) in items:
+        kc, vc = cmap[li]
+        ks = synth.sign_mask(wl, li, "k") if kc in ROTATED else None
+        vs = synth.sign_mask(wl, li, "v") if vc in ROTATED else None
+        kx = synth.kv_rows(wl, "k", li, s, h, 0, rows)
+        vx = synth.kv_rows(wl, "v", li, s, h, 0, rows)
+        qx = synth.q_rows(wl, li, s, Hq)[h * G:(h + 1) * G]
+        prep.append((kc, vc, ks, vs, codecs.quantize(kc, kx[:rows - n_new], ks),
+                     codecs.quantize(vc, vx[:rows - n_new], vs), kx[rows - n_new:], vx[rows - n_new:], qx, q_len))
+    _CPU_ITEMS = prep
+    return len(prep)
+
+
+_CPU_BARRIER = None
+
+
+_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
+def _one_thread():
+    """Hold numpy's BLAS to one thread in this process (numpy loaded first,
+    so that its library is there to be limited)."""
+    import numpy  # noqa: F401
 
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+
+        return threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
-    wl, L, S, H, Hq, QL = r["wl"], r["L"], r["S"], r["H"], r["Hq"], r["QL"]
-    G = Hq // H
-    kc, vc = r["cmap"][0]
-    ks = synth.sign_mask(wl, 0, "k") if kc in ROTATED else None
-    vs = synth.sign_mask(wl, 0, "v") if vc in ROTATED else None
-    units = [(s, h) for s in range(S) for h in range(H)]
-    rows_unit = min(L, 8192)  # longer contexts are timed on an 8192-row slice and scaled
-    prep = []
-    for (s, h) in units[:4]:
-        kx = synth.kv_rows(wl, "k", 0, s, h, 0, rows_unit)
-        vx = synth.kv_rows(wl, "v", 0, s, h, 0, rows_unit)
-        qx = synth.q_rows(wl, 0, s, Hq)[h * G:(h + 1) * G]
-        prep.append((codecs.quantize(kc, kx[:-QL], ks), codecs.quantize(vc, vx[:-QL], vs),
-                     kx[-QL:], vx[-QL:], qx))
-    scale = 1.0 / math.sqrt(D)
-    n_done = 0
+        return None
+
+
+def _cpu_pool_init(barrier):
+    """Pool worker start-up: one BLAS thread per worker process (set before
+    numpy is imported here, and again through threadpoolctl)."""
+    global _CPU_BARRIER
+    for v in _THREAD_VARS:
+        os.environ[v] = "1"
+    _one_thread()
+    _CPU_BARRIER = barrier
+
+
+def _cpu_pool_prepare(a):
+    _cpu_prepare(*a)
+    _CPU_BARRIER.wait()
+
+
+def _cpu_unit(i):
+    """Timed work of one sampled unit: encode its new K/V rows, decode the
+    cache, fp64 attention of each new query token over the rows up to its
+    own.  Returns (encode seconds, decode + attention seconds)."""
+    import numpy as np
+
+    from oracle import attention, codecs
+
+    kc, vc, ks, vs, kq, vq, kn, vn, qx, ql = _CPU_ITEMS[i]
+    t0 = time.perf_counter()
+    kq_new = codecs.quantize(kc, kn, ks) if len(kn) else None
+    vq_new = codecs.quantize(vc, vn, vs) if len(vn) else None
+    t1 = time.perf_counter()
+    kq2 = kq if kq_new is None else {k: np.concatenate([kq[k], kq_new[k]]) for k in kq}
+    vq2 = vq if vq_new is None else {k: np.concatenate([vq[k], vq_new[k]]) for k in vq}
+    kd, vd = codecs.dequant(kc, kq2, ks), codecs.dequant(vc, vq2, vs)
+    n = kd.shape[0]
+    for t in range(ql):  # token t sees rows 0 .. n - ql + t (the timing does not depend on q's values)
+        attention.attend(qx, kd[:n - ql + 1 + t], vd[:n - ql + 1 + t], 1.0 / math.sqrt(D))
+    return t1 - t0, time.perf_counter() - t1
+
+
+def cpu_baseline(wl, q_len, budget_s=15.0):
+    """The numpy oracle, untuned, on the host's cores: for sampled
+    (layer, sequence, KV head) units of the step, encode the new rows, decode
+    the cache and attend in fp64; scaled to the whole step.
+
+    One pass runs the units one after another on one core (the 1-core time,
+    also split into encode and attention); a second pass runs them in a
+    process pool over every core this process may use, for a wall-clock
+    time.  Contexts longer than 8192 rows are attended over an 8192-row
+    slice (the new rows included) and the attention time scaled by
+    L / slice.  Runs before the process touches the GPU (spawned workers)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import synth
+
+    cfg = synth.CONFIGS[wl]
+    S, H, L, n_layers = cfg["seqs"], cfg["hkv"], cfg["ctx"], cfg["layers"]
+    n_new = cfg.get("ubatch", q_len)        # rows encoded per unit per step
+    rows = min(L, max(8192, n_new + 4096))  # rows attended in the sample
+    att_scale = L / rows
+    items = _cpu_items(wl, q_len)
+    units_per_layer = S * H
+    cores = len(os.sched_getaffinity(0))
+    # 1 core: every sampled unit once (after one untimed run of each)
+    limiter = _one_thread()
+    _cpu_prepare(wl, q_len, rows, n_new, items)
+    for i in range(len(items)):
+        _cpu_unit(i)
+    tq, ta = np.zeros(len(items)), np.zeros(len(items))
+    reps1 = 0
     t0 = time.perf_counter()
     while True:
-        for kq, vq, kn, vn, qx in prep:
-            kq2 = {k: np.concatenate([a, b]) for (k, a), b in
-                   zip(kq.items(), codecs.quantize(kc, kn, ks).values())}
-            vq2 = {k: np.concatenate([a, b]) for (k, a), b in
-                   zip(vq.items(), codecs.quantize(vc, vn, vs).values())}
-            kd, vd = codecs.dequant(kc, kq2, ks), codecs.dequant(vc, vq2, vs)
-            n = kd.shape[0]
-            for t in range(QL):  # token t sees rows 0 .. n - QL + t (the timing does not depend on q's values)
-                attention.attend(qx, kd[:n - QL + 1 + t], vd[:n - QL + 1 + t], scale)
-            n_done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        for i in range(len(items)):
+            a, b = _cpu_unit(i)
+            tq[i] += a
+            ta[i] += b
+        reps1 += 1
+        if time.perf_counter() - t0 >= budget_s / 3:
             break
+    tq /= reps1
+    ta /= reps1
     if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    per_unit = el / n_done * (L / rows_unit)
-    step_s = per_unit * len(units) * r["n_layers"]
-    return {"value": S * QL / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{n_done} (sequence, KV head) units of the step ({kc}/{vc}, G={G}, {QL} new token(s)) over "
-                       f"{rows_unit} rows each, {el:.1f} s on 1 thread, scaled to {len(units)} units x "
-                       f"{L} rows x {r['n_layers']} layer(s) per step; step = quantize new row(s) + "
-                       "dequantize cache + fp64 attention")}
+        limiter.restore_original_limits()
+    per_layer = {}
+    for (li, _, _), a, b in zip(items, tq, ta):
+        per_layer.setdefault(li, []).append(a + b * att_scale)
+    # each layer's units cost the mean of its sampled units
+    one_core_step = sum(units_per_layer * float(np.mean(v)) for v in per_layer.values()) * (n_layers / len(per_layer))
+    sample_work = float(np.sum(tq + ta))  # one pass over the sampled units, as executed
+    # all cores: the same units in a process pool.  Every worker prepares
+    # them (untimed) and waits at a barrier, so each worker takes exactly one
+    # set-up task and none is still setting up when the timing starts.
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(cores)
+    reps = max(math.ceil(2 * cores / len(items)), math.ceil((budget_s / 3) * cores / sample_work))
+    with ctx.Pool(cores, initializer=_cpu_pool_init, initargs=(barrier,)) as pool:
+        pool.map(_cpu_pool_prepare, [(wl, q_len, rows, n_new, items)] * cores, chunksize=1)
+        pool.map(_cpu_unit, list(range(len(items))) * math.ceil(cores / len(items)), chunksize=1)  # warm
+        t0 = time.perf_counter()
+        pool.map(_cpu_unit, list(range(len(items))) * reps, chunksize=1)
+        wall = time.perf_counter() - t0
+    full_work = one_core_step
+    pool_step = wall * full_work / (reps * sample_work)
+    tokens = S * q_len
+    pairs = sorted({synth.codec_map(wl)[li] for li, _, _ in items})
+    return {"value": round(tokens / pool_step, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "one_core_value": round(tokens / one_core_step, 4),
+            "step_s": round(pool_step, 3), "one_core_step_s": round(one_core_step, 3),
+            "sample": (f"{len(items)} sampled (layer, sequence, KV head) units of the {wl} step"
+                       f" ({len(pairs)} (K, V) codec pairs), each: encode its {n_new} new row(s) per side, decode "
+                       f"{rows} cached rows, fp64 attention of its query heads; 1 core: {reps1} pass(es), "
+                       f"{1e3 * sample_work:.0f} ms per pass; {cores} cores: {reps} x {len(items)} units in a "
+                       f"process pool, {wall:.2f} s wall; scaled to {units_per_layer} units x {n_layers} layer(s)"
+                       + (f" and attention over {L} rows (x{att_scale:.2f})" if att_scale > 1 else "")
+                       + " per step")}
 
 
 def profile_tag(workload, q_len, codecs=None):
@@ -967,7 +1097,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="batched", choices=WORKLOADS)
+    ap.add_argument("--workload", default="ladder", choices=WORKLOADS)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed blocks of --steps steps each; ms_per_step is the median block")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0, help="split count (default: the library heuristic)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -1051,10 +1183,20 @@ def main():
     if args.append:
         main_append(args)
         return
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on the host's cores, before this process touches the GPU
+        cpu = cpu_baseline(args.workload, args.q_len, args.cpu_seconds)
+        print(f"# cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} cores ({cpu['cpu_model']})",
+              file=sys.stderr, flush=True)
     r = run_gpu(args)
     cfg = r["cfg"]
     tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
     traffic = load_traffic("decode", profile_tag(args.workload, r["QL"], args.codecs), r["n_splits"])
+    pairs = sorted(set(r["cmap"]))
+    codec_txt = (f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}" if r["n_layers"] == 1 else
+                 f"per-layer (K, V) codecs from {{{', '.join(sorted({c for p in pairs for c in p}))}}} "
+                 f"({len(pairs)} pairs over {r['n_layers']} layers)")
     line = {
         "metric": "decode-attention tokens/s + effective KV-read GB/s (% of HBM peak), 1 GPU",
         "value": round(tok_s, 1),
@@ -1063,16 +1205,20 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 5),
+        "ms_per_step_min": round(min(r["block_ms"]), 5),
+        "ms_per_step_max": round(max(r["block_ms"]), 5),
+        "repeats": args.repeats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q8_0/q4_0/rot4/rot3/f16 codes, fp16 MFMA operands (hi+lo split), fp32 accumulate",
+        "dtype": f"{codec_txt} codes; fp16 MFMA operands (hi+lo split), fp32 accumulate",
         "data": "synthetic (seeded device normals shaped like the workload; no model weights or dataset)",
         "config": {
             "workload": profile_tag(cfg["name"], r["QL"], args.codecs),
             "n_seqs": r["S"], "n_q_heads": r["Hq"], "n_kv_heads": r["H"], "head_dim": D,
             "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"], "query_tokens_per_seq": r["QL"],
-            "codecs": "ladder (seeded per layer/side)" if r["n_layers"] > 1 else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
+            "codecs": ("ladder: " + ", ".join(f"{k}/{v}" for k, v in r["cmap"])) if r["n_layers"] > 1
+            else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
             "n_splits": r["n_splits"], "cold_cache_replicas": r["replicas"], "launch": r["mode"],
         },
         "graph_ms_per_step": None if r["graph_ms_per_step"] is None else round(r["graph_ms_per_step"], 5),
@@ -1092,8 +1238,8 @@ def main():
         },
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(r, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

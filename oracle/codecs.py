@@ -128,9 +128,14 @@ def level_index(t, thr):
 
     Equivalently: the nearest level, exact midpoints resolved away from zero.
     Both rotated codecs (rot4 with 15 thresholds, rot3 with 7) use this rule.
+    Counted as: for t >= 0 (-0 included) the thresholds at or below t, for
+    t < 0 the thresholds strictly below t.
     """
-    tt = np.asarray(t, dtype=np.float32)[..., None]
-    return (tt > thr).sum(axis=-1) + ((tt == thr) & (tt >= 0)).sum(axis=-1)
+    t = np.asarray(t, dtype=np.float32)
+    thr = np.asarray(thr, dtype=np.float32)
+    at_or_below = np.searchsorted(thr, t, side="right")
+    strictly_below = np.searchsorted(thr, t, side="left")
+    return np.where(t >= 0, at_or_below, strictly_below)
 
 
 def whiten_rot4(x, signs16):

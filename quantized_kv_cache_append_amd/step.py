@@ -1,0 +1,91 @@
+"""The multi-layer decode step: per layer, append a ubatch of new K/V rows,
+then decode and merge, with the appends overlapped with the decodes.
+
+This is the step of the per-(layer, side) codec ladder: every layer's K and
+V tensors have their own codec (buun-llama-cpp page, "VBR -- Variable
+Bit-Rate KV Cache"), each step appends a ubatch of new rows to every
+(layer, side) plane -- 2048 rows in the serverAppConfigs commit log's
+"BATCH_SIZE 2048 -> 4096, UBATCH_SIZE 1024 -> 2048" commit, at rows of its
+256-aligned 200,704-row slots ("CTX_SIZE 540672 -> 401408" commit) -- and
+then decodes one token per sequence through every layer.
+
+Schedule.  The appends go to a second stream.  Decode l waits on an event
+recorded after layer l's two appends, so the later layers' appends run while
+the first layers decode.  Each step's appends wait on an event recorded on
+the decode stream when the step starts, because they rewrite rows that the
+previous step's decodes read.  (Valid when all of a step's inputs are known
+up front; in a model's forward pass layer l + 1's rows depend on layer l.)
+
+Everything here is argument marshalling and stream ordering: every
+operation of the step is a call into libvit.so.
+"""
+
+from . import prepare_append, prepare_decode, prepare_reduce, vit_arm_kernel_events
+
+HEAD_DIM = 128
+
+
+class DecodeStep:
+    """One step over ``layers`` = [(K plane, V plane)] with the per-layer
+    inputs prepared once.
+
+    q[l]        fp32 [S, Hq, 128] query rows of layer l
+    new_rows[l] (k, v) fp32 [S, T, Hkv, 128]: the ubatch stored at rows
+                p_new .. p_new + T - 1 of every sequence before layer l decodes
+    out[l]      fp32 [S, Hq, 128] outputs
+    lens        rows attended per sequence (they count the ubatch rows)
+    workspace   split partials (shared by the layers: the decodes are
+                ordered on one stream), n_splits > 1
+    stream, append_stream   torch streams (default priority)
+    """
+
+    def __init__(self, layers, q, new_rows, out, lens, p_new, n_q_heads, n_splits, workspace, stream,
+                 append_stream):
+        import torch
+
+        self.stream, self.append_stream = stream, append_stream
+        S = layers[0][0].n_seqs
+        self.n_layers = len(layers)
+        self.appends, self.decodes = [], []
+        for (K, V), ql, (kn, vn), o in zip(layers, q, new_rows, out):
+            self.appends.append((prepare_append(K, kn, [p_new] * S, stream=append_stream),
+                                 prepare_append(V, vn, [p_new] * S, stream=append_stream)))
+            d = prepare_decode(K, V, ql, n_q_heads, lens, o, n_splits=n_splits,
+                               workspace=workspace if n_splits > 1 else None, stream=stream)
+            r = prepare_reduce(workspace, S, n_q_heads, n_splits, V, o, stream=stream) if n_splits > 1 else None
+            self.decodes.append((d, r))
+        self.fork = torch.cuda.Event()
+        self.app_done = [torch.cuda.Event() for _ in range(self.n_layers)]
+
+    def __call__(self, kernel_events=None):
+        """Issue one step.  ``kernel_events`` = (starts, stops), one pair per
+        layer, armed so that each decode dispatch records its own pair."""
+        self.fork.record(self.stream)  # everything issued on the decode stream before this step
+        self.append_stream.wait_event(self.fork)
+        for li, (ck, cv) in enumerate(self.appends):
+            ck()
+            cv()
+            self.app_done[li].record(self.append_stream)
+        for li, (d, r) in enumerate(self.decodes):
+            self.stream.wait_event(self.app_done[li])
+            if kernel_events is not None:
+                vit_arm_kernel_events(kernel_events[0][li], kernel_events[1][li])
+            d()
+            if r is not None:
+                r()
+
+    def run_serial(self):
+        """The same calls with no overlap: every append, then every decode
+        (the reference schedule the overlapped step must agree with)."""
+        import torch
+
+        torch.cuda.synchronize()
+        for ck, cv in self.appends:
+            ck()
+            cv()
+        torch.cuda.synchronize()
+        for d, r in self.decodes:
+            d()
+            if r is not None:
+                r()
+        torch.cuda.synchronize()
