@@ -159,10 +159,15 @@ typedef struct vit_kv_plane {
   void *codes;
   uint16_t *scales;    /* fp16 bits; NULL for F16 */
   uint16_t *norms;     /* fp16 bits; ROT4 only, else NULL */
-  const uint8_t *signs;/* [host] 16 bytes; ROT4 only, else NULL */
+  const uint8_t *signs;/* [host] 16 bytes; ROT4 and ROT3 only, else NULL */
 } vit_kv_plane;
 
-/* Byte sizes of the three arrays of a plane (host only, no device work).
+/* Byte sizes of the three arrays of a plane (host only, no device work):
+ * bits per value 16 (f16), 8.5 (q8_0), 4.5 (q4_0) as in the buun-llama-cpp
+ * page's "Codecs" table, 4.625 (rot4: codes, block scales and a row norm) and
+ * 3.5 (rot3, the Randozart/VITRIOL page's tq3_0 size in "What sets VITRIOL
+ * apart"); capacity a multiple of 256 (serverAppConfigs commit log,
+ * "CTX_SIZE 540672 -> 401408" commit: slots aligned to 256 for the FA path).
  * Returns VIT_OK or a negative status; any out pointer may be NULL. */
 int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_t head_dim,
                        int64_t capacity, size_t *codes_bytes, size_t *scales_bytes,
@@ -191,8 +196,9 @@ int vit_kv_append_quant(const vit_kv_plane *dst, const float *src, const int64_t
  * (so codes, scales and norms are bit-exact with the codec definitions).
  *  src, dst  planes with equal side, n_seqs, n_kv_heads and capacity, whose
  *            arrays do not overlap (VIT_E_ARG).  The codec pair is one of
- *            f16 -> q8_0, q4_0 or rot4 and q8_0 -> q4_0 or rot4 (rot4 being
- *            the rotated 4-bit rung); any other pair is VIT_E_UNSUPPORTED.
+ *            f16 -> q8_0, q4_0, rot4 or rot3; q8_0 -> q4_0, rot4 or rot3;
+ *            q4_0 -> rot3 (rot4 and rot3 being the rotated 4-bit and 3-bit
+ *            rungs); any other pair is VIT_E_UNSUPPORTED.
  *  n_rows    [host] int64 [n_seqs]: rows 0 .. n_rows[s]-1 of every KV head of
  *            sequence s are re-encoded, 0 <= n_rows[s] <= capacity
  *            (VIT_E_CAPACITY otherwise).  Rows of dst past them are left
@@ -203,10 +209,10 @@ int vit_kv_transcode(const vit_kv_plane *src, const vit_kv_plane *dst, const int
                      void *stream);
 
 /* Host only: the next step of the classic ladder f16 -> q8_0 -> q4_0 (same
- * page and section: the order is strictly banded, i.e. every movable tensor
- * reaches q8_0 before any goes on to q4_0; a side pinned to a fixed type is
- * never degraded; degrades stop at the last step whose aggregate bits/value
- * is still at or above the floor).
+ * page and section).  The classic order moves tensors band by band: no tensor
+ * goes from q8_0 to q4_0 while a movable tensor is still at f16.  A side
+ * pinned to a fixed type never moves, and no step is taken that would bring
+ * the aggregate bits/value below the floor.
  *  codecs       [host] int32 [n_tensors]: each tensor's codec, f16, q8_0 or
  *               q4_0 (VIT_E_ARG otherwise); tensors are equally sized.
  *  price_order  [host] int32 [n_tensors]: tensor indices, cheapest to degrade
@@ -221,8 +227,10 @@ int vit_vbr_classic_next_step(int32_t n_tensors, const int32_t *codecs, const in
                               const uint8_t *movable, double floor_bpv, int32_t *tensor,
                               int32_t *new_codec);
 
-/* Workspace bytes vit_attn_decode needs for n_splits > 1: fp32 partial
- * outputs [S][Hq][n_splits][128] followed by (max, sum) pairs
+/* Workspace bytes vit_attn_decode needs for n_splits > 1 (the split-K
+ * partials of the flash-decode path the buun-llama-cpp page's
+ * "Requirements" paragraph requires): fp32 partial outputs
+ * [S][Hq][n_splits][128] (256-byte padded) followed by (max, sum) pairs
  * [S][Hq][n_splits][2].  Returns 0 for invalid sizes. */
 size_t vit_attn_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t head_dim,
                                 int32_t n_splits);
@@ -233,7 +241,11 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
 
 /* Decode attention for one new query token per sequence over rows
  * 0 .. seq_len[s]-1 of its KV head (grouped-query: kv_head = q_head / G,
- * G = n_q_heads / n_kv_heads), dequantizing K and V on the fly.
+ * G = n_q_heads / n_kv_heads), dequantizing K and V on the fly: flash
+ * attention over a quantized KV cache (buun-llama-cpp page, "Requirements"
+ * paragraph: quantized KV needs the flash-attention path; "Codecs" table for
+ * the per-side codecs; Randozart/VITRIOL page, "Configuration" table for
+ * separate K and V cache types).
  *  k, v      planes with equal n_seqs, n_kv_heads, capacity; sides K and V.
  *  q         fp32 [n_seqs][n_q_heads][128] in the model domain.
  *  seq_len   [host] int64 [n_seqs], 1 .. capacity, counting the new row.
@@ -282,10 +294,14 @@ int vit_attn_decode_mq(const vit_kv_plane *k, const vit_kv_plane *v, const float
                        const float *k_new, const float *v_new, float scale, int32_t n_splits,
                        float *workspace, float *out, void *stream);
 
-/* Merge the split partials of vit_attn_decode: M = max m_s,
- * L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L (max values are kept
- * in base-2 units); for a ROT4 V plane the merged row is rotated back to the
- * model domain with v's sign mask.  `v` is read only for its codec and signs.
+/* Merge the split partials of vit_attn_decode (the second pass of the
+ * split-K flash decode): M = max m_s, L = sum l_s 2^(m_s - M),
+ * O = sum o_s 2^(m_s - M) / L (max values are kept in base-2 units); for a
+ * ROT4 or ROT3 V plane the merged row is rotated back to the model domain
+ * with v's sign mask (x = s .* WHT(o) / 128; buun-llama-cpp page, "How it
+ * works", step 1: the rotation is an orthogonal transform after sign flips).
+ * `v` is read only for its codec and signs.  Empty partials (l_s = 0) are
+ * skipped.
  *  out  fp32 [n_seqs][n_q_heads][128]. */
 int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_heads,
                            int32_t head_dim, int32_t n_splits, const vit_kv_plane *v,
@@ -297,10 +313,10 @@ int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_h
 size_t vit_attn_probe_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int64_t capacity);
 
 /* Attention-probe cell scores for sparse KV eviction (Randozart/VITRIOL page:
- * "What sets VITRIOL apart" -- probe scoring decides which KV cells earn
- * their keep; "How It Works -- Resident mode" -- a probe graph of a q.K
- * softmax with exponential decay, run every 16 steps; draft tokens are
- * excluded).  For every sequence s and every query head, the softmax of
+ * "What sets VITRIOL apart" -- an attention probe ranks the cache cells for
+ * eviction, with the first and the latest cells kept; "How It Works --
+ * Resident mode" -- a probe graph of a q.K softmax with exponential decay,
+ * run every 16 steps; draft tokens are left out).  For every sequence s and every query head, the softmax of
  * scale * q . k over its KV head's cells 0 .. seq_len[s]-1 (keys dequantized
  * on the fly, as decode does) gives one probability per cell; a cell is a
  * token position holding every KV head, so its mass is the sum over all
@@ -320,8 +336,9 @@ size_t vit_attn_probe_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int64_t
 int vit_attn_probe_scores(const vit_kv_plane *k, const float *q, int32_t n_q_heads, const int64_t *seq_len,
                           float scale, float decay, float *workspace, float *scores, void *stream);
 
-/* The cells to evict (same page and section: the lowest-scored middle cells
- * go first; sinks and recent cells are protected).  For each sequence s, the
+/* The cells to evict (same page and sections: the middle cells with the
+ * lowest scores are evicted first; the first (sink) and the latest cells are
+ * never chosen).  For each sequence s, the
  * middle cells are n_sink <= j < seq_len[s] - n_recent; the n_evict lowest
  * (score, cell) pairs among them (equal scores: lower cell first, so the
  * choice is unique) are written in increasing cell order.

@@ -19,7 +19,7 @@ What it computes (numpy, written for a reader to check by eye):
                     plus split partials and their merge.
 * ``bytes_model``-- bits/value, bytes per row and the per-token KV arithmetic.
 * ``vbr``        -- a VBR degrade step (stored rows decoded and re-encoded one
-                    rung down) and the classic ladder's strictly banded order.
+                    rung down) and the classic ladder's band-by-band order.
 * ``probe``      -- attention-probe cell scores (per-cell softmax mass with
                     exponential decay) and the choice of cells to evict.
 

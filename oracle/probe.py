@@ -4,8 +4,8 @@ cells to evict.
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: the Randozart/VITRIOL page -- "What sets VITRIOL apart" table
-(probe-scored sparse eviction: attention-probe scoring decides which KV cells
-earn their keep; sinks and recent cells are protected), "Configuration" table
+(sparse eviction driven by an attention probe that ranks the cache cells;
+the first and the latest cells are kept), "Configuration" table
 (score=probe, score_every=16) and "How It Works -- Resident mode" (a probe
 graph of a q.K softmax with exponential decay runs every 16 steps; the
 lowest-scored middle cells are evicted first; sinks and recent cells are

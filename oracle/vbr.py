@@ -6,8 +6,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 Source: the buun-llama-cpp page, "VBR -- Variable Bit-Rate KV Cache".  The
 cache starts at f16 and, under budget pressure, degrades one (layer, side)
 tensor at a time down a ladder of codecs, following a per-model price order.
-The classic ladder is f16 -> q8_0 -> q4_0, and its order is strictly banded:
-every movable tensor reaches q8_0 before any tensor goes on to q4_0.  A side
+The classic ladder is f16 -> q8_0 -> q4_0, taken band by band: no tensor
+moves from q8_0 to q4_0 while a movable tensor is still at f16.  A side
 pinned to a fixed type never degrades, and degrades stop at the last step
 whose aggregate bits/value is still at or above the floor.
 

@@ -1,5 +1,5 @@
 """Pins of oracle/vbr.py: the degrade step (re-encoding stored rows) and the
-classic ladder's strictly banded order (buun-llama-cpp page, "VBR -- Variable
+classic ladder's band-by-band order (buun-llama-cpp page, "VBR -- Variable
 Bit-Rate KV Cache").  CPU only."""
 
 import numpy as np
