@@ -261,9 +261,9 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
  *            `workspace` and vit_attn_splitk_reduce produces `out`.
  *  out       fp32 [n_seqs][n_q_heads][128], model domain.
  * The result equals softmax(scale * q K^T) V over the dequantized rows to
- * fp32 accumulation accuracy: not bitwise across split counts, and not
- * bitwise between calls when a split holds more than 16 tiles (its waves
- * then take tiles as they free up, so the summation order follows timing). */
+ * fp32 accumulation accuracy.  It is bitwise repeatable for the same inputs
+ * and split count (the summation order is fixed); it is not bitwise across
+ * split counts. */
 int vit_attn_decode(const vit_kv_plane *k, const vit_kv_plane *v, const float *q,
                     int32_t n_q_heads, const int64_t *seq_len, const float *k_new,
                     const float *v_new, float scale, int32_t n_splits, float *workspace,

@@ -1,11 +1,12 @@
 // Flash-decode attention over a quantized KV plane pair, for gfx950.
 //
 // One workgroup of 8 waves per (split, KV head, sequence), the only one on
-// its compute unit.  Split s owns the 32-row tiles s, s + n_splits, ...; the
-// waves take them one at a time from an LDS counter, each handling all query
-// rows of the KV head, keeping its own online softmax state and prefetching
-// its next tiles into registers while it computes the current one.  The
-// waves are merged through LDS at the end.
+// its compute unit.  Split s owns the 32-row tiles s, s + n_splits, ...;
+// wave w of the workgroup takes every 8th of them, starting at the w-th,
+// handles all query rows of the KV head, keeps its own online softmax state
+// and prefetches its next tiles into registers while it computes the current
+// one.  The waves are merged through LDS at the end, in a fixed order, so
+// the result is bitwise repeatable.
 //
 // Both products run on MFMA 16x16x32 f16 with exact operands:
 //   * K and V codes are exact in fp16 (f16 values, int8 / 4-bit integers,
@@ -250,14 +251,29 @@ __device__ inline float row16_sum(float v) {
   return v + dpp<0x128>(v);
 }
 
+// x + nb * (fp16 in half HI of w), in fp32, one rounding: one v_fma_mix_f32
+// (the fp16 operand is converted exactly).
+template <int HI>
+__device__ inline float fma_f16(uint32_t w, float nb, float x) {
+  float r;
+  if constexpr (HI) __asm__("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nb), "v"(x));
+  else __asm__("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(nb), "v"(x));
+  return r;
+}
+
+// Part of the hi/lo fp16 split of a pair (x0, x1): nb = 0 gives the hi part
+// fp16(x) toward zero, nb = -1 the lo part fp16(x - hi) (x - hi is exact).
+// Four operations per pair: two conversions and two v_fma_mix_f32.
+__device__ inline uint32_t split_part(float x0, float x1, float nb) {
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fma_f16<0>(hi, nb, x0), fma_f16<1>(hi, nb, x1)));
+}
+
 // hi + lo fp16 split of two fp32 values: hi = fp16(x) toward zero (so x - hi
 // is exact in fp32), lo = fp16(x - hi); |x - hi - lo| <= 2^-21 |x| + 2^-25.
 __device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  const float r0 = x0 - static_cast<float>(h[0]);
-  const float r1 = x1 - static_cast<float>(h[1]);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fma_f16<0>(hi, -1.0f, x0), fma_f16<1>(hi, -1.0f, x1)));
 }
 __device__ inline void split8(const float v[8], half8& hi, half8& lo) {
   u32x4 h, l;
@@ -728,6 +744,7 @@ __device__ __forceinline__ void v_block_factors(const TileRegs<KC, VC, NT>& cur,
         for (int j = 0; j < 8; ++j) vf[b][j] = f16_to_float(cur.vs[b][j >> 1] >> ((j & 1) * 16)) * nrm[j];
       if (partial) {
         // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const bool dead = t * kTile + 8 * qg + j >= L;
@@ -746,7 +763,9 @@ __device__ __forceinline__ void v_block_factors(const TileRegs<KC, VC, NT>& cur,
 #pragma unroll
         for (int i = 0; i < 4; ++i) fw[b][i] = cur.vs[b][i];
       if (partial) {
-        // rows past L may hold any bits: their factor is 0 (their p is 0 too)
+        // rows past L may hold any bits: their factor is 0 (their p is 0 too).
+        // (The empty asm keeps this a branch: only a tile cut by L pays.)
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r0 = t * kTile + 8 * qg + 2 * i;
@@ -812,15 +831,20 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
       acc[b] = mfma16(aq.w[b], unpack_k<KC>(cur.kd[h], b, lut), float4v{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const bool dead = partial && t * kTile + 16 * h + n16 >= lim[jj];
       float d[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) d[b] = acc[b][2 * jj] + acc[b][2 * jj + 1];
-      float v;
-      if constexpr (KC == F16) v = (d[0] + d[1]) + (d[2] + d[3]);
-      else v = (d[0] * kf[h][0] + d[1] * kf[h][1]) + (d[2] * kf[h][2] + d[3] * kf[h][3]);
-      s[jj][h] = dead ? -INFINITY : v;
+      if constexpr (KC == F16) s[jj][h] = (d[0] + d[1]) + (d[2] + d[3]);
+      else s[jj][h] = (d[0] * kf[h][0] + d[1] * kf[h][1]) + (d[2] * kf[h][2] + d[3] * kf[h][3]);
     }
+  }
+  if (partial) {  // rows at or past a query's length
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        if (t * kTile + 16 * h + n16 >= lim[jj]) s[jj][h] = -INFINITY;
   }
 
   // ---- online softmax (base 2); the 16 lanes of a lane group share the
@@ -870,16 +894,11 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
   // ---- O += P V ----
   // Part p of x: hi rows take fp16(x) toward zero, lo rows fp16(x - hi), the
   // same split as split8, chosen per lane by the row's parity.
-  const float lom = (n16 & 1) ? 1.0f : 0.0f;
+  const float nb = (n16 & 1) ? -1.0f : 0.0f;
   auto part = [&](const float x[8]) {
     u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
-      const float r0 = x[2 * i] - static_cast<float>(hh[0]) * lom;
-      const float r1 = x[2 * i + 1] - static_cast<float>(hh[1]) * lom;
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-    }
+    for (int i = 0; i < 4; ++i) r[i] = split_part(x[2 * i], x[2 * i + 1], nb);
     return __builtin_bit_cast(half8, r);
   };
   half8 ap[4];
@@ -955,12 +974,17 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool dead = partial && t * kTile + 16 * h + n16 >= lim[i];
-      float v;
-      if constexpr (KC == F16) v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
-      else v = (acc[0][i] * kf[h][0] + acc[1][i] * kf[h][1]) + (acc[2][i] * kf[h][2] + acc[3][i] * kf[h][3]);
-      s[i][h] = dead ? -INFINITY : v;
+      if constexpr (KC == F16) s[i][h] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      else s[i][h] = (acc[0][i] * kf[h][0] + acc[1][i] * kf[h][1]) + (acc[2][i] * kf[h][2] + acc[3][i] * kf[h][3]);
     }
+  }
+  if (partial) {  // rows at or past a query's length
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t * kTile + 16 * h + n16 >= lim[i]) s[i][h] = -INFINITY;
   }
 
   // ---- online softmax (base 2); the 16 lanes of a lane group share the
@@ -1049,9 +1073,10 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
 // Decode kernel: one workgroup of kDecodeWaves waves per (split, KV head,
 // sequence), sized to be the only workgroup on its compute unit (two waves
 // per SIMD).  Every wave handles all query rows of its KV head (RW = 4*NT
-// >= G rows, padded with zero rows).  The waves take the split's tiles from
-// a shared LDS counter as they go, so a wave that issues more slowly (the
-// SIMD arbiter favours older waves) simply takes fewer tiles.
+// >= G rows, padded with zero rows).  The split's tiles are dealt to the
+// waves statically (tile slot k to wave k mod 8); with one workgroup per
+// compute unit this measured within 1.5 % of waves taking tiles from an LDS
+// counter as they free up, and it fixes the summation order.
 template <int KC, int VC, int NT>
 __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   constexpr int RW = 4 * NT;
@@ -1088,7 +1113,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   float (*const s_o)[RW][kD] = reinterpret_cast<float (*)[RW][kD]>(kOutInLut ? static_cast<void*>(lut) : s_o_own);
   __shared__ float s_m[kDecodeWaves][RW];
   __shared__ float s_l[kDecodeWaves][RW];
-  __shared__ int s_next;  // next tile slot to hand out
   __shared__ uint8_t s_row[5][256];
 
   const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
@@ -1157,10 +1181,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 
   // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
   // k = 0, 1, ... (so at any moment the splits of one stream read one
-  // contiguous window).  The slots k go to the waves in order: wave w starts
-  // with D = prefetch_depth + 1 slots (w, w + kDecodeWaves, ...) and then
-  // takes the next free slot from s_next whenever it refills a buffer.  Loads of slots past the last tile are clamped to it; a split
-  // without tiles re-reads tile 0 (always there).
+  // contiguous window).  Wave w owns the slots k = w, w + kDecodeWaves,
+  // w + 2 kDecodeWaves, ..., in that order, so every wave's summation order
+  // (and the result) is fixed.  It starts with its first D = prefetch_depth
+  // + 1 slots in flight and loads its next slot into a buffer as soon as the
+  // buffer is consumed.  Loads of slots past the last tile are clamped to
+  // it; a split without tiles re-reads tile 0 (always there).
   constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
   const int n_mine = split < n_tiles ? (n_tiles - 1 - split) / a.n_splits + 1 : 0;  // this split's tiles
   const int t_last = split < n_tiles ? split + a.n_splits * (n_mine - 1) : 0;
@@ -1168,7 +1194,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   auto load_slot = [&](TileRegs<KC, VC, NT>& r, int k) {
     load_tile<KC, VC>(r, min(tile_of(k), t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
   };
-  if (tid == 0) s_next = D * kDecodeWaves;
   TileRegs<KC, VC, NT> ta, tb;
   [[maybe_unused]] TileRegs<KC, VC, NT> tc;
   load_slot(ta, wave);
@@ -1251,7 +1276,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       aq.w[b] = (n16 & 1) ? l : h;
     }
   }
-  // (s_next and the LUT were written before the staging barrier)
+  // (the LUT was written before the staging barrier)
 
   WaveState<NT> st;
 #pragma unroll
@@ -1275,13 +1300,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) lim[nt] = min(lmin + state_row(nt) / a.gqa, L);
 
-  // slot k is live while its tile exists; slots taken later are larger, so
-  // a wave stops at its first dead slot
+  // slot k is live while its tile exists; a wave's slots increase, so it
+  // stops at its first dead slot
   auto live_slot = [&](int k) { return k < n_mine; };
-  auto take = [&]() {  // one LDS atomic per wave, broadcast from lane 0
-    int k = 0;
-    if (lane == 0) k = atomicAdd(&s_next, 1);
-    return __builtin_amdgcn_readfirstlane(k);
+  int next_slot = wave + D * kDecodeWaves;
+  auto take = [&]() {  // the wave's next slot
+    const int k = next_slot;
+    next_slot += kDecodeWaves;
+    return k;
   };
   auto proc = [&](const TileRegs<KC, VC, NT>& r, int t) {
     if constexpr (NT == 1) process_tile<KC, VC, NT>(r, t, L, lmin, lim, lane, aq, st, s_p[wave], lutr);

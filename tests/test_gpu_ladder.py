@@ -15,7 +15,9 @@ wrong output.  Each layer has its own sampled (sequence, KV head) unit --
 units get seeded device normals.  Per layer: the stored ubatch rows of the
 unit are bit-exact against the oracle's encoders, and the decode output of
 its 4 query heads is within 2e-3 x RMS of the oracle's fp64 attention over
-all 200,704 rows.  Same split count and launch configuration as bench.py.
+all 200,704 rows, and every output equals a serial replay of the same calls
+(all appends, then all decodes) bit for bit.  Same split count and launch
+configuration as bench.py.
 """
 
 import math
@@ -83,6 +85,13 @@ def ladder_step():
         step()
     torch.cuda.synchronize()
     outs = [o.cpu().numpy() for o in out]
+    # the same calls with no overlap (every append, then every decode): the
+    # decode's summation order is fixed, so the outputs must match bitwise
+    say("[ladder step] serial replay of the same calls")
+    for o in out:
+        o.fill_(float("nan"))
+    step.run_serial()
+    serial = [o.cpu().numpy() for o in out]
     # the sampled unit's stored ubatch rows (logical codes, scales, norms)
     stored = []
     for li, (K, V) in enumerate(layers):
@@ -92,7 +101,7 @@ def ladder_step():
             view = unit_view(P, s, h)
             sv[side] = {key: a[pre:pre + ub] for key, a in view.items()}
         stored.append(sv)
-    res = dict(outs=outs, q=q_host, rows=rows, stored=stored, cmap=cmap, n_splits=n_splits, G=Hq // H, pre=pre,
+    res = dict(outs=outs, serial=serial, q=q_host, rows=rows, stored=stored, cmap=cmap, n_splits=n_splits, G=Hq // H, pre=pre,
                ub=ub, L=L)
     del layers, step, new_rows, out, ws
     torch.cuda.empty_cache()
@@ -128,5 +137,7 @@ def test_ladder_step_layer(ladder_step, layer):
             assert np.array_equal(g.reshape(w.shape), w), f"layer {layer} {side} {codec} ubatch {key} differ"
     ref = ref_unit(r["q"][layer][s, h * G:(h + 1) * G], kr, vr, kc, vc, 1.0 / math.sqrt(D), ks, vs)
     check_close(r["outs"][layer][s, h * G:(h + 1) * G], ref, f"ladder layer {layer} ({kc},{vc}) unit ({s},{h}) L={L}")
-    # every output of the step is finite (no unit read poison)
+    # every output of the step is finite (no unit read poison), and the
+    # overlapped step equals its serial replay bit for bit
     assert np.isfinite(r["outs"][layer]).all()
+    assert np.array_equal(r["outs"][layer], r["serial"][layer]), f"layer {layer}: overlapped != serial"

@@ -4,9 +4,9 @@ vit_attn_decode_mq + vit_attn_splitk_reduce with a caller workspace.
 
 Two calls in a row, the second with a smaller input (fewer sequences, rows,
 splits; several new tokens), then a third with one split (no scratch use).
-Every split of these calls holds at most 16 tiles, so the decode's
-summation order is fixed and the two entry points must agree bit for bit;
-both are also held to the oracle's bar (max |o - ref| <= 2e-3 x RMS(ref)).
+The decode's summation order is fixed, so the two entry points must agree
+bit for bit; both are also held to the oracle's bar (max |o - ref| <=
+2e-3 x RMS(ref)).
 """
 
 import math
@@ -34,7 +34,6 @@ def _case(kc, vc, S, H, G, q_len, lens, n_splits, fused, seed):
     ks = rng.integers(0, 256, 16, dtype=np.uint8) if kc in ("rot4", "rot3") else None
     vs = rng.integers(0, 256, 16, dtype=np.uint8) if vc in ("rot4", "rot3") else None
     cap = 256 * ((max(lens) + 255) // 256)
-    assert all((l + 31) // 32 <= 16 * n_splits for l in lens)  # <= 16 tiles per split
     K = make_plane(kc, "k", S, H, cap, ks)
     V = make_plane(vc, "v", S, H, cap, vs)
     Lmax = max(lens)
