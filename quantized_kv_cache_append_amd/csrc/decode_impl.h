@@ -555,7 +555,11 @@ struct QOperands<2> {
 };
 template <>
 struct QOperands<4> {
-  half8 h[4], l[4];  // MFMA b: row n16 = query n16, chunk qg of block b, fp16 hi and lo parts
+  // MFMA b: row n16 = query n16, chunk qg of block b, fp16 hi and lo parts.
+  // They are the same in every wave, so they live in LDS (one copy per
+  // workgroup, 8 KB) and are read per tile: held in registers they pushed
+  // the 16-row kernels past 256 VGPRs.  ops[(part * 4 + b) * 64 + lane].
+  const half8* ops;
 };
 
 // K factors of the lane's tile row 16h + n16 for blocks 0..3: the fp16 block
@@ -722,65 +726,57 @@ __device__ __forceinline__ void process_tile(const TileRegs<KC, VC, NT>& cur, in
 
 // V factors of (tile row 8qg + j, block b) for all four blocks, as the 8-
 // and 16-row layouts use them, with the rows past L zeroed, and the wave's V
-// exponent check.  For q8_0 and q4_0 the factor is the fp16 scale itself: it
-// stays in fp16 (fw[b][i]: rows 8qg + 2i and 2i + 1; the largest magnitude is
-// an integer max over the bit patterns, and the products take the fp16
-// operand directly); rot4 multiplies in the row norm in fp32 (vf[b][j]).
+// exponent check.  The fp16 block scales stay in fp16 (fw[b][i]: rows
+// 8qg + 2i and 2i + 1; the largest magnitude is an integer max over the bit
+// patterns, and the products take the fp16 operand directly); rot4's row
+// norms come back in fp32 (nrm[j]), and its factor norm x scale is formed
+// where it is used.
 template <int KC, int VC, int NT>
 __device__ __forceinline__ void v_block_factors(const TileRegs<KC, VC, NT>& cur, int t, int L, int qg, bool partial,
-                                                WaveState<NT>& st, float (&vf)[4][8], uint32_t (&fw)[4][4],
+                                                WaveState<NT>& st, float (&nrm)[8], uint32_t (&fw)[4][4],
                                                 float& vexp_new, bool& v_rescale) {
   vexp_new = st.vexp;
   v_rescale = false;
   if constexpr (VC != F16) {
-    float vm;  // largest |factor| among this lane's rows
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fw[b][i] = cur.vs[b][i];
     if constexpr (VC == ROT4) {
-      float nrm[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) nrm[j] = f16_to_float(cur.vn[j >> 1] >> ((j & 1) * 16));
+    }
+    if (partial) {
+      // rows past L may hold any bits: their scale (and rot4 norm) is 0, so
+      // their factor is 0 (their p is 0 too).  (The empty asm keeps this a
+      // branch: only a tile cut by L pays.)
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = t * kTile + 8 * qg + 2 * i;
+        const uint32_t keep = (r0 < L ? 0x0000FFFFu : 0u) | (r0 + 1 < L ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vf[b][j] = f16_to_float(cur.vs[b][j >> 1] >> ((j & 1) * 16)) * nrm[j];
-      if (partial) {
-        // rows past L may hold any bits: their factor is 0 (their p is 0 too)
-        __asm__ volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool dead = t * kTile + 8 * qg + j >= L;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) vf[b][j] = dead ? 0.0f : vf[b][j];
+        for (int b = 0; b < 4; ++b) fw[b][i] = fw[b][i] & keep;
+        if constexpr (VC == ROT4) {
+          nrm[2 * i] = r0 < L ? nrm[2 * i] : 0.0f;
+          nrm[2 * i + 1] = r0 + 1 < L ? nrm[2 * i + 1] : 0.0f;
         }
       }
-      vm = 0.0f;
+    }
+    // largest |scale| among this lane's rows (fp16 magnitudes order like
+    // their bit patterns); for rot4 times the largest norm, a bound on the
+    // largest |norm x scale| within the scale spread of one row
+    u16x2 mx = {0, 0};
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vm = fmaxf(vm, fabsf(vf[b][j]));
-    } else {
+      for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, fw[b][i] & 0x7FFF7FFFu));
+    float vm = f16_to_float(mx[0] > mx[1] ? mx[0] : mx[1]);
+    if constexpr (VC == ROT4) {
+      float nm = nrm[0];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fw[b][i] = cur.vs[b][i];
-      if (partial) {
-        // rows past L may hold any bits: their factor is 0 (their p is 0 too).
-        // (The empty asm keeps this a branch: only a tile cut by L pays.)
-        __asm__ volatile("" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r0 = t * kTile + 8 * qg + 2 * i;
-          const uint32_t keep = (r0 < L ? 0x0000FFFFu : 0u) | (r0 + 1 < L ? 0xFFFF0000u : 0u);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) fw[b][i] = fw[b][i] & keep;
-        }
-      }
-      // fp16 magnitudes order like their bit patterns
-      u16x2 mx = {0, 0};
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, fw[b][i] & 0x7FFF7FFFu));
-      vm = f16_to_float(mx[0] > mx[1] ? mx[0] : mx[1]);
+      for (int j = 1; j < 8; ++j) nm = fmaxf(nm, nrm[j]);
+      vm *= nm;
     }
     if (__builtin_amdgcn_ballot_w64(vm > st.vhi) || !__builtin_amdgcn_ballot_w64(vm >= st.vlo)) {
       int e;
@@ -791,7 +787,6 @@ __device__ __forceinline__ void v_block_factors(const TileRegs<KC, VC, NT>& cur,
       v_rescale = true;
     }
   }
-
 }
 
 // One 32-row tile for one wave with 8 query rows.  Both products use rows
@@ -813,11 +808,11 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
   const bool partial = (t + 1) * kTile > lmin;
   // ---- V factors of (tile row 8qg + j, block b) and the wave's V exponent
   //      check, first so that they overlap the S^T products ----
-  [[maybe_unused]] float vf[4][8];
+  [[maybe_unused]] float nrm[8];
   [[maybe_unused]] uint32_t fw[4][4];
   float vexp_new;
   bool v_rescale;
-  v_block_factors(cur, t, L, qg, partial, st, vf, fw, vexp_new, v_rescale);
+  v_block_factors(cur, t, L, qg, partial, st, nrm, fw, vexp_new, v_rescale);
 
   // ---- S^T: lane (n16, qg) gets queries 2qg + jj at tile row 16h + n16 ----
   float kf[2][4];
@@ -909,8 +904,12 @@ __device__ __forceinline__ void process_tile_wide(const TileRegs<KC, VC, 2>& cur
     for (int b = 0; b < 4; ++b) {
       float x[8];
       if constexpr (VC == ROT4) {
+        // norm x scale is exact in fp32 (two fp16 values); then times P
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = pv[2 * i] * mul_f16<0>(nrm[2 * i], fw[b][i]);
+          x[2 * i + 1] = pv[2 * i + 1] * mul_f16<1>(nrm[2 * i + 1], fw[b][i]);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -953,11 +952,11 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
                                                 WaveState<4>& st, float* s_p, const Lut& lut) {
   const int n16 = lane & 15, qg = lane >> 4;
   const bool partial = (t + 1) * kTile > lmin;
-  [[maybe_unused]] float vf[4][8];
+  [[maybe_unused]] float nrm[8];
   [[maybe_unused]] uint32_t fw[4][4];
   float vexp_new;
   bool v_rescale;
-  v_block_factors(cur, t, L, qg, partial, st, vf, fw, vexp_new, v_rescale);
+  v_block_factors(cur, t, L, qg, partial, st, nrm, fw, vexp_new, v_rescale);
 
   // ---- S^T ----
   float kf[2][4];
@@ -969,8 +968,8 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const half8 kb = unpack_k<KC>(cur.kd[h], b, lut);
-      acc[b] = mfma16(aq.h[b], kb, float4v{0.0f, 0.0f, 0.0f, 0.0f});
-      acc[b] = mfma16(aq.l[b], kb, acc[b]);
+      acc[b] = mfma16(aq.ops[b * 64 + lane], kb, float4v{0.0f, 0.0f, 0.0f, 0.0f});
+      acc[b] = mfma16(aq.ops[(4 + b) * 64 + lane], kb, acc[b]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1032,17 +1031,26 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
   }
   wave_lds_fence();
 
-  // ---- O += P V ----
-  half8 ah[4], al[4];
-  if constexpr (VC == F16) {
-    split8(pv, ah[0], al[0]);
-  } else {
+  // ---- O += P V: block b's hi and lo operands are built just before its
+  //      two N-tiles, so only one pair is live at a time ----
+  const int row8 = t * kTile + 8 * qg;
+  [[maybe_unused]] half8 fh, fl;  // f16 planes: one P operand pair for all N-tiles
+  if constexpr (VC == F16) split8(pv, fh, fl);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < 4; ++b) {
+    half8 ah, al;
+    if constexpr (VC == F16) {
+      ah = fh;
+      al = fl;
+    } else {
       float x[8];
       if constexpr (VC == ROT4) {
+        // norm x scale is exact in fp32 (two fp16 values); then times P
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = pv[j] * vf[b][j];
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = pv[2 * i] * mul_f16<0>(nrm[2 * i], fw[b][i]);
+          x[2 * i + 1] = pv[2 * i + 1] * mul_f16<1>(nrm[2 * i + 1], fw[b][i]);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1050,23 +1058,21 @@ __device__ __forceinline__ void process_tile_16(const TileRegs<KC, VC, 4>& cur, 
           x[2 * i + 1] = mul_f16<1>(pv[2 * i + 1], fw[b][i]);
         }
       }
-      split8(x, ah[b], al[b]);
+      split8(x, ah, al);
     }
-  }
-  const int row8 = t * kTile + 8 * qg;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    half8 bv = unpack_v<VC>(cur.vd, c, lut);
-    if constexpr (VC == F16) {
-      if (partial) {
+    for (int c = 2 * b; c < 2 * b + 2; ++c) {
+      half8 bv = unpack_v<VC>(cur.vd, c, lut);
+      if constexpr (VC == F16) {
+        if (partial) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
+          for (int j = 0; j < 8; ++j)
+            if (row8 + j >= L) bv[j] = static_cast<_Float16>(0.0f);
+        }
       }
+      st.oacc[c] = mfma16(ah, bv, st.oacc[c]);
+      st.oacc[c] = mfma16(al, bv, st.oacc[c]);
     }
-    const int b = VC == F16 ? 0 : c >> 1;
-    st.oacc[c] = mfma16(ah[b], bv, st.oacc[c]);
-    st.oacc[c] = mfma16(al[b], bv, st.oacc[c]);
   }
 }
 
@@ -1253,15 +1259,32 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
   } else if constexpr (NT == 4) {
     // row n16 = query row: in MFMA b the lane holds chunk qg of block b,
-    // hi and lo parts in separate operands
-    const int g = n16;
+    // hi and lo parts in separate operands.  Wave 0 builds them and stores
+    // them over the staged query rows (which every wave has read by the
+    // barrier), where they stay until the tile loop ends.
+    half8 oh[4], ol[4];
+    if (wave == 0) {
+      const int g = n16;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float v[8];
+      for (int b = 0; b < 4; ++b) {
+        float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, b, j)] * qs;
-      split8(v, aq.h[b], aq.l[b]);
+        for (int j = 0; j < 8; ++j) v[j] = sq[g][k_chan<KC>(qg, b, j)] * qs;
+        split8(v, oh[b], ol[b]);
+      }
     }
+    __syncthreads();
+    half8* ops = reinterpret_cast<half8*>(&sq[0][0]);
+    static_assert(sizeof(half8) * 8 * 64 <= sizeof(sq), "operands fit the staging rows");
+    if (wave == 0) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        ops[b * 64 + lane] = oh[b];
+        ops[(4 + b) * 64 + lane] = ol[b];
+      }
+    }
+    __syncthreads();
+    aq.ops = ops;
   } else {
     // row n16 = 2 * (query row) + part: in MFMA b the lane holds part
     // n16 & 1 of chunk qg of block b of its query row
