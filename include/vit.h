@@ -254,8 +254,9 @@ int32_t vit_attn_default_splits(int32_t n_seqs, int32_t n_kv_heads, int32_t n_q_
  *            at row seq_len[s]-1 first, exactly as vit_kv_append_quant would.
  *  scale     softmax scale (typically 1/sqrt(128)).
  *  n_splits  1 .. VIT_MAX_SPLITS.  The 32-row tiles of each sequence's
- *            context are dealt to n_splits partial results, tile t to split
- *            t % n_splits (a split may get none).  With n_splits == 1 the
+ *            context are dealt to n_splits partial results in contiguous
+ *            runs of ceil(tiles / n_splits) tiles (the last splits may get
+ *            fewer or none).  With n_splits == 1 the
  *            normalised output is written to
  *            `out` and `workspace` may be NULL; otherwise partials go to
  *            `workspace` and vit_attn_splitk_reduce produces `out`.

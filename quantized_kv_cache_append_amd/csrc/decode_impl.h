@@ -1104,6 +1104,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   constexpr int kThreads = 64 * kDecodeWaves;
   static_assert(RW <= GMAX, "query rows per wave");
   const int n_tiles = (L + kTile - 1) / kTile;
+  // contiguous tile ranges per split (the last ones may be short or empty)
+  const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
 
   __shared__ float sq[GMAX][kD];
   constexpr bool kRot4 = KC == ROT4 || VC == ROT4;
@@ -1135,7 +1137,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   //      rows go in order on wave 1, because 4-bit V rows of one 8-row group
   //      share 32-bit words that each store rewrites ----
   if (a.k_new != nullptr) {
-    auto owned = [&](int i) { return ((lmin - 1 + i) / kTile) % a.n_splits == split; };
+    auto owned = [&](int i) { return ((lmin - 1 + i) / kTile) / tiles_per_split == split; };
     bool mine = false;
     for (int i = 0; i < QL; ++i) mine = mine || owned(i);
     if (mine) {
@@ -1185,18 +1187,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   if constexpr (kRot4) lv = kLevelBits[lane & 15];
   if constexpr (kRot3) lv3 = kLevelBits3[lane & 7];
 
-  // Tiles are dealt out interleaved: split s owns tiles s + n_splits * k,
-  // k = 0, 1, ... (so at any moment the splits of one stream read one
-  // contiguous window).  Wave w owns the slots k = w, w + kDecodeWaves,
-  // w + 2 kDecodeWaves, ..., in that order, so every wave's summation order
-  // (and the result) is fixed.  It starts with its first D = prefetch_depth
+  // Split s owns the contiguous tiles s * tiles_per_split .. (s + 1) *
+  // tiles_per_split - 1 of the stream (slot k is tile first + k), so each
+  // workgroup streams one run of memory.  Wave w owns the slots k = w,
+  // w + kDecodeWaves, w + 2 kDecodeWaves, ..., in that order, so every
+  // wave's summation order (and the result) is fixed.  It starts with its first D = prefetch_depth
   // + 1 slots in flight and loads its next slot into a buffer as soon as the
   // buffer is consumed.  Loads of slots past the last tile are clamped to
   // it; a split without tiles re-reads tile 0 (always there).
   constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
-  const int n_mine = split < n_tiles ? (n_tiles - 1 - split) / a.n_splits + 1 : 0;  // this split's tiles
-  const int t_last = split < n_tiles ? split + a.n_splits * (n_mine - 1) : 0;
-  auto tile_of = [&](int k) { return split + a.n_splits * k; };
+  const int first = split * tiles_per_split;
+  const int n_mine = max(0, min(n_tiles - first, tiles_per_split));  // this split's tiles
+  const int t_last = n_mine > 0 ? first + n_mine - 1 : 0;
+  auto tile_of = [&](int k) { return first + k; };
   auto load_slot = [&](TileRegs<KC, VC, NT>& r, int k) {
     load_tile<KC, VC>(r, min(tile_of(k), t_last), lane, kbase, vbase, ksb, knb, vsb, vnb);
   };
