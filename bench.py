@@ -36,7 +36,9 @@ each replica's step once into a HIP graph and replays one graph per step
 
 Prints ONE JSON line.  ``value`` is decode tokens/s (sequences / step time).
 ``roofline`` describes the dominant kernel (decode): algorithmic KV bytes per
-launch / its mean duration, against the 8 TB/s HBM peak.  ``traffic``
+launch / its mean duration, against the 8 TB/s HBM peak, and against the
+read bandwidth measured in the same run with the library's read-only
+streaming kernel (vit_stream_read, 1 GiB).  ``traffic``
 is the HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by
 a copy-kernel calibration), read from profiles/ only when it was measured on
 the current kernel sources.  ``cpu_baseline`` times the numpy oracle on the
@@ -743,6 +745,35 @@ def main_transcode(args):
     print(json.dumps(line), flush=True)
 
 
+def measure_stream_read(n_bytes=1 << 30, launches=10):
+    """GB/s of the library's read-only streaming kernel (vit_stream_read: 16-byte
+    nontemporal loads of a 1 GiB buffer over the whole GPU, nothing else), the
+    read bandwidth this part reaches in practice; kernel events recorded by its
+    dispatch, mean over the launches."""
+    import torch
+
+    import quantized_kv_cache_append_amd as vit
+
+    buf = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            vit.vit_stream_read(buf, sink, stream=stream)
+        for a, b in evs:
+            vit.vit_arm_kernel_events(a, b)
+            vit.vit_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / launches
+    del buf
+    torch.cuda.empty_cache()
+    return n_bytes / (ms * 1e-3) / 1e9
+
+
 def run_copy_calibration(steps):
     """A plain device copy of known size, for scaling rocprofv3 counters."""
     import torch
@@ -1185,6 +1216,8 @@ def main():
         print(f"# cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} cores ({cpu['cpu_model']})",
               file=sys.stderr, flush=True)
     r = run_gpu(args)
+    stream_peak = measure_stream_read()
+    print(f"# measured stream-read peak: {stream_peak:.1f} GB/s", file=sys.stderr, flush=True)
     cfg = r["cfg"]
     tok_s = r["S"] * r["QL"] / (r["ms_per_step"] * 1e-3)
     traffic = load_traffic("decode", profile_tag(args.workload, r["QL"], args.codecs), r["n_splits"])
@@ -1230,6 +1263,8 @@ def main():
             "algorithmic_bytes_per_launch": r["per_launch_bytes"],
             "mean_launch_ms": round(r["dec_mean_ms"], 5),
             "min_launch_ms": round(r["dec_min_ms"], 5),
+            "stream_read_peak": round(stream_peak, 1),
+            "frac_of_stream_read_peak": round(r["achieved_gbs"] / stream_peak, 4),
         },
         "kernel_source_hash": kernel_source_hash(),
     }

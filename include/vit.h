@@ -394,7 +394,7 @@ int vit_attn_decode_noalloc(const vit_kv_plane *k, const vit_kv_plane *v, const 
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
  * thread's next vit_kv_append_quant, vit_attn_decode, vit_attn_decode_mq,
- * vit_attn_decode_noalloc, vit_kv_transcode or vit_attn_probe_scores call (for the latter: its
+ * vit_attn_decode_noalloc, vit_kv_transcode, vit_stream_read or vit_attn_probe_scores call (for the latter: its
  * logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it
  * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and
@@ -403,6 +403,15 @@ int vit_attn_decode_noalloc(const vit_kv_plane *k, const vit_kv_plane *v, const 
  * Both NULL disarms; exactly one NULL returns VIT_E_ARG.  The events stay
  * owned by the caller. */
 int vit_arm_kernel_events(void *start_event, void *stop_event);
+
+/* Measurement aid (no operation of the method): read `bytes` bytes of `buf`
+ * (device, 16-B aligned, a multiple of 16) with 16-byte nontemporal loads
+ * spread over the whole GPU, each wave reading contiguous 8 KB chunks as a
+ * decode wave reads its tiles, and do nothing else -- the read bandwidth this part reaches in practice, the
+ * "measured stream-read peak" beside the 8 TB/s HBM figure.  `sink` (device,
+ * 4 bytes) is written only if the xor of the data equals a fixed constant.
+ * Kernel events armed by vit_arm_kernel_events bracket its kernel. */
+int vit_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* A static string for a status code. */
 const char *vit_status_string(int status);

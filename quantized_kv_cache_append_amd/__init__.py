@@ -10,7 +10,7 @@ names mirror the C entry points:
     vit_attn_default_splits, vit_attn_decode, vit_attn_decode_mq,
     vit_attn_decode_noalloc, vit_attn_splitk_reduce, vit_attn_probe_workspace_bytes,
     vit_attn_probe_scores, vit_probe_select_evictions,
-    vit_arm_kernel_events (a measurement aid)
+    vit_arm_kernel_events, vit_stream_read (measurement aids)
 
 ``KVPlane`` allocates the three arrays of one (layer, side) cache tensor.
 """
@@ -30,7 +30,7 @@ __all__ = [
     "vit_attn_splitk_reduce",
     "vit_attn_probe_workspace_bytes", "vit_attn_probe_scores", "vit_probe_select_evictions",
     "vit_probe_select_workspace_bytes",
-    "vit_arm_kernel_events",
+    "vit_arm_kernel_events", "vit_stream_read",
 ]
 
 HEAD_DIM = 128
@@ -334,6 +334,14 @@ def vit_arm_kernel_events(start, stop):
     (both None disarms)."""
     st = _lib.load().vit_arm_kernel_events(_event_handle(start), _event_handle(stop))
     return _lib.check("vit_arm_kernel_events", st)
+
+
+def vit_stream_read(buf, sink, stream=None):
+    """Measurement aid: read every byte of the uint8 CUDA tensor ``buf`` once
+    (16-byte nontemporal loads over the whole GPU, nothing else)."""
+    st = _lib.load().vit_stream_read(_fptr(buf, "buf", "uint8"), ctypes.c_size_t(buf.numel()),
+                                     _fptr(sink, "sink", "int32"), _stream_handle(stream))
+    return _lib.check("vit_stream_read", st)
 
 
 class _Prepared:

@@ -39,6 +39,7 @@ EXPORTS = (
     "vit_probe_select_evictions",
     "vit_probe_select_workspace_bytes",
     "vit_arm_kernel_events",
+    "vit_stream_read",
     "vit_status_string",
 )
 
@@ -112,6 +113,8 @@ def load():
     lib.vit_probe_select_evictions.restype = ctypes.c_int
     lib.vit_probe_select_workspace_bytes.argtypes = [i32]
     lib.vit_probe_select_workspace_bytes.restype = sz
+    lib.vit_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.vit_stream_read.restype = ctypes.c_int
     lib.vit_status_string.argtypes = [ctypes.c_int]
     lib.vit_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -459,6 +459,16 @@ int vit_attn_decode_mq(const vit_kv_plane* k, const vit_kv_plane* v, const float
                              static_cast<hipStream_t>(stream), ev);
 }
 
+int vit_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  const vit::KernelEvents ev = vit::take_armed_events();  // one-shot, whatever the outcome
+  if (!buf || !sink || bytes == 0) return VIT_E_ARG;
+  if (!aligned(buf, 16) || !aligned(sink, 4) || bytes % 16 != 0) return VIT_E_ALIGN;
+  return vit::launch_stream_read(buf, static_cast<int64_t>(bytes / 16), sink, static_cast<hipStream_t>(stream), ev) ==
+                 hipSuccess
+             ? VIT_OK
+             : VIT_E_HIP;
+}
+
 int vit_arm_kernel_events(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr)) return VIT_E_ARG;
   g_armed.start = static_cast<hipEvent_t>(start_event);

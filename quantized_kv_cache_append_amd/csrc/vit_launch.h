@@ -143,6 +143,8 @@ hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const
 hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode_k4(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
+hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, hipStream_t stream,
+                              const KernelEvents& ev);
 // both probe kernels (logits over grid (n_chunks, Hkv, S), then the mass);
 // ev brackets the logits kernel
 hipError_t launch_probe(int kc, int n_seqs, int max_seq_len, hipStream_t stream, const ProbeArgs& args,
