@@ -209,6 +209,11 @@ def run_gpu(args):
     # step's decodes (they rewrite the rows those read).
     fused = "ubatch" not in cfg
     astream = None if fused else torch.cuda.Stream()
+    # decode and split merge in one launch (vit_attn_decode_merged) where the
+    # shape allows it; the arrival counters are zeroed once and every call
+    # leaves them zero
+    merged = (n_splits > 1 and not args.no_merge and vit.merge_fits(Hq, H, QL, n_splits))
+    counters = torch.zeros((S, H), dtype=torch.int32, device="cuda") if merged else None
 
     # every call of a step, marshalled once per replica (the host then only
     # issues the C calls, so the GPU queue never runs dry).  One (or q_len)
@@ -220,7 +225,7 @@ def run_gpu(args):
             from quantized_kv_cache_append_amd.step import DecodeStep
 
             calls.append(DecodeStep([(lay.K[r], lay.V[r]) for lay in layers], q, new_rows, out, lens, p_new, Hq,
-                                    n_splits, ws, stream, astream))
+                                    n_splits, ws, stream, astream, counters=counters))
             continue
         dec = []
         for li, lay in enumerate(layers):
@@ -228,6 +233,12 @@ def run_gpu(args):
             # [S][H][128] rows for one token, [S][q_len][H][128] for several
             k_in = kn[:, 0].contiguous() if QL == 1 else kn
             v_in = vn[:, 0].contiguous() if QL == 1 else vn
+            if merged:
+                shp = (S, QL, Hq, D)  # new rows kn, vn: [S][q_len][Hkv][128]
+                d = vit.prepare_merged(lay.K[r], lay.V[r], q[li].reshape(shp), Hq, QL, lens, out[li].reshape(shp),
+                                       ws, counters, k_new=kn, v_new=vn, n_splits=n_splits, stream=stream)
+                dec.append((d, None))
+                continue
             d = vit.prepare_decode(lay.K[r], lay.V[r], q[li], Hq, lens, out[li], n_splits=n_splits,
                                    k_new=k_in, v_new=v_in, workspace=ws if n_splits > 1 else None,
                                    stream=stream, q_len=QL if QL > 1 else None)
@@ -337,6 +348,7 @@ def run_gpu(args):
     # algorithmic bytes of all timed decode launches / their summed duration
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
     return dict(cfg=cfg, wl=wl, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
+                merge="in-kernel (vit_attn_decode_merged)" if merged else ("reduce kernel" if n_splits > 1 else "none"),
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
                 block_ms=block_ms,
                 dec_mean_ms=dec_mean_ms,
@@ -1141,6 +1153,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="time an attention-probe scoring event (+ eviction choice) on --workload's K plane instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="decode + separate reduce launch even where vit_attn_decode_merged applies")
     ap.add_argument("--graph", action="store_true",
                     help="also time the steps as HIP graph replays (one captured graph per replica)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -1247,7 +1261,8 @@ def main():
             "context": r["L"], "layers": r["n_layers"], "new_tokens_per_seq": r["T"], "query_tokens_per_seq": r["QL"],
             "codecs": ("ladder: " + ", ".join(f"{k}/{v}" for k, v in r["cmap"])) if r["n_layers"] > 1
             else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
-            "n_splits": r["n_splits"], "cold_cache_replicas": r["replicas"], "launch": r["mode"],
+            "n_splits": r["n_splits"], "split_merge": r["merge"], "cold_cache_replicas": r["replicas"],
+            "launch": r["mode"],
         },
         "graph_ms_per_step": None if r["graph_ms_per_step"] is None else round(r["graph_ms_per_step"], 5),
         "effective_kv_read_gbs": round(r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),

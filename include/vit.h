@@ -143,6 +143,8 @@ typedef enum vit_status {
 #define VIT_MAX_GQA 16 /* query rows per KV head: G, or G * q_len for vit_attn_decode_mq */
 #define VIT_MAX_QLEN 4 /* new tokens per sequence in one vit_attn_decode_mq call */
 #define VIT_MAX_SPLITS 4096
+#define VIT_MERGE_MAX_SPLITS 64    /* vit_attn_decode_merged: split count */
+#define VIT_MERGE_MAX_PARTIALS 128 /* vit_attn_decode_merged: query rows per KV head x splits */
 #define VIT_MAX_CAPACITY (1 << 30) /* rows per (sequence, KV head) */
 
 /* One (layer, side) cache tensor: caller-owned device memory in the layout
@@ -308,6 +310,31 @@ int vit_attn_splitk_reduce(const float *workspace, int32_t n_seqs, int32_t n_q_h
                            int32_t head_dim, int32_t n_splits, const vit_kv_plane *v,
                            float *out, void *stream);
 
+/* Decode attention (vit_attn_decode_mq) and its split merge
+ * (vit_attn_splitk_reduce) in one launch: the flash decode over the quantized
+ * cache (buun-llama-cpp page, "Requirements" paragraph; per-side codecs of
+ * its "Codecs" table) without the second pass's launch.  Each split's
+ * workgroup writes its partial as before; the last of a (sequence, KV head)'s
+ * workgroups to finish merges that head's partials with the arithmetic of
+ * vit_attn_splitk_reduce, so `out` equals the two-call result bit for bit.
+ *  workspace  as vit_attn_decode_mq: vit_attn_workspace_bytes(n_seqs,
+ *             n_q_heads * q_len, 128, n_splits) bytes.  The partials stay in
+ *             it (vit_attn_splitk_reduce may still be called on them).
+ *  counters   device uint32 [n_seqs][n_kv_heads], 8-B aligned: arrival
+ *             counts, which must all be zero before the first call (one
+ *             hipMemset when they are allocated); every call leaves them 0.
+ *  Limits: n_splits <= VIT_MERGE_MAX_SPLITS and (n_q_heads / n_kv_heads) *
+ *  q_len * n_splits <= VIT_MERGE_MAX_PARTIALS (the partial rows the merging
+ *  workgroup reads); beyond them VIT_E_UNSUPPORTED: use the two calls.  With
+ *  n_splits == 1 this is vit_attn_decode_mq (workspace, counters may be NULL).
+ * Calls that share counters or a workspace and may run at the same time race.
+ * Other arguments, errors and accuracy as vit_attn_decode_mq; NULL counters
+ * with n_splits > 1 is VIT_E_ARG. */
+int vit_attn_decode_merged(const vit_kv_plane *k, const vit_kv_plane *v, const float *q,
+                           int32_t n_q_heads, int32_t q_len, const int64_t *seq_len,
+                           const float *k_new, const float *v_new, float scale, int32_t n_splits,
+                           float *workspace, uint32_t *counters, float *out, void *stream);
+
 /* Workspace bytes of vit_attn_probe_scores: fp32 logits [n_seqs][n_q_heads]
  * [capacity] (256-byte padded) followed by softmax partials [n_seqs]
  * [n_q_heads][64][2].  Returns 0 for invalid sizes (n_q_heads up to 256). */
@@ -394,7 +421,7 @@ int vit_attn_decode_noalloc(const vit_kv_plane *k, const vit_kv_plane *v, const 
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
  * thread's next vit_kv_append_quant, vit_attn_decode, vit_attn_decode_mq,
- * vit_attn_decode_noalloc, vit_kv_transcode, vit_stream_read or vit_attn_probe_scores call (for the latter: its
+ * vit_attn_decode_merged, vit_attn_decode_noalloc, vit_kv_transcode, vit_stream_read or vit_attn_probe_scores call (for the latter: its
  * logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it
  * ends (hipExtLaunchKernel), i.e. the pair brackets that one kernel and

@@ -221,6 +221,39 @@ def vit_attn_decode_mq(k, v, q, n_q_heads, q_len, seq_len, k_new=None, v_new=Non
     return out
 
 
+def merge_fits(n_q_heads, n_kv_heads, q_len, n_splits):
+    """Whether vit_attn_decode_merged takes this shape (else decode + reduce)."""
+    rows = (n_q_heads // n_kv_heads) * q_len
+    return n_splits == 1 or (n_splits <= _lib.MERGE_MAX_SPLITS and rows * n_splits <= _lib.MERGE_MAX_PARTIALS)
+
+
+def merge_counters(k, device=None):
+    """Zeroed arrival counters for vit_attn_decode_merged on ``k``'s shape
+    (uint32 [S][Hkv], stored as int32; every call leaves them zero)."""
+    import torch
+
+    return torch.zeros((k.n_seqs, k.n_kv_heads), dtype=torch.int32, device=device or "cuda")
+
+
+def vit_attn_decode_merged(k, v, q, n_q_heads, q_len, seq_len, out, workspace=None, counters=None, k_new=None,
+                           v_new=None, scale=None, n_splits=1, stream=None):
+    """Decode attention and its split merge in one launch: q, out fp32
+    [S, q_len, Hq, 128]; ``counters`` from merge_counters (zero between calls)."""
+    lib = _lib.load()
+    if scale is None:
+        scale = 1.0 / np.sqrt(HEAD_DIM)
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    st = lib.vit_attn_decode_merged(ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len),
+                                    sl, _fptr(k_new, "k_new"), _fptr(v_new, "v_new"), ctypes.c_float(scale),
+                                    int(n_splits),
+                                    _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
+                                    _fptr(counters, "counters", "int32") if counters is not None else None,
+                                    _fptr(out, "out"), _stream_handle(stream))
+    _lib.check("vit_attn_decode_merged", st)
+    return out
+
+
 def vit_attn_decode_noalloc(k, v, q, n_q_heads, q_len, seq_len, out, k_new=None, v_new=None, scale=None,
                             n_splits=1, stream=None):
     """Decode attention (+ split-K merge) with the split partials in the
@@ -410,6 +443,21 @@ def prepare_decode(k, v, q, n_q_heads, seq_len, out, k_new=None, v_new=None, sca
         return _Prepared("vit_attn_decode", lib.vit_attn_decode, args, keep)
     args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len), sl) + tail
     return _Prepared("vit_attn_decode_mq", lib.vit_attn_decode_mq, args, keep)
+
+
+def prepare_merged(k, v, q, n_q_heads, q_len, seq_len, out, workspace, counters, k_new=None, v_new=None,
+                   scale=None, n_splits=1, stream=None):
+    lib = _lib.load()
+    scale = 1.0 / np.sqrt(HEAD_DIM) if scale is None else scale
+    sl = (ctypes.c_int64 * len(seq_len))(*[int(x) for x in seq_len])
+    kp, vp = k.struct(), v.struct()
+    args = (ctypes.byref(kp), ctypes.byref(vp), _fptr(q, "q"), int(n_q_heads), int(q_len), sl,
+            _fptr(k_new, "k_new"), _fptr(v_new, "v_new"), ctypes.c_float(scale), int(n_splits),
+            _fptr(workspace, "workspace", "uint8") if workspace is not None else None,
+            _fptr(counters, "counters", "int32") if counters is not None else None, _fptr(out, "out"),
+            _stream_handle(stream))
+    keep = (kp, vp, sl, q, k_new, v_new, workspace, counters, out, k, v)
+    return _Prepared("vit_attn_decode_merged", lib.vit_attn_decode_merged, args, keep)
 
 
 def prepare_reduce(workspace, n_seqs, n_q_heads, n_splits, v, out, stream=None):

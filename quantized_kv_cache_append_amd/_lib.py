@@ -18,6 +18,8 @@ VIT_E_ALIGN = -4
 VIT_E_HIP = -5
 VIT_E_SCRATCH = -6
 NOALLOC_SCRATCH_BYTES = 4 << 20  # VIT_NOALLOC_SCRATCH_BYTES
+MERGE_MAX_SPLITS = 64  # VIT_MERGE_MAX_SPLITS
+MERGE_MAX_PARTIALS = 128  # VIT_MERGE_MAX_PARTIALS
 
 CODEC_IDS = {"f16": 0, "q8_0": 1, "q4_0": 2, "rot4": 3, "rot3": 4}
 SIDE_IDS = {"k": 0, "v": 1}
@@ -32,6 +34,7 @@ EXPORTS = (
     "vit_attn_default_splits",
     "vit_attn_decode",
     "vit_attn_decode_mq",
+    "vit_attn_decode_merged",
     "vit_attn_decode_noalloc",
     "vit_attn_splitk_reduce",
     "vit_attn_probe_workspace_bytes",
@@ -101,6 +104,8 @@ def load():
     lib.vit_attn_decode.restype = ctypes.c_int
     lib.vit_attn_decode_mq.argtypes = [plane_p, plane_p, vp, i32, i32, P(i64), vp, vp, f32, i32, vp, vp, vp]
     lib.vit_attn_decode_mq.restype = ctypes.c_int
+    lib.vit_attn_decode_merged.argtypes = [plane_p, plane_p, vp, i32, i32, P(i64), vp, vp, f32, i32, vp, vp, vp, vp]
+    lib.vit_attn_decode_merged.restype = ctypes.c_int
     lib.vit_attn_decode_noalloc.argtypes = [plane_p, plane_p, vp, i32, i32, P(i64), vp, vp, f32, i32, vp, vp]
     lib.vit_attn_decode_noalloc.restype = ctypes.c_int
     lib.vit_attn_splitk_reduce.argtypes = [vp, i32, i32, i32, i32, plane_p, vp, vp]

@@ -26,6 +26,7 @@
 //   <= 16 rows: query rows, hi and lo in two chained MFMAs.
 #pragma once
 
+#include "merge.h"
 #include "vit_device.h"
 #include "vit_launch.h"
 
@@ -1131,15 +1132,24 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const uint16_t* knb = has_norms(KC) ? a.knorms + ph * a.capacity : nullptr;
   const uint16_t* vnb = has_norms(VC) ? a.vnorms + ph * a.capacity : nullptr;
 
+  // Tiles each wave has in flight from the start (its first D slots).
+  constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
+
   // ---- fused append: the new rows p = lmin - 1 + i (i < q_len) are stored
-  //      by the workgroup owning their tile, before it reads any tile (no
-  //      other workgroup reads that tile).  K row i goes on wave 2i; the V
-  //      rows go in order on wave 1, because 4-bit V rows of one 8-row group
-  //      share 32-bit words that each store rewrites ----
+  //      by the workgroup owning their tile, before it reads that tile (no
+  //      other workgroup reads it).  K row i goes on wave 2i; the V rows go
+  //      in order on wave 1, because 4-bit V rows of one 8-row group share
+  //      32-bit words that each store rewrites ----
   if (a.k_new != nullptr) {
     auto owned = [&](int i) { return ((lmin - 1 + i) / kTile) / tiles_per_split == split; };
     bool mine = false;
-    for (int i = 0; i < QL; ++i) mine = mine || owned(i);
+    int first_slot = n_tiles;  // the lowest slot of this split that gets a new row
+    for (int i = 0; i < QL; ++i) {
+      if (owned(i)) {
+        mine = true;
+        first_slot = min(first_slot, (lmin - 1 + i) / kTile - split * tiles_per_split);
+      }
+    }
     if (mine) {
       auto src = [&](int i) { return ((static_cast<int64_t>(seq) * QL + i) * a.n_kv_heads + head) * kD; };
       for (int i = 0; i < QL; ++i) {
@@ -1155,10 +1165,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
                                   s_row[4]);
       }
       // Only waves of this workgroup read the rows back, and they share its
-      // L1: the barrier's workgroup-scope release/acquire is enough.  (A
+      // L1: a barrier's workgroup-scope release/acquire is enough.  (A
       // device-scope fence here writes back and invalidates the L2 and costs
-      // tens of us.)
-      __syncthreads();
+      // tens of us.)  When no wave prefetches the tile of a new row (it is
+      // past every wave's first D slots), the query staging barrier below
+      // orders the stores before its first read, and the other waves go on
+      // to issue their prefetch while the rows are encoded.
+      if (first_slot < D * kDecodeWaves) __syncthreads();
     }
   }
 
@@ -1179,13 +1192,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     const float* qsrc = a.q + qrow_index(min(qs_row, G - 1)) * kD + ((8 * tid) & 127);
     q0 = *reinterpret_cast<const float4v*>(qsrc);
     q1 = *reinterpret_cast<const float4v*>(qsrc + 4);
-    if constexpr (rotated(KC)) ksw = a.ksigns[((8 * tid) & 127) >> 5];  // sign bits of those 8 channels
+    if constexpr (rotated(KC)) {
+      // sign bits of those 8 channels (selected, not indexed: an indexed
+      // read of the arguments is a vector load that the staging would wait on)
+      const int si = ((8 * tid) & 127) >> 5;
+      ksw = si == 0 ? a.ksigns[0] : si == 1 ? a.ksigns[1] : si == 2 ? a.ksigns[2] : a.ksigns[3];
+    }
   }
   // rot4 levels: lane l (< 16) fetches level l; issued before the tile loads
   // so that building the table below does not wait for them
   [[maybe_unused]] uint32_t lv = 0, lv3 = 0;
   if constexpr (kRot4) lv = kLevelBits[lane & 15];
   if constexpr (kRot3) lv3 = kLevelBits3[lane & 7];
+  // Keep those loads ahead of the tile prefetch: loads complete in issue
+  // order, so the staging below then waits only for them, and the query
+  // rotation overlaps the tiles' latency (left to itself the compiler
+  // issues them after the tiles and waits for everything).
+  __asm__ volatile("" ::: "memory");
 
   // Split s owns the contiguous tiles s * tiles_per_split .. (s + 1) *
   // tiles_per_split - 1 of the stream (slot k is tile first + k), so each
@@ -1195,7 +1218,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // + 1 slots in flight and loads its next slot into a buffer as soon as the
   // buffer is consumed.  Loads of slots past the last tile are clamped to
   // it; a split without tiles re-reads tile 0 (always there).
-  constexpr int D = prefetch_depth<KC, VC, NT>() + 1;
   const int first = split * tiles_per_split;
   const int n_mine = max(0, min(n_tiles - first, tiles_per_split));  // this split's tiles
   const int t_last = n_mine > 0 ? first + n_mine - 1 : 0;
@@ -1397,29 +1419,113 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   const bool final_out = a.n_splits == 1;
   for (int i = tid; i < RW * kD; i += kThreads) {
     const int g = i >> 7, c = i & 127;
-    float M = -INFINITY;
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float O = 0.0f, Ls = 0.0f;
+    // all reads first, then no branch: a wave without rows (l = 0) gets
+    // weight 0 by a select
+    float mw[kDecodeWaves], lw[kDecodeWaves], ow[kDecodeWaves];
+#pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
-      const float lw = s_l[w][g];
-      if (lw > 0.0f) {
-        const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-        O += s_o[w][g][c] * f;
-        Ls += lw * f;
-      }
+      mw[w] = s_m[w][g];
+      lw[w] = s_l[w][g];
+      ow[w] = s_o[w][g][c];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mw[w]);
+    float O = 0.0f, Ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = lw[w] > 0.0f ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.0f;
+      O += ow[w] * f;
+      Ls += lw[w] * f;
     }
     if (final_out) {
       sq[g][c] = Ls > 0.0f ? O / Ls : 0.0f;
     } else if (g < G) {
+      // agent-scope stores: coherent across the GPU's L2 caches without a
+      // cache write-back, so a workgroup anywhere can merge them in-kernel
       const int64_t row = qrow_index(g) * a.n_splits + split;
-      a.ws_o[row * kD + c] = O;
+      __hip_atomic_store(&a.ws_o[row * kD + c], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (c == 0) {
-        a.ws_ml[row * 2] = M;
-        a.ws_ml[row * 2 + 1] = Ls;
+        __hip_atomic_store(&a.ws_ml[row * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ws_ml[row * 2 + 1], Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  if (final_out) {
+  bool write_final = final_out;
+  if (!final_out && a.arrive != nullptr) {
+    // ---- in-kernel split merge: the last of the n_splits workgroups of this
+    //      (sequence, KV head) to get here merges the partials of its rows.
+    //      Each thread waits until its partial stores have completed; after
+    //      the barrier one thread counts the workgroup in.  The count and the
+    //      merge's loads are agent-scope atomics too, issued after those
+    //      stores completed, so the last arrival reads every split's
+    //      partial.  It also puts the count back to 0 for the next call ----
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&a.arrive[ph], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev == static_cast<uint32_t>(a.n_splits - 1);
+      if (last) __hip_atomic_store(&a.arrive[ph], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_last == 0) return;
+    // thread (row r, channel group cg) merges every split of its row's 4
+    // channels with the reduce kernel's arithmetic: split s goes to lane
+    // s mod 8, each lane in split order, then the lanes in order; 16 splits'
+    // loads are in flight at a time
+    const int r = tid >> 5, cg = tid & 31;
+    if (r < G) {
+      constexpr int SL = kMergeLanesFew;
+      const int64_t row0 = qrow_index(r) * a.n_splits;
+      const float* ml = a.ws_ml + row0 * 2;
+      const float* po = a.ws_o + row0 * kD + 4 * cg;
+      // two floats in one agent-scope 8-byte load, split with scalar shifts
+      // (a bit cast of an ext-vector element such as v[1] compiles to a
+      // read of element 0 on this toolchain, so none is used)
+      struct F2 {
+        float x, y;
+      };
+      auto ld2 = [](const float* p) {
+        const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        return F2{__builtin_bit_cast(float, static_cast<uint32_t>(w)),
+                  __builtin_bit_cast(float, static_cast<uint32_t>(w >> 32))};
+      };
+      float lm[SL], ll[SL];
+      float4v lo[SL];
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        lm[i] = -INFINITY;
+        ll[i] = 0.0f;
+        lo[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      for (int s0 = 0; s0 < a.n_splits; s0 += 2 * SL) {
+        F2 w_ml[2 * SL], w_o0[2 * SL], w_o1[2 * SL];
+#pragma unroll
+        for (int j = 0; j < 2 * SL; ++j) {
+          const int s = min(s0 + j, a.n_splits - 1);
+          w_ml[j] = ld2(ml + 2 * s);
+          w_o0[j] = ld2(po + static_cast<int64_t>(s) * kD);
+          w_o1[j] = ld2(po + static_cast<int64_t>(s) * kD + 2);
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * SL; ++j) {
+          if (s0 + j < a.n_splits) {
+            const float4v pv = {w_o0[j].x, w_o0[j].y, w_o1[j].x, w_o1[j].y};
+            merge_into(lm[j % SL], ll[j % SL], lo[j % SL], w_ml[j].x, w_ml[j].y, pv);
+          }
+        }
+      }
+      const float4v v = combine_lanes<SL>([&](int i) { return lm[i]; }, [&](int i) { return ll[i]; },
+                                          [&](int i) { return lo[i]; });
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sq[r][4 * cg + c] = v[c];
+    }
+    write_final = true;
+  }
+  if (write_final) {
     __syncthreads();
     if constexpr (rotated(VC)) {
       for (int h = 1; h < kD; h <<= 1) {

@@ -54,7 +54,7 @@ extern "C" int vit_attn_decode_noalloc(const vit_kv_plane* k, const vit_kv_plane
     if (st != VIT_OK) return st;
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = vit::enqueue_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, ws, out, hs, ev);
+  st = vit::enqueue_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, ws, out, nullptr, hs, ev);
   if (st != VIT_OK || n_splits == 1) return st;
   return vit::enqueue_reduce(ws, k->n_seqs, rows, n_splits, v, out, hs);
 }

@@ -3,29 +3,15 @@
 // One workgroup per (query head, sequence) of 32 x SL threads (SL = 8, or 32
 // above 64 splits).  Thread t owns channels 4*(t & 31) .. +3 and the partials
 // s = (t >> 5), (t >> 5) + SL, ... ; each thread merges its partials online,
-// then the SL partial merges per channel are combined through LDS.  Partial s
-// of a row is (o_s[128] unnormalised, m_s in base-2 units, l_s):
-// M = max m_s, L = sum l_s 2^(m_s - M), O = sum o_s 2^(m_s - M) / L.  Empty partials (l_s = 0, m_s = -inf) are
-// skipped.  For a rot4 V plane the merged row is in the rotated domain scaled
-// by sqrt(128); it is mapped back with x = s .* (H o) / 128.
+// then the SL lane results are combined through LDS (the arithmetic of
+// merge.h, which the decode kernel's in-kernel merge shares).  For a rotated
+// V plane the merged row is in the rotated domain scaled by sqrt(128); it is
+// mapped back with x = s .* (H o) / 128.
+#include "merge.h"
 #include "vit_device.h"
 #include "vit_launch.h"
 
 namespace vit {
-
-__device__ inline void merge_into(float& M, float& L, float4v& O, float pm, float pl, float4v po) {
-  if (pl > 0.0f) {
-    if (pm > M) {
-      const float sc = __builtin_amdgcn_exp2f(M - pm);
-      O *= sc;
-      L *= sc;
-      M = pm;
-    }
-    const float f = __builtin_amdgcn_exp2f(pm - M);
-    O += po * f;
-    L += pl * f;
-  }
-}
 
 // SL split lanes x 32 channel groups; SL = 8 for few splits, 32 for many.
 template <int SL>
@@ -39,7 +25,7 @@ __global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
   const float* o = a.ws_o + row * a.n_splits * kD + 4 * cg;
 
   __shared__ float s_m[SL], s_l[SL];
-  __shared__ float s_o[SL][kD];
+  __shared__ __align__(16) float s_o[SL][kD];
   __shared__ float v[kD];
 
   float M = -INFINITY, L = 0.0f;
@@ -67,22 +53,14 @@ __global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
   for (int i = 0; i < 4; ++i) s_o[sl][4 * cg + i] = O[i];
   __syncthreads();
 
-  if (t < kD) {
-    float Mf = -INFINITY, Lf = 0.0f, Of = 0.0f;
+  if (t < 32) {
+    const float4v r = combine_lanes<SL>([&](int i) { return s_m[i]; }, [&](int i) { return s_l[i]; },
+                                        [&](int i) { return *reinterpret_cast<const float4v*>(&s_o[i][4 * t]); });
 #pragma unroll
-    for (int i = 0; i < SL; ++i) Mf = fmaxf(Mf, s_m[i]);
-#pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      if (s_l[i] > 0.0f) {
-        const float f = __builtin_amdgcn_exp2f(s_m[i] - Mf);
-        Of += s_o[i][t] * f;
-        Lf += s_l[i] * f;
-      }
-    }
-    v[t] = Lf > 0.0f ? Of / Lf : 0.0f;
+    for (int c = 0; c < 4; ++c) v[4 * t + c] = r[c];
   }
+  __syncthreads();  // v is written 4 channels per thread and read 1 per thread
   if (a.rotate) {
-    __syncthreads();
     for (int h = 1; h < kD; h <<= 1) {
       if (t < 64) {
         const int lo = ((t & ~(h - 1)) << 1) | (t & (h - 1));
@@ -146,8 +124,8 @@ hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, hipS
 }
 
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args) {
-  if (args.n_splits > 64) hipLaunchKernelGGL(reduce_kernel<32>, grid, dim3(1024), 0, stream, args);
-  else hipLaunchKernelGGL(reduce_kernel<8>, grid, dim3(256), 0, stream, args);
+  if (args.n_splits > kMergeFewMaxSplits) hipLaunchKernelGGL(reduce_kernel<kMergeLanesMany>, grid, dim3(1024), 0, stream, args);
+  else hipLaunchKernelGGL(reduce_kernel<kMergeLanesFew>, grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

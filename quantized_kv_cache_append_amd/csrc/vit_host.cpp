@@ -115,7 +115,7 @@ int check_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, i
 
 int enqueue_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
                    const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
-                   float* workspace, float* out, hipStream_t stream, const KernelEvents& ev) {
+                   float* workspace, float* out, uint32_t* arrive, hipStream_t stream, const KernelEvents& ev) {
   const int32_t gqa = n_q_heads / k->n_kv_heads;
   DecodeArgs a{};
   a.kcodes = static_cast<const uint8_t*>(k->codes);
@@ -132,6 +132,7 @@ int enqueue_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q,
                                                  ws_o_bytes(k->n_seqs, n_q_heads * q_len, n_splits))
                       : nullptr;
   a.out = out;
+  a.arrive = n_splits > 1 ? arrive : nullptr;
   a.capacity = k->capacity;
   a.n_kv_heads = k->n_kv_heads;
   a.n_q_heads = n_q_heads;
@@ -456,7 +457,26 @@ int vit_attn_decode_mq(const vit_kv_plane* k, const vit_kv_plane* v, const float
                                    workspace != nullptr, workspace, out);
   if (st != VIT_OK) return st;
   return vit::enqueue_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, workspace, out,
-                             static_cast<hipStream_t>(stream), ev);
+                             nullptr, static_cast<hipStream_t>(stream), ev);
+}
+
+int vit_attn_decode_merged(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads,
+                           int32_t q_len, const int64_t* seq_len, const float* k_new, const float* v_new,
+                           float scale, int32_t n_splits, float* workspace, uint32_t* counters, float* out,
+                           void* stream) {
+  const vit::KernelEvents ev = vit::take_armed_events();  // one-shot, whatever the outcome
+  int st = vit::check_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits,
+                             workspace != nullptr, workspace, out);
+  if (st != VIT_OK) return st;
+  if (n_splits > 1) {
+    if (!counters) return VIT_E_ARG;
+    if (!aligned(counters, 8)) return VIT_E_ALIGN;
+    if (is_rotated(v->codec) && !v->signs) return VIT_E_ARG;
+    const int32_t rows = (n_q_heads / k->n_kv_heads) * q_len;  // query rows per KV head
+    if (n_splits > VIT_MERGE_MAX_SPLITS || rows * n_splits > VIT_MERGE_MAX_PARTIALS) return VIT_E_UNSUPPORTED;
+  }
+  return vit::enqueue_decode(k, v, q, n_q_heads, q_len, seq_len, k_new, v_new, scale, n_splits, workspace, out,
+                             counters, static_cast<hipStream_t>(stream), ev);
 }
 
 int vit_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -102,6 +102,7 @@ struct DecodeArgs {
   float* ws_o;     // [S][q_len][Hq][n_splits][128]
   float* ws_ml;    // [S][q_len][Hq][n_splits][2]
   float* out;      // [S][q_len][Hq][128]
+  uint32_t* arrive;  // in-kernel split merge: arrival counts [S][Hkv] (0 between calls), or null
   int64_t capacity;
   int32_t n_kv_heads;
   int32_t n_q_heads;
@@ -160,7 +161,7 @@ int check_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, i
                  bool have_workspace, const void* workspace, const float* out);
 int enqueue_decode(const vit_kv_plane* k, const vit_kv_plane* v, const float* q, int32_t n_q_heads, int32_t q_len,
                    const int64_t* seq_len, const float* k_new, const float* v_new, float scale, int32_t n_splits,
-                   float* workspace, float* out, hipStream_t stream, const KernelEvents& ev);
+                   float* workspace, float* out, uint32_t* arrive, hipStream_t stream, const KernelEvents& ev);
 int check_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t head_dim, int32_t n_splits,
                  const vit_kv_plane* v, const float* out);
 int enqueue_reduce(const float* workspace, int32_t n_seqs, int32_t n_q_heads, int32_t n_splits,

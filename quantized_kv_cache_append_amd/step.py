@@ -20,7 +20,7 @@ Everything here is argument marshalling and stream ordering: every
 operation of the step is a call into libvit.so.
 """
 
-from . import prepare_append, prepare_decode, prepare_reduce, vit_arm_kernel_events
+from . import merge_fits, prepare_append, prepare_decode, prepare_merged, prepare_reduce, vit_arm_kernel_events
 
 HEAD_DIM = 128
 
@@ -36,20 +36,31 @@ class DecodeStep:
     lens        rows attended per sequence (they count the ubatch rows)
     workspace   split partials (shared by the layers: the decodes are
                 ordered on one stream), n_splits > 1
+    counters    zeroed arrival counters (merge_counters): each layer's decode
+                and split merge then run as one vit_attn_decode_merged launch
+                when the shape allows; otherwise (or None) decode + reduce
     stream, append_stream   torch streams (default priority)
     """
 
     def __init__(self, layers, q, new_rows, out, lens, p_new, n_q_heads, n_splits, workspace, stream,
-                 append_stream):
+                 append_stream, counters=None):
         import torch
 
         self.stream, self.append_stream = stream, append_stream
         S = layers[0][0].n_seqs
         self.n_layers = len(layers)
+        self.merged = (counters is not None and n_splits > 1
+                       and merge_fits(n_q_heads, layers[0][0].n_kv_heads, 1, n_splits))
         self.appends, self.decodes = [], []
         for (K, V), ql, (kn, vn), o in zip(layers, q, new_rows, out):
             self.appends.append((prepare_append(K, kn, [p_new] * S, stream=append_stream),
                                  prepare_append(V, vn, [p_new] * S, stream=append_stream)))
+            if self.merged:
+                d = prepare_merged(K, V, ql.reshape(S, 1, n_q_heads, -1), n_q_heads, 1, lens,
+                                   o.reshape(S, 1, n_q_heads, -1), workspace, counters, n_splits=n_splits,
+                                   stream=stream)
+                self.decodes.append((d, None))
+                continue
             d = prepare_decode(K, V, ql, n_q_heads, lens, o, n_splits=n_splits,
                                workspace=workspace if n_splits > 1 else None, stream=stream)
             r = prepare_reduce(workspace, S, n_q_heads, n_splits, V, o, stream=stream) if n_splits > 1 else None

@@ -185,6 +185,43 @@ def test_decode_noalloc_validation(lib):
     assert _lib.status_string(_lib.VIT_E_SCRATCH).startswith("split partials larger than the static scratch")
 
 
+def _decode_merged(lib, k, v, hq=4, q_len=1, seq_len=(10, 10), ns=2, ws=FAKE, counters=FAKE, out=FAKE):
+    arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
+    return lib.vit_attn_decode_merged(ctypes.byref(k), ctypes.byref(v), FAKE, hq, q_len, arr, None, None, 0.088, ns,
+                                      ws, counters, out, None)
+
+
+def test_decode_merged_validation(lib):
+    """The one-launch decode + merge checks its arguments like
+    vit_attn_decode_mq, then its own: arrival counters present and 8-B
+    aligned, at most 64 splits and 128 partial rows per KV head (query rows
+    per KV head x splits), all on the host (no compute: every case fails)."""
+    K, V = _plane(side=0), _plane(side=1)  # 2 KV heads
+    assert _decode_merged(lib, K, V, seq_len=(0, 1)) == _lib.VIT_E_ARG
+    assert _decode_merged(lib, K, V, q_len=5) == _lib.VIT_E_UNSUPPORTED
+    assert _decode_merged(lib, K, V, ws=None) == _lib.VIT_E_ARG
+    assert _decode_merged(lib, K, V, out=FAKE + 8) == _lib.VIT_E_ALIGN
+    assert _decode_merged(lib, V, K) == _lib.VIT_E_ARG
+    assert _decode_merged(lib, K, V, counters=None) == _lib.VIT_E_ARG
+    assert _decode_merged(lib, K, V, counters=FAKE + 4) == _lib.VIT_E_ALIGN
+    assert _lib.MERGE_MAX_SPLITS == 64 and _lib.MERGE_MAX_PARTIALS == 128
+    assert _decode_merged(lib, K, V, ns=65) == _lib.VIT_E_UNSUPPORTED            # 2 rows x 65 splits
+    assert _decode_merged(lib, K, V, hq=16, ns=17) == _lib.VIT_E_UNSUPPORTED     # 8 rows x 17 splits
+    assert _decode_merged(lib, K, V, hq=8, q_len=2, ns=17) == _lib.VIT_E_UNSUPPORTED  # 4 x 2 rows x 17
+    assert _decode_merged(lib, K, _plane(side=1, codec=3, signs=None)) == _lib.VIT_E_ARG  # rotated V, no signs
+
+
+def test_merge_fits_matches_the_limits():
+    import quantized_kv_cache_append_amd as vit
+
+    assert vit.merge_fits(32, 8, 1, 16)           # the 16-split ladder: 4 rows x 16
+    assert vit.merge_fits(40, 8, 3, 8)            # 15 rows x 8 = 120
+    assert not vit.merge_fits(40, 8, 3, 9)        # 135
+    assert not vit.merge_fits(16, 2, 1, 128)      # 8 rows x 128
+    assert not vit.merge_fits(4, 4, 1, 65)        # 65 splits
+    assert vit.merge_fits(16, 2, 1, 1)            # one split: nothing to merge
+
+
 def _transcode(lib, src, dst, n_rows=(10, 10)):
     arr = None if n_rows is None else (ctypes.c_int64 * len(n_rows))(*n_rows)
     return lib.vit_kv_transcode(ctypes.byref(src), ctypes.byref(dst), arr, None)

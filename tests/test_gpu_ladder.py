@@ -6,7 +6,8 @@ balanced map (8 each of f16, q8_0, q4_0, rot4; 10 distinct (K, V) pairs),
 step driver (quantized_kv_cache_append_amd.step.DecodeStep) on planes that
 were poisoned and then pre-filled with rows 0 .. 198,655: the 2048-row
 ubatch (rows 198,656 .. 200,703) is appended to all 32 planes on a second
-stream while the decodes run, decode l waiting only for layer l's appends.
+stream while the decodes run, decode l waiting only for layer l's appends;
+each layer's decode and split merge is one vit_attn_decode_merged launch.
 
 The rows a decode would read before its layer's appends finished are still
 poison (NaN fp16 scales, all-ones codes), so a wrong schedule shows up as a
@@ -79,8 +80,11 @@ def ladder_step():
     n_splits = vit.vit_attn_default_splits(S, H, Hq, L)
     ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq, D, n_splits), dtype=torch.uint8, device="cuda")
     stream, astream = torch.cuda.Stream(), torch.cuda.Stream()
-    step = DecodeStep(layers, q_dev, new_rows, out, [L] * S, pre, Hq, n_splits, ws, stream, astream)
-    say(f"[ladder step] one overlapped step, {n_splits} splits")
+    counters = vit.merge_counters(layers[0][0])
+    step = DecodeStep(layers, q_dev, new_rows, out, [L] * S, pre, Hq, n_splits, ws, stream, astream,
+                      counters=counters)
+    assert step.merged, "the ladder's decodes run as one merged launch each, as bench.py runs them"
+    say(f"[ladder step] one overlapped step, {n_splits} splits, decode and merge in one launch")
     with torch.cuda.stream(stream):
         step()
     torch.cuda.synchronize()
@@ -101,6 +105,7 @@ def ladder_step():
             view = unit_view(P, s, h)
             sv[side] = {key: a[pre:pre + ub] for key, a in view.items()}
         stored.append(sv)
+    assert int(counters.abs().sum()) == 0, "arrival counters not back at zero"
     res = dict(outs=outs, serial=serial, q=q_host, rows=rows, stored=stored, cmap=cmap, n_splits=n_splits, G=Hq // H, pre=pre,
                ub=ub, L=L)
     del layers, step, new_rows, out, ws
