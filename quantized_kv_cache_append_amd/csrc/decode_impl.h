@@ -1100,6 +1100,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // q-head g < gqa; row r attends rows 0 .. lmin - 1 + t of the stream.
   const int L = a.seq_len[seq];  // rows attended by the last new token
   const int QL = a.q_len;
+  // Fetch every scalar argument the prologue uses in one round trip: read
+  // one by one where they are first needed, the compiler waited for each
+  // fetch in turn (four serial trips, about 1.3 us before the query loads
+  // could be issued).
+  const uint32_t ks0 = rotated(KC) ? a.ksigns[0] : 0u, ks1 = rotated(KC) ? a.ksigns[1] : 0u;
+  const uint32_t ks2 = rotated(KC) ? a.ksigns[2] : 0u, ks3 = rotated(KC) ? a.ksigns[3] : 0u;
+  __asm__ volatile("" ::"s"(L), "s"(QL), "s"(a.gqa), "s"(a.n_splits), "s"(a.n_kv_heads), "s"(a.n_q_heads),
+                   "s"(a.capacity), "s"(a.q), "s"(a.k_new), "s"(a.kcodes), "s"(a.vcodes), "s"(a.qscale), "s"(ks0),
+                   "s"(ks1), "s"(ks2), "s"(ks3));
   const int lmin = L - QL + 1;    // rows attended by the first new token
   const int G = a.gqa * QL;       // query rows
   constexpr int kThreads = 64 * kDecodeWaves;
@@ -1196,7 +1205,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       // sign bits of those 8 channels (selected, not indexed: an indexed
       // read of the arguments is a vector load that the staging would wait on)
       const int si = ((8 * tid) & 127) >> 5;
-      ksw = si == 0 ? a.ksigns[0] : si == 1 ? a.ksigns[1] : si == 2 ? a.ksigns[2] : a.ksigns[3];
+      ksw = si == 0 ? ks0 : si == 1 ? ks1 : si == 2 ? ks2 : ks3;
     }
   }
   // rot4 levels: lane l (< 16) fetches level l; issued before the tile loads
@@ -1227,8 +1236,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   };
   TileRegs<KC, VC, NT> ta, tb;
   [[maybe_unused]] TileRegs<KC, VC, NT> tc;
+  // the first tile now; the second after the query staging barrier, so that
+  // the waves reach the barrier without waiting for the whole compute unit's
+  // prefetch to be issued (each 1 KB load takes the vector memory unit ~16
+  // cycles: 8 waves x 2 tiles are ~1.2 us of issue)
   load_slot(ta, wave);
-  load_slot(tb, wave + kDecodeWaves);
 
   if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
   if constexpr (kRot3) fill_rot3_lut<kThreads>(lut3, tid, lv3);
@@ -1248,6 +1260,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
     }
   }
   __syncthreads();
+  // (rotated keys: after the query rotation, whose barriers would otherwise
+  // wait for every wave's issue of it)
+  if constexpr (!rotated(KC)) load_slot(tb, wave + kDecodeWaves);
   float qs = a.qscale;
   if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (WHT); the keys reconstruct as
@@ -1263,6 +1278,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
       __syncthreads();
     }
     qs *= 1.0f / 128.0f;
+    load_slot(tb, wave + kDecodeWaves);
   }
   // the lane's row is block slot = n16 & 3 of its query row (rows past G
   // are zero in sq); its operand is that block's chunk qg in MFMA m = slot
