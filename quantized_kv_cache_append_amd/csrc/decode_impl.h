@@ -1117,7 +1117,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // contiguous tile ranges per split (the last ones may be short or empty)
   const int tiles_per_split = (n_tiles + a.n_splits - 1) / a.n_splits;
 
-  __shared__ float sq[GMAX][kD];
+  __shared__ __align__(16) float sq[GMAX][kD];
   constexpr bool kRot4 = KC == ROT4 || VC == ROT4;
   constexpr bool kRot3 = KC == ROT3 || VC == ROT3;
   __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
@@ -1267,16 +1267,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (WHT); the keys reconstruct as
     // N*S*level/sqrt(128) (rot3: S*level/sqrt(128)) against q~ = H(s.q)/sqrt(128)
-    for (int h = 1; h < kD; h <<= 1) {
-      for (int i = tid; i < RW * 64; i += kThreads) {
-        const int g = i >> 6, k = i & 63;
-        const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
-        const float x = sq[g][lo], y = sq[g][lo + h];
-        sq[g][lo] = x + y;
-        sq[g][lo + h] = x - y;
-      }
-      __syncthreads();
-    }
+    wht128_lds<kThreads>(&sq[0][0], RW, tid);
     qs *= 1.0f / 128.0f;
     load_slot(tb, wave + kDecodeWaves);
   }
@@ -1543,18 +1534,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   }
   if (write_final) {
     __syncthreads();
-    if constexpr (rotated(VC)) {
-      for (int h = 1; h < kD; h <<= 1) {
-        for (int i = tid; i < RW * 64; i += kThreads) {
-          const int g = i >> 6, k = i & 63;
-          const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
-          const float x = sq[g][lo], y = sq[g][lo + h];
-          sq[g][lo] = x + y;
-          sq[g][lo + h] = x - y;
-        }
-        __syncthreads();
-      }
-    }
+    if constexpr (rotated(VC)) wht128_lds<kThreads>(&sq[0][0], RW, tid);
     for (int i = tid; i < G * kD; i += kThreads) {
       const int g = i >> 7, c = i & 127;
       float v = sq[g][c];

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
   const int G = a.gqa;
   const int n_tiles = (L + kTile - 1) / kTile;
 
-  __shared__ float sq[16][kD];
+  __shared__ __align__(16) float sq[16][kD];
   __shared__ uint32_t lut[kRot4 ? 256 * 64 : 1];
   __shared__ uint32_t lut3[kRot3 ? 64 * 64 : 1];
   __shared__ float s_m[kProbeWaves][16], s_l[kProbeWaves][16];
@@ -116,16 +116,7 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
   float qs = a.qscale;
   if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (unnormalised WHT; 1/128 folded in)
-    for (int h = 1; h < kD; h <<= 1) {
-      for (int i = tid; i < 16 * 64; i += kThreads) {
-        const int g = i >> 6, k = i & 63;
-        const int lo = ((k & ~(h - 1)) << 1) | (k & (h - 1));
-        const float x = sq[g][lo], y = sq[g][lo + h];
-        sq[g][lo] = x + y;
-        sq[g][lo + h] = x - y;
-      }
-      __syncthreads();
-    }
+    wht128_lds<kThreads>(&sq[0][0], 16, tid);
     qs *= 1.0f / 128.0f;
   }
   // A operand of MFMA b: row n16 = query n16, chunk qg of block b, hi and lo

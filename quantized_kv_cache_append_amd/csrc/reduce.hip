@@ -26,7 +26,7 @@ __global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
 
   __shared__ float s_m[SL], s_l[SL];
   __shared__ __align__(16) float s_o[SL][kD];
-  __shared__ float v[kD];
+  __shared__ __align__(16) float v[kD];
 
   float M = -INFINITY, L = 0.0f;
   float4v O = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -61,15 +61,7 @@ __global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
   }
   __syncthreads();  // v is written 4 channels per thread and read 1 per thread
   if (a.rotate) {
-    for (int h = 1; h < kD; h <<= 1) {
-      if (t < 64) {
-        const int lo = ((t & ~(h - 1)) << 1) | (t & (h - 1));
-        const float x = v[lo], y = v[lo + h];
-        v[lo] = x + y;
-        v[lo + h] = x - y;
-      }
-      __syncthreads();
-    }
+    wht128_lds<32 * SL>(v, 1, t);
     if (t < kD) {
       float r = v[t] * (1.0f / 128.0f);
       v[t] = ((a.vsigns[t >> 5] >> (t & 31)) & 1u) ? -r : r;

@@ -542,6 +542,60 @@ __device__ inline void encode_rows(const float (&x0)[R], const float (&x1)[R], i
   else encode_rot3(x0, x1, lane, signs, rc);
 }
 
+// In-place unnormalised WHT of n_rows rows of 128 floats in LDS (16-byte
+// aligned), by every thread of a workgroup of NTHREADS: stages h = 1, 2,
+// ..., 64 in that order, each pair (i, i + h) becoming (x + y, x - y).
+// Stages 1..8 run in registers on 16 consecutive channels per thread, then
+// stages 16..64 on 8 channels 16 apart: two barriers instead of one per stage,
+// with the same operations in the same order.
+template <int NTHREADS>
+__device__ inline void wht128_lds(float* rows, int n_rows, int tid) {
+  for (int u = tid; u < n_rows * 8; u += NTHREADS) {  // (row, 16-channel group)
+    float4v* p = reinterpret_cast<float4v*>(rows + (u >> 3) * 128 + (u & 7) * 16);
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v w = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * q + j] = w[j];
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (!(i & h)) {
+          const float x = v[i], y = v[i + h];
+          v[i] = x + y;
+          v[i + h] = x - y;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q] = float4v{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  }
+  __syncthreads();
+  for (int u = tid; u < n_rows * 16; u += NTHREADS) {  // (row, channel within the groups)
+    float* p = rows + (u >> 4) * 128 + (u & 15);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[16 * k];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (!(k & h)) {
+          const float x = v[k], y = v[k + h];
+          v[k] = x + y;
+          v[k + h] = x - y;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[16 * k] = v[k];
+  }
+  __syncthreads();
+}
+
 template <int CODEC>
 __device__ inline RowCodes encode_row(float x0, float x1, int lane, const uint32_t signs[4]) {
   const float a[1] = {x0}, b[1] = {x1};
