@@ -233,6 +233,10 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a)
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
   const int64_t p_begin = a.pos0[seq];
+  // every scalar argument in one round trip (fetched where each is first
+  // used, they were waited for one after another)
+  __asm__ volatile("" ::"s"(p_begin), "s"(a.n_tokens), "s"(a.n_kv_heads), "s"(a.capacity), "s"(a.src), "s"(a.codes),
+                   "s"(a.scales), "s"(a.norms), "s"(a.signs[0]), "s"(a.signs[1]), "s"(a.signs[2]), "s"(a.signs[3]));
   const int64_t p_end = p_begin + a.n_tokens;
   const int64_t g = (p_begin >> 3) + static_cast<int64_t>(blockIdx.x) * kAppendWaves + wave;  // 8-row group
   const int64_t g_first_row = g * 8;
@@ -280,6 +284,9 @@ __global__ __launch_bounds__(64 * kAppendWaves) void transcode_kernel(TranscodeA
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
   const int64_t n = a.n_rows[seq];
+  // every scalar argument in one round trip, as in append_kernel
+  __asm__ volatile("" ::"s"(n), "s"(a.n_kv_heads), "s"(a.capacity), "s"(a.src_codes), "s"(a.src_scales), "s"(a.codes),
+                   "s"(a.scales), "s"(a.norms), "s"(a.signs[0]), "s"(a.signs[1]), "s"(a.signs[2]), "s"(a.signs[3]));
   const int64_t row0 = tile * kTile;
   if (row0 >= n) return;  // uniform per workgroup
 

@@ -71,6 +71,10 @@ __global__ __launch_bounds__(64 * kProbeWaves) __attribute__((amdgpu_waves_per_e
   const int head = blockIdx.y;
   const int seq = blockIdx.z;
   const int L = a.seq_len[seq];
+  // every scalar argument in one round trip (fetched where each is first
+  // used, they were waited for one after another)
+  __asm__ volatile("" ::"s"(L), "s"(a.gqa), "s"(a.n_chunks), "s"(a.n_kv_heads), "s"(a.n_q_heads), "s"(a.capacity),
+                   "s"(a.kcodes), "s"(a.kscales), "s"(a.knorms), "s"(a.q), "s"(a.logits), "s"(a.part), "s"(a.qscale));
   const int G = a.gqa;
   const int n_tiles = (L + kTile - 1) / kTile;
 
@@ -207,6 +211,8 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(ProbeArgs a) {
   const int tid = threadIdx.x;
   const int seq = blockIdx.y;
   const int L = a.seq_len[seq];
+  __asm__ volatile("" ::"s"(L), "s"(a.n_chunks), "s"(a.n_q_heads), "s"(a.capacity), "s"(a.logits), "s"(a.part),
+                   "s"(a.scores), "s"(a.decay));  // one round trip, as in probe_logits_kernel
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kMassCells;
   if (j0 >= L) return;  // uniform per workgroup
   __shared__ float s_max[kProbeMaxHeads], s_inv[kProbeMaxHeads];
@@ -338,6 +344,14 @@ __device__ inline void select_state(const SelectArgs& a, int seq, int passes, in
   }
 }
 
+// Every scalar argument of a select kernel in one round trip (fetched where
+// each is first used, they were waited for one after another).
+__device__ inline void fetch_select_args(const SelectArgs& a, int seq) {
+  __asm__ volatile("" ::"s"(a.seq_len[seq]), "s"(a.capacity), "s"(a.n_sink), "s"(a.n_recent), "s"(a.n_evict),
+                   "s"(a.n_seqs), "s"(a.cells_per_block), "s"(a.n_blocks), "s"(a.max_mid), "s"(a.scores),
+                   "s"(a.rows_out), "s"(a.n_out), "s"(a.hist), "s"(a.counts));
+}
+
 __global__ __launch_bounds__(kSelectThreads) void select_zero_kernel(SelectArgs a) {
   const int seq = blockIdx.x;
   for (int p = 0; p < 3; ++p)
@@ -352,6 +366,7 @@ template <int P>
 __global__ __launch_bounds__(kSelectThreads) void select_hist_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int seq = blockIdx.y;
+  fetch_select_args(a, seq);
   const SelectRange r = select_range(a, seq);
   const int64_t b0 = r.lo + static_cast<int64_t>(blockIdx.x) * a.cells_per_block;
   if (r.k == 0 || b0 >= r.hi) return;  // uniform per workgroup
@@ -392,6 +407,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_hist_kernel(SelectArgs 
 __global__ __launch_bounds__(kSelectThreads) void select_count_kernel(SelectArgs a) {
   const int tid = threadIdx.x;
   const int seq = blockIdx.y;
+  fetch_select_args(a, seq);
   const SelectRange r = select_range(a, seq);
   const int64_t b0 = r.lo + static_cast<int64_t>(blockIdx.x) * a.cells_per_block;
   if (r.k == 0 || b0 >= r.hi) return;  // uniform per workgroup
@@ -424,6 +440,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_count_kernel(SelectArgs
 __global__ __launch_bounds__(kSelectThreads) void select_write_kernel(SelectArgs a) {
   const int tid = threadIdx.x;
   const int seq = blockIdx.y;
+  fetch_select_args(a, seq);
   const SelectRange r = select_range(a, seq);
   int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
   if (blockIdx.x == 0) {
@@ -501,6 +518,7 @@ constexpr int kSmallThreads = 1024;  // threads of the one-workgroup select
 __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int seq = blockIdx.x;
+  fetch_select_args(a, seq);
   const SelectRange r = select_range(a, seq);
   int64_t* out = a.rows_out + static_cast<int64_t>(seq) * a.n_evict;
   for (int64_t i = r.k + tid; i < a.n_evict; i += kSmallThreads) out[i] = -1;

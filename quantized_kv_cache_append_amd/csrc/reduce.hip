@@ -18,6 +18,9 @@ template <int SL>
 __global__ __launch_bounds__(32 * SL) void reduce_kernel(ReduceArgs a) {
   const int hq = blockIdx.x;
   const int seq = blockIdx.y;
+  // every scalar argument in one round trip (fetched where each is first
+  // used, they were waited for one after another)
+  __asm__ volatile("" ::"s"(a.n_q_heads), "s"(a.n_splits), "s"(a.ws_ml), "s"(a.ws_o), "s"(a.out), "s"(a.rotate));
   const int t = threadIdx.x;
   const int cg = t & 31, sl = t >> 5;
   const int64_t row = static_cast<int64_t>(seq) * a.n_q_heads + hq;
