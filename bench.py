@@ -7,11 +7,11 @@ A step is one pass of the whole hot path over one batch.  The default
 workload is the ladder, the largest configuration: 16 layers whose K and V
 tensors each carry a codec from a seeded map over {f16, q8_0, q4_0, rot4},
 2 sequences, 32 query heads on 8 KV heads, head_dim 128, 200,704-row slots;
-a step appends a 2048-row ubatch to every (layer, side) plane with
-vit_kv_append_quant on a second stream and decodes one token per sequence
-through all 16 layers (decode + split-K merge per layer; decode l waits for
-layer l's two appends only, and each step's appends wait for the previous
-step's decodes).  The single-layer workloads (tiny, batched, lowbit,
+a step appends a 2048-row ubatch to every (layer, side) plane in one
+vit_kv_append_quant_multi launch and then decodes one token per sequence
+through all 16 layers (decode + split-K merge per layer).
+``--overlap-appends`` instead issues per-plane appends on a second stream,
+decode l waiting for layer l's two appends only.  The single-layer workloads (tiny, batched, lowbit,
 rotated) are available with --workload: a step there is the fused append of
 the new token's K/V rows, the decode and the merge.  ``--q-len N`` (2 .. 4,
 single-layer workloads) makes each step verify N new tokens per sequence at
@@ -202,12 +202,14 @@ def run_gpu(args):
     lens = [L] * S
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
-    # The ladder's ubatch appends go to a second stream (default priority
-    # too), scheduled by the step driver (quantized_kv_cache_append_amd.step):
-    # decode l waits only for layer l's appends, so the later layers' appends
-    # run beside the first decodes; each step's appends wait for the previous
-    # step's decodes (they rewrite the rows those read).
+    # The ladder's ubatch appends, scheduled by the step driver
+    # (quantized_kv_cache_append_amd.step): by default one launch appends to
+    # all planes before the decodes; with --overlap-appends per-plane appends
+    # go to a second stream (default priority too) and decode l waits only for
+    # layer l's appends, each step's appends waiting for the previous step's
+    # decodes (they rewrite the rows those read).
     fused = "ubatch" not in cfg
+    append_mode = "overlapped" if args.overlap_appends else "batched"
     astream = None if fused else torch.cuda.Stream()
     # decode and split merge in one launch (vit_attn_decode_merged) where the
     # shape allows it; the arrival counters are zeroed once and every call
@@ -225,7 +227,7 @@ def run_gpu(args):
             from quantized_kv_cache_append_amd.step import DecodeStep
 
             calls.append(DecodeStep([(lay.K[r], lay.V[r]) for lay in layers], q, new_rows, out, lens, p_new, Hq,
-                                    n_splits, ws, stream, astream, counters=counters))
+                                    n_splits, ws, stream, astream, counters=counters, append_mode=append_mode))
             continue
         dec = []
         for li, lay in enumerate(layers):
@@ -323,13 +325,14 @@ def run_gpu(args):
         assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output (graph replay)"
         del graphs
     if not fused:
-        # The two-stream step must compute what a serial one does.  The timed
-        # steps append the same rows every time, which would hide a decode
-        # that ran before its layer's appends; so the ubatch rows are scaled
-        # by 8 first (their logits then dominate the softmax, and a stale read
-        # would move the output by O(1)), then one overlapped step and the
-        # same calls serially (every append done before the first decode) must
-        # agree bit for bit (the decode's summation order is fixed).
+        # The step must compute what the per-plane calls issued serially do.
+        # The timed steps append the same rows every time, which would hide a
+        # decode that ran before its layer's appends; so the ubatch rows are
+        # scaled by 8 first (their logits then dominate the softmax, and a
+        # stale read would move the output by O(1)), then one step and the
+        # per-plane appends followed by the decodes, each call finished
+        # before the next, must agree bit for bit (the decode's summation
+        # order is fixed).
         for kv in new_rows:
             for x in kv:
                 x.mul_(8.0)
@@ -337,18 +340,22 @@ def run_gpu(args):
         with torch.cuda.stream(stream):
             step(0)
         torch.cuda.synchronize()
-        overlapped = [o.clone() for o in out]
+        stepped = [o.clone() for o in out]
         with torch.cuda.stream(stream):
             calls[0].run_serial()
-        for li, (a, b) in enumerate(zip(overlapped, out)):
-            assert torch.equal(a, b), f"layer {li}: overlapped step differs from the serial step"
-        print("# overlap check: overlapped step == serial step, bit for bit, all layers", file=sys.stderr, flush=True)
+        for li, (a, b) in enumerate(zip(stepped, out)):
+            assert torch.equal(a, b), f"layer {li}: {append_mode} step differs from the serial per-plane calls"
+        print(f"# step check: {append_mode} step == serial per-plane calls, bit for bit, all layers", file=sys.stderr,
+              flush=True)
     dec_mean_ms = float(np.mean(dec_ms))
     per_launch_bytes = kv_bytes / n_layers
     # algorithmic bytes of all timed decode launches / their summed duration
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
     return dict(cfg=cfg, wl=wl, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
                 merge="in-kernel (vit_attn_decode_merged)" if merged else ("reduce kernel" if n_splits > 1 else "none"),
+                appends=None if fused else (
+                    "one vit_kv_append_quant_multi launch before the decodes" if append_mode == "batched"
+                    else "per-plane vit_kv_append_quant on a second stream, overlapped with the decodes"),
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
                 block_ms=block_ms,
                 dec_mean_ms=dec_mean_ms,
@@ -1153,6 +1160,9 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="time an attention-probe scoring event (+ eviction choice) on --workload's K plane instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-appends", action="store_true",
+                    help="ladder: per-plane appends on a second stream, overlapped with the decodes, "
+                    "instead of one multi-plane append launch")
     ap.add_argument("--no-merge", action="store_true",
                     help="decode + separate reduce launch even where vit_attn_decode_merged applies")
     ap.add_argument("--graph", action="store_true",
@@ -1263,6 +1273,7 @@ def main():
             else f"K {r['cmap'][0][0]} / V {r['cmap'][0][1]}",
             "n_splits": r["n_splits"], "split_merge": r["merge"], "cold_cache_replicas": r["replicas"],
             "launch": r["mode"],
+            **({"ubatch_appends": r["appends"]} if r["appends"] else {}),
         },
         "graph_ms_per_step": None if r["graph_ms_per_step"] is None else round(r["graph_ms_per_step"], 5),
         "effective_kv_read_gbs": round(r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),

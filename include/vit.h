@@ -144,6 +144,7 @@ typedef enum vit_status {
 #define VIT_MAX_QLEN 4 /* new tokens per sequence in one vit_attn_decode_mq call */
 #define VIT_MAX_SPLITS 4096
 #define VIT_MERGE_MAX_SPLITS 64    /* vit_attn_decode_merged: split count */
+#define VIT_MAX_APPEND_PLANES 32   /* vit_kv_append_quant_multi: planes per call */
 #define VIT_MERGE_MAX_PARTIALS 128 /* vit_attn_decode_merged: query rows per KV head x splits */
 #define VIT_MAX_CAPACITY (1 << 30) /* rows per (sequence, KV head) */
 
@@ -186,6 +187,25 @@ int vit_kv_plane_sizes(int32_t codec, int32_t n_seqs, int32_t n_kv_heads, int32_
  * Rows not in the range are left untouched. */
 int vit_kv_append_quant(const vit_kv_plane *dst, const float *src, const int64_t *pos0,
                         int32_t n_tokens, void *stream);
+
+/* The same append for several planes in one launch: rows pos0[s] ..
+ * pos0[s]+n_tokens-1 of each sequence s of every plane i, from src[i] (the
+ * ubatch appended to every (layer, side) tensor of a step: serverAppConfigs
+ * commit log, "BATCH_SIZE 2048 -> 4096, UBATCH_SIZE 1024 -> 2048" commit;
+ * the per-(layer, side) codecs of the buun-llama-cpp page's "VBR" section).
+ * Each plane is written exactly as vit_kv_append_quant(&planes[i], src[i],
+ * pos0, n_tokens) would write it; one launch pays the fixed start cost once.
+ *  planes   [host] n_planes planes (any codecs and sides) with equal n_seqs
+ *           and n_kv_heads; the arrays of no two planes overlap.
+ *  src      [host] n_planes device pointers, each fp32
+ *           [n_seqs][n_tokens][n_kv_heads][128], 16-B aligned.
+ *  n_planes 1 .. VIT_MAX_APPEND_PLANES.
+ * Errors as vit_kv_append_quant (any plane); mismatched geometry or arrays
+ * of two planes that overlap is VIT_E_ARG, n_planes outside 1..VIT_MAX_APPEND_PLANES is
+ * VIT_E_UNSUPPORTED.  Kernel events armed by vit_arm_kernel_events bracket
+ * its one kernel. */
+int vit_kv_append_quant_multi(const vit_kv_plane *planes, int32_t n_planes, const float *const *src,
+                              const int64_t *pos0, int32_t n_tokens, void *stream);
 
 /* One degrade step of a variable bit-rate cache: re-encode the rows one
  * (layer, side) tensor holds into a plane of a codec with fewer bits per
@@ -420,7 +440,7 @@ int vit_attn_decode_noalloc(const vit_kv_plane *k, const vit_kv_plane *v, const 
 
 /* Measurement aid (no operation of the method): arm two caller-created
  * hipEvent_t handles (timing enabled) so that the kernel of this host
- * thread's next vit_kv_append_quant, vit_attn_decode, vit_attn_decode_mq,
+ * thread's next vit_kv_append_quant, vit_kv_append_quant_multi, vit_attn_decode, vit_attn_decode_mq,
  * vit_attn_decode_merged, vit_attn_decode_noalloc, vit_kv_transcode, vit_stream_read or vit_attn_probe_scores call (for the latter: its
  * logits kernel)
  * records `start_event` when its dispatch begins and `stop_event` when it

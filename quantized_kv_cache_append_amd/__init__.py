@@ -5,10 +5,11 @@ include/vit.h).  This module only marshals torch tensors into those calls:
 PyTorch provides device memory and the stream, nothing else.  The Python
 names mirror the C entry points:
 
-    vit_kv_plane_sizes, vit_kv_append_quant, vit_kv_transcode,
-    vit_vbr_classic_next_step, vit_attn_workspace_bytes,
+    vit_kv_plane_sizes, vit_kv_append_quant, vit_kv_append_quant_multi,
+    vit_kv_transcode, vit_vbr_classic_next_step, vit_attn_workspace_bytes,
     vit_attn_default_splits, vit_attn_decode, vit_attn_decode_mq,
-    vit_attn_decode_noalloc, vit_attn_splitk_reduce, vit_attn_probe_workspace_bytes,
+    vit_attn_decode_merged, vit_attn_decode_noalloc, vit_attn_splitk_reduce,
+    vit_attn_probe_workspace_bytes,
     vit_attn_probe_scores, vit_probe_select_evictions,
     vit_arm_kernel_events, vit_stream_read (measurement aids)
 
@@ -24,9 +25,10 @@ from ._lib import CODEC_IDS, SIDE_IDS, VitError, VitKvPlane
 
 __all__ = [
     "KVPlane", "VitError", "layout",
-    "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_kv_transcode", "vit_vbr_classic_next_step",
-    "vit_attn_workspace_bytes",
-    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_decode_noalloc",
+    "vit_kv_plane_sizes", "vit_kv_append_quant", "vit_kv_append_quant_multi", "vit_kv_transcode",
+    "vit_vbr_classic_next_step", "vit_attn_workspace_bytes",
+    "vit_attn_default_splits", "vit_attn_decode", "vit_attn_decode_mq", "vit_attn_decode_merged",
+    "vit_attn_decode_noalloc",
     "vit_attn_splitk_reduce",
     "vit_attn_probe_workspace_bytes", "vit_attn_probe_scores", "vit_probe_select_evictions",
     "vit_probe_select_workspace_bytes",
@@ -34,6 +36,7 @@ __all__ = [
 ]
 
 HEAD_DIM = 128
+MAX_APPEND_PLANES = _lib.MAX_APPEND_PLANES  # planes per vit_kv_append_quant_multi call
 
 
 def _stream_handle(stream):
@@ -140,6 +143,25 @@ def vit_kv_append_quant(plane, src, pos0, n_tokens=None, stream=None):
     p = plane.struct()
     st = lib.vit_kv_append_quant(ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
     return _lib.check("vit_kv_append_quant", st)
+
+
+def _multi_args(planes, srcs, pos0, n_tokens):
+    if len(planes) != len(srcs):
+        raise ValueError("one source per plane")
+    arr = (_lib.VitKvPlane * len(planes))(*[p.struct() for p in planes])
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_fptr(x, "src").value for x in srcs])
+    p0 = (ctypes.c_int64 * len(pos0))(*[int(x) for x in pos0])
+    n_tokens = srcs[0].shape[1] if n_tokens is None else n_tokens
+    return arr, ptrs, p0, int(n_tokens)
+
+
+def vit_kv_append_quant_multi(planes, srcs, pos0, n_tokens=None, stream=None):
+    """vit_kv_append_quant of srcs[i] (fp32 [S, T, Hkv, 128]) into planes[i]
+    for every i, in one launch (planes of equal S and Hkv)."""
+    lib = _lib.load()
+    arr, ptrs, p0, n = _multi_args(planes, srcs, pos0, n_tokens)
+    st = lib.vit_kv_append_quant_multi(arr, len(planes), ptrs, p0, n, _stream_handle(stream))
+    return _lib.check("vit_kv_append_quant_multi", st)
 
 
 def vit_kv_transcode(src, dst, n_rows, stream=None):
@@ -397,6 +419,14 @@ def prepare_append(plane, src, pos0, n_tokens=None, stream=None):
     p = plane.struct()
     args = (ctypes.byref(p), _fptr(src, "src"), p0, int(n_tokens), _stream_handle(stream))
     return _Prepared("vit_kv_append_quant", lib.vit_kv_append_quant, args, (p, p0, src, plane))
+
+
+def prepare_append_multi(planes, srcs, pos0, n_tokens=None, stream=None):
+    lib = _lib.load()
+    arr, ptrs, p0, n = _multi_args(planes, srcs, pos0, n_tokens)
+    args = (arr, len(planes), ptrs, p0, n, _stream_handle(stream))
+    return _Prepared("vit_kv_append_quant_multi", lib.vit_kv_append_quant_multi, args,
+                     (arr, ptrs, p0, tuple(planes), tuple(srcs)))
 
 
 def prepare_transcode(src, dst, n_rows, stream=None):

@@ -20,6 +20,7 @@ VIT_E_SCRATCH = -6
 NOALLOC_SCRATCH_BYTES = 4 << 20  # VIT_NOALLOC_SCRATCH_BYTES
 MERGE_MAX_SPLITS = 64  # VIT_MERGE_MAX_SPLITS
 MERGE_MAX_PARTIALS = 128  # VIT_MERGE_MAX_PARTIALS
+MAX_APPEND_PLANES = 32  # VIT_MAX_APPEND_PLANES
 
 CODEC_IDS = {"f16": 0, "q8_0": 1, "q4_0": 2, "rot4": 3, "rot3": 4}
 SIDE_IDS = {"k": 0, "v": 1}
@@ -28,6 +29,7 @@ SIDE_IDS = {"k": 0, "v": 1}
 EXPORTS = (
     "vit_kv_plane_sizes",
     "vit_kv_append_quant",
+    "vit_kv_append_quant_multi",
     "vit_kv_transcode",
     "vit_vbr_classic_next_step",
     "vit_attn_workspace_bytes",
@@ -89,6 +91,8 @@ def load():
     lib.vit_kv_plane_sizes.restype = ctypes.c_int
     lib.vit_kv_append_quant.argtypes = [plane_p, vp, P(i64), i32, vp]
     lib.vit_kv_append_quant.restype = ctypes.c_int
+    lib.vit_kv_append_quant_multi.argtypes = [plane_p, i32, P(vp), P(i64), i32, vp]
+    lib.vit_kv_append_quant_multi.restype = ctypes.c_int
     lib.vit_kv_transcode.argtypes = [plane_p, plane_p, P(i64), vp]
     lib.vit_kv_transcode.restype = ctypes.c_int
     lib.vit_vbr_classic_next_step.argtypes = [i32, P(i32), P(i32), P(ctypes.c_uint8), ctypes.c_double,

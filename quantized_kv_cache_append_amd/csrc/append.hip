@@ -225,6 +225,41 @@ __device__ inline void store_group(uint8_t* codes, uint16_t* scales, uint16_t* n
   }
 }
 
+// One 8-row group of one (sequence, KV head) stream: load the rows, encode
+// them together, store them (rows outside [p_begin, p_begin + n_tokens) are
+// neither encoded into the plane nor written).
+template <int CODEC, int SIDE>
+__device__ __forceinline__ void append_group(void* codes_base, uint16_t* scales_base, uint16_t* norms_base,
+                                             const float* src_base, int64_t capacity, const uint32_t (&signs)[4],
+                                             int64_t p_begin, int n_tokens, int n_kv_heads, int seq, int head,
+                                             int64_t g, int lane, uint8_t (*rowbuf)[256]) {
+  const int64_t p_end = p_begin + n_tokens;
+  const int64_t g_first_row = g * 8;
+  if (g_first_row >= p_end) return;  // past this sequence's range (uniform per wave)
+
+  constexpr int RB = row_code_bytes(CODEC);
+  const int64_t ph = static_cast<int64_t>(seq) * n_kv_heads + head;
+  uint8_t* codes = static_cast<uint8_t*>(codes_base) + ph * capacity * RB;
+  uint16_t* scales = has_scales(CODEC) ? scales_base + ph * capacity * 4 : nullptr;
+  uint16_t* norms = has_norms(CODEC) ? norms_base + ph * capacity : nullptr;
+
+  bool live[8];
+  float x0[8], x1[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int64_t p = g_first_row + r;
+    live[r] = p >= p_begin && p < p_end;
+    // rows outside the range read a row inside it (clamped) and are not stored
+    const int64_t pc = p < p_begin ? p_begin : (p >= p_end ? p_end - 1 : p);
+    const float* src = src_base + ((static_cast<int64_t>(seq) * n_tokens + (pc - p_begin)) * n_kv_heads + head) * kD;
+    x0[r] = src[lane];
+    x1[r] = src[lane + 64];
+  }
+  RowCodes rc[8];
+  encode_rows<CODEC, 8>(x0, x1, lane, signs, rc);
+  store_group<CODEC, SIDE>(codes, scales, norms, g_first_row, rc, live, lane, rowbuf);
+}
+
 template <int CODEC, int SIDE>
 __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a) {
   const int tid = threadIdx.x;
@@ -237,35 +272,51 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(AppendArgs a)
   // used, they were waited for one after another)
   __asm__ volatile("" ::"s"(p_begin), "s"(a.n_tokens), "s"(a.n_kv_heads), "s"(a.capacity), "s"(a.src), "s"(a.codes),
                    "s"(a.scales), "s"(a.norms), "s"(a.signs[0]), "s"(a.signs[1]), "s"(a.signs[2]), "s"(a.signs[3]));
-  const int64_t p_end = p_begin + a.n_tokens;
   const int64_t g = (p_begin >> 3) + static_cast<int64_t>(blockIdx.x) * kAppendWaves + wave;  // 8-row group
-  const int64_t g_first_row = g * 8;
-  if (g_first_row >= p_end) return;  // past this sequence's range (uniform per wave)
-
-  constexpr int RB = row_code_bytes(CODEC);
-  const int64_t ph = static_cast<int64_t>(seq) * a.n_kv_heads + head;
-  uint8_t* codes = static_cast<uint8_t*>(a.codes) + ph * a.capacity * RB;
-  uint16_t* scales = has_scales(CODEC) ? a.scales + ph * a.capacity * 4 : nullptr;
-  uint16_t* norms = has_norms(CODEC) ? a.norms + ph * a.capacity : nullptr;
   const uint32_t signs[4] = {a.signs[0], a.signs[1], a.signs[2], a.signs[3]};
-
   __shared__ uint8_t rowbuf[kAppendWaves][8][256];
+  append_group<CODEC, SIDE>(a.codes, a.scales, a.norms, a.src, a.capacity, signs, p_begin, a.n_tokens, a.n_kv_heads,
+                            seq, head, g, lane, rowbuf[wave]);
+}
 
-  bool live[8];
-  float x0[8], x1[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int64_t p = g_first_row + r;
-    live[r] = p >= p_begin && p < p_end;
-    // rows outside the range read a row inside it (clamped) and are not stored
-    const int64_t pc = p < p_begin ? p_begin : (p >= p_end ? p_end - 1 : p);
-    const float* src = a.src + ((static_cast<int64_t>(seq) * a.n_tokens + (pc - p_begin)) * a.n_kv_heads + head) * kD;
-    x0[r] = src[lane];
-    x1[r] = src[lane + 64];
+// Several planes in one launch: blockIdx.z = plane * n_seqs + sequence, and
+// each workgroup runs the encoder of its plane's codec and side (uniform
+// per workgroup), so the launch's fixed start cost is paid once.
+__global__ __launch_bounds__(64 * kAppendWaves) void append_multi_kernel(AppendMultiArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int head = blockIdx.y;
+  const int pl = static_cast<int>(blockIdx.z) / a.n_seqs;
+  const int seq = static_cast<int>(blockIdx.z) - pl * a.n_seqs;
+  const AppendPlane& P = a.planes[pl];
+  const int64_t p_begin = a.pos0[seq];
+  __asm__ volatile("" ::"s"(p_begin), "s"(a.n_tokens), "s"(a.n_kv_heads), "s"(P.capacity), "s"(P.src), "s"(P.codes),
+                   "s"(P.scales), "s"(P.norms), "s"(P.codec_side), "s"(P.signs[0]), "s"(P.signs[1]),
+                   "s"(P.signs[2]), "s"(P.signs[3]));  // one round trip, as in append_kernel
+  const int64_t g = (p_begin >> 3) + static_cast<int64_t>(blockIdx.x) * kAppendWaves + wave;
+  const uint32_t signs[4] = {P.signs[0], P.signs[1], P.signs[2], P.signs[3]};
+  __shared__ uint8_t rowbuf[kAppendWaves][8][256];
+#define VIT_APPEND_GROUP(C, S)                                                                                    \
+  case (C)*2 + (S):                                                                                               \
+    append_group<C, S>(P.codes, P.scales, P.norms, P.src, P.capacity, signs, p_begin, a.n_tokens, a.n_kv_heads,  \
+                       seq, head, g, lane, rowbuf[wave]);                                                         \
+    break;
+  switch (P.codec_side) {
+    VIT_APPEND_GROUP(F16, 0)
+    VIT_APPEND_GROUP(F16, 1)
+    VIT_APPEND_GROUP(Q8_0, 0)
+    VIT_APPEND_GROUP(Q8_0, 1)
+    VIT_APPEND_GROUP(Q4_0, 0)
+    VIT_APPEND_GROUP(Q4_0, 1)
+    VIT_APPEND_GROUP(ROT4, 0)
+    VIT_APPEND_GROUP(ROT4, 1)
+    VIT_APPEND_GROUP(ROT3, 0)
+    VIT_APPEND_GROUP(ROT3, 1)
+    default:
+      break;
   }
-  RowCodes rc[8];
-  encode_rows<CODEC, 8>(x0, x1, lane, signs, rc);
-  store_group<CODEC, SIDE>(codes, scales, norms, g_first_row, rc, live, lane, rowbuf[wave]);
+#undef VIT_APPEND_GROUP
 }
 
 // Re-encode (a VBR degrade step): one workgroup per 32-row tile of one
@@ -375,6 +426,11 @@ hipError_t launch_append(int codec, int side, dim3 grid, hipStream_t stream, con
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_multi(dim3 grid, hipStream_t stream, const AppendMultiArgs& args, const KernelEvents& ev) {
+  hipExtLaunchKernelGGL(append_multi_kernel, grid, dim3(64 * kAppendWaves), 0, stream, ev.start, ev.stop, 0, args);
   return hipGetLastError();
 }
 

@@ -47,6 +47,22 @@ void load_signs(const vit_kv_plane* p, uint32_t out[4]) {
   }
 }
 
+// True when an array of plane a shares a byte with an array of plane b.
+bool planes_overlap(const vit_kv_plane* a, const vit_kv_plane* b) {
+  const void* ap[3] = {a->codes, a->scales, a->norms};
+  const void* bp[3] = {b->codes, b->scales, b->norms};
+  size_t ab[3], bb[3];
+  vit_kv_plane_sizes(a->codec, a->n_seqs, a->n_kv_heads, VIT_HEAD_DIM, a->capacity, &ab[0], &ab[1], &ab[2]);
+  vit_kv_plane_sizes(b->codec, b->n_seqs, b->n_kv_heads, VIT_HEAD_DIM, b->capacity, &bb[0], &bb[1], &bb[2]);
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) {
+      if (!ap[i] || !bp[j] || ab[i] == 0 || bb[j] == 0) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(ap[i]), b0 = reinterpret_cast<uintptr_t>(bp[j]);
+      if (a0 < b0 + bb[j] && b0 < a0 + ab[i]) return true;
+    }
+  return false;
+}
+
 size_t ws_o_bytes(int32_t s, int32_t hq, int32_t ns) {
   const size_t b = static_cast<size_t>(s) * hq * ns * VIT_HEAD_DIM * sizeof(float);
   return (b + 255) & ~size_t{255};
@@ -225,6 +241,55 @@ int vit_kv_append_quant(const vit_kv_plane* dst, const float* src, const int64_t
   return enqueue_append(dst, src, pos0, n_tokens, static_cast<hipStream_t>(stream), ev);
 }
 
+int vit_kv_append_quant_multi(const vit_kv_plane* planes, int32_t n_planes, const float* const* src,
+                              const int64_t* pos0, int32_t n_tokens, void* stream) {
+  const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
+  g_armed = vit::KernelEvents{};
+  if (!planes || !src || !pos0) return VIT_E_ARG;
+  if (n_planes < 1 || n_planes > VIT_MAX_APPEND_PLANES) return VIT_E_UNSUPPORTED;
+  if (n_tokens < 0) return VIT_E_ARG;
+  for (int i = 0; i < n_planes; ++i) {
+    const vit_kv_plane* p = &planes[i];
+    const int st = check_plane(p);
+    if (st != VIT_OK) return st;
+    if (p->n_seqs != planes[0].n_seqs || p->n_kv_heads != planes[0].n_kv_heads) return VIT_E_ARG;
+    for (int j = 0; j < i; ++j)
+      if (planes_overlap(&planes[j], p)) return VIT_E_ARG;  // every plane's arrays disjoint from the others
+    if (n_tokens > 0) {
+      if (!src[i]) return VIT_E_ARG;
+      if (!aligned(src[i], 16)) return VIT_E_ALIGN;
+    }
+    for (int s = 0; s < p->n_seqs; ++s)
+      if (pos0[s] < 0 || pos0[s] + n_tokens > p->capacity) return VIT_E_CAPACITY;
+  }
+  if (n_tokens == 0) return VIT_OK;
+  vit::AppendMultiArgs a{};
+  const int32_t S = planes[0].n_seqs;
+  for (int i = 0; i < n_planes; ++i) {
+    vit::AppendPlane& d = a.planes[i];
+    d.codes = planes[i].codes;
+    d.scales = planes[i].scales;
+    d.norms = planes[i].norms;
+    d.src = src[i];
+    d.capacity = planes[i].capacity;
+    d.codec_side = planes[i].codec * 2 + planes[i].side;
+    load_signs(&planes[i], d.signs);
+  }
+  a.n_kv_heads = planes[0].n_kv_heads;
+  a.n_tokens = n_tokens;
+  a.n_seqs = S;
+  a.n_planes = n_planes;
+  int64_t groups = 0;
+  for (int s = 0; s < S; ++s) {
+    a.pos0[s] = pos0[s];
+    const int64_t g = ((pos0[s] + n_tokens - 1) >> 3) - (pos0[s] >> 3) + 1;
+    if (g > groups) groups = g;
+  }
+  const dim3 grid(static_cast<unsigned>((groups + vit::kAppendWaves - 1) / vit::kAppendWaves),
+                  static_cast<unsigned>(a.n_kv_heads), static_cast<unsigned>(S * n_planes));
+  return vit::launch_append_multi(grid, static_cast<hipStream_t>(stream), a, ev) == hipSuccess ? VIT_OK : VIT_E_HIP;
+}
+
 int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int64_t* n_rows, void* stream) {
   const vit::KernelEvents ev = g_armed;  // one-shot: consumed by this call whatever its outcome
   g_armed = vit::KernelEvents{};
@@ -242,18 +307,7 @@ int vit_kv_transcode(const vit_kv_plane* src, const vit_kv_plane* dst, const int
                     (src->codec == VIT_CODEC_Q8_0 && (dst->codec == VIT_CODEC_Q4_0 || is_rotated(dst->codec))) ||
                     (src->codec == VIT_CODEC_Q4_0 && dst->codec == VIT_CODEC_ROT3);
   if (!step) return VIT_E_UNSUPPORTED;
-  // the two planes' arrays must be disjoint
-  const void* sp[3] = {src->codes, src->scales, src->norms};
-  const void* dp[3] = {dst->codes, dst->scales, dst->norms};
-  size_t sb[3], db[3];
-  vit_kv_plane_sizes(src->codec, src->n_seqs, src->n_kv_heads, VIT_HEAD_DIM, src->capacity, &sb[0], &sb[1], &sb[2]);
-  vit_kv_plane_sizes(dst->codec, dst->n_seqs, dst->n_kv_heads, VIT_HEAD_DIM, dst->capacity, &db[0], &db[1], &db[2]);
-  for (int i = 0; i < 3; ++i)
-    for (int j = 0; j < 3; ++j) {
-      if (!sp[i] || !dp[j] || sb[i] == 0 || db[j] == 0) continue;
-      const uintptr_t a0 = reinterpret_cast<uintptr_t>(sp[i]), b0 = reinterpret_cast<uintptr_t>(dp[j]);
-      if (a0 < b0 + db[j] && b0 < a0 + sb[i]) return VIT_E_ARG;
-    }
+  if (planes_overlap(src, dst)) return VIT_E_ARG;  // the two planes' arrays must be disjoint
   int64_t max_rows = 0;
   for (int s = 0; s < src->n_seqs; ++s) {
     if (n_rows[s] < 0 || n_rows[s] > src->capacity) return VIT_E_CAPACITY;

@@ -25,6 +25,28 @@ struct AppendArgs {
   int64_t pos0[kMaxSeqs];
 };
 
+// Several planes of one geometry appended in one launch (the same token
+// range of each plane's own fp32 rows); each workgroup handles one plane.
+constexpr int kMaxAppendPlanes = 32;
+struct AppendPlane {
+  void* codes;
+  uint16_t* scales;
+  uint16_t* norms;
+  const float* src;   // [S][n_tokens][Hkv][128]
+  int64_t capacity;
+  int32_t codec_side;  // codec * 2 + side
+  int32_t reserved;
+  uint32_t signs[4];
+};
+struct AppendMultiArgs {
+  AppendPlane planes[kMaxAppendPlanes];
+  int64_t pos0[kMaxSeqs];
+  int32_t n_kv_heads;
+  int32_t n_tokens;
+  int32_t n_seqs;
+  int32_t n_planes;
+};
+
 // Re-encoding the rows a plane holds into a plane of another codec (same
 // geometry and side).
 struct TranscodeArgs {
@@ -144,6 +166,7 @@ hipError_t launch_decode_k2(int vc, int nt, dim3 grid, hipStream_t stream, const
 hipError_t launch_decode_k3(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_decode_k4(int vc, int nt, dim3 grid, hipStream_t stream, const DecodeArgs& args, const KernelEvents& ev);
 hipError_t launch_reduce(dim3 grid, hipStream_t stream, const ReduceArgs& args);
+hipError_t launch_append_multi(dim3 grid, hipStream_t stream, const AppendMultiArgs& args, const KernelEvents& ev);
 hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, hipStream_t stream,
                               const KernelEvents& ev);
 // both probe kernels (logits over grid (n_chunks, Hkv, S), then the mass);

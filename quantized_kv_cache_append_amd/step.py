@@ -1,5 +1,5 @@
-"""The multi-layer decode step: per layer, append a ubatch of new K/V rows,
-then decode and merge, with the appends overlapped with the decodes.
+"""The multi-layer decode step: append a ubatch of new K/V rows to every
+layer's planes, then decode and merge through every layer.
 
 This is the step of the per-(layer, side) codec ladder: every layer's K and
 V tensors have their own codec (buun-llama-cpp page, "VBR -- Variable
@@ -9,18 +9,25 @@ Bit-Rate KV Cache"), each step appends a ubatch of new rows to every
 256-aligned 200,704-row slots ("CTX_SIZE 540672 -> 401408" commit) -- and
 then decodes one token per sequence through every layer.
 
-Schedule.  The appends go to a second stream.  Decode l waits on an event
-recorded after layer l's two appends, so the later layers' appends run while
-the first layers decode.  Each step's appends wait on an event recorded on
-the decode stream when the step starts, because they rewrite rows that the
-previous step's decodes read.  (Valid when all of a step's inputs are known
-up front; in a model's forward pass layer l + 1's rows depend on layer l.)
+Schedules.  "batched" (the default): one vit_kv_append_quant_multi launch
+stores the ubatch in all 2 x layers planes, then the decodes run back to
+back on the same stream.  "overlapped": the per-plane appends go to a second
+stream and decode l waits on an event recorded after layer l's two appends,
+so the later layers' appends run while the first layers decode; each step's
+appends wait on an event recorded on the decode stream when the step
+starts, because they rewrite rows that the previous step's decodes read.
+(Overlap is valid when all of a step's inputs are known up front; in a
+model's forward pass layer l + 1's rows depend on layer l.)  A decode fills
+every compute unit's registers, so the overlapped appends run only in the
+decodes' tails, and decodes then wait for them; the batched launch is
+faster.
 
 Everything here is argument marshalling and stream ordering: every
 operation of the step is a call into libvit.so.
 """
 
-from . import merge_fits, prepare_append, prepare_decode, prepare_merged, prepare_reduce, vit_arm_kernel_events
+from . import (merge_fits, prepare_append, prepare_append_multi, prepare_decode, prepare_merged, prepare_reduce,
+               vit_arm_kernel_events)
 
 HEAD_DIM = 128
 
@@ -39,16 +46,25 @@ class DecodeStep:
     counters    zeroed arrival counters (merge_counters): each layer's decode
                 and split merge then run as one vit_attn_decode_merged launch
                 when the shape allows; otherwise (or None) decode + reduce
-    stream, append_stream   torch streams (default priority)
+    stream, append_stream   torch streams (default priority); append_stream
+                is used by the "overlapped" schedule only
+    append_mode "batched" or "overlapped" (see the module docstring)
     """
 
     def __init__(self, layers, q, new_rows, out, lens, p_new, n_q_heads, n_splits, workspace, stream,
-                 append_stream, counters=None):
+                 append_stream, counters=None, append_mode="batched"):
         import torch
 
+        if append_mode not in ("batched", "overlapped"):
+            raise ValueError(f"append_mode {append_mode!r}")
+        self.append_mode = append_mode
         self.stream, self.append_stream = stream, append_stream
         S = layers[0][0].n_seqs
         self.n_layers = len(layers)
+        planes = [P for kv in layers for P in kv]
+        srcs = [x for kv in new_rows for x in kv]
+        self.append_all = (prepare_append_multi(planes, srcs, [p_new] * S, stream=stream)
+                           if append_mode == "batched" else None)
         self.merged = (counters is not None and n_splits > 1
                        and merge_fits(n_q_heads, layers[0][0].n_kv_heads, 1, n_splits))
         self.appends, self.decodes = [], []
@@ -71,6 +87,15 @@ class DecodeStep:
     def __call__(self, kernel_events=None):
         """Issue one step.  ``kernel_events`` = (starts, stops), one pair per
         layer, armed so that each decode dispatch records its own pair."""
+        if self.append_mode == "batched":
+            self.append_all()
+            for li, (d, r) in enumerate(self.decodes):
+                if kernel_events is not None:
+                    vit_arm_kernel_events(kernel_events[0][li], kernel_events[1][li])
+                d()
+                if r is not None:
+                    r()
+            return
         self.fork.record(self.stream)  # everything issued on the decode stream before this step
         self.append_stream.wait_event(self.fork)
         for li, (ck, cv) in enumerate(self.appends):
@@ -91,7 +116,7 @@ class DecodeStep:
         import torch
 
         torch.cuda.synchronize()
-        for ck, cv in self.appends:
+        for ck, cv in self.appends:  # the per-plane appends, one after another
             ck()
             cv()
         torch.cuda.synchronize()

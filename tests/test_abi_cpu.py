@@ -115,6 +115,49 @@ def test_append_validation(lib):
     assert _append(lib, _plane(cap=(1 << 30) + 256)) == _lib.VIT_E_UNSUPPORTED
 
 
+def _append_multi(lib, planes, srcs=None, pos0=(0, 0), n=1, n_planes=None):
+    arr = (_lib.VitKvPlane * len(planes))(*planes)
+    srcs = [FAKE] * len(planes) if srcs is None else srcs
+    ptrs = (ctypes.c_void_p * len(srcs))(*srcs)
+    p0 = (ctypes.c_int64 * len(pos0))(*pos0)
+    return lib.vit_kv_append_quant_multi(arr, len(planes) if n_planes is None else n_planes, ptrs, p0, n, None)
+
+
+def test_append_multi_validation(lib):
+    """Every plane is checked as vit_kv_append_quant checks it, then the
+    batch: equal geometry, pairwise disjoint arrays, 1..32 planes (no compute:
+    every case fails or has no rows)."""
+    MB = 0x100000
+
+    def pl(i, **kw):  # plane i: q8_0 K, arrays in their own 1 MiB windows
+        return _plane(codes=(2 * i + 16) * MB, scales=(2 * i + 17) * MB, norms=None, **kw)
+
+    two = [pl(0), pl(1, side=1)]
+    assert _append_multi(lib, two, n=0) == _lib.VIT_OK  # no-op, nothing enqueued
+    assert _append_multi(lib, two, n=-1) == _lib.VIT_E_ARG
+    assert _append_multi(lib, two, pos0=(500, 0), n=13) == _lib.VIT_E_CAPACITY
+    assert _append_multi(lib, two, pos0=(-1, 0)) == _lib.VIT_E_CAPACITY
+    assert _append_multi(lib, two, n_planes=0) == _lib.VIT_E_UNSUPPORTED
+    assert _lib.MAX_APPEND_PLANES == 32
+    many = [pl(i) for i in range(33)]
+    assert _append_multi(lib, many, n=0, n_planes=33) == _lib.VIT_E_UNSUPPORTED
+    assert _append_multi(lib, many[:32], n=0) == _lib.VIT_OK
+    assert _append_multi(lib, [pl(0), pl(1, H=4)]) == _lib.VIT_E_ARG                   # geometry
+    assert _append_multi(lib, [pl(0), pl(1, S=3)], pos0=(0, 0, 0)) == _lib.VIT_E_ARG   # geometry
+    assert _append_multi(lib, [pl(0), pl(1, codec=9)]) == _lib.VIT_E_UNSUPPORTED        # a bad plane
+    assert _append_multi(lib, [pl(0), pl(1, codec=3)]) == _lib.VIT_E_ARG               # rotated, no signs
+    assert _append_multi(lib, two, srcs=[FAKE, None]) == _lib.VIT_E_ARG
+    assert _append_multi(lib, two, srcs=[FAKE, FAKE + 4]) == _lib.VIT_E_ALIGN
+    assert _append_multi(lib, two, srcs=[FAKE, None], n=0) == _lib.VIT_OK             # no rows, no sources
+    # arrays of two planes that overlap: the same codes, codes inside another
+    # plane's scales, scales inside another plane's codes
+    assert _append_multi(lib, [pl(0), pl(0, side=1)]) == _lib.VIT_E_ARG
+    assert _append_multi(lib, [pl(0), _plane(codes=17 * MB + 0x100, scales=40 * MB, norms=None)]) == _lib.VIT_E_ARG
+    assert _append_multi(lib, [pl(0), _plane(codes=40 * MB, scales=16 * MB + 0x1000, norms=None)]) == _lib.VIT_E_ARG
+    # adjacent arrays do not overlap (q8_0 codes of 2 x 2 x 512 rows: 256 KiB)
+    assert _append_multi(lib, [pl(0), _plane(codes=16 * MB + 0x40000, scales=40 * MB, norms=None)], n=0) == _lib.VIT_OK
+
+
 def _decode(lib, k, v, hq=4, seq_len=(10, 10), k_new=None, v_new=None, scale=0.088, ns=1, ws=None, q=FAKE, out=FAKE):
     arr = (ctypes.c_int64 * len(seq_len))(*seq_len)
     return lib.vit_attn_decode(ctypes.byref(k), ctypes.byref(v), q, hq, arr, k_new, v_new, scale, ns, ws, out, None)

@@ -5,20 +5,27 @@ balanced map (8 each of f16, q8_0, q4_0, rot4; 10 distinct (K, V) pairs),
 2 sequences x 8 KV heads x 200,704-row slots, Hq 32.  One step through the
 step driver (quantized_kv_cache_append_amd.step.DecodeStep) on planes that
 were poisoned and then pre-filled with rows 0 .. 198,655: the 2048-row
-ubatch (rows 198,656 .. 200,703) is appended to all 32 planes on a second
-stream while the decodes run, decode l waiting only for layer l's appends;
-each layer's decode and split merge is one vit_attn_decode_merged launch.
+ubatch (rows 198,656 .. 200,703) is appended to all 32 planes by one
+vit_kv_append_quant_multi launch, then the 16 decodes run; each layer's
+decode and split merge is one vit_attn_decode_merged launch.
 
-The rows a decode would read before its layer's appends finished are still
-poison (NaN fp16 scales, all-ones codes), so a wrong schedule shows up as a
-wrong output.  Each layer has its own sampled (sequence, KV head) unit --
+The rows a decode would read before the append finished are still poison
+(NaN fp16 scales, all-ones codes), so a wrong order shows up as a wrong
+output.  Each layer has its own sampled (sequence, KV head) unit --
 16 distinct units -- whose rows and queries come from ``synth``; the other
 units get seeded device normals.  Per layer: the stored ubatch rows of the
 unit are bit-exact against the oracle's encoders, and the decode output of
 its 4 query heads is within 2e-3 x RMS of the oracle's fp64 attention over
-all 200,704 rows, and every output equals a serial replay of the same calls
-(all appends, then all decodes) bit for bit.  Same split count and launch
-configuration as bench.py.
+all 200,704 rows, and every output equals a serial replay with per-plane
+appends (vit_kv_append_quant, then all decodes) bit for bit.  Same split
+count and launch configuration as bench.py.
+
+The step driver's other schedule, per-plane appends on a second stream
+overlapped with the decodes (decode l waiting only for layer l's appends),
+is then checked the same way on a ubatch scaled by 8 in place: a decode
+that ran before its layer's appends would read the unscaled rows, whose
+logits differ by O(1), so the overlapped step must equal its serial replay
+bit for bit.
 """
 
 import math
@@ -84,14 +91,16 @@ def ladder_step():
     step = DecodeStep(layers, q_dev, new_rows, out, [L] * S, pre, Hq, n_splits, ws, stream, astream,
                       counters=counters)
     assert step.merged, "the ladder's decodes run as one merged launch each, as bench.py runs them"
-    say(f"[ladder step] one overlapped step, {n_splits} splits, decode and merge in one launch")
+    assert step.append_mode == "batched"
+    say(f"[ladder step] one step (one multi-plane append), {n_splits} splits, decode and merge in one launch")
     with torch.cuda.stream(stream):
         step()
     torch.cuda.synchronize()
     outs = [o.cpu().numpy() for o in out]
-    # the same calls with no overlap (every append, then every decode): the
-    # decode's summation order is fixed, so the outputs must match bitwise
-    say("[ladder step] serial replay of the same calls")
+    # per-plane appends, then every decode, each call finished before the
+    # next: the decode's summation order is fixed, so the outputs must match
+    # bitwise
+    say("[ladder step] serial replay with per-plane appends")
     for o in out:
         o.fill_(float("nan"))
     step.run_serial()
@@ -106,9 +115,28 @@ def ladder_step():
             sv[side] = {key: a[pre:pre + ub] for key, a in view.items()}
         stored.append(sv)
     assert int(counters.abs().sum()) == 0, "arrival counters not back at zero"
-    res = dict(outs=outs, serial=serial, q=q_host, rows=rows, stored=stored, cmap=cmap, n_splits=n_splits, G=Hq // H, pre=pre,
-               ub=ub, L=L)
-    del layers, step, new_rows, out, ws
+    # the overlapped schedule, on the ubatch scaled by 8
+    for kv in new_rows:
+        for x in kv:
+            x.mul_(8.0)
+    torch.cuda.synchronize()
+    ostep = DecodeStep(layers, q_dev, new_rows, out, [L] * S, pre, Hq, n_splits, ws, stream, astream,
+                       counters=counters, append_mode="overlapped")
+    say("[ladder step] one overlapped step (appends on a second stream), ubatch x 8")
+    for o in out:
+        o.fill_(float("nan"))
+    with torch.cuda.stream(stream):
+        ostep()
+    torch.cuda.synchronize()
+    o_outs = [o.cpu().numpy() for o in out]
+    for o in out:
+        o.fill_(float("nan"))
+    ostep.run_serial()
+    o_serial = [o.cpu().numpy() for o in out]
+    assert int(counters.abs().sum()) == 0, "arrival counters not back at zero"
+    res = dict(outs=outs, serial=serial, o_outs=o_outs, o_serial=o_serial, q=q_host, rows=rows, stored=stored,
+               cmap=cmap, n_splits=n_splits, G=Hq // H, pre=pre, ub=ub, L=L)
+    del layers, step, ostep, new_rows, out, ws
     torch.cuda.empty_cache()
     return res
 
@@ -133,7 +161,7 @@ def test_ladder_step_layer(ladder_step, layer):
     ks = synth.sign_mask(CFG, layer, "k") if kc in ("rot4", "rot3") else None
     vs = synth.sign_mask(CFG, layer, "v") if vc in ("rot4", "rot3") else None
     kr, vr = r["rows"][(layer, "k")], r["rows"][(layer, "v")]
-    # the ubatch rows as stored by the overlapped appends
+    # the ubatch rows as stored by the multi-plane append
     for side, codec, x, sg in (("k", kc, kr, ks), ("v", vc, vr, vs)):
         want = codecs.quantize(codec, x[pre:pre + ub], sg)
         got = r["stored"][layer][side]
@@ -143,6 +171,11 @@ def test_ladder_step_layer(ladder_step, layer):
     ref = ref_unit(r["q"][layer][s, h * G:(h + 1) * G], kr, vr, kc, vc, 1.0 / math.sqrt(D), ks, vs)
     check_close(r["outs"][layer][s, h * G:(h + 1) * G], ref, f"ladder layer {layer} ({kc},{vc}) unit ({s},{h}) L={L}")
     # every output of the step is finite (no unit read poison), and the
-    # overlapped step equals its serial replay bit for bit
+    # step equals its serial replay bit for bit
     assert np.isfinite(r["outs"][layer]).all()
-    assert np.array_equal(r["outs"][layer], r["serial"][layer]), f"layer {layer}: overlapped != serial"
+    assert np.array_equal(r["outs"][layer], r["serial"][layer]), f"layer {layer}: step != serial replay"
+    # the overlapped schedule: equal to its serial replay, and not the
+    # first step's output (its ubatch was scaled)
+    assert np.isfinite(r["o_outs"][layer]).all()
+    assert np.array_equal(r["o_outs"][layer], r["o_serial"][layer]), f"layer {layer}: overlapped != serial"
+    assert not np.array_equal(r["o_outs"][layer], r["outs"][layer])
