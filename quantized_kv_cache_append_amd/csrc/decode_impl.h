@@ -1241,6 +1241,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   // prefetch to be issued (each 1 KB load takes the vector memory unit ~16
   // cycles: 8 waves x 2 tiles are ~1.2 us of issue)
   load_slot(ta, wave);
+  // f16 keys at 8 query rows: the second tile now too (issued later, it is
+  // live across the query operand build and the kernel spills)
+  constexpr bool kSecondEarly = KC == F16 && NT == 2;
+  if constexpr (kSecondEarly) load_slot(tb, wave + kDecodeWaves);
 
   if constexpr (kRot4) fill_rot4_lut<kThreads>(lut, tid, lv);
   if constexpr (kRot3) fill_rot3_lut<kThreads>(lut3, tid, lv3);
@@ -1262,7 +1266,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_
   __syncthreads();
   // (rotated keys: after the query rotation, whose barriers would otherwise
   // wait for every wave's issue of it)
-  if constexpr (!rotated(KC)) load_slot(tb, wave + kDecodeWaves);
+  if constexpr (!rotated(KC) && !kSecondEarly) load_slot(tb, wave + kDecodeWaves);
   float qs = a.qscale;
   if constexpr (rotated(KC)) {
     // rotate the query rows like the keys (WHT); the keys reconstruct as

@@ -453,3 +453,24 @@ def test_scales_layout_roundtrip(side):
     rng = np.random.default_rng(4)
     s = rng.integers(0, 65536, (2, 3, 256, 4)).astype(np.uint16)
     assert np.array_equal(layout.unpack_scales(side, layout.pack_scales(side, s), 2, 3, 256), s)
+
+
+def test_no_kernel_spills_to_scratch():
+    """The build records the compiler's resource usage per kernel: no kernel
+    may use scratch memory (register spills cost the decode its stream
+    rate), and every decode instantiation must fit two 8-wave workgroups'
+    worth of waves per SIMD, the occupancy its launch is planned for."""
+    import json
+    import os
+
+    from quantized_kv_cache_append_amd import build
+
+    if not os.path.exists(build.RESOURCES):
+        pytest.skip("library not built here")
+    res = json.load(open(build.RESOURCES))
+    spilled = {k: v["scratch"] for k, v in res.items() if v.get("scratch", 0) or v.get("vgpr_spill", 0)}
+    assert not spilled, f"kernels with scratch: {spilled}"
+    decode = {k: v for k, v in res.items() if "decode_kernel" in k}
+    assert len(decode) == 75, "5 K codecs x 5 V codecs x 3 row layouts"
+    assert all(v["waves_per_simd"] >= 2 for v in decode.values())
+
