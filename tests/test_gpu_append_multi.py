@@ -4,7 +4,7 @@ a plane of the same codec and side from the same rows (compared array by
 array, bit for bit, poisoned rows included), and the oracle's codes, scales
 and norms for the appended rows.  Covers all ten (codec, side) pairs in one
 call, ragged and misaligned positions, a single row, the 32-plane limit,
-and a call with no rows."""
+a call with no rows, and kernel events armed on the call."""
 
 import numpy as np
 import pytest
@@ -115,3 +115,31 @@ def test_append_multi_no_rows_writes_nothing():
     torch.cuda.synchronize()
     for multi, single in pairs:  # both still poisoned
         _same_arrays(multi, single, "no rows")
+
+
+@pytest.mark.gpu
+def test_append_multi_kernel_events():
+    """Armed kernel events bracket the multi-plane append's one kernel, the
+    arming is consumed by the call, and the planes equal an unarmed call's."""
+    torch = torch_cuda()
+    import quantized_kv_cache_append_amd as vit
+
+    say("[append-multi] kernel events")
+    rng = np.random.default_rng(23)
+    pairs = _pairs(rng, 2, 2, 512, [("q8_0", "k"), ("rot4", "v"), ("f16", "v")])
+    srcs = [torch.from_numpy(_rows(rng, (2, 200, 2, D))).cuda() for _ in pairs]
+    vit.vit_kv_append_quant_multi([s for _, s in pairs], srcs, [7, 300])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    vit.vit_arm_kernel_events(e0, e1)
+    vit.vit_kv_append_quant_multi([m for m, _ in pairs], srcs, [7, 300])
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0, ms
+    for multi, single in pairs:
+        _same_arrays(multi, single, "armed call")
+    vit.vit_kv_append_quant_multi([m for m, _ in pairs], srcs, [7, 300])
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
