@@ -10,8 +10,8 @@ Bit-Rate KV Cache"), each step appends a ubatch of new rows to every
 then decodes one token per sequence through every layer.
 
 Schedules.  "batched" (the default): one vit_kv_append_quant_multi launch
-stores the ubatch in all 2 x layers planes, then the decodes run back to
-back on the same stream.  "overlapped": the per-plane appends go to a second
+per 32 planes (16 layers' K and V) stores the ubatch in all 2 x layers
+planes, then the decodes run back to back on the same stream.  "overlapped": the per-plane appends go to a second
 stream and decode l waits on an event recorded after layer l's two appends,
 so the later layers' appends run while the first layers decode; each step's
 appends wait on an event recorded on the decode stream when the step
@@ -26,8 +26,8 @@ Everything here is argument marshalling and stream ordering: every
 operation of the step is a call into libvit.so.
 """
 
-from . import (merge_fits, prepare_append, prepare_append_multi, prepare_decode, prepare_merged, prepare_reduce,
-               vit_arm_kernel_events)
+from . import (MAX_APPEND_PLANES, merge_fits, prepare_append, prepare_append_multi, prepare_decode, prepare_merged,
+               prepare_reduce, vit_arm_kernel_events)
 
 HEAD_DIM = 128
 
@@ -63,8 +63,11 @@ class DecodeStep:
         self.n_layers = len(layers)
         planes = [P for kv in layers for P in kv]
         srcs = [x for kv in new_rows for x in kv]
-        self.append_all = (prepare_append_multi(planes, srcs, [p_new] * S, stream=stream)
-                           if append_mode == "batched" else None)
+        # one multi-plane call per MAX_APPEND_PLANES planes (16 layers' K and V)
+        self.append_all = ([prepare_append_multi(planes[i:i + MAX_APPEND_PLANES], srcs[i:i + MAX_APPEND_PLANES],
+                                                 [p_new] * S, stream=stream)
+                            for i in range(0, len(planes), MAX_APPEND_PLANES)]
+                           if append_mode == "batched" else [])
         self.merged = (counters is not None and n_splits > 1
                        and merge_fits(n_q_heads, layers[0][0].n_kv_heads, 1, n_splits))
         self.appends, self.decodes = [], []
@@ -88,7 +91,8 @@ class DecodeStep:
         """Issue one step.  ``kernel_events`` = (starts, stops), one pair per
         layer, armed so that each decode dispatch records its own pair."""
         if self.append_mode == "batched":
-            self.append_all()
+            for c in self.append_all:
+                c()
             for li, (d, r) in enumerate(self.decodes):
                 if kernel_events is not None:
                     vit_arm_kernel_events(kernel_events[0][li], kernel_events[1][li])
