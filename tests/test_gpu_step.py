@@ -1,7 +1,8 @@
 """GPU checks of the step driver (quantized_kv_cache_append_amd.step.DecodeStep)
 at a small shape with more layers than one multi-plane append call takes:
 20 layers, so 40 planes go out as two vit_kv_append_quant_multi calls (32 +
-8).  For both schedules the step's outputs equal a serial replay with
+8).  For both schedules, with the split merge in the decode launch and as
+a separate reduce launch, the step's outputs equal a serial replay with
 per-plane appends bit for bit, every plane holds the oracle's encoding of
 its ubatch rows, and every layer's output is within 2e-3 x RMS of the
 oracle's attention over all its rows."""
@@ -18,8 +19,9 @@ CODECS = ["f16", "q8_0", "q4_0", "rot4", "rot3"]
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("merged", [True, False])
 @pytest.mark.parametrize("mode", ["batched", "overlapped"])
-def test_step_more_layers_than_one_append_call(mode):
+def test_step_more_layers_than_one_append_call(mode, merged):
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
     from quantized_kv_cache_append_amd.step import DecodeStep
@@ -48,13 +50,13 @@ def test_step_more_layers_than_one_append_call(mode):
     n_splits = 4
     ws = torch.empty(vit.vit_attn_workspace_bytes(S, Hq, D, n_splits), dtype=torch.uint8, device="cuda")
     stream, astream = torch.cuda.Stream(), torch.cuda.Stream()
-    counters = vit.merge_counters(layers[0][0])
+    counters = vit.merge_counters(layers[0][0]) if merged else None
     step = DecodeStep(layers, q_dev, new_rows, out, [L] * S, pre, Hq, n_splits, ws, stream, astream,
                       counters=counters, append_mode=mode)
-    assert step.merged
+    assert step.merged == merged  # without counters: decode + reduce launches
     if mode == "batched":
         assert len(step.append_all) == 2
-    say(f"[step] {mode}: {n_layers} layers, {2 * n_layers} planes, ubatch {T} rows at {pre}")
+    say(f"[step] {mode}, merged={merged}: {n_layers} layers, {2 * n_layers} planes, ubatch {T} rows at {pre}")
     with torch.cuda.stream(stream):
         step()
     torch.cuda.synchronize()
@@ -63,7 +65,8 @@ def test_step_more_layers_than_one_append_call(mode):
         o.fill_(float("nan"))
     step.run_serial()
     serial = [o.cpu().numpy() for o in out]
-    assert int(counters.abs().sum()) == 0
+    if merged:
+        assert int(counters.abs().sum()) == 0
     for li, ((K, V), (kc, vc, ks, vs, kx, vx, q)) in enumerate(zip(layers, host)):
         assert np.array_equal(got[li], serial[li]), f"layer {li}: step != serial replay"
         for P, x in ((K, kx), (V, vx)):
