@@ -16,11 +16,13 @@ stream and decode l waits on an event recorded after layer l's two appends,
 so the later layers' appends run while the first layers decode; each step's
 appends wait on an event recorded on the decode stream when the step
 starts, because they rewrite rows that the previous step's decodes read.
-(Overlap is valid when all of a step's inputs are known up front; in a
-model's forward pass layer l + 1's rows depend on layer l.)  A decode fills
-every compute unit's registers, so the overlapped appends run only in the
-decodes' tails, and decodes then wait for them; the batched launch is
-faster.
+Both schedules need every layer's new rows when the step starts, which is
+how this workload is defined (all appends, then all decodes).  In a model's
+forward pass layer l + 1's rows depend on layer l, so there each layer's K
+and V would be appended (one vit_kv_append_quant_multi call for the pair)
+just before that layer's decode.  A decode fills every compute unit's
+registers, so the overlapped appends run only in the decodes' tails, and
+decodes then wait for them; the batched launch is faster.
 
 Everything here is argument marshalling and stream ordering: every
 operation of the step is a call into libvit.so.
