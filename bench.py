@@ -10,8 +10,10 @@ tensors each carry a codec from a seeded map over {f16, q8_0, q4_0, rot4},
 a step appends a 2048-row ubatch to every (layer, side) plane in one
 vit_kv_append_quant_multi launch and then decodes one token per sequence
 through all 16 layers (decode + split-K merge per layer).
-``--overlap-appends`` instead issues per-plane appends on a second stream,
-decode l waiting for layer l's two appends only.  The single-layer workloads (tiny, batched, lowbit,
+``--append-schedule per_layer`` appends each layer's K and V with one
+two-plane launch just before that layer's decode (the order a model's
+forward pass allows); ``overlapped`` issues per-plane appends on a second
+stream, decode l waiting for layer l's two appends only.  The single-layer workloads (tiny, batched, lowbit,
 rotated) are available with --workload: a step there is the fused append of
 the new token's K/V rows, the decode and the merge.  ``--q-len N`` (2 .. 4,
 single-layer workloads) makes each step verify N new tokens per sequence at
@@ -204,12 +206,13 @@ def run_gpu(args):
     stream = torch.cuda.Stream()  # the bench's own stream (default priority): it can be captured
     # The ladder's ubatch appends, scheduled by the step driver
     # (quantized_kv_cache_append_amd.step): by default one launch appends to
-    # all planes before the decodes; with --overlap-appends per-plane appends
-    # go to a second stream (default priority too) and decode l waits only for
-    # layer l's appends, each step's appends waiting for the previous step's
+    # all planes before the decodes; --append-schedule per_layer appends each
+    # layer's pair just before its decode; overlapped puts per-plane appends
+    # on a second stream (default priority too), decode l waiting only for
+    # layer l's appends and each step's appends for the previous step's
     # decodes (they rewrite the rows those read).
     fused = "ubatch" not in cfg
-    append_mode = "overlapped" if args.overlap_appends else "batched"
+    append_mode = args.append_schedule
     astream = None if fused else torch.cuda.Stream()
     # decode and split merge in one launch (vit_attn_decode_merged) where the
     # shape allows it; the arrival counters are zeroed once and every call
@@ -353,9 +356,11 @@ def run_gpu(args):
     achieved = kv_bytes * args.steps / (float(np.sum(dec_ms)) * 1e-3) / 1e9
     return dict(cfg=cfg, wl=wl, cmap=cmap, S=S, Hq=Hq, H=H, L=L, n_layers=n_layers, T=T, QL=QL, mode=mode,
                 merge="in-kernel (vit_attn_decode_merged)" if merged else ("reduce kernel" if n_splits > 1 else "none"),
-                appends=None if fused else (
-                    "one vit_kv_append_quant_multi launch before the decodes" if append_mode == "batched"
-                    else "per-plane vit_kv_append_quant on a second stream, overlapped with the decodes"),
+                appends=None if fused else {
+                    "batched": "one vit_kv_append_quant_multi launch before the decodes",
+                    "per_layer": "one two-plane vit_kv_append_quant_multi launch before each layer's decode",
+                    "overlapped": "per-plane vit_kv_append_quant on a second stream, overlapped with the decodes",
+                }[append_mode],
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
                 block_ms=block_ms,
                 dec_mean_ms=dec_mean_ms,
@@ -1160,9 +1165,10 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="time an attention-probe scoring event (+ eviction choice) on --workload's K plane instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--overlap-appends", action="store_true",
-                    help="ladder: per-plane appends on a second stream, overlapped with the decodes, "
-                    "instead of one multi-plane append launch")
+    ap.add_argument("--append-schedule", default="batched", choices=("batched", "per_layer", "overlapped"),
+                    help="ladder: one multi-plane append launch before the decodes (batched), one two-plane "
+                    "launch before each layer's decode (per_layer), or per-plane appends on a second stream "
+                    "overlapped with the decodes (overlapped)")
     ap.add_argument("--no-merge", action="store_true",
                     help="decode + separate reduce launch even where vit_attn_decode_merged applies")
     ap.add_argument("--graph", action="store_true",

@@ -11,16 +11,17 @@ then decodes one token per sequence through every layer.
 
 Schedules.  "batched" (the default): one vit_kv_append_quant_multi launch
 per 32 planes (16 layers' K and V) stores the ubatch in all 2 x layers
-planes, then the decodes run back to back on the same stream.  "overlapped": the per-plane appends go to a second
+planes, then the decodes run back to back on the same stream.  "per_layer":
+layer l's K and V rows go in with one two-plane call just before layer l's
+decode, on the same stream (the order a model's forward pass allows).  "overlapped": the per-plane appends go to a second
 stream and decode l waits on an event recorded after layer l's two appends,
 so the later layers' appends run while the first layers decode; each step's
 appends wait on an event recorded on the decode stream when the step
 starts, because they rewrite rows that the previous step's decodes read.
-Both schedules need every layer's new rows when the step starts, which is
-how this workload is defined (all appends, then all decodes).  In a model's
-forward pass layer l + 1's rows depend on layer l, so there each layer's K
-and V would be appended (one vit_kv_append_quant_multi call for the pair)
-just before that layer's decode.  A decode fills every compute unit's
+The batched and overlapped schedules need every layer's new rows when the
+step starts, which is how this workload is defined (all appends, then all
+decodes); in a model's forward pass layer l + 1's rows depend on layer l,
+which leaves the per-layer schedule.  A decode fills every compute unit's
 registers, so the overlapped appends run only in the decodes' tails, and
 decodes then wait for them; the batched launch is faster.
 
@@ -50,14 +51,15 @@ class DecodeStep:
                 when the shape allows; otherwise (or None) decode + reduce
     stream, append_stream   torch streams (default priority); append_stream
                 is used by the "overlapped" schedule only
-    append_mode "batched" or "overlapped" (see the module docstring)
+    append_mode "batched", "per_layer" or "overlapped" (see the module
+                docstring)
     """
 
     def __init__(self, layers, q, new_rows, out, lens, p_new, n_q_heads, n_splits, workspace, stream,
                  append_stream, counters=None, append_mode="batched"):
         import torch
 
-        if append_mode not in ("batched", "overlapped"):
+        if append_mode not in ("batched", "per_layer", "overlapped"):
             raise ValueError(f"append_mode {append_mode!r}")
         self.append_mode = append_mode
         self.stream, self.append_stream = stream, append_stream
@@ -70,6 +72,9 @@ class DecodeStep:
                                                  [p_new] * S, stream=stream)
                             for i in range(0, len(planes), MAX_APPEND_PLANES)]
                            if append_mode == "batched" else [])
+        self.layer_appends = ([prepare_append_multi([K, V], [kn, vn], [p_new] * S, stream=stream)
+                               for (K, V), (kn, vn) in zip(layers, new_rows)]
+                              if append_mode == "per_layer" else [])
         self.merged = (counters is not None and n_splits > 1
                        and merge_fits(n_q_heads, layers[0][0].n_kv_heads, 1, n_splits))
         self.appends, self.decodes = [], []
@@ -92,10 +97,12 @@ class DecodeStep:
     def __call__(self, kernel_events=None):
         """Issue one step.  ``kernel_events`` = (starts, stops), one pair per
         layer, armed so that each decode dispatch records its own pair."""
-        if self.append_mode == "batched":
+        if self.append_mode in ("batched", "per_layer"):
             for c in self.append_all:
                 c()
             for li, (d, r) in enumerate(self.decodes):
+                if self.layer_appends:
+                    self.layer_appends[li]()
                 if kernel_events is not None:
                     vit_arm_kernel_events(kernel_events[0][li], kernel_events[1][li])
                 d()

@@ -1,11 +1,11 @@
 """GPU checks of the step driver (quantized_kv_cache_append_amd.step.DecodeStep)
 at a small shape with more layers than one multi-plane append call takes:
 20 layers, so 40 planes go out as two vit_kv_append_quant_multi calls (32 +
-8).  For both schedules, with the split merge in the decode launch and as
-a separate reduce launch, the step's outputs equal a serial replay with
-per-plane appends bit for bit, every plane holds the oracle's encoding of
-its ubatch rows, and every layer's output is within 2e-3 x RMS of the
-oracle's attention over all its rows."""
+8), or as 20 two-plane calls.  For all three schedules, with the split
+merge in the decode launch and as a separate reduce launch, the step's
+outputs equal a serial replay with per-plane appends bit for bit, every
+plane holds the oracle's encoding of its ubatch rows, and every layer's
+output is within 2e-3 x RMS of the oracle's attention over all its rows."""
 
 import math
 
@@ -20,7 +20,7 @@ CODECS = ["f16", "q8_0", "q4_0", "rot4", "rot3"]
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("merged", [True, False])
-@pytest.mark.parametrize("mode", ["batched", "overlapped"])
+@pytest.mark.parametrize("mode", ["batched", "per_layer", "overlapped"])
 def test_step_more_layers_than_one_append_call(mode, merged):
     torch = torch_cuda()
     import quantized_kv_cache_append_amd as vit
@@ -28,7 +28,7 @@ def test_step_more_layers_than_one_append_call(mode, merged):
 
     n_layers, S, H, G, cap, pre, T = 20, 2, 2, 4, 512, 300, 45
     Hq, L = H * G, pre + T
-    rng = np.random.default_rng(2024 + (mode == "overlapped"))
+    rng = np.random.default_rng(2024 + ["batched", "per_layer", "overlapped"].index(mode))
     layers, host, q_dev, new_rows, out = [], [], [], [], []
     for li in range(n_layers):
         kc, vc = CODECS[li % 5], CODECS[(3 * li + 1) % 5]
@@ -56,6 +56,8 @@ def test_step_more_layers_than_one_append_call(mode, merged):
     assert step.merged == merged  # without counters: decode + reduce launches
     if mode == "batched":
         assert len(step.append_all) == 2
+    if mode == "per_layer":
+        assert len(step.layer_appends) == n_layers
     say(f"[step] {mode}, merged={merged}: {n_layers} layers, {2 * n_layers} planes, ubatch {T} rows at {pre}")
     with torch.cuda.stream(stream):
         step()
