@@ -124,8 +124,9 @@ class DecodeStep:
                 r()
 
     def run_serial(self):
-        """The same calls with no overlap: every append, then every decode
-        (the reference schedule the overlapped step must agree with)."""
+        """The same work as one call at a time: every per-plane append, then
+        every decode (the reference each schedule must agree with, bit for
+        bit)."""
         import torch
 
         torch.cuda.synchronize()
