@@ -13,7 +13,9 @@ through all 16 layers (decode + split-K merge per layer).
 ``--append-schedule per_layer`` appends each layer's K and V with one
 two-plane launch just before that layer's decode (the order a model's
 forward pass allows); ``overlapped`` issues per-plane appends on a second
-stream, decode l waiting for layer l's two appends only.  The single-layer workloads (tiny, batched, lowbit,
+stream, decode l waiting for layer l's two appends only.  With the default
+schedule the line also carries ``per_layer_appends_ms_per_step`` (and its
+tokens/s), the same steps timed in the per-layer order.  The single-layer workloads (tiny, batched, lowbit,
 rotated) are available with --workload: a step there is the fused append of
 the new token's K/V rows, the decode and the merge.  ``--q-len N`` (2 .. 4,
 single-layer workloads) makes each step verify N new tokens per sequence at
@@ -327,6 +329,30 @@ def run_gpu(args):
         graph_ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
         assert all(np.isfinite(o.cpu().numpy()).all() for o in out), "non-finite decode output (graph replay)"
         del graphs
+    per_layer_ms = None
+    if not fused and append_mode == "batched":
+        # the same step in the order a model's forward pass allows: each
+        # layer's K and V appended by one two-plane launch just before its
+        # decode (reported beside ms_per_step, which times the workload's
+        # all-appends-first order)
+        from quantized_kv_cache_append_amd.step import DecodeStep
+
+        pl = DecodeStep([(lay.K[0], lay.V[0]) for lay in layers], q, new_rows, out, lens, p_new, Hq, n_splits, ws,
+                        stream, astream, counters=counters, append_mode="per_layer")
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                pl()
+        pl_blocks = []
+        for rep in range(args.repeats):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                for _ in range(args.steps):
+                    pl()
+            torch.cuda.synchronize()
+            pl_blocks.append(1e3 * (time.perf_counter() - t0) / args.steps)
+        per_layer_ms = float(np.median(pl_blocks))
+        del pl
     if not fused:
         # The step must compute what the per-plane calls issued serially do.
         # The timed steps append the same rows every time, which would hide a
@@ -362,6 +388,7 @@ def run_gpu(args):
                     "overlapped": "per-plane vit_kv_append_quant on a second stream, overlapped with the decodes",
                 }[append_mode],
                 replicas=replicas, n_splits=n_splits, ms_per_step=ms_per_step, graph_ms_per_step=graph_ms_per_step,
+                per_layer_ms_per_step=per_layer_ms,
                 block_ms=block_ms,
                 dec_mean_ms=dec_mean_ms,
                 dec_min_ms=float(np.min(dec_ms)), kv_bytes=kv_bytes, per_launch_bytes=per_launch_bytes,
@@ -1282,6 +1309,9 @@ def main():
             **({"ubatch_appends": r["appends"]} if r["appends"] else {}),
         },
         "graph_ms_per_step": None if r["graph_ms_per_step"] is None else round(r["graph_ms_per_step"], 5),
+        **({} if r["per_layer_ms_per_step"] is None else {
+            "per_layer_appends_ms_per_step": round(r["per_layer_ms_per_step"], 5),
+            "per_layer_appends_tokens_per_s": round(r["S"] * r["QL"] / (r["per_layer_ms_per_step"] * 1e-3), 1)}),
         "effective_kv_read_gbs": round(r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
         "effective_kv_read_pct_of_hbm_peak": round(100 * r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": {
